@@ -1,0 +1,407 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something independent of its own code:
+a brute-force formulation, a library routine, an identity of the mathematics
+or a value derived by hand from the pages. A plausible mistake in the oracle
+(dropped term, wrong sign or index, off-by-one causality, transposed
+operand, wrong tie rule) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import segmla_oracle as O
+from workload import CONFIGS, SMALL_CONFIGS, make_inputs, segment_table
+from workload.gen import pool_placement
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _oracle_inputs(inp):
+    """Torch inputs -> the fp64 arrays the oracle consumes (stored values upcast exactly)."""
+    d = dict(inp)
+    if inp["cfg"]["kv_dtype"] == "e4m3":
+        d["latent"] = O.e4m3_b128_values(inp["kv"].numpy(), inp["kv_scale"].numpy(),
+                                         inp["kv_rope"].double().numpy())
+    else:
+        d["latent"] = inp["kv"].double().numpy()
+    d["q"] = inp["q"].double().numpy()
+    d["w"] = inp["w"].double().numpy()
+    d["z_cached"] = inp["z_cached"].double().numpy()
+    d["scores"] = inp["scores"].numpy()
+    return d
+
+
+def _geom(cfg, mode="identity"):
+    kinds, lens, offsets = segment_table(cfg)
+    pr, n_pool = pool_placement(lens, mode, cfg["seed"])
+    return O.geometry(kinds, lens, offsets, pr, n_pool)
+
+
+# ---------------------------------------------------------------- protected rows
+def _golden_intervals(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = map(int, line.split())
+            rows.extend(range(a, b))
+    return np.array(rows, dtype=np.int64)
+
+
+def test_tiny_worked_example():
+    cfg = CONFIGS[0]
+    g = _geom(cfg)
+    assert g["T"] == 274
+    p = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"])
+    ref = _golden_intervals("tiny_fp32_protected_rows.txt")
+    np.testing.assert_array_equal(p["A"], ref)
+    gp, lp = O.flops_pairs(g["T"], p["A"], 1, 7)
+    assert (gp, lp) == (37675, 82908)
+
+
+@pytest.mark.parametrize("idx,expect", [(1, (2432, 999, 3431)), (2, (38784, 0, 38784)),
+                                        (4, (4224, 12416, 16640))])
+def test_workload_protected_sizes(idx, expect):
+    """|F|, need and |A| derived by hand from the rule for the long workloads."""
+    cfg = CONFIGS[idx]
+    g = _geom(cfg)
+    scores = np.random.default_rng(idx).integers(0, 2**32, g["T"], dtype=np.uint64)
+    p = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                         scores=scores)
+    assert (int(p["forced"].sum()), p["need"], len(p["A"])) == expect
+
+
+def _brute_forced(g, b, tau, dirty):
+    """Row-by-row membership predicate, written independently of the interval painting."""
+    T = g["T"]
+    out = np.zeros(T, dtype=bool)
+    dirty = set(int(d) for d in dirty)
+    for t in range(T):
+        i = int(np.searchsorted(g["offsets"], t, side="right") - 1)
+        j = t - int(g["offsets"][i])
+        n = int(g["lens"][i])
+        kind = int(g["kinds"][i])
+        edge = kind == O.SEG_DOC and g["offsets"][i] != 0 and (j < b or j >= n - b)
+        out[t] = kind == O.SEG_NEW or t in dirty or edge or t >= T - tau
+    return out
+
+
+def _random_geometry(rng):
+    n = int(rng.integers(1, 9))
+    kinds = rng.choice([0, 1, 1, 1, 2], n).astype(np.uint8)
+    if rng.random() < 0.5:
+        kinds[0] = 0
+    lens = rng.integers(1, 40, n).astype(np.int64)
+    offsets = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    return O.geometry(kinds, lens, offsets, offsets, int(lens.sum()))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_protected_fuzz(seed):
+    rng = np.random.default_rng([77, seed])
+    g = _random_geometry(rng)
+    T = g["T"]
+    b = int(rng.integers(0, 12))
+    tau = int(rng.integers(0, 30))
+    beta = int(rng.integers(0, 1001))
+    dirty = rng.choice(T, int(rng.integers(0, 3)), replace=False) if T > 2 else []
+    # adversarial scores half the time: few distinct values, so the row tie-break decides
+    if seed % 2:
+        scores = rng.integers(0, 3, T).astype(np.uint64)
+    else:
+        scores = rng.integers(0, 2**32, T, dtype=np.uint64)
+    p = O.protected_rows(g, b, tau, beta, dirty, scores)
+    forced = _brute_forced(g, b, tau, dirty)
+    np.testing.assert_array_equal(p["forced"], forced)
+    cand = g["kinds"][g["seg_of_row"]] != O.SEG_NEW
+    K = math.ceil(beta * int(cand.sum()) / 1000)
+    assert p["K"] == K
+    sel = p["indexer"]
+    assert int(sel.sum()) == max(0, K - int((forced & cand).sum()))
+    assert not np.any(sel & (forced | ~cand))
+    # every chosen row beats every unchosen eligible row in (score desc, row asc)
+    elig = np.nonzero(cand & ~forced & ~sel)[0]
+    for x in np.nonzero(sel)[0]:
+        for y in elig:
+            assert (scores[x] > scores[y]) or (scores[x] == scores[y] and x < y)
+    np.testing.assert_array_equal(p["A"], np.nonzero(forced | sel)[0])
+
+
+def test_protected_all_equal_scores_take_smallest_rows():
+    cfg = SMALL_CONFIGS[1]
+    g = _geom(cfg)
+    T = g["T"]
+    p = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                         scores=np.full(T, 12345, dtype=np.uint64))
+    elig = np.nonzero((g["kinds"][g["seg_of_row"]] != O.SEG_NEW) & ~p["forced"])[0]
+    np.testing.assert_array_equal(np.nonzero(p["indexer"])[0], elig[:p["need"]])
+
+
+# ----------------------------------------------------------------------------- RoPE
+def test_rotation_group_identities():
+    theta = O.rope_theta(64, 10000.0)
+    rng = np.random.default_rng(5)
+    a, b = rng.uniform(-2e5, 2e5, 2)
+    Ra, Rb, Rab = O.rot_blocks(a, theta), O.rot_blocks(b, theta), O.rot_blocks(a + b, theta)
+    eye = np.broadcast_to(np.eye(2), Ra.shape)
+    np.testing.assert_allclose(np.swapaxes(Ra, -1, -2) @ Ra, eye, atol=1e-15, rtol=0)
+    # the product identity carries the rounding of the angles (|a|*theta ~ 2e5 rad)
+    np.testing.assert_allclose(Ra @ Rb, Rab, atol=1e-9, rtol=0)
+    small = O.rot_blocks(3.0, theta) @ O.rot_blocks(4.0, theta)
+    np.testing.assert_allclose(small, O.rot_blocks(7.0, theta), atol=1e-15, rtol=0)
+    # theta_0 = 1 and theta_{last} = base^{-(d-2)/d}
+    assert theta[0] == 1.0 and math.isclose(theta[-1], 10000.0 ** (-62 / 64))
+    # counter-clockwise convention: R(pi/2) maps (1, 0) to (0, 1) on pair 0
+    x = np.zeros(64)
+    x[0] = 1.0
+    y = O.apply_blocks(O.rot_blocks(math.pi / 2, theta), x)
+    assert abs(y[0]) < 1e-15 and abs(y[1] - 1.0) < 1e-15
+
+
+# ----------------------------------------------------------- brute force, tiny case
+def _rot2(angle):
+    c, s = math.cos(angle), math.sin(angle)
+    return np.array([[c, -s], [s, c]])
+
+
+def test_brute_force_tiny():
+    """T = 11, d_nope = d_rope = 2, H = 2: raw unrotated vectors, explicit 2x2 matrices,
+    softmax without max subtraction."""
+    rng = np.random.default_rng(3)
+    kinds = np.array([0, 1, 1, 2], dtype=np.uint8)
+    lens = np.array([2, 3, 4, 2])
+    offsets = np.array([0, 2, 5, 9])
+    T, H, base = 11, 2, 10000.0
+    theta0 = 1.0  # d_rope = 2: a single pair with theta_0 = 1
+    kh = rng.normal(size=(T, 4))      # true (unrotated) key content per request row
+    qh = rng.normal(size=(T, H, 4))   # true (unrotated) query content
+    seg = np.repeat(np.arange(4), lens)
+    j = np.arange(T) - offsets[seg]
+    # stored latent: documents at canonical j, prefix/new at request position
+    stored_pos = np.where(kinds[seg] == 1, j, np.arange(T))
+    lat = kh.copy()
+    q = qh.copy()
+    for p in range(T):
+        lat[p, 2:] = _rot2(stored_pos[p] * theta0) @ kh[p, 2:]
+        for h in range(H):
+            q[p, h, 2:] = _rot2(p * theta0) @ qh[p, h, 2:]
+    W = rng.normal(size=(H, 3, 4))
+    cfg = dict(d_nope=2, d_rope=2, rope_base=base, softmax_scale=0.7, v_has_rope=1,
+               edge_rows=1, tail_rows=2, budget_permille=0)
+    inp = dict(cfg=cfg, kinds=kinds, lens=lens, offsets=offsets, pool_rows=offsets, n_pool=T,
+               head_is_global=np.array([1, 1], dtype=np.uint8), q=q, latent=lat, w=W,
+               z_cached=np.zeros((T, 0, 3)), scores=np.zeros(T))
+    res = O.layer_forward(inp)
+    for t in range(T):
+        for h in range(H):
+            sc = []
+            for p in range(t + 1):
+                k_true = np.concatenate([kh[p, :2], _rot2(p * theta0) @ kh[p, 2:]])
+                sc.append(0.7 * float(q[t, h] @ k_true))
+            e = np.exp(np.array(sc))
+            P = e / e.sum()
+            o = np.zeros(4)
+            u = np.zeros(4)
+            for p in range(t + 1):
+                o[:2] += P[p] * kh[p, :2]
+                o[2:] += P[p] * (_rot2(p * theta0) @ kh[p, 2:])
+                # projected-state input: RoPE part in the frame relative to the query
+                u[:2] += P[p] * kh[p, :2]
+                u[2:] += P[p] * (_rot2((p - t) * theta0) @ kh[p, 2:])
+            np.testing.assert_allclose(res["O"][t, h], o, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(res["Z"][t, h], W[h] @ u, rtol=0, atol=1e-12)
+            # scores depend on relative position only
+            rel = qh[t, h, :2] @ kh[:t + 1, :2].T + np.array(
+                [qh[t, h, 2:] @ _rot2((p - t) * theta0) @ kh[p, 2:] for p in range(t + 1)])
+            np.testing.assert_allclose(np.array(sc), 0.7 * rel, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------- library routine
+def test_sdpa_float64_pin():
+    cfg = CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    res = O.layer_forward(inp)
+    g = res["geom"]
+    keys = O.relocated_keys(inp["latent"], g, cfg["d_nope"], cfg["d_rope"], cfg["rope_base"])
+    kt = torch.from_numpy(keys)[None, None]            # [1, 1, T, d]
+    for h in range(cfg["n_heads"]):
+        qt = torch.from_numpy(np.ascontiguousarray(inp["q"][:, h]))[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, kt, is_causal=True, scale=cfg["softmax_scale"])[0, 0].numpy()
+        rows = res["computed"][:, h]
+        np.testing.assert_allclose(res["O"][rows, h], ref[rows], rtol=0, atol=1e-12)
+    assert res["computed"][:, 0].all()                  # the Global head covers every row
+    assert res["computed"][:, 1].sum() == len(res["A"])
+
+
+# ------------------------------------------------------- segmented fp64 computation
+def _segmented_fp64(inp, rows, rng):
+    """The method itself in fp64, written independently: for each visible segment
+    rotate q's RoPE part by -rot_i, attend the stored latent in place, restore the
+    partial output's phase by +rot_i, then merge (max, sum, partial) statistics with
+    a log-sum-exp merge taken in a random segment order."""
+    cfg = inp["cfg"]
+    dn, dr, base, sig = cfg["d_nope"], cfg["d_rope"], cfg["rope_base"], cfg["softmax_scale"]
+    k = np.arange(dr // 2)
+    theta = base ** (-2.0 * k / dr)
+
+    def rot(x, ang):  # rotate pairs of x[..., dn:] by angles ang[k]
+        y = x.copy()
+        c, s = np.cos(ang), np.sin(ang)
+        xe, xo = x[..., dn::2], x[..., dn + 1::2]
+        y[..., dn::2] = xe * c - xo * s
+        y[..., dn + 1::2] = xe * s + xo * c
+        return y
+
+    kinds, lens, offs, pr = inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"]
+    lat = inp["latent"]
+    out = {}
+    for t in rows:
+        stats = []
+        for i in range(len(lens)):
+            if offs[i] > t:
+                break
+            nvis = min(int(lens[i]), t - int(offs[i]) + 1)
+            rot_i = float(offs[i]) if kinds[i] == 1 else 0.0
+            C = lat[pr[i]:pr[i] + nvis]
+            q = rot(inp["q"][t], -rot_i * theta)            # [H, d]
+            s = sig * q @ C.T
+            m = s.max(axis=1)
+            e = np.exp(s - m[:, None])
+            part = rot(e @ C, rot_i * theta)
+            stats.append((m, e.sum(axis=1), part))
+        order = rng.permutation(len(stats))
+        M = np.max([stats[i][0] for i in order], axis=0)
+        num = sum(np.exp(stats[i][0] - M)[:, None] * stats[i][2] for i in order)
+        den = sum(np.exp(stats[i][0] - M) * stats[i][1] for i in order)
+        out[t] = num / den[:, None]
+    return out
+
+
+@pytest.mark.parametrize("cfg,mode", [(CONFIGS[0], "identity"), (SMALL_CONFIGS[0], "shuffled"),
+                                      (SMALL_CONFIGS[0], "aliased")])
+def test_relocation_identity(cfg, mode):
+    inp = _oracle_inputs(make_inputs(cfg, "cpu", pool=mode))
+    T = inp["T"]
+    rows = sorted(set([0, 1, T - 1] + list(np.random.default_rng(1).choice(T, 25, replace=False))))
+    res = O.layer_forward(inp, rows=rows, A_override=np.arange(T))
+    seg = _segmented_fp64(inp, rows, np.random.default_rng(9))
+    for i, t in enumerate(rows):
+        np.testing.assert_allclose(res["O"][i], seg[t], rtol=0, atol=1e-10)
+
+
+def test_stored_frame_equivalence():
+    """A document stored at canonical positions and placed at Delta gives the same
+    outputs as the same rows given as a prefix-kind segment stored at request
+    positions (rope part pre-rotated by R(Delta))."""
+    cfg = SMALL_CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    g = O.geometry(inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"], inp["n_pool"])
+    theta = O.rope_theta(cfg["d_rope"], cfg["rope_base"])
+    alt = dict(inp)
+    lat = inp["latent"].copy()
+    kinds = inp["kinds"].copy()
+    for i in range(len(kinds)):
+        if kinds[i] == 1:
+            s, n, p0 = int(inp["offsets"][i]), int(inp["lens"][i]), int(inp["pool_rows"][i])
+            R = O.rot_blocks(np.arange(s, s + n) - np.arange(n) + 0.0, theta)  # R(Delta)
+            lat[p0:p0 + n, cfg["d_nope"]:] = O.apply_blocks(R, lat[p0:p0 + n, cfg["d_nope"]:])
+            kinds[i] = 0
+    alt["latent"], alt["kinds"] = lat, kinds
+    T = g["T"]
+    a = O.layer_forward(inp, A_override=np.arange(T))
+    b = O.layer_forward(alt, A_override=np.arange(T))
+    np.testing.assert_allclose(a["O"], b["O"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a["Z"], b["Z"], rtol=0, atol=1e-12)
+
+
+def test_projected_state_shift_invariance():
+    """Rotating every output's RoPE part by R(c) while moving the query position
+    from t to t + c leaves the projected state unchanged."""
+    rng = np.random.default_rng(4)
+    dn, dr, base = 8, 16, 10000.0
+    theta = O.rope_theta(dr, base)
+    Orows = rng.normal(size=(5, 3, dn + dr))
+    t = np.array([0, 3, 17, 400, 12345])
+    W = rng.normal(size=(3, 6, dn + dr))
+    c = 9876.0
+    shifted = Orows.copy()
+    shifted[..., dn:] = O.apply_blocks(O.rot_blocks(np.full((5, 1), c), theta), Orows[..., dn:])
+    z0 = O.project_rows(Orows, t, [0, 1, 2], W, dn, dr, base, True)
+    z1 = O.project_rows(shifted, t + c, [0, 1, 2], W, dn, dr, base, True)
+    np.testing.assert_allclose(z0, z1, rtol=0, atol=1e-9)
+    # without the inverse RoPE the state would not be shift invariant
+    zr = O.project_rows(shifted, t, [0, 1, 2], W, dn, dr, base, True)
+    assert np.max(np.abs(zr - z0)) > 1e-3
+
+
+# ----------------------------------------------------------------------- replacement
+def test_exact_cache_identity_and_overwrite():
+    """With the cached Local state equal to full recomputation, the replaced state
+    equals full recomputation whatever A is (exactness of the projected-state sum,
+    RedKnot-MLA paper, projected-state paragraph); NaN-poisoned cached rows inside A
+    never reach the output (overwrite, never add); rows outside A copy the cache."""
+    cfg = SMALL_CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    T = inp["T"]
+    full = O.layer_forward(inp, A_override=np.arange(T))
+    g = full["geom"]
+    local = np.nonzero(inp["head_is_global"] == 0)[0]
+    zc = np.full_like(inp["z_cached"], np.nan)
+    zc[g["pool_of_row"]] = full["Z"][:, local]
+    res = O.layer_forward(inp, zc_override=zc)
+    np.testing.assert_allclose(res["Z"], full["Z"], rtol=0, atol=1e-12)
+    outside = np.setdiff1d(np.arange(T), res["A"])
+    np.testing.assert_array_equal(res["Z"][outside][:, local], full["Z"][outside][:, local])
+    poisoned = inp["z_cached"].copy()
+    A = res["A"]
+    poisoned[g["pool_of_row"][A]] = np.nan
+    res2 = O.layer_forward(inp, zc_override=poisoned)
+    assert np.isfinite(res2["Z"]).all()
+    notA = np.setdiff1d(np.arange(T), A)
+    np.testing.assert_array_equal(res2["Z"][notA][:, local],
+                                  inp["z_cached"][g["pool_of_row"][notA]])
+
+
+# ---------------------------------------------------------------------------- ledger
+def test_head_row_ceilings_printed_values():
+    """Flash 3F-37R-3F with 56/64 Local heads: 75.29 %; Pro 3F-55R-3F with 112/128:
+    78.89 % (RedKnot-MLA paper, profiles paragraph; explainer, DeepSeek-V4 section)."""
+    assert round(100 * O.head_row_ceiling(3, 37, 3, 64, 56), 2) == 75.29
+    assert round(100 * O.head_row_ceiling(3, 55, 3, 128, 112), 2) == 78.89
+    assert O.head_row_ceiling(3, 37, 3, 64, 56) == 2072 / 2752
+    lg, ph, op = O.ledger(3, 37, 3, 64, 56, 274, np.arange(274))
+    assert ph == 0.0 and op == 0.0
+    lg, ph, op = O.ledger(0, 1, 0, 8, 7, 4, np.array([3]))
+    # dense triples 8*10 = 80; computed 1*10 + 7*4 = 38
+    assert ph == 7 * 3 / (8 * 4) and op == 1 - 38 / 80
+
+
+# ------------------------------------------------------------------------------ E4M3
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0xB8] == -1.0
+
+
+def test_e4m3_generator_roundtrip_error():
+    """The stored E4M3 + fp32 scale rows reproduce the drawn values to the
+    format's half-ulp bound (relative 2^-4 for normals)."""
+    cfg = SMALL_CONFIGS[4]
+    inp = make_inputs(cfg, "cpu")
+    vals = O.e4m3_b128_values(inp["kv"].numpy(), inp["kv_scale"].numpy(),
+                              inp["kv_rope"].double().numpy())
+    assert np.isfinite(vals).all()
+    sc = inp["kv_scale"].double().numpy()
+    amax = np.abs(vals[:, :512]).reshape(-1, 4, 128).max(-1)
+    np.testing.assert_allclose(amax, 448 * sc, rtol=2 ** -4)

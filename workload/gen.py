@@ -1,0 +1,156 @@
+"""Seeded synthetic tensors for one layer of segment-relocated MLA attention.
+
+Every tensor is drawn by torch's generator on the requested device, in chunks
+of rows with one seed per (workload seed, tensor tag, chunk), so a run is
+reproducible and the chunk size does not depend on memory. Distributions:
+latent ~ N(0, 1); q ~ N(0, 1) / sqrt(d_nope + d_rope); each head's projection
+slice ~ N(0, 1) / sqrt(d_v); the cached projected Local state ~ N(0, 1);
+Indexer scores uniform over uint32 (a stand-in for a trained Indexer: picking
+the top scores then draws a uniformly random subset of rows).
+
+The E4M3 latent follows the 1x128 E4M3 + fp32-scale storage format described
+for DeepSeek-V4's FP8 dataflow (TensorRT-LLM reading notes, Part I): each row's
+512 nope values are split into blocks of 128, the block scale is amax / 448 in
+fp32 (1 when amax is 0) and the code is torch's round-to-nearest-even cast of
+value / scale to float8_e4m3fn; the RoPE dims are kept in bf16. This is the
+artifact's storage format (producer side), not part of the attention method.
+"""
+import numpy as np
+import torch
+
+from .configs import segment_table
+
+SEG_PREFIX, SEG_DOC, SEG_NEW = 0, 1, 2
+
+TAG_Q, TAG_LAT, TAG_W, TAG_ZC, TAG_SCORE, TAG_POOL = 1, 2, 3, 4, 5, 7
+CHUNK_ROWS = 2048
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _seed(seed, tag, chunk):
+    return (int(seed) * 1_000_003 + int(tag) * 10_007 + int(chunk)) % (2**63 - 1)
+
+
+def _gen(device, seed, tag, chunk):
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(seed, tag, chunk))
+    return g
+
+
+def randn_rows(shape, seed, tag, device, dtype, std=1.0):
+    """N(0, std^2) tensor of `shape`, drawn CHUNK_ROWS rows at a time in fp32."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    rows = shape[0]
+    for ci, r0 in enumerate(range(0, rows, CHUNK_ROWS)):
+        n = min(CHUNK_ROWS, rows - r0)
+        x = torch.randn((n,) + tuple(shape[1:]), generator=_gen(device, seed, tag, ci),
+                        device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[r0:r0 + n] = x.to(dtype)
+    return out
+
+
+def uint32_scores(n, seed, device):
+    """Uniform uint32 values, returned as an int32 tensor holding the same bits."""
+    g = _gen(device, seed, TAG_SCORE, 0)
+    x = torch.randint(0, 2**32, (n,), generator=g, device=device, dtype=torch.int64)
+    x = torch.where(x >= 2**31, x - 2**32, x)
+    return x.to(torch.int32)
+
+
+def quantize_e4m3_b128(x):
+    """fp32 [rows, d] (d a multiple of 128) -> (codes uint8 [rows, d], scales fp32 [rows, d/128])."""
+    rows, d = x.shape
+    xb = x.reshape(rows, d // 128, 128)
+    amax = xb.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    y = (xb / scale.unsqueeze(-1)).clamp_(-448.0, 448.0)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows, d)
+    return codes, scale.to(torch.float32)
+
+
+def pool_placement(lens, mode, seed):
+    """First pool row of each segment and the pool size.
+
+    identity: pool row = request row. shuffled: segment blocks in a random order
+    with random gaps (unused pool rows). aliased: every document whose length
+    equals an earlier document's reuses that document's pool range (the same
+    cached document placed twice in one request).
+    """
+    n = len(lens)
+    if mode == "identity":
+        pr = np.zeros(n, dtype=np.int64)
+        pr[1:] = np.cumsum(lens[:-1], dtype=np.int64)
+        return pr, int(np.sum(lens, dtype=np.int64))
+    rng = np.random.default_rng([seed, TAG_POOL])
+    if mode == "shuffled":
+        order = rng.permutation(n)
+        gaps = rng.integers(0, 9, n)
+        pr = np.zeros(n, dtype=np.int64)
+        cur = int(rng.integers(0, 9))
+        for i in order:
+            pr[i] = cur
+            cur += int(lens[i]) + int(gaps[i])
+        return pr, cur
+    if mode == "aliased":
+        pr = np.zeros(n, dtype=np.int64)
+        first_of_len = {}
+        cur = 0
+        for i in range(n):
+            n_i = int(lens[i])
+            if n_i in first_of_len and i > 0:
+                pr[i] = first_of_len[n_i]
+            else:
+                pr[i] = cur
+                first_of_len.setdefault(n_i, cur)
+                cur += n_i
+        return pr, cur
+    raise ValueError(mode)
+
+
+def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
+    """All inputs of one layer forward for workload `cfg` on `device`."""
+    kinds, lens, offsets = segment_table(cfg)
+    T = int(np.sum(lens, dtype=np.int64))
+    seed = cfg["seed"]
+    pool_rows, n_pool = pool_placement(lens, pool, seed)
+    H = cfg["n_heads"]
+    d_nope, d_rope = cfg["d_nope"], cfg["d_rope"]
+    d_qk = d_nope + d_rope
+    d_v = d_qk if cfg["v_has_rope"] else d_nope
+    head_is_global = np.zeros(H, dtype=np.uint8)
+    head_is_global[cfg["global_heads"]] = 1
+    n_local = H - int(head_is_global.sum())
+    io = _TORCH_DT[cfg["dtype"]]
+
+    used = np.zeros(n_pool, dtype=bool)
+    for p, n in zip(pool_rows, lens):
+        used[p:p + n] = True
+    unused = torch.from_numpy(~used).to(device)
+
+    out = dict(cfg=cfg, kinds=kinds, lens=lens, offsets=offsets, pool_rows=pool_rows,
+               n_pool=n_pool, T=T, head_is_global=head_is_global, n_local=n_local, d_v=d_v)
+    out["q"] = randn_rows((T, H, d_qk), seed, TAG_Q, device, io, std=cfg["q_std"])
+    lat = randn_rows((n_pool, d_qk), seed, TAG_LAT, device, torch.float32)
+    if cfg["kv_dtype"] == "e4m3":
+        codes, scales = quantize_e4m3_b128(lat[:, :d_nope])
+        rope = lat[:, d_nope:].to(torch.bfloat16)
+        if bool(unused.any()):
+            codes[unused] = 0x7F  # E4M3 NaN code
+            scales[unused] = float("nan")
+            rope[unused] = float("nan")
+        out["kv"], out["kv_scale"], out["kv_rope"] = codes, scales, rope
+    else:
+        lat = lat.to(_TORCH_DT[cfg["kv_dtype"]])
+        if bool(unused.any()):
+            lat[unused] = float("nan")
+        out["kv"] = lat
+    del lat
+    out["w"] = randn_rows((H, cfg["d_state"], d_v), seed, TAG_W, device, io,
+                          std=1.0 / np.sqrt(d_v))
+    out["z_cached"] = randn_rows((n_pool, n_local, cfg["d_state"]), seed, TAG_ZC, device, io)
+    if with_scores:
+        out["scores"] = uint32_scores(T, seed, device)
+    return out
