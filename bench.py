@@ -1,0 +1,222 @@
+"""Benchmark of one segment-relocated MLA attention layer on one MI355X.
+
+A step is one pass of the whole hot path on resident inputs: plan build (segment
+geometry and RoPE tables, protected row set, work list) followed by the forward
+(per-segment rotate / attend / restore with the log-sum-exp merge, then the
+row-replacement epilogue). The default workload is the Flash-like 32K layer
+(64 heads, 56 Local / 8 Global, 512 + 64 latent, 8 x 4096 documents after a 256-row
+prefix, 128 question rows, 10 % Local budget); the 128K layer is measured as a
+secondary figure. Throughput is algorithmic attention TFLOP/s, 2 * (576 + 576) FLOP per
+computed (row, head, key) triple, divided by the step time.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
+                [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "segmented-MLA attention TFLOP/s and µs/layer at 32K/128K ctx, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def flops_per_pair(cfg):
+    d_qk = cfg["d_nope"] + cfg["d_rope"]
+    d_v = d_qk if cfg["v_has_rope"] else cfg["d_nope"]
+    return 2.0 * (d_qk + d_v)
+
+
+def measure(cfg_name, steps, warmup):
+    import torch
+    from segmented_attention_amd import segmla as S
+    from workload import config_by_name, make_inputs
+
+    cfg = config_by_name(cfg_name)
+    log("workload %s: generating inputs" % cfg_name)
+    inp = make_inputs(cfg, "cuda")
+    T, H = inp["T"], cfg["n_heads"]
+    dt = inp["q"].dtype
+    out = torch.empty((T, H, inp["d_v"]), dtype=dt, device="cuda")
+    z = torch.empty((T, H, cfg["d_state"]), dtype=dt, device="cuda")
+    plan = S.Plan.for_inputs(inp)
+
+    def step():
+        plan.build(inp["scores"])
+        plan.forward(inp, out, z)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log("workload %s: timing %d steps" % (cfg_name, steps))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # kernel-level times from HIP events on the launch stream (separate profiled pass of
+    # the same steps: the profiled forward waits for the previous one's events)
+    S.segmla_profile_enable(plan.handle, True)
+    for _ in range(steps):
+        step()
+    ms, n_fwd, n_build = S.segmla_profile_read(plan.handle)
+    S.segmla_profile_enable(plan.handle, False)
+    torch.cuda.synchronize()
+    g_pairs, l_pairs = plan.pairs()
+    fpp = flops_per_pair(cfg)
+    flops = fpp * (g_pairs + l_pairs)
+    attn_ms = ms[0] / max(1, n_fwd)
+    res = dict(
+        cfg=cfg, T=T, n_protected=plan.n_protected, wall_s=wall, flops=flops,
+        g_pairs=g_pairs, l_pairs=l_pairs,
+        attn_ms=attn_ms, merge_ms=ms[1] / max(1, n_fwd), epi_ms=ms[2] / max(1, n_fwd),
+        build_ms=ms[3] / max(1, n_build),
+        attn_tflops=flops / (attn_ms * 1e-3) / 1e12,
+        tflops=flops / wall / 1e12,
+        tflops_576_512=(2.0 * (576 + 512)) * (g_pairs + l_pairs) / wall / 1e12,
+    )
+    plan.close()
+    del inp, out, z
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg_name, budget_s=20.0):
+    """The fp64 oracle, as it stands, on a bounded row sample of the same workload."""
+    import numpy as np
+    import torch
+    from oracle import segmla_oracle as O
+    from workload import config_by_name, make_inputs
+
+    cfg = config_by_name(cfg_name)
+    inp = make_inputs(cfg, "cuda")
+    d = {k: v for k, v in inp.items() if not torch.is_tensor(v)}
+    d["latent"] = inp["kv"].double().cpu().numpy()
+    d["w"] = inp["w"].double().cpu().numpy()
+    d["scores"] = inp["scores"].cpu().numpy()
+
+    class Rows:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, i):
+            return self.t[int(i)].double().cpu().numpy()
+
+    d["q"], d["z_cached"] = Rows(inp["q"]), Rows(inp["z_cached"])
+    T = inp["T"]
+    g = O.geometry(d["kinds"], d["lens"], d["offsets"], d["pool_rows"], d["n_pool"])
+    A = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"], (),
+                         d["scores"])["A"]
+    in_a = np.zeros(T, bool)
+    in_a[A] = True
+    rng = np.random.default_rng(123)
+    # sample: rows spread over the request, protected and unprotected alike
+    cand = rng.permutation(T)
+    n_g, n_l = len(cfg["global_heads"]), cfg["n_heads"] - len(cfg["global_heads"])
+    rows, est = [], 0.0
+    for t in cand[:4]:  # calibrate: time a few rows first
+        rows.append(int(t))
+    t0 = time.perf_counter()
+    O.layer_forward(d, rows=rows)
+    first = time.perf_counter() - t0
+    per_row = first / len(rows)
+    n_more = int(max(0, budget_s - first) / max(per_row, 1e-3))
+    rows = sorted(int(t) for t in cand[:4 + n_more])
+    t0 = time.perf_counter()
+    O.layer_forward(d, rows=rows)
+    secs = time.perf_counter() - t0
+    pairs = sum((n_g + (n_l if in_a[t] else 0)) * (t + 1) for t in rows)
+    flops = flops_per_pair(cfg) * pairs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    del inp
+    torch.cuda.empty_cache()
+    return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample="%d of %d request rows of %s (uniform random, seed 123; Global heads on each, "
+                       "Local heads on the %d sampled rows in A), fp64 numpy incl. key re-rotation "
+                       "of all rows; %.1f s" % (len(rows), T, cfg_name, int(in_a[rows].sum()), secs),
+                seconds=secs)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="flash_32k_bf16")
+    ap.add_argument("--secondary", default="long_128k_bf16")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every GPU box has one "
+              "GPU); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    main_res = measure(args.workload, args.steps, args.warmup)
+    sec = None
+    if not args.no_secondary and args.secondary:
+        sec = measure(args.secondary, max(2, args.steps // 3), 1)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
+
+    r = main_res
+    cfg = r["cfg"]
+    achieved = r["flops"] / (r["attn_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(r["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg["kv_dtype"] == "bf16" else cfg["kv_dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": r["cfg"]["name"],
+            "rows": r["T"], "heads": cfg["n_heads"], "global_heads": len(cfg["global_heads"]),
+            "latent": "%d+%d" % (cfg["d_nope"], cfg["d_rope"]),
+            "protected_rows": r["n_protected"],
+            "us_per_layer": round(r["wall_s"] * 1e6, 1),
+            "flop_per_triple": flops_per_pair(cfg),
+            "tflops_576_512_convention": round(r["tflops_576_512"], 3),
+            "stage_ms": {"attention": round(r["attn_ms"], 4), "split_merge": round(r["merge_ms"], 4),
+                         "epilogue": round(r["epi_ms"], 4), "plan_build": round(r["build_ms"], 4)},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
+                                                  for k, v in cpu.items() if k != "seconds"},
+    }
+    if sec is not None:
+        line["secondary"] = {
+            "workload": sec["cfg"]["name"], "rows": sec["T"], "protected_rows": sec["n_protected"],
+            "tflops": round(sec["tflops"], 3), "us_per_layer": round(sec["wall_s"] * 1e6, 1),
+            "attention_tflops": round(sec["attn_tflops"], 3),
+            "attention_frac_bf16_peak": round(sec["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": {"attention": round(sec["attn_ms"], 3), "epilogue": round(sec["epi_ms"], 3),
+                         "plan_build": round(sec["build_ms"], 3)},
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

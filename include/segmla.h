@@ -1,0 +1,244 @@
+/*
+ * segmla.h - C ABI of libsegmla, segment-relocated MLA attention for AMD MI355X (gfx950).
+ *
+ * One reusable MLA layer of RedKnot-MLA (arXiv 2609.07008): logical heads are
+ * split into Local and Global roles (head-partition paragraph, Eq. 1). All heads
+ * share one packed latent row per token. Cached documents were built alone at
+ * canonical positions 0..n_i-1 and are placed at request offsets Delta_i
+ * (relocation paragraph, Eq. 5). For every computed (query row, head) the library
+ * rotates the query's RoPE part by -Delta_i per segment, attends the canonical
+ * latent in place, restores the partial output's phase and merges segments with
+ * a stable log-sum-exp merge. Global heads run on every row, Local heads only
+ * on the protected row set A (protected-row paragraph, Eq. 6). The epilogue then
+ * undoes output RoPE at the query position, applies each head's slice of the
+ * bias-free first output projection (Eq. 2) and writes a request-ordered
+ * projected state. On rows outside A, Local heads' slots receive their cached
+ * contribution unchanged (replacement, never addition).
+ *
+ * Conventions shared by every entry point
+ *  - Ownership: the caller owns all device memory, including the workspace. The
+ *    library never allocates or frees device memory. A plan is host memory owned
+ *    by the library until segmla_plan_destroy.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *    All device work is enqueued on it with no hidden synchronization; only the
+ *    segmla_copy_* calls synchronize that stream.
+ *  - Errors: arguments are validated on the host before anything is enqueued; on
+ *    any status other than SEGMLA_OK nothing has been written to caller memory and
+ *    no work has been enqueued, so the caller chooses the fallback (there is never
+ *    a silent one). SEGMLA_E_HIP reports a failed HIP call or launch; faults of
+ *    enqueued kernels surface at the caller's next synchronization.
+ *  - Immutability: the latent pool, the cached projected state and the Indexer
+ *    scores are read only.
+ *  - Aliasing: segment pool ranges may alias (one document placed twice); outputs
+ *    and the workspace must not alias any input or each other.
+ *  - Row and head indices are int32; pool indices are int64; T < 2^31.
+ */
+#ifndef SEGMLA_H
+#define SEGMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SEGMLA_ABI_VERSION 1
+
+typedef enum segmla_status {
+  SEGMLA_OK = 0,
+  SEGMLA_E_NULL = -1,        /* a required pointer is NULL */
+  SEGMLA_E_GEOMETRY = -2,    /* malformed segment list (see segmla_geometry) */
+  SEGMLA_E_SHAPE = -3,       /* invalid head / latent / state sizes or role mask */
+  SEGMLA_E_DTYPE = -4,       /* unknown dtype or unsupported dtype combination */
+  SEGMLA_E_PROTECT = -5,     /* invalid protection parameters, or scores missing */
+  SEGMLA_E_WORKSPACE = -6,   /* workspace NULL, too small or not 256-byte aligned */
+  SEGMLA_E_HIP = -7,         /* a HIP runtime call or kernel launch failed */
+  SEGMLA_E_UNSUPPORTED = -8, /* valid request outside what the kernels implement */
+  SEGMLA_E_STATE = -9        /* plan not built yet */
+} segmla_status;
+
+typedef enum segmla_seg_kind {
+  SEGMLA_SEG_PREFIX = 0, /* computed in the request; latent stored at request positions */
+  SEGMLA_SEG_DOC = 1,    /* cached document; latent stored at canonical positions 0..n-1 */
+  SEGMLA_SEG_NEW = 2     /* question / new rows; latent stored at request positions */
+} segmla_seg_kind;
+
+typedef enum segmla_dtype {
+  SEGMLA_F32 = 0,
+  SEGMLA_BF16 = 1,
+  SEGMLA_E4M3_B128 = 2 /* latent only: nope dims as OCP E4M3 codes with one fp32 scale per 128
+                          values, RoPE dims bf16 (DeepSeek-V4 FP8 dataflow, TensorRT-LLM
+                          reading notes, Part I) */
+} segmla_dtype;
+
+/* Segment list of one request, host memory, read only during segmla_plan_create.
+ * Segment i covers request rows [offset[i], offset[i] + len[i]) and latent-pool
+ * rows [pool_row[i], pool_row[i] + len[i]). Requirements (else SEGMLA_E_GEOMETRY):
+ * n_seg >= 1; len[i] >= 1; offset[0] = 0 and offset[i+1] = offset[i] + len[i];
+ * 0 <= pool_row[i] and pool_row[i] + len[i] <= n_pool; kind[i] a segmla_seg_kind;
+ * T = offset[n-1] + len[n-1] < 2^31. A DOC at a nonzero offset is "relocated". */
+typedef struct segmla_geometry {
+  int32_t n_seg;
+  const int64_t *pool_row;
+  const int32_t *len;
+  const int64_t *offset;
+  const uint8_t *kind;
+} segmla_geometry;
+
+/* Layer shape and roles (RedKnot-MLA paper, head-partition paragraph). The latent
+ * row holds d_nope dims followed by d_rope RoPE dims. RoPE pairs are (2k, 2k+1)
+ * with theta_k = rope_base^(-2k/d_rope). Values are the full latent row when
+ * v_has_rope = 1 (d_v = d_nope + d_rope), else its nope dims (d_v = d_nope).
+ * Supported: kv_dtype F32 with io_dtype F32 (any even d_rope, d_nope + d_rope
+ * <= 1024, d_state <= 1024); kv_dtype BF16 or E4M3_B128 with io_dtype BF16 and
+ * d_nope = 512, d_rope = 64, d_state a multiple of 64. Other combinations return
+ * SEGMLA_E_UNSUPPORTED. */
+typedef struct segmla_layer {
+  int32_t n_heads;               /* H >= 1 */
+  int32_t d_nope;                /* >= 0 */
+  int32_t d_rope;                /* even, >= 2 */
+  int32_t d_state;               /* rows of each head's projection slice, >= 1 */
+  int32_t v_has_rope;            /* 1 or 0, see above */
+  const uint8_t *head_is_global; /* host [n_heads]: 1 Global, 0 Local; read at plan_create */
+  double rope_base;              /* > 1 */
+  float softmax_scale;           /* sigma multiplying q.k, > 0 */
+  int32_t kv_dtype;              /* segmla_dtype of the latent pool */
+  int32_t io_dtype;              /* segmla_dtype of q, W, cached state, out and z */
+  int32_t split_keys;            /* 0: library decides; -1: never split the key range;
+                                    > 0 (a multiple of 64): each work item covers at most
+                                    this many keys and split partials are merged by the
+                                    log-sum-exp merge */
+} segmla_layer;
+
+/* Protected-row rule (RedKnot-MLA paper, protected-row paragraph, Eq. 6):
+ * A = new rows U dirty rows U first/last edge_rows rows of every relocated
+ * document U the last tail_rows request rows (the forced set F), then, when
+ * budget_permille > 0, the Indexer rows: with C = prefix + document rows and
+ * K = ceil(budget_permille * |C| / 1000), the max(0, K - |F & C|) rows of C \ F
+ * with the largest score (ties: smaller row first). Forced rows are kept even
+ * when they exceed K. Requirements (else SEGMLA_E_PROTECT): edge_rows, tail_rows
+ * >= 0; 0 <= budget_permille <= 1000; n_dirty >= 0; each dirty row in [0, T). */
+typedef struct segmla_protect {
+  int32_t edge_rows;
+  int32_t tail_rows;
+  int32_t budget_permille;
+  int32_t n_dirty;
+  const int32_t *dirty_rows; /* host [n_dirty], may be NULL when n_dirty = 0 */
+} segmla_protect;
+
+/* Device tensors of one forward, all row-major and caller-owned.
+ *  q        [T][H][d_nope + d_rope] io_dtype, stored post-RoPE at request position t
+ *  kv       F32/BF16: [n_pool][d_nope + d_rope]; E4M3_B128: codes uint8 [n_pool][d_nope]
+ *  kv_scale E4M3_B128 only: fp32 [n_pool][d_nope / 128], else NULL
+ *  kv_rope  E4M3_B128 only: bf16 [n_pool][d_rope], else NULL
+ *  w        [H][d_state][d_v] io_dtype, head h's slice of the first output projection
+ *  z_cached [n_pool][H_L][d_state] io_dtype, cached projected contribution of the Local
+ *           heads (in head order), indexed by latent-pool row; may be NULL when H_L = 0
+ *  out      [T][H][d_v] io_dtype: merged head outputs in request phase; written for
+ *           Global heads on every row and for Local heads on rows in A only
+ *  z        [T][H][d_state] io_dtype: projected state, every (row, head) written
+ *  lse      optional fp32 [T][H]: natural-log log-sum-exp of sigma*q.k for every computed
+ *           (row, head); NULL to skip */
+typedef struct segmla_tensors {
+  const void *q;
+  const void *kv;
+  const float *kv_scale;
+  const void *kv_rope;
+  const void *w;
+  const void *z_cached;
+  void *out;
+  void *z;
+  float *lse;
+} segmla_tensors;
+
+typedef struct segmla_plan segmla_plan;
+
+/* Validate geometry, roles and protection (host only, no HIP call) and size the
+ * plan. n_pool = rows of the latent pool. On success *out_plan owns a new plan. */
+segmla_status segmla_plan_create(const segmla_geometry *geom, const segmla_layer *layer,
+                                 const segmla_protect *prot, int64_t n_pool,
+                                 segmla_plan **out_plan);
+
+/* Device workspace bytes segmla_plan_build needs (host only). */
+segmla_status segmla_plan_workspace_bytes(const segmla_plan *plan, size_t *bytes);
+
+/* Host only, no synchronization: request rows T and |A|. |A| = |F| + need is fixed
+ * by geometry and protection; only which Indexer rows are chosen needs the scores. */
+segmla_status segmla_plan_rows(const segmla_plan *plan, int64_t *n_rows, int64_t *n_protected);
+
+/* Build the plan's device descriptors into `workspace` (>= segmla_plan_workspace_bytes,
+ * 256-byte aligned): segment descriptors and RoPE tables (fp64-built), the row maps,
+ * the protected set A and the ordered work list. indexer_score: device uint32 [T],
+ * required iff the budget needs Indexer rows, else may be NULL. The workspace must
+ * stay allocated and unmodified while the plan is used. */
+segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t workspace_bytes,
+                                const uint32_t *indexer_score, void *stream);
+
+/* One layer forward (per-segment rotate / attend / restore, LSE merge, replacement
+ * epilogue) on a built plan. A plan may run many forwards with new tensors. */
+segmla_status segmla_forward(const segmla_plan *plan, const segmla_tensors *t, void *stream);
+
+/* Copy A (sorted ascending, |A| rows) to host memory; synchronizes `stream`. */
+segmla_status segmla_copy_protected(const segmla_plan *plan, int32_t *host_rows, int64_t cap,
+                                    void *stream);
+
+/* Copy the device row maps to host memory for inspection: seg_of_row[T] (segment of
+ * each request row) and pool_of_row[T] (latent-pool row of each request row); either
+ * may be NULL. cap = capacity in elements of each array. Synchronizes `stream`. */
+segmla_status segmla_copy_geometry(const segmla_plan *plan, int32_t *seg_of_row,
+                                   int64_t *pool_of_row, int64_t cap, void *stream);
+
+/* Stable log-sum-exp merge of split attention partials (RedKnot-MLA paper,
+ * relocation paragraph). For each vector v < n_vec and split s < n_split:
+ * partial_ml[s][v] = (m, l) with m the max of sigma*q.k over the split's keys
+ * (natural log units, -inf when the split saw no key) and l = sum exp(sigma*q.k - m);
+ * partial_o[s][v][0..d) = sum exp(sigma*q.k - m) * value (unnormalized, request phase).
+ * Writes out[v][0..d) = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s in out_dtype
+ * (F32 or BF16) and, if lse != NULL, lse[v] = M + log(sum_s e^(m_s - M) l_s) with
+ * M = max_s m_s. A vector that saw no key at all gets out = 0 and lse = -inf.
+ * All pointers are device memory; 1 <= n_split, 1 <= d <= 4096. */
+segmla_status segmla_lse_merge(const float *partial_o, const float *partial_ml, int32_t n_split,
+                               int64_t n_vec, int32_t d, void *out, int32_t out_dtype,
+                               float *lse, void *stream);
+
+/* Number of (row, head, key) triples the forward computes, by role: out[0] Global
+ * heads (every row), out[1] Local heads (rows in A). Needs a built plan; copies the
+ * device-side sum over A and synchronizes `stream`. */
+segmla_status segmla_plan_pairs(const segmla_plan *plan, double out[2], void *stream);
+
+/* The analytic ledger, namespaces kept apart (RedKnot-MLA paper, namespaces
+ * paragraph; head-row ceiling Eq. 8). Host only:
+ * out[0] logical head-row saving (r / (f_front + r + f_back)) * (h_local / h);
+ * out[1] physical token-row saving of one reusable layer, h_local * (T - n_protected) / (h * T);
+ * out[2] analytic attention operator saving of one reusable layer,
+ *        1 - (global_pairs + local_pairs) / (h * T * (T + 1) / 2), with the pair counts
+ *        of segmla_plan_pairs; NaN when local_pairs < 0.
+ * Wall-clock time, the fourth namespace, is measured by the caller. */
+segmla_status segmla_ledger(int32_t f_front, int32_t r, int32_t f_back, int32_t h,
+                            int32_t h_local, int64_t T, int64_t n_protected,
+                            double global_pairs, double local_pairs, double out[3]);
+
+/* Stage timing with HIP events on the forward's stream (tracing aid). enable = 1 creates the
+ * plan's events and zeroes the totals; 0 stops recording. While enabled, each forward and
+ * build records events around its stages, and the next forward first waits for the previous
+ * forward's last event (so at most one profiled forward is in flight). Host only apart from
+ * the event calls; returns SEGMLA_E_HIP if event creation fails. */
+segmla_status segmla_profile_enable(segmla_plan *plan, int32_t enable);
+
+/* Wait for the last recorded events and return accumulated milliseconds per stage since
+ * segmla_profile_enable(plan, 1): ms[0] attention kernel (rotate / attend / restore / merge),
+ * ms[1] split-partial merge kernel, ms[2] epilogue (projection + cached-state copy),
+ * ms[3] plan build (geometry, protected rows, work list); *n_forward = profiled forwards. */
+segmla_status segmla_profile_read(segmla_plan *plan, double ms[4], int64_t *n_forward,
+                                  int64_t *n_build);
+
+void segmla_plan_destroy(segmla_plan *plan);
+const char *segmla_status_string(int32_t status);
+int32_t segmla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEGMLA_H */

@@ -1,0 +1,129 @@
+// Internal declarations shared by the libsegmla HIP sources (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace segmla {
+
+// Device segment descriptor (one per segment, 32 bytes).
+struct SegDesc {
+  int64_t pool_row;  // first latent-pool row
+  int32_t offset;    // Delta_i: request position of the segment's first row
+  int32_t len;       // n_i
+  int32_t rot;       // phase shift the stored latent needs: Delta_i for documents (stored at
+                     // canonical 0..n-1), 0 for prefix/new rows (stored at request positions)
+  int32_t kind;      // segmla_seg_kind
+  int32_t relocated; // document at a nonzero offset
+  int32_t pad;
+};
+
+// Row flag bits written by the protected-row builder.
+enum : uint8_t { kFlagForced = 1, kFlagCand = 2, kFlagIndexer = 4 };
+
+// Work decomposition of the attention: (row, head) query vectors ("qvecs") come from two
+// streams. Stream F: rows of A with every head, flattened (a * H + h). Stream G: rows
+// outside A with the Global heads only (a * HG + g). Each stream is cut into tiles of
+// kTileQ consecutive qvecs; tiles [0, nF) are F tiles, [nF, nF + nG) are G tiles.
+constexpr int kTileQ = 64;
+
+struct TileMap {
+  const int32_t* alist;   // [nA] rows of A, ascending
+  const int32_t* nalist;  // [T - nA] rows outside A, ascending
+  const int32_t* ghead;   // [HG] Global head ids
+  int32_t nA, nNA, H, HG, nF, nG;
+};
+
+__device__ __forceinline__ bool tile_qvec(const TileMap& m, int tile, int qi, int& t, int& h) {
+  if (tile < m.nF) {
+    int64_t f = (int64_t)tile * kTileQ + qi;
+    if (f >= (int64_t)m.nA * m.H) return false;
+    int a = (int)(f / m.H);
+    h = (int)(f - (int64_t)a * m.H);
+    t = m.alist[a];
+  } else {
+    int64_t f = (int64_t)(tile - m.nF) * kTileQ + qi;
+    if (f >= (int64_t)m.nNA * m.HG) return false;
+    int a = (int)(f / m.HG);
+    h = m.ghead[(int)(f - (int64_t)a * m.HG)];
+    t = m.nalist[a];
+  }
+  return true;
+}
+
+// Largest request row among a tile's qvecs (lists are ascending).
+__device__ __forceinline__ int tile_max_row(const TileMap& m, int tile) {
+  if (tile < m.nF) {
+    int64_t last = (int64_t)tile * kTileQ + kTileQ - 1;
+    int64_t cap = (int64_t)m.nA * m.H - 1;
+    if (last > cap) last = cap;
+    return m.alist[(int)(last / m.H)];
+  }
+  int64_t last = (int64_t)(tile - m.nF) * kTileQ + kTileQ - 1;
+  int64_t cap = (int64_t)m.nNA * m.HG - 1;
+  if (last > cap) last = cap;
+  return m.nalist[(int)(last / m.HG)];
+}
+
+// Index of the segment containing request row `row` (segments contiguous from 0).
+__device__ __forceinline__ int seg_of(const SegDesc* seg, int n_seg, int row) {
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (seg[mid].offset <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Arguments of the attention kernels (one struct so every variant shares the launch code).
+struct AttnArgs {
+  const void* q;          // [T][H][d_qk] io dtype
+  const void* kv;         // latent pool (f32 / bf16 rows, or E4M3 codes)
+  const float* kv_scale;  // E4M3: [n_pool][d_nope/128]
+  const void* kv_rope;    // E4M3: [n_pool][d_rope] bf16
+  void* out;              // [T][H][d_v] io dtype (unsplit)
+  float* lse;             // [T][H] or null (unsplit)
+  float* part_o;          // [n_split][nTiles*kTileQ][d_v] (split)
+  float* part_ml;         // [n_split][nTiles*kTileQ][2] (split)
+  const SegDesc* seg;
+  const float2* segcs;    // [n_seg][d_rope/2] cos/sin(rot_i * theta_k)
+  const float2* stepcs;   // [n_seg][d_rope/2] cos/sin((rot_i - rot_{i+1}) * theta_k)
+  const int32_t* work;    // [nF + nG] tile ids in decreasing cost order
+  TileMap map;
+  int32_t n_seg, T, d_nope, d_rope, d_v;
+  int32_t n_split, split_keys;
+  float sigma;            // softmax scale
+};
+
+// Launchers (defined in the kernel sources), all on `stream`.
+hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, double base,
+                           int32_t* seg_of_row, float2* segcs, float2* stepcs, float2* rowcs,
+                           hipStream_t stream);
+hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_row, int T,
+                          int edge_rows, int tail_rows, const int32_t* dirty, int n_dirty,
+                          const uint32_t* score, int64_t need, uint8_t* flags,
+                          uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,
+                          int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
+                          hipStream_t stream);
+hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
+hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream);
+hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
+                            int d, void* out, int out_dtype, float* lse, hipStream_t stream);
+
+struct EpiArgs {
+  const void* out;        // [T][H][d_v] merged head outputs
+  const void* w;          // [H][d_state][d_v]
+  const void* z_cached;   // [n_pool][HL][d_state]
+  void* z;                // [T][H][d_state]
+  const float2* rowcs;    // [T][d_rope/2]
+  const int32_t* alist;
+  const int32_t* nalist;
+  const int32_t* ghead;   // [HG]
+  const int32_t* lhead;   // [HL]
+  const int32_t* seg_of_row;
+  const SegDesc* seg;
+  int32_t T, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;
+};
+hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
+
+}  // namespace segmla

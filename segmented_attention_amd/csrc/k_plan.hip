@@ -1,0 +1,297 @@
+// Plan-building kernels: segment geometry / RoPE tables, the protected row set and the
+// ordered attention work list. Integer outputs are exact; RoPE tables are computed in
+// fp64 and stored as fp32.
+#include "internal.h"
+
+namespace segmla {
+
+// ------------------------------------------------------------------------ geometry
+// theta_k = base^(-2k/d_rope) in fp64 (RoPE pairs (2k, 2k+1)).
+__device__ __forceinline__ double rope_theta(double base, int k, int d_rope) {
+  return pow(base, -2.0 * (double)k / (double)d_rope);
+}
+
+// Per-row segment map and the inverse-output-RoPE table cos/sin(t * theta_k).
+__global__ void k_geom_rows(const SegDesc* __restrict__ seg, int n_seg, int T, int d_rope,
+                            double base, int32_t* __restrict__ seg_of_row,
+                            float2* __restrict__ rowcs) {
+  const int half = d_rope / 2;
+  int64_t n = (int64_t)T * half;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int t = (int)(i / half), k = (int)(i - (int64_t)t * half);
+    double s, c;
+    sincos((double)t * rope_theta(base, k, d_rope), &s, &c);
+    rowcs[i] = make_float2((float)c, (float)s);
+    if (k == 0) seg_of_row[t] = seg_of(seg, n_seg, t);
+  }
+}
+
+// Per-segment query-rotation table cos/sin(rot_i * theta_k) and the frame-change table
+// cos/sin((rot_i - rot_{i+1}) * theta_k) used when the accumulated output moves from
+// segment i's frame to segment i+1's.
+__global__ void k_geom_segs(const SegDesc* __restrict__ seg, int n_seg, int d_rope, double base,
+                            float2* __restrict__ segcs, float2* __restrict__ stepcs) {
+  const int half = d_rope / 2;
+  int n = n_seg * half;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    int s = i / half, k = i - s * half;
+    double th = rope_theta(base, k, d_rope);
+    double sn, cs;
+    sincos((double)seg[s].rot * th, &sn, &cs);
+    segcs[i] = make_float2((float)cs, (float)sn);
+    double step = (s + 1 < n_seg) ? (double)(seg[s].rot - seg[s + 1].rot) : 0.0;
+    sincos(step * th, &sn, &cs);
+    stepcs[i] = make_float2((float)cs, (float)sn);
+  }
+}
+
+hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, double base,
+                           int32_t* seg_of_row, float2* segcs, float2* stepcs, float2* rowcs,
+                           hipStream_t stream) {
+  int64_t n = (int64_t)T * (d_rope / 2);
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_geom_rows, dim3(blocks), dim3(256), 0, stream, seg, n_seg, T, d_rope, base,
+                     seg_of_row, rowcs);
+  int ns = n_seg * (d_rope / 2);
+  hipLaunchKernelGGL(k_geom_segs, dim3((ns + 255) / 256), dim3(256), 0, stream, seg, n_seg,
+                     d_rope, base, segcs, stepcs);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ protected rows
+// Forced set F (new rows, dirty rows, edges of relocated documents, recent tail) and the
+// candidate flag (prefix and document rows).
+__global__ void k_protect_mark(const SegDesc* __restrict__ seg, const int32_t* __restrict__ seg_of_row,
+                               int T, int b, int tau, const int32_t* __restrict__ dirty, int n_dirty,
+                               uint8_t* __restrict__ flags) {
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+    const SegDesc d = seg[seg_of_row[t]];
+    int j = t - d.offset;
+    bool forced = d.kind == 2 || (d.relocated && (j < b || j >= d.len - b)) || t >= T - tau;
+    if (!forced && n_dirty > 0) {  // dirty rows are sorted and unique
+      int lo = 0, hi = n_dirty - 1;
+      while (lo <= hi) {
+        int mid = (lo + hi) >> 1;
+        int v = dirty[mid];
+        if (v == t) { forced = true; break; }
+        if (v < t) lo = mid + 1; else hi = mid - 1;
+      }
+    }
+    flags[t] = (uint8_t)((forced ? kFlagForced : 0) | (d.kind != 2 ? kFlagCand : 0));
+  }
+}
+
+// Indexer fill: pick the `need` eligible rows (candidate, not forced) with the largest uint32
+// score, ties to the smaller row. One workgroup: a 4-pass MSB-first radix select finds the
+// need-th largest score thr; rows above thr are taken, and among rows equal to thr the
+// smallest ones are taken in row order until `need` is reached.
+constexpr int kSelThreads = 1024;
+__global__ __launch_bounds__(kSelThreads) void k_protect_select(uint8_t* __restrict__ flags,
+                                                                const uint32_t* __restrict__ score,
+                                                                int T, uint32_t need) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix, s_mask, s_remaining;
+  __shared__ uint32_t wave_cnt[kSelThreads / 64];
+  const int tid = threadIdx.x;
+  if (tid == 0) { s_prefix = 0; s_mask = 0; s_remaining = need; }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix, mask = s_mask;
+    for (int t = tid; t < T; t += kSelThreads) {
+      if ((flags[t] & (kFlagCand | kFlagForced)) != kFlagCand) continue;
+      uint32_t s = score[t];
+      if ((s & mask) == prefix) atomicAdd(&hist[(s >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t rem = s_remaining, cum = 0;
+      int bsel = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        if (cum + hist[bin] >= rem) { bsel = bin; break; }
+        cum += hist[bin];
+      }
+      s_remaining = rem - cum;
+      s_prefix = prefix | ((uint32_t)bsel << shift);
+      s_mask = mask | (255u << shift);
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = s_prefix;
+  const uint32_t take_eq = s_remaining;  // rows with score == thr to take, smallest rows first
+  uint32_t taken = 0;                    // uniform across the workgroup
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int base = 0; base < T; base += kSelThreads) {
+    int t = base + tid;
+    bool elig = false, eq = false;
+    uint32_t s = 0;
+    if (t < T) {
+      elig = (flags[t] & (kFlagCand | kFlagForced)) == kFlagCand;
+      s = score[t];
+      eq = elig && s == thr;
+    }
+    uint64_t bal = __ballot(eq);
+    uint32_t before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    uint32_t before = taken + before_in_wave;
+    uint32_t blk_total = 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      if (w < wave) before += wave_cnt[w];
+      blk_total += wave_cnt[w];
+    }
+    if (elig && (s > thr || (eq && before < take_eq))) flags[t] |= kFlagIndexer;
+    taken += blk_total;
+    __syncthreads();
+  }
+}
+
+// Compaction of A (forced or Indexer rows) and of its complement, both ascending.
+constexpr int kScanBlock = 1024;
+
+__device__ __forceinline__ bool in_a(uint8_t f) { return (f & (kFlagForced | kFlagIndexer)) != 0; }
+
+__global__ __launch_bounds__(kScanBlock) void k_count_a(const uint8_t* __restrict__ flags, int T,
+                                                        int32_t* __restrict__ blk_count,
+                                                        uint64_t* __restrict__ blk_sum) {
+  __shared__ uint32_t c[kScanBlock / 64];
+  __shared__ uint64_t sm[kScanBlock / 64];
+  int t = blockIdx.x * kScanBlock + threadIdx.x;
+  bool a = t < T && in_a(flags[t]);
+  uint64_t v = a ? (uint64_t)t + 1 : 0;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  uint64_t bal = __ballot(a);
+  if ((threadIdx.x & 63) == 0) { c[threadIdx.x >> 6] = __popcll(bal); sm[threadIdx.x >> 6] = v; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    uint64_t s = 0;
+    for (int w = 0; w < kScanBlock / 64; ++w) { tot += c[w]; s += sm[w]; }
+    blk_count[blockIdx.x] = (int32_t)tot;
+    blk_sum[blockIdx.x] = s;
+  }
+}
+
+// Exclusive scan of the per-block counts (in place) and the total of sum(t + 1) over A.
+__global__ __launch_bounds__(1024) void k_scan_counts(int32_t* __restrict__ blk_count,
+                                                      const uint64_t* __restrict__ blk_sum,
+                                                      int n_blk, uint64_t* __restrict__ sum_a) {
+  __shared__ int32_t part[1024];
+  __shared__ uint64_t psum[1024];
+  const int tid = threadIdx.x;
+  const int per = (n_blk + 1023) / 1024;
+  int32_t local = 0;
+  uint64_t ls = 0;
+  for (int i = 0; i < per; ++i) {
+    int k = tid * per + i;
+    if (k < n_blk) { local += blk_count[k]; ls += blk_sum[k]; }
+  }
+  part[tid] = local;
+  psum[tid] = ls;
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    uint64_t s = 0;
+    for (int i = 0; i < 1024; ++i) { int32_t v = part[i]; part[i] = run; run += v; s += psum[i]; }
+    *sum_a = s;
+  }
+  __syncthreads();
+  int32_t run = part[tid];
+  for (int i = 0; i < per; ++i) {
+    int k = tid * per + i;
+    if (k < n_blk) { int32_t v = blk_count[k]; blk_count[k] = run; run += v; }
+  }
+}
+
+__global__ __launch_bounds__(kScanBlock) void k_scatter_a(const uint8_t* __restrict__ flags, int T,
+                                                          const int32_t* __restrict__ blk_off,
+                                                          int32_t* __restrict__ alist,
+                                                          int32_t* __restrict__ nalist, int nA) {
+  __shared__ uint32_t c[kScanBlock / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int t = blockIdx.x * kScanBlock + threadIdx.x;
+  bool valid = t < T;
+  bool a = valid && in_a(flags[t]);
+  uint64_t bal = __ballot(a);
+  if (lane == 0) c[wave] = __popcll(bal);
+  __syncthreads();
+  uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+  for (int w = 0; w < wave; ++w) before += c[w];
+  if (valid) {
+    int32_t off = blk_off[blockIdx.x];
+    // the host sized both lists from the same rule; the bounds only guard the workspace
+    if (a) {
+      if (off + (int)before < nA) alist[off + before] = t;
+    } else {
+      int local_idx = threadIdx.x;
+      int32_t na_before = blockIdx.x * kScanBlock - off + (local_idx - (int)before);
+      if (na_before >= 0 && na_before < T - nA) nalist[na_before] = t;
+    }
+  }
+}
+
+hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_row, int T,
+                          int edge_rows, int tail_rows, const int32_t* dirty, int n_dirty,
+                          const uint32_t* score, int64_t need, uint8_t* flags,
+                          uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,
+                          int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
+                          hipStream_t stream) {
+  (void)n_seg;
+  (void)sel_state;
+  int blocks = (T + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_protect_mark, dim3(blocks), dim3(256), 0, stream, seg, seg_of_row, T,
+                     edge_rows, tail_rows, dirty, n_dirty, flags);
+  if (need > 0)
+    hipLaunchKernelGGL(k_protect_select, dim3(1), dim3(kSelThreads), 0, stream, flags, score, T,
+                       (uint32_t)need);
+  hipLaunchKernelGGL(k_count_a, dim3(n_blk), dim3(kScanBlock), 0, stream, flags, T, blk_count,
+                     blk_sum);
+  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, stream, blk_count, blk_sum, n_blk,
+                     sum_a);
+  hipLaunchKernelGGL(k_scatter_a, dim3(n_blk), dim3(kScanBlock), 0, stream, flags, T, blk_count,
+                     alist, nalist, n_a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------ work list
+// Tiles sorted by decreasing largest row (their key count), F and G tiles interleaved by a
+// merge-by-rank: each tile's rank = its position in its own descending list plus the number
+// of tiles of the other list that sort before it (equal costs: F tiles first).
+__global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
+  int n = m.nF + m.nG;
+  for (int tile = blockIdx.x * blockDim.x + threadIdx.x; tile < n; tile += gridDim.x * blockDim.x) {
+    int c = tile_max_row(m, tile);
+    int rank;
+    if (tile < m.nF) {
+      // G tiles with cost > c: nG - (#G tiles with cost <= c)
+      int lo = 0, hi = m.nG;  // first G index with cost > c
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (tile_max_row(m, m.nF + mid) > c) hi = mid; else lo = mid + 1;
+      }
+      rank = (m.nF - 1 - tile) + (m.nG - lo);
+    } else {
+      int k = tile - m.nF;
+      int lo = 0, hi = m.nF;  // first F index with cost >= c
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if (tile_max_row(m, mid) >= c) hi = mid; else lo = mid + 1;
+      }
+      rank = (m.nG - 1 - k) + (m.nF - lo);
+    }
+    work[rank] = tile;
+  }
+}
+
+hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream) {
+  int n = map.nF + map.nG;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_worklist, dim3((n + 255) / 256), dim3(256), 0, stream, map, work);
+  return hipGetLastError();
+}
+
+}  // namespace segmla

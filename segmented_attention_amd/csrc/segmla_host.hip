@@ -1,0 +1,534 @@
+// Host side of libsegmla: argument validation, plan sizing, workspace layout and launch
+// sequencing on the caller's stream. Every entry point validates before it enqueues anything.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/segmla.h"
+#include "internal.h"
+
+using namespace segmla;
+
+struct segmla_plan {
+  // geometry
+  int32_t n_seg = 0;
+  int32_t T = 0;
+  int64_t n_pool = 0;
+  std::vector<SegDesc> segs;
+  // layer
+  int32_t H = 0, HG = 0, HL = 0, d_nope = 0, d_rope = 0, d_qk = 0, d_v = 0, d_state = 0;
+  int32_t v_has_rope = 1, kv_dtype = 0, io_dtype = 0;
+  double rope_base = 10000.0;
+  float sigma = 1.f;
+  std::vector<int32_t> ghead, lhead;
+  // protection
+  int32_t edge_rows = 0, tail_rows = 0, budget_permille = 0;
+  std::vector<int32_t> dirty;  // sorted, unique
+  int64_t n_forced = 0, n_cand = 0, K = 0, need = 0, nA = 0;
+  // work decomposition
+  int32_t nF = 0, nG = 0, n_split = 1, split_keys = 0, n_blk = 0;
+  // workspace layout (byte offsets, 256-aligned)
+  size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
+         o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
+         o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0,
+         ws_bytes = 0;
+  // profiling (events on the caller's stream)
+  bool prof = false, fwd_pending = false, build_pending = false;
+  hipEvent_t ev[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  double prof_ms[4] = {0, 0, 0, 0};
+  int64_t prof_fwd = 0, prof_build = 0;
+  // build state
+  bool built = false;
+  char* ws = nullptr;
+  template <typename X>
+  X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
+};
+
+namespace {
+
+constexpr int kNumCU = 256;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+float elapsed(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  return hipEventElapsedTime(&ms, a, b) == hipSuccess ? ms : 0.f;
+}
+
+// Fold the previous profiled forward / build into the totals (waits for their events).
+hipError_t flush_profile(segmla_plan* p) {
+  if (p->fwd_pending) {
+    hipError_t e = hipEventSynchronize(p->ev[3]);
+    if (e != hipSuccess) return e;
+    p->prof_ms[0] += elapsed(p->ev[0], p->ev[1]);
+    p->prof_ms[1] += elapsed(p->ev[1], p->ev[2]);
+    p->prof_ms[2] += elapsed(p->ev[2], p->ev[3]);
+    p->prof_fwd += 1;
+    p->fwd_pending = false;
+  }
+  if (p->build_pending) {
+    hipError_t e = hipEventSynchronize(p->ev[5]);
+    if (e != hipSuccess) return e;
+    p->prof_ms[3] += elapsed(p->ev[4], p->ev[5]);
+    p->prof_build += 1;
+    p->build_pending = false;
+  }
+  return hipSuccess;
+}
+
+bool is_dtype(int32_t d) { return d == SEGMLA_F32 || d == SEGMLA_BF16 || d == SEGMLA_E4M3_B128; }
+
+segmla_status check_layer(const segmla_layer* L) {
+  if (!L->head_is_global) return SEGMLA_E_NULL;
+  if (L->n_heads < 1 || L->d_nope < 0 || L->d_rope < 2 || (L->d_rope & 1) || L->d_state < 1)
+    return SEGMLA_E_SHAPE;
+  if (L->v_has_rope != 0 && L->v_has_rope != 1) return SEGMLA_E_SHAPE;
+  if (!(L->rope_base > 1.0) || !std::isfinite(L->rope_base)) return SEGMLA_E_SHAPE;
+  if (!(L->softmax_scale > 0.f) || !std::isfinite(L->softmax_scale)) return SEGMLA_E_SHAPE;
+  for (int h = 0; h < L->n_heads; ++h)
+    if (L->head_is_global[h] > 1) return SEGMLA_E_SHAPE;
+  if (!is_dtype(L->kv_dtype) || !is_dtype(L->io_dtype)) return SEGMLA_E_DTYPE;
+  if (L->io_dtype == SEGMLA_E4M3_B128) return SEGMLA_E_DTYPE;
+  if (L->split_keys < -1 || (L->split_keys > 0 && (L->split_keys % 64) != 0)) return SEGMLA_E_SHAPE;
+  const int d_qk = L->d_nope + L->d_rope;
+  if (L->kv_dtype == SEGMLA_F32) {
+    if (L->io_dtype != SEGMLA_F32) return SEGMLA_E_UNSUPPORTED;
+    if (d_qk > 1024 || L->d_state > 1024 || (L->d_nope & 1)) return SEGMLA_E_UNSUPPORTED;
+  } else {
+    if (L->io_dtype != SEGMLA_BF16) return SEGMLA_E_UNSUPPORTED;
+    if (L->d_nope != 512 || L->d_rope != 64 || (L->d_state % 64) != 0 || L->d_state > 4096)
+      return SEGMLA_E_UNSUPPORTED;
+  }
+  return SEGMLA_OK;
+}
+
+segmla_status check_geometry(const segmla_geometry* G, int64_t n_pool, int64_t* T_out) {
+  if (!G->pool_row || !G->len || !G->offset || !G->kind) return SEGMLA_E_NULL;
+  if (G->n_seg < 1 || n_pool < 1) return SEGMLA_E_GEOMETRY;
+  int64_t pos = 0;
+  for (int i = 0; i < G->n_seg; ++i) {
+    if (G->len[i] < 1 || G->kind[i] > 2) return SEGMLA_E_GEOMETRY;
+    if (G->offset[i] != pos) return SEGMLA_E_GEOMETRY;
+    if (G->pool_row[i] < 0 || G->pool_row[i] > n_pool - G->len[i]) return SEGMLA_E_GEOMETRY;
+    pos += G->len[i];
+    if (pos >= ((int64_t)1 << 31)) return SEGMLA_E_GEOMETRY;
+  }
+  *T_out = pos;
+  return SEGMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t segmla_abi_version(void) { return SEGMLA_ABI_VERSION; }
+
+const char* segmla_status_string(int32_t s) {
+  switch (s) {
+    case SEGMLA_OK: return "ok";
+    case SEGMLA_E_NULL: return "required pointer is NULL";
+    case SEGMLA_E_GEOMETRY: return "malformed segment geometry";
+    case SEGMLA_E_SHAPE: return "invalid layer shape or role mask";
+    case SEGMLA_E_DTYPE: return "invalid dtype";
+    case SEGMLA_E_PROTECT: return "invalid protection parameters or missing Indexer scores";
+    case SEGMLA_E_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SEGMLA_E_HIP: return "HIP runtime call or kernel launch failed";
+    case SEGMLA_E_UNSUPPORTED: return "shape/dtype combination not implemented";
+    case SEGMLA_E_STATE: return "plan not built";
+    default: return "unknown status";
+  }
+}
+
+segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer* layer,
+                                 const segmla_protect* prot, int64_t n_pool,
+                                 segmla_plan** out_plan) {
+  if (!geom || !layer || !prot || !out_plan) return SEGMLA_E_NULL;
+  segmla_status st = check_layer(layer);
+  if (st != SEGMLA_OK) return st;
+  int64_t T64 = 0;
+  st = check_geometry(geom, n_pool, &T64);
+  if (st != SEGMLA_OK) return st;
+  const int32_t T = (int32_t)T64;
+  if (prot->edge_rows < 0 || prot->tail_rows < 0 || prot->budget_permille < 0 ||
+      prot->budget_permille > 1000 || prot->n_dirty < 0)
+    return SEGMLA_E_PROTECT;
+  if (prot->n_dirty > 0 && !prot->dirty_rows) return SEGMLA_E_NULL;
+  for (int i = 0; i < prot->n_dirty; ++i)
+    if (prot->dirty_rows[i] < 0 || prot->dirty_rows[i] >= T) return SEGMLA_E_PROTECT;
+
+  segmla_plan* p = new (std::nothrow) segmla_plan();
+  if (!p) return SEGMLA_E_UNSUPPORTED;
+  p->n_seg = geom->n_seg;
+  p->T = T;
+  p->n_pool = n_pool;
+  p->segs.resize(geom->n_seg);
+  for (int i = 0; i < geom->n_seg; ++i) {
+    SegDesc& d = p->segs[i];
+    d.pool_row = geom->pool_row[i];
+    d.offset = (int32_t)geom->offset[i];
+    d.len = geom->len[i];
+    d.kind = geom->kind[i];
+    d.relocated = (geom->kind[i] == SEGMLA_SEG_DOC && geom->offset[i] != 0) ? 1 : 0;
+    d.rot = geom->kind[i] == SEGMLA_SEG_DOC ? d.offset : 0;
+    d.pad = 0;
+  }
+  p->H = layer->n_heads;
+  for (int h = 0; h < p->H; ++h) (layer->head_is_global[h] ? p->ghead : p->lhead).push_back(h);
+  p->HG = (int32_t)p->ghead.size();
+  p->HL = (int32_t)p->lhead.size();
+  p->d_nope = layer->d_nope;
+  p->d_rope = layer->d_rope;
+  p->d_qk = layer->d_nope + layer->d_rope;
+  p->d_v = layer->v_has_rope ? p->d_qk : p->d_nope;
+  if (p->d_v < 1) { delete p; return SEGMLA_E_SHAPE; }
+  p->d_state = layer->d_state;
+  p->v_has_rope = layer->v_has_rope;
+  p->kv_dtype = layer->kv_dtype;
+  p->io_dtype = layer->io_dtype;
+  p->rope_base = layer->rope_base;
+  p->sigma = layer->softmax_scale;
+  p->edge_rows = prot->edge_rows;
+  p->tail_rows = prot->tail_rows;
+  p->budget_permille = prot->budget_permille;
+  p->dirty.assign(prot->dirty_rows, prot->dirty_rows + prot->n_dirty);
+  std::sort(p->dirty.begin(), p->dirty.end());
+  p->dirty.erase(std::unique(p->dirty.begin(), p->dirty.end()), p->dirty.end());
+
+  // |F|, |C| and |F & C| on the host (the protected-row rule, counted row by row).
+  {
+    std::vector<uint8_t> forced(T, 0);
+    const int b = p->edge_rows;
+    for (const SegDesc& d : p->segs) {
+      if (d.kind == SEGMLA_SEG_NEW) std::fill(forced.begin() + d.offset, forced.begin() + d.offset + d.len, 1);
+      if (d.relocated) {
+        int e = std::min(b, d.len);
+        std::fill(forced.begin() + d.offset, forced.begin() + d.offset + e, 1);
+        std::fill(forced.begin() + d.offset + std::max(0, d.len - b), forced.begin() + d.offset + d.len, 1);
+      }
+    }
+    for (int32_t r : p->dirty) forced[r] = 1;
+    for (int64_t t = std::max<int64_t>(0, (int64_t)T - p->tail_rows); t < T; ++t) forced[t] = 1;
+    int64_t nf = 0, nc = 0, nfc = 0;
+    for (const SegDesc& d : p->segs) {
+      bool cand = d.kind != SEGMLA_SEG_NEW;
+      for (int j = 0; j < d.len; ++j) {
+        bool f = forced[d.offset + j] != 0;
+        nf += f;
+        nc += cand;
+        nfc += (f && cand);
+      }
+    }
+    p->n_forced = nf;
+    p->n_cand = nc;
+    p->K = ((int64_t)p->budget_permille * nc + 999) / 1000;
+    p->need = std::max<int64_t>(0, p->K - nfc);
+    p->nA = nf + p->need;
+  }
+
+  // Work decomposition: qvec tiles of stream F (rows of A x all heads) and stream G (other
+  // rows x Global heads), optionally split along the key axis.
+  const int64_t qF = p->nA * p->H, qG = ((int64_t)T - p->nA) * p->HG;
+  const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
+  if (nF + nG > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
+  p->nF = (int32_t)nF;
+  p->nG = (int32_t)nG;
+  const int64_t n_tiles = nF + nG;
+  int32_t sk = layer->split_keys;
+  if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
+    sk = -1;
+    if (n_tiles > 0 && n_tiles < 2 * kNumCU && T > 2048) {
+      int64_t want = std::min<int64_t>((4 * kNumCU + n_tiles - 1) / n_tiles, (T + 1023) / 1024);
+      if (want > 1) sk = (int32_t)((((T + want - 1) / want) + 63) / 64 * 64);
+    }
+  }
+  if (sk > 0 && sk < T) {
+    p->split_keys = sk;
+    p->n_split = (int32_t)((T + sk - 1) / sk);
+  } else {
+    p->split_keys = 0;
+    p->n_split = 1;
+  }
+  p->n_blk = (T + 1023) / 1024;
+
+  // Workspace layout.
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
+  const size_t half = (size_t)p->d_rope / 2;
+  p->o_seg = take(sizeof(SegDesc) * p->n_seg);
+  p->o_segcs = take(sizeof(float2) * half * p->n_seg);
+  p->o_stepcs = take(sizeof(float2) * half * p->n_seg);
+  p->o_rowcs = take(sizeof(float2) * half * (size_t)T);
+  p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
+  p->o_flags = take((size_t)T);
+  p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
+  p->o_ghead = take(sizeof(int32_t) * p->ghead.size());
+  p->o_lhead = take(sizeof(int32_t) * p->lhead.size());
+  p->o_alist = take(sizeof(int32_t) * (size_t)p->nA);
+  p->o_nalist = take(sizeof(int32_t) * (size_t)(T - p->nA));
+  p->o_blk_count = take(sizeof(int32_t) * p->n_blk);
+  p->o_blk_sum = take(sizeof(uint64_t) * p->n_blk);
+  p->o_sum_a = take(sizeof(uint64_t));
+  p->o_sel = take(sizeof(uint32_t) * 4);
+  p->o_work = take(sizeof(int32_t) * (size_t)n_tiles);
+  if (p->n_split > 1) {
+    const size_t nvec = (size_t)n_tiles * kTileQ;
+    p->o_part_o = take(sizeof(float) * (size_t)p->n_split * nvec * p->d_v);
+    p->o_part_ml = take(sizeof(float) * 2 * (size_t)p->n_split * nvec);
+  }
+  p->ws_bytes = o;
+  *out_plan = p;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_plan_workspace_bytes(const segmla_plan* p, size_t* bytes) {
+  if (!p || !bytes) return SEGMLA_E_NULL;
+  *bytes = p->ws_bytes;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_plan_rows(const segmla_plan* p, int64_t* n_rows, int64_t* n_protected) {
+  if (!p || !n_rows || !n_protected) return SEGMLA_E_NULL;
+  *n_rows = p->T;
+  *n_protected = p->nA;
+  return SEGMLA_OK;
+}
+
+static TileMap tile_map(const segmla_plan* p) {
+  TileMap m;
+  m.alist = p->at<int32_t>(p->o_alist);
+  m.nalist = p->at<int32_t>(p->o_nalist);
+  m.ghead = p->at<int32_t>(p->o_ghead);
+  m.nA = (int32_t)p->nA;
+  m.nNA = p->T - (int32_t)p->nA;
+  m.H = p->H;
+  m.HG = p->HG;
+  m.nF = p->nF;
+  m.nG = p->nG;
+  return m;
+}
+
+segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspace_bytes,
+                                const uint32_t* indexer_score, void* stream) {
+  if (!p || !workspace) return p ? SEGMLA_E_WORKSPACE : SEGMLA_E_NULL;
+  if (workspace_bytes < p->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return SEGMLA_E_WORKSPACE;
+  if (p->need > 0 && !indexer_score) return SEGMLA_E_PROTECT;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (p->prof) {
+    if (flush_profile(p) != hipSuccess || hipEventRecord(p->ev[4], s) != hipSuccess) return SEGMLA_E_HIP;
+  }
+  p->ws = (char*)workspace;
+  p->built = false;
+  auto up = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
+  };
+  up(p->o_seg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
+  up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
+  up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
+  up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_seg, p->T, p->d_rope, p->rope_base,
+                      p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
+                      p->at<float2>(p->o_stepcs), p->at<float2>(p->o_rowcs), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_protect(p->at<SegDesc>(p->o_seg), p->n_seg, p->at<int32_t>(p->o_seg_of_row), p->T,
+                     p->edge_rows, p->tail_rows, p->at<int32_t>(p->o_dirty), (int)p->dirty.size(),
+                     indexer_score, p->need, p->at<uint8_t>(p->o_flags), p->at<uint32_t>(p->o_sel),
+                     p->at<int32_t>(p->o_blk_count), p->at<uint64_t>(p->o_blk_sum), p->n_blk,
+                     p->at<int32_t>(p->o_alist), p->at<int32_t>(p->o_nalist), (int)p->nA,
+                     p->at<uint64_t>(p->o_sum_a), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  if (p->prof) {
+    if (hipEventRecord(p->ev[5], s) != hipSuccess) return SEGMLA_E_HIP;
+    p->build_pending = true;
+  }
+  p->built = true;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void* stream) {
+  if (!p || !t) return SEGMLA_E_NULL;
+  if (!p->built) return SEGMLA_E_STATE;
+  if (!t->q || !t->kv || !t->w || !t->out || !t->z) return SEGMLA_E_NULL;
+  if (p->HL > 0 && !t->z_cached) return SEGMLA_E_NULL;
+  if (p->kv_dtype == SEGMLA_E4M3_B128 && (!t->kv_scale || !t->kv_rope)) return SEGMLA_E_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a;
+  a.q = t->q;
+  a.kv = t->kv;
+  a.kv_scale = t->kv_scale;
+  a.kv_rope = t->kv_rope;
+  a.out = t->out;
+  a.lse = t->lse;
+  a.part_o = p->n_split > 1 ? p->at<float>(p->o_part_o) : nullptr;
+  a.part_ml = p->n_split > 1 ? p->at<float>(p->o_part_ml) : nullptr;
+  a.seg = p->at<SegDesc>(p->o_seg);
+  a.segcs = p->at<float2>(p->o_segcs);
+  a.stepcs = p->at<float2>(p->o_stepcs);
+  a.work = p->at<int32_t>(p->o_work);
+  a.map = tile_map(p);
+  a.n_seg = p->n_seg;
+  a.T = p->T;
+  a.d_nope = p->d_nope;
+  a.d_rope = p->d_rope;
+  a.d_v = p->d_v;
+  a.n_split = p->n_split;
+  a.split_keys = p->split_keys;
+  a.sigma = p->sigma;
+  hipError_t e = hipSuccess;
+  segmla_plan* pm = const_cast<segmla_plan*>(p);  // profiling state only
+  if (p->prof) {
+    if (flush_profile(pm) != hipSuccess || hipEventRecord(p->ev[0], s) != hipSuccess)
+      return SEGMLA_E_HIP;
+  }
+  if (p->nF + p->nG > 0) e = launch_attn(a, p->kv_dtype, p->v_has_rope, s);
+  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
+  if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1) e = launch_merge_tiles(a, p->io_dtype, s);
+  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[2], s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  EpiArgs ep;
+  ep.out = t->out;
+  ep.w = t->w;
+  ep.z_cached = t->z_cached;
+  ep.z = t->z;
+  ep.rowcs = p->at<float2>(p->o_rowcs);
+  ep.alist = p->at<int32_t>(p->o_alist);
+  ep.nalist = p->at<int32_t>(p->o_nalist);
+  ep.ghead = p->at<int32_t>(p->o_ghead);
+  ep.lhead = p->at<int32_t>(p->o_lhead);
+  ep.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
+  ep.seg = p->at<SegDesc>(p->o_seg);
+  ep.T = p->T;
+  ep.H = p->H;
+  ep.HG = p->HG;
+  ep.HL = p->HL;
+  ep.nA = (int32_t)p->nA;
+  ep.nNA = p->T - (int32_t)p->nA;
+  ep.d_nope = p->d_nope;
+  ep.d_rope = p->d_rope;
+  ep.d_v = p->d_v;
+  ep.d_state = p->d_state;
+  ep.v_has_rope = p->v_has_rope;
+  e = launch_epilogue(ep, p->io_dtype, s);
+  if (e == hipSuccess && p->prof) {
+    e = hipEventRecord(p->ev[3], s);
+    pm->fwd_pending = e == hipSuccess;
+  }
+  return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+}
+
+segmla_status segmla_profile_enable(segmla_plan* p, int32_t enable) {
+  if (!p) return SEGMLA_E_NULL;
+  if (enable) {
+    for (hipEvent_t& ev : p->ev)
+      if (!ev && hipEventCreate(&ev) != hipSuccess) return SEGMLA_E_HIP;
+    p->fwd_pending = p->build_pending = false;
+    for (double& x : p->prof_ms) x = 0;
+    p->prof_fwd = p->prof_build = 0;
+    p->prof = true;
+  } else {
+    if (flush_profile(p) != hipSuccess) return SEGMLA_E_HIP;
+    p->prof = false;
+  }
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_profile_read(segmla_plan* p, double ms[4], int64_t* n_forward,
+                                  int64_t* n_build) {
+  if (!p || !ms) return SEGMLA_E_NULL;
+  if (flush_profile(p) != hipSuccess) return SEGMLA_E_HIP;
+  for (int i = 0; i < 4; ++i) ms[i] = p->prof_ms[i];
+  if (n_forward) *n_forward = p->prof_fwd;
+  if (n_build) *n_build = p->prof_build;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_copy_protected(const segmla_plan* p, int32_t* host_rows, int64_t cap,
+                                    void* stream) {
+  if (!p || !host_rows) return SEGMLA_E_NULL;
+  if (!p->built) return SEGMLA_E_STATE;
+  if (cap < p->nA) return SEGMLA_E_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->nA > 0 && hipMemcpyAsync(host_rows, p->ws + p->o_alist, sizeof(int32_t) * p->nA,
+                                  hipMemcpyDeviceToHost, s) != hipSuccess)
+    return SEGMLA_E_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+}
+
+segmla_status segmla_copy_geometry(const segmla_plan* p, int32_t* seg_of_row, int64_t* pool_of_row,
+                                   int64_t cap, void* stream) {
+  if (!p) return SEGMLA_E_NULL;
+  if (!p->built) return SEGMLA_E_STATE;
+  if (cap < p->T) return SEGMLA_E_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> tmp;
+  int32_t* dst = seg_of_row;
+  if (!dst && pool_of_row) { tmp.resize(p->T); dst = tmp.data(); }
+  if (dst && hipMemcpyAsync(dst, p->ws + p->o_seg_of_row, sizeof(int32_t) * p->T,
+                            hipMemcpyDeviceToHost, s) != hipSuccess)
+    return SEGMLA_E_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SEGMLA_E_HIP;
+  if (pool_of_row) {
+    for (int32_t r = 0; r < p->T; ++r) {
+      int32_t i = dst[r];
+      if (i < 0 || i >= p->n_seg) { pool_of_row[r] = -1; continue; }
+      pool_of_row[r] = p->segs[i].pool_row + (r - p->segs[i].offset);
+    }
+  }
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_plan_pairs(const segmla_plan* p, double out[2], void* stream) {
+  if (!p || !out) return SEGMLA_E_NULL;
+  if (!p->built) return SEGMLA_E_STATE;
+  uint64_t sum_a = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&sum_a, p->ws + p->o_sum_a, sizeof(uint64_t), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SEGMLA_E_HIP;
+  const double T = (double)p->T;
+  out[0] = (double)p->HG * T * (T + 1.0) / 2.0;
+  out[1] = (double)p->HL * (double)sum_a;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_ledger(int32_t f_front, int32_t r, int32_t f_back, int32_t h,
+                            int32_t h_local, int64_t T, int64_t n_protected, double global_pairs,
+                            double local_pairs, double out[3]) {
+  if (!out) return SEGMLA_E_NULL;
+  if (f_front < 0 || r < 0 || f_back < 0 || f_front + r + f_back < 1 || h < 1 || h_local < 0 ||
+      h_local > h || T < 1 || n_protected < 0 || n_protected > T)
+    return SEGMLA_E_SHAPE;
+  out[0] = ((double)r / (double)(f_front + r + f_back)) * ((double)h_local / (double)h);
+  out[1] = (double)h_local * (double)(T - n_protected) / ((double)h * (double)T);
+  const double dense = (double)h * (double)T * ((double)T + 1.0) / 2.0;
+  out[2] = local_pairs < 0 ? NAN : 1.0 - (global_pairs + local_pairs) / dense;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_lse_merge(const float* partial_o, const float* partial_ml, int32_t n_split,
+                               int64_t n_vec, int32_t d, void* out, int32_t out_dtype, float* lse,
+                               void* stream) {
+  if (!partial_o || !partial_ml || !out) return SEGMLA_E_NULL;
+  if (n_split < 1 || n_vec < 0 || d < 1 || d > 4096) return SEGMLA_E_SHAPE;
+  if (out_dtype != SEGMLA_F32 && out_dtype != SEGMLA_BF16) return SEGMLA_E_DTYPE;
+  if (n_vec == 0) return SEGMLA_OK;
+  hipError_t e = launch_lse_merge(partial_o, partial_ml, n_split, n_vec, d, out, out_dtype, lse,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+}
+
+void segmla_plan_destroy(segmla_plan* p) {
+  if (!p) return;
+  for (hipEvent_t ev : p->ev)
+    if (ev) (void)hipEventDestroy(ev);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,298 @@
+"""ctypes binding of libsegmla (include/segmla.h): argument marshalling only.
+
+Functions carry the C names. Host arrays are numpy arrays; device buffers are torch
+tensors on the GPU (PyTorch provides device memory and streams only). Every call
+raises SegmlaError on a non-OK status; nothing here computes any part of the method.
+The library must be built (__graft_entry__.build()); loading fails loudly otherwise.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsegmla.so")
+
+SEGMLA_OK = 0
+SEGMLA_E_NULL, SEGMLA_E_GEOMETRY, SEGMLA_E_SHAPE, SEGMLA_E_DTYPE = -1, -2, -3, -4
+SEGMLA_E_PROTECT, SEGMLA_E_WORKSPACE, SEGMLA_E_HIP, SEGMLA_E_UNSUPPORTED, SEGMLA_E_STATE = (
+    -5, -6, -7, -8, -9)
+SEGMLA_SEG_PREFIX, SEGMLA_SEG_DOC, SEGMLA_SEG_NEW = 0, 1, 2
+SEGMLA_F32, SEGMLA_BF16, SEGMLA_E4M3_B128 = 0, 1, 2
+
+EXPORTED = [
+    "segmla_plan_create", "segmla_plan_workspace_bytes", "segmla_plan_rows", "segmla_plan_build",
+    "segmla_forward", "segmla_copy_protected", "segmla_copy_geometry", "segmla_lse_merge",
+    "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
+    "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
+]
+
+
+class SegmlaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (what, _status_string(status), status))
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [("n_seg", ctypes.c_int32), ("pool_row", ctypes.POINTER(ctypes.c_int64)),
+                ("len", ctypes.POINTER(ctypes.c_int32)), ("offset", ctypes.POINTER(ctypes.c_int64)),
+                ("kind", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("v_has_rope", ctypes.c_int32),
+                ("head_is_global", ctypes.POINTER(ctypes.c_uint8)), ("rope_base", ctypes.c_double),
+                ("softmax_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("split_keys", ctypes.c_int32)]
+
+
+class Protect(ctypes.Structure):
+    _fields_ = [("edge_rows", ctypes.c_int32), ("tail_rows", ctypes.c_int32),
+                ("budget_permille", ctypes.c_int32), ("n_dirty", ctypes.c_int32),
+                ("dirty_rows", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Tensors(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+                ("kv_rope", ctypes.c_void_p), ("w", ctypes.c_void_p), ("z_cached", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsegmla.so is not built at %s; run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        sig = {
+            "segmla_plan_create": (i32, [ctypes.POINTER(Geometry), ctypes.POINTER(Layer),
+                                         ctypes.POINTER(Protect), i64, ctypes.POINTER(P)]),
+            "segmla_plan_workspace_bytes": (i32, [P, ctypes.POINTER(ctypes.c_size_t)]),
+            "segmla_plan_rows": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+            "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
+            "segmla_forward": (i32, [P, ctypes.POINTER(Tensors), P]),
+            "segmla_copy_protected": (i32, [P, ctypes.POINTER(i32), i64, P]),
+            "segmla_copy_geometry": (i32, [P, ctypes.POINTER(i32), ctypes.POINTER(i64), i64, P]),
+            "segmla_lse_merge": (i32, [P, P, i32, i64, i32, P, i32, P, P]),
+            "segmla_plan_pairs": (i32, [P, ctypes.POINTER(dbl), P]),
+            "segmla_ledger": (i32, [i32, i32, i32, i32, i32, i64, i64, dbl, dbl, ctypes.POINTER(dbl)]),
+            "segmla_plan_destroy": (None, [P]),
+            "segmla_status_string": (ctypes.c_char_p, [i32]),
+            "segmla_abi_version": (i32, []),
+            "segmla_profile_enable": (i32, [P, i32]),
+            "segmla_profile_read": (i32, [P, ctypes.POINTER(dbl), ctypes.POINTER(i64),
+                                          ctypes.POINTER(i64)]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _status_string(status):
+    try:
+        return lib().segmla_status_string(int(status)).decode()
+    except Exception:  # library missing while formatting an error
+        return "status"
+
+
+def _check(status, what):
+    if status != SEGMLA_OK:
+        raise SegmlaError(status, what)
+
+
+def _ptr(t):
+    """Device (or host) address of a torch tensor, or None."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _arr(a, dtype):
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+# ------------------------------------------------------------------- C entry points
+def segmla_abi_version():
+    return int(lib().segmla_abi_version())
+
+
+def segmla_status_string(status):
+    return _status_string(status)
+
+
+def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is_global, d_nope,
+                       d_rope, d_state, v_has_rope=1, rope_base=10000.0, softmax_scale=1.0,
+                       kv_dtype=SEGMLA_BF16, io_dtype=SEGMLA_BF16, split_keys=0, edge_rows=0,
+                       tail_rows=0, budget_permille=0, dirty_rows=()):
+    """Validate and size a plan; returns (plan handle, keepalive) -- see Plan for lifetime."""
+    keep = dict(kind=_arr(kinds, np.uint8), len=_arr(lens, np.int32), offset=_arr(offsets, np.int64),
+                pool=_arr(pool_rows, np.int64), glob=_arr(head_is_global, np.uint8),
+                dirty=_arr(list(dirty_rows), np.int32))
+    g = Geometry(len(keep["kind"]), keep["pool"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                 keep["len"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                 keep["offset"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                 keep["kind"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    L = Layer(n_heads, d_nope, d_rope, d_state, v_has_rope,
+              keep["glob"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), rope_base, softmax_scale,
+              kv_dtype, io_dtype, split_keys)
+    pr = Protect(edge_rows, tail_rows, budget_permille, len(keep["dirty"]),
+                 keep["dirty"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(keep["dirty"])
+                 else None)
+    h = ctypes.c_void_p()
+    _check(lib().segmla_plan_create(ctypes.byref(g), ctypes.byref(L), ctypes.byref(pr), int(n_pool),
+                                    ctypes.byref(h)), "segmla_plan_create")
+    return h
+
+
+def segmla_plan_workspace_bytes(plan):
+    n = ctypes.c_size_t()
+    _check(lib().segmla_plan_workspace_bytes(plan, ctypes.byref(n)), "segmla_plan_workspace_bytes")
+    return int(n.value)
+
+
+def segmla_plan_rows(plan):
+    T, nA = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().segmla_plan_rows(plan, ctypes.byref(T), ctypes.byref(nA)), "segmla_plan_rows")
+    return int(T.value), int(nA.value)
+
+
+def segmla_plan_build(plan, workspace, indexer_score=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().segmla_plan_build(plan, _ptr(workspace), nbytes, _ptr(indexer_score),
+                                   _stream(stream)), "segmla_plan_build")
+
+
+def segmla_forward(plan, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope=None, lse=None,
+                   stream=None):
+    t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
+                _ptr(z), _ptr(lse))
+    _check(lib().segmla_forward(plan, ctypes.byref(t), _stream(stream)), "segmla_forward")
+
+
+def segmla_copy_protected(plan, n_protected, stream=None):
+    buf = np.empty(max(1, n_protected), dtype=np.int32)
+    _check(lib().segmla_copy_protected(plan, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                       len(buf), _stream(stream)), "segmla_copy_protected")
+    return buf[:n_protected]
+
+
+def segmla_copy_geometry(plan, T, stream=None):
+    seg = np.empty(T, dtype=np.int32)
+    pool = np.empty(T, dtype=np.int64)
+    _check(lib().segmla_copy_geometry(plan, seg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      pool.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), T,
+                                      _stream(stream)), "segmla_copy_geometry")
+    return seg, pool
+
+
+def segmla_lse_merge(partial_o, partial_ml, out, lse=None, stream=None):
+    """partial_o fp32 [n_split, n_vec, d], partial_ml fp32 [n_split, n_vec, 2] (device tensors)."""
+    n_split, n_vec, d = partial_o.shape
+    import torch
+    dt = SEGMLA_F32 if out.dtype == torch.float32 else SEGMLA_BF16
+    _check(lib().segmla_lse_merge(_ptr(partial_o), _ptr(partial_ml), n_split, n_vec, d, _ptr(out), dt,
+                                  _ptr(lse), _stream(stream)), "segmla_lse_merge")
+
+
+def segmla_plan_pairs(plan, stream=None):
+    out = (ctypes.c_double * 2)()
+    _check(lib().segmla_plan_pairs(plan, out, _stream(stream)), "segmla_plan_pairs")
+    return float(out[0]), float(out[1])
+
+
+def segmla_ledger(f_front, r, f_back, h, h_local, T, n_protected, global_pairs=-1.0,
+                  local_pairs=-1.0):
+    out = (ctypes.c_double * 3)()
+    _check(lib().segmla_ledger(f_front, r, f_back, h, h_local, T, n_protected, global_pairs,
+                               local_pairs, out), "segmla_ledger")
+    return tuple(float(x) for x in out)
+
+
+def segmla_profile_enable(plan, enable=True):
+    _check(lib().segmla_profile_enable(plan, 1 if enable else 0), "segmla_profile_enable")
+
+
+def segmla_profile_read(plan):
+    """Accumulated ms per stage: (attention, split merge, epilogue, build), n_forward, n_build."""
+    ms = (ctypes.c_double * 4)()
+    nf, nb = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().segmla_profile_read(plan, ms, ctypes.byref(nf), ctypes.byref(nb)),
+           "segmla_profile_read")
+    return tuple(float(x) for x in ms), int(nf.value), int(nb.value)
+
+
+def segmla_plan_destroy(plan):
+    if plan:
+        lib().segmla_plan_destroy(plan)
+
+
+# ------------------------------------------------------------------ convenience
+_DT = {"f32": SEGMLA_F32, "bf16": SEGMLA_BF16, "e4m3": SEGMLA_E4M3_B128}
+
+
+class Plan:
+    """A plan plus its device workspace (torch uint8 tensor on the current GPU)."""
+
+    def __init__(self, cfg, kinds, lens, offsets, pool_rows, n_pool, head_is_global, split_keys=0,
+                 dirty_rows=()):
+        d_v = cfg["d_nope"] + cfg["d_rope"] if cfg["v_has_rope"] else cfg["d_nope"]
+        self.cfg, self.d_v = cfg, d_v
+        self.handle = segmla_plan_create(
+            kinds, lens, offsets, pool_rows, n_pool, cfg["n_heads"], head_is_global, cfg["d_nope"],
+            cfg["d_rope"], cfg["d_state"], cfg["v_has_rope"], cfg["rope_base"], cfg["softmax_scale"],
+            _DT[cfg["kv_dtype"]], _DT[cfg["dtype"]], split_keys, cfg["edge_rows"], cfg["tail_rows"],
+            cfg["budget_permille"], dirty_rows)
+        self.T, self.n_protected = segmla_plan_rows(self.handle)
+        self.workspace = None
+
+    def build(self, scores=None, stream=None):
+        import torch
+        nbytes = segmla_plan_workspace_bytes(self.handle)
+        if self.workspace is None or self.workspace.numel() < nbytes:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        segmla_plan_build(self.handle, self.workspace, scores, stream)
+
+    def forward(self, inp, out, z, lse=None, stream=None):
+        segmla_forward(self.handle, inp["q"], inp["kv"], inp["w"], out, z, inp.get("z_cached"),
+                       inp.get("kv_scale"), inp.get("kv_rope"), lse, stream)
+
+    def protected(self):
+        return segmla_copy_protected(self.handle, self.n_protected)
+
+    def geometry(self):
+        return segmla_copy_geometry(self.handle, self.T)
+
+    def pairs(self):
+        return segmla_plan_pairs(self.handle)
+
+    def close(self):
+        if self.handle:
+            segmla_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @classmethod
+    def for_inputs(cls, inp, split_keys=0):
+        return cls(inp["cfg"], inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"],
+                   inp["n_pool"], inp["head_is_global"], split_keys, inp["cfg"].get("dirty_rows", ()))

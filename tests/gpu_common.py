@@ -1,0 +1,94 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and the fp64
+oracle on exactly the same seeded inputs, and compare."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import segmla_oracle as O
+from segmented_attention_amd.segmla import Plan
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+
+
+def tol_of(cfg):
+    return TOL["e4m3"] if cfg["kv_dtype"] == "e4m3" else TOL[cfg["dtype"]]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class _Rows:
+    """Row-wise lazy host view of a device tensor (the oracle indexes q / Zc by row)."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, i):
+        return self.t[int(i)].double().cpu().numpy()
+
+
+def oracle_inputs(inp, lazy=False):
+    """The oracle's view of the generated inputs: stored values upcast exactly to fp64."""
+    d = {k: v for k, v in inp.items() if not torch.is_tensor(v)}
+    cfg = inp["cfg"]
+    if cfg["kv_dtype"] == "e4m3":
+        d["latent"] = O.e4m3_b128_values(inp["kv"].cpu().numpy(), inp["kv_scale"].cpu().numpy(),
+                                         inp["kv_rope"].double().cpu().numpy())
+    else:
+        d["latent"] = inp["kv"].double().cpu().numpy()
+    d["w"] = inp["w"].double().cpu().numpy()
+    d["scores"] = inp["scores"].cpu().numpy()
+    if lazy:
+        d["q"] = _Rows(inp["q"])
+        d["z_cached"] = _Rows(inp["z_cached"])
+    else:
+        d["q"] = inp["q"].double().cpu().numpy()
+        d["z_cached"] = inp["z_cached"].double().cpu().numpy()
+    return d
+
+
+def run_gpu(inp, split_keys=0, with_lse=True, plan=None):
+    """Plan + build + forward through the C ABI; outputs pre-filled with a NaN sentinel."""
+    cfg = inp["cfg"]
+    T, H = inp["T"], cfg["n_heads"]
+    own = plan is None
+    if own:
+        plan = Plan.for_inputs(inp, split_keys)
+        plan.build(inp["scores"])
+    dt = inp["q"].dtype
+    out = torch.full((T, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+    z = torch.full((T, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
+    plan.forward(inp, out, z, lse)
+    torch.cuda.synchronize()
+    return plan, out, z, lse
+
+
+def compare(cfg, ref, out, z, lse, zc_rows, rows=None):
+    """Assert parity of one forward against the oracle result `ref` (computed on `rows`)."""
+    tol = tol_of(cfg)
+    rows = ref["rows"] if rows is None else rows
+    o = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()
+    zz = z[torch.as_tensor(rows, device=z.device)].double().cpu().numpy()
+    comp = ref["computed"]
+    e_o = O.rel_err_rows(o[comp], ref["O"][comp])
+    assert np.all(np.isfinite(o[comp])), "non-finite merged output"
+    assert e_o.max() <= tol, "O max rel err %.3g > %.1g" % (e_o.max(), tol)
+    # Local heads outside A are never written to `out`
+    assert np.all(np.isnan(o[~comp])), "out written for a Local head outside A"
+    e_z = O.rel_err_rows(zz[comp], ref["Z"][comp])
+    assert e_z.max() <= tol, "Z max rel err %.3g > %.1g" % (e_z.max(), tol)
+    # replaced, never added: copied rows are bit-equal to the cached state
+    if (~comp).any():
+        np.testing.assert_array_equal(zz[~comp], ref["Z"][~comp])
+    if lse is not None:
+        ls = lse[torch.as_tensor(rows, device=lse.device)].double().cpu().numpy()
+        err = np.abs(ls[comp] - ref["lse"][comp])
+        lim = max(10 * tol, 1e-4) if cfg["dtype"] != "f32" else 1e-5
+        assert err.max() <= lim, "lse max abs err %.3g" % err.max()
+        assert np.all(np.isnan(ls[~comp]))
+    return float(e_o.max()), float(e_z.max())

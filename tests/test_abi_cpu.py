@@ -1,0 +1,257 @@
+"""C-ABI checks that need no GPU: exported symbols, host validation and error paths,
+host-side sizing of the protected set, and the analytic ledger.
+
+Every call here returns before any HIP call is made (validation happens first), so it
+runs on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import segmla_oracle as O
+from workload import CONFIGS, SMALL_CONFIGS, segment_table
+from workload.configs import FLASH_TAIL32K
+from workload.gen import pool_placement
+
+S = pytest.importorskip("segmented_attention_amd.segmla")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(S.LIB_PATH):
+        pytest.skip("libsegmla.so not built")
+    return S.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "segmla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(segmla_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    decl = _declared()
+    assert len(decl) >= 13
+    for name in decl:
+        assert hasattr(L, name), name
+    assert sorted(S.EXPORTED) == decl
+
+
+def test_abi_version_and_status_strings(L):
+    assert S.segmla_abi_version() == 1
+    for st in range(-9, 1):
+        assert S.segmla_status_string(st) not in ("", "unknown status")
+    assert S.segmla_status_string(-100) == "unknown status"
+
+
+def _create(cfg, **over):
+    kinds, lens, offsets = segment_table(cfg)
+    pr, n_pool = pool_placement(lens, "identity", cfg["seed"])
+    glob = np.zeros(cfg["n_heads"], np.uint8)
+    glob[cfg["global_heads"]] = 1
+    args = dict(kinds=kinds, lens=lens, offsets=offsets, pool_rows=pr, n_pool=n_pool,
+                n_heads=cfg["n_heads"], head_is_global=glob, d_nope=cfg["d_nope"],
+                d_rope=cfg["d_rope"], d_state=cfg["d_state"], v_has_rope=cfg["v_has_rope"],
+                kv_dtype=S._DT[cfg["kv_dtype"]], io_dtype=S._DT[cfg["dtype"]],
+                edge_rows=cfg["edge_rows"], tail_rows=cfg["tail_rows"],
+                budget_permille=cfg["budget_permille"])
+    args.update(over)
+    return S.segmla_plan_create(**args)
+
+
+def _status(cfg, **over):
+    try:
+        p = _create(cfg, **over)
+    except S.SegmlaError as e:
+        return e.status
+    S.segmla_plan_destroy(p)
+    return S.SEGMLA_OK
+
+
+@pytest.mark.parametrize("cfg", CONFIGS + SMALL_CONFIGS + [FLASH_TAIL32K], ids=lambda c: c["name"])
+def test_plan_rows_match_oracle(L, cfg):
+    """|A| = |F| + need is fixed on the host by geometry and the protection rule."""
+    p = _create(cfg)
+    try:
+        T, nA = S.segmla_plan_rows(p)
+        kinds, lens, offsets = segment_table(cfg)
+        g = O.geometry(kinds, lens, offsets, offsets, int(lens.sum()))
+        scores = np.random.default_rng(0).integers(0, 2**32, g["T"], dtype=np.uint64)
+        ref = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                               scores=scores)
+        assert T == g["T"] and nA == len(ref["A"])
+        assert S.segmla_plan_workspace_bytes(p) > 0
+    finally:
+        S.segmla_plan_destroy(p)
+
+
+def test_geometry_errors(L):
+    cfg = SMALL_CONFIGS[1]
+    kinds, lens, offsets = segment_table(cfg)
+    pr, n_pool = pool_placement(lens, "identity", 0)
+    bad_off = offsets.copy()
+    bad_off[2] += 1
+    assert _status(cfg, offsets=bad_off) == S.SEGMLA_E_GEOMETRY
+    first = offsets.copy()
+    first += 3
+    assert _status(cfg, offsets=first) == S.SEGMLA_E_GEOMETRY
+    zero_len = lens.copy()
+    zero_len[1] = 0
+    assert _status(cfg, lens=zero_len) == S.SEGMLA_E_GEOMETRY
+    bad_kind = kinds.copy()
+    bad_kind[0] = 7
+    assert _status(cfg, kinds=bad_kind) == S.SEGMLA_E_GEOMETRY
+    out_of_pool = pr.copy()
+    out_of_pool[-1] = n_pool - lens[-1] + 1
+    assert _status(cfg, pool_rows=out_of_pool) == S.SEGMLA_E_GEOMETRY
+    neg_pool = pr.copy()
+    neg_pool[0] = -1
+    assert _status(cfg, pool_rows=neg_pool) == S.SEGMLA_E_GEOMETRY
+    assert _status(cfg, n_pool=0) == S.SEGMLA_E_GEOMETRY
+    # aliased pool ranges are legal
+    alias = pr.copy()
+    alias[2] = alias[1]
+    assert _status(cfg, pool_rows=alias) == S.SEGMLA_OK
+
+
+def test_shape_dtype_protect_errors(L):
+    cfg = SMALL_CONFIGS[1]
+    assert _status(cfg, n_heads=0, head_is_global=np.zeros(0, np.uint8)) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, d_rope=63) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, d_state=0) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, v_has_rope=2) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, rope_base=1.0) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, softmax_scale=0.0) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, softmax_scale=float("nan")) == S.SEGMLA_E_SHAPE
+    glob = np.zeros(cfg["n_heads"], np.uint8)
+    glob[3] = 2
+    assert _status(cfg, head_is_global=glob) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, split_keys=100) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, split_keys=-2) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, kv_dtype=9) == S.SEGMLA_E_DTYPE
+    assert _status(cfg, io_dtype=S.SEGMLA_E4M3_B128) == S.SEGMLA_E_DTYPE
+    assert _status(cfg, io_dtype=S.SEGMLA_F32) == S.SEGMLA_E_UNSUPPORTED
+    assert _status(cfg, d_nope=256) == S.SEGMLA_E_UNSUPPORTED
+    assert _status(cfg, d_state=100) == S.SEGMLA_E_UNSUPPORTED
+    tiny = CONFIGS[0]
+    assert _status(tiny, io_dtype=S.SEGMLA_BF16) == S.SEGMLA_E_UNSUPPORTED
+    assert _status(tiny, d_nope=63) == S.SEGMLA_E_UNSUPPORTED
+    assert _status(cfg, edge_rows=-1) == S.SEGMLA_E_PROTECT
+    assert _status(cfg, tail_rows=-5) == S.SEGMLA_E_PROTECT
+    assert _status(cfg, budget_permille=1001) == S.SEGMLA_E_PROTECT
+    assert _status(cfg, budget_permille=-1) == S.SEGMLA_E_PROTECT
+    kinds, lens, _ = segment_table(cfg)
+    assert _status(cfg, dirty_rows=[int(lens.sum())]) == S.SEGMLA_E_PROTECT
+    assert _status(cfg, dirty_rows=[-1]) == S.SEGMLA_E_PROTECT
+    assert _status(cfg, dirty_rows=[3, 3, 5]) == S.SEGMLA_OK
+
+
+def test_dirty_rows_counted_once(L):
+    cfg = dict(SMALL_CONFIGS[1], budget_permille=0)
+    p = _create(cfg)
+    q = _create(cfg, dirty_rows=[100, 100, 101, 5])   # 100, 101 lie inside no forced range
+    try:
+        kinds, lens, offsets = segment_table(cfg)
+        g = O.geometry(kinds, lens, offsets, offsets, int(lens.sum()))
+        ref = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], 0, [100, 101, 5])
+        assert S.segmla_plan_rows(q)[1] == len(ref["A"])
+        assert S.segmla_plan_rows(q)[1] > S.segmla_plan_rows(p)[1]
+    finally:
+        S.segmla_plan_destroy(p)
+        S.segmla_plan_destroy(q)
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="passes fake device addresses; host-only check")
+def test_null_and_state_errors(L):
+    lib = S.lib()
+    h = ctypes.c_void_p()
+    assert lib.segmla_plan_create(None, None, None, 10, ctypes.byref(h)) == S.SEGMLA_E_NULL
+    cfg = SMALL_CONFIGS[4]
+    kinds, lens, offsets = segment_table(cfg)
+    g = O.geometry(kinds, lens, offsets, offsets, int(lens.sum()))
+    assert O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                            scores=np.zeros(g["T"]))["need"] > 0
+    p = _create(cfg)
+    try:
+        t = S.Tensors()
+        # not built yet -> state error, before any device work
+        assert lib.segmla_forward(p, ctypes.byref(t), None) == S.SEGMLA_E_STATE
+        assert lib.segmla_forward(None, ctypes.byref(t), None) == S.SEGMLA_E_NULL
+        # NULL / misaligned / short workspace, missing scores -> rejected before any HIP call
+        assert lib.segmla_plan_build(p, None, 0, None, None) == S.SEGMLA_E_WORKSPACE
+        assert lib.segmla_plan_build(p, ctypes.c_void_p(0x1008), 1 << 40, None, None) == \
+            S.SEGMLA_E_WORKSPACE
+        need = S.segmla_plan_workspace_bytes(p)
+        assert lib.segmla_plan_build(p, ctypes.c_void_p(0x10000), need - 1, None, None) == \
+            S.SEGMLA_E_WORKSPACE
+        assert lib.segmla_plan_build(p, ctypes.c_void_p(0x10000), need, None, None) == \
+            S.SEGMLA_E_PROTECT
+        buf = (ctypes.c_int32 * 4)()
+        assert lib.segmla_copy_protected(p, buf, 4, None) == S.SEGMLA_E_STATE
+        out = (ctypes.c_double * 2)()
+        assert lib.segmla_plan_pairs(p, out, None) == S.SEGMLA_E_STATE
+    finally:
+        S.segmla_plan_destroy(p)
+    S.segmla_plan_destroy(None)
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="passes fake device addresses; host-only check")
+def test_lse_merge_argument_errors(L):
+    lib = S.lib()
+    P = ctypes.c_void_p
+    assert lib.segmla_lse_merge(None, P(16), 1, 1, 4, P(16), 0, None, None) == S.SEGMLA_E_NULL
+    assert lib.segmla_lse_merge(P(16), P(16), 0, 1, 4, P(16), 0, None, None) == S.SEGMLA_E_SHAPE
+    assert lib.segmla_lse_merge(P(16), P(16), 1, 1, 5000, P(16), 0, None, None) == S.SEGMLA_E_SHAPE
+    assert lib.segmla_lse_merge(P(16), P(16), 1, 1, 4, P(16), 2, None, None) == S.SEGMLA_E_DTYPE
+    assert lib.segmla_lse_merge(P(16), P(16), 1, 0, 4, P(16), 0, None, None) == S.SEGMLA_OK
+
+
+def test_ledger_matches_printed_ceilings(L):
+    lg, ph, op = S.segmla_ledger(3, 37, 3, 64, 56, 1000, 250)
+    assert round(100 * lg, 2) == 75.29
+    assert ph == 56 * 750 / (64 * 1000)
+    assert np.isnan(op)
+    lg, _, _ = S.segmla_ledger(3, 55, 3, 128, 112, 10, 1)
+    assert round(100 * lg, 2) == 78.89
+    T = 274
+    A = _golden_tiny_a()
+    g_pairs, l_pairs = O.flops_pairs(T, A, 1, 7)
+    lg, ph, op = S.segmla_ledger(0, 1, 0, 8, 7, T, len(A), float(g_pairs), float(l_pairs))
+    ref = O.ledger(0, 1, 0, 8, 7, T, A)
+    assert np.allclose((lg, ph, op), ref, rtol=0, atol=1e-15)
+    with pytest.raises(S.SegmlaError):
+        S.segmla_ledger(0, 0, 0, 8, 7, T, 10)
+    with pytest.raises(S.SegmlaError):
+        S.segmla_ledger(3, 37, 3, 8, 9, T, 10)
+
+
+def _golden_tiny_a():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "tiny_fp32_protected_rows.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            a, b = map(int, line.split())
+            rows.extend(range(a, b))
+    return np.array(rows)
+
+
+def test_product_path_does_not_import_oracle():
+    """The package and the C sources never reference the oracle."""
+    pkg = os.path.join(ROOT, "segmented_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), os.path.join(dirpath, f)

@@ -1,0 +1,215 @@
+"""GPU parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Integer outputs (segment geometry, protected rows) must be bit-exact; merged head outputs
+and the projected state must match within 1e-5 (fp32), 2e-2 (bf16) or 6e-2 (E4M3 latent)
+as max over (row, head) of ||x - ref|| / ||ref||; Local-head rows outside A must equal the
+cached state bit for bit and `out` must stay untouched there.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import segmla_oracle as O
+from tests.gpu_common import compare, oracle_inputs, run_gpu, say, tol_of
+from workload import CONFIGS, SMALL_CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [CONFIGS[0]] + SMALL_CONFIGS
+
+
+def _full_case(cfg, pool="identity", split_keys=0):
+    say("case %s pool=%s split_keys=%d" % (cfg["name"], pool, split_keys))
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    plan, out, z, lse = run_gpu(inp, split_keys)
+    ref = O.layer_forward(oracle_inputs(inp))
+    # geometry and protected rows: bit-exact
+    seg, pool_row = plan.geometry()
+    np.testing.assert_array_equal(seg, ref["geom"]["seg_of_row"])
+    np.testing.assert_array_equal(pool_row, ref["geom"]["pool_of_row"])
+    np.testing.assert_array_equal(plan.protected(), ref["A"])
+    e = compare(cfg, ref, out, z, lse, None)
+    say("  max rel err O %.2e Z %.2e" % e)
+    g_pairs, l_pairs = plan.pairs()
+    rg, rl = O.flops_pairs(inp["T"], ref["A"], len(cfg["global_heads"]),
+                           cfg["n_heads"] - len(cfg["global_heads"]))
+    assert (g_pairs, l_pairs) == (rg, rl)
+    plan.close()
+    return inp, out, z
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c["name"])
+def test_parity_small(cfg):
+    _full_case(cfg)
+
+
+@pytest.mark.parametrize("cfg,pool", [(CONFIGS[0], "shuffled"), (CONFIGS[0], "aliased"),
+                                      (SMALL_CONFIGS[1], "shuffled"), (SMALL_CONFIGS[3], "aliased"),
+                                      (SMALL_CONFIGS[4], "shuffled")],
+                         ids=lambda x: x["name"] if isinstance(x, dict) else x)
+def test_parity_pool_placement(cfg, pool):
+    """Unused pool rows hold NaN: a kernel that reads outside its segments fails here."""
+    _full_case(cfg, pool=pool)
+
+
+@pytest.mark.parametrize("cfg,split", [(CONFIGS[0], 64), (SMALL_CONFIGS[0], 64),
+                                       (SMALL_CONFIGS[1], 256), (SMALL_CONFIGS[3], 192),
+                                       (SMALL_CONFIGS[4], 128)],
+                         ids=lambda x: x["name"] if isinstance(x, dict) else str(x))
+def test_parity_split_keys(cfg, split):
+    """Key-range splits + log-sum-exp merge give the same result as one pass."""
+    _full_case(cfg, split_keys=split)
+
+
+def test_pool_permutation_bitwise_and_determinism():
+    cfg = SMALL_CONFIGS[1]
+    say("case determinism %s" % cfg["name"])
+    inp = make_inputs(cfg, "cuda")
+    _, o1, z1, l1 = run_gpu(inp)
+    _, o2, z2, l2 = run_gpu(inp)
+    assert torch.equal(o1.nan_to_num(7.0), o2.nan_to_num(7.0))
+    assert torch.equal(z1, z2)
+    # the same request with its documents stored at other pool rows
+    perm = np.random.default_rng(0).permutation(len(inp["lens"]))
+    lens = inp["lens"]
+    pr = np.zeros(len(lens), dtype=np.int64)
+    cur = 5
+    for i in perm:
+        pr[i] = cur
+        cur += int(lens[i]) + 3
+    alt = dict(inp)
+    alt["pool_rows"], alt["n_pool"] = pr, cur
+    kv = torch.full((cur,) + tuple(inp["kv"].shape[1:]), float("nan"), dtype=inp["kv"].dtype,
+                    device="cuda")
+    zc = torch.full((cur,) + tuple(inp["z_cached"].shape[1:]), float("nan"),
+                    dtype=inp["z_cached"].dtype, device="cuda")
+    for i in range(len(lens)):
+        a, b, n = int(inp["pool_rows"][i]), int(pr[i]), int(lens[i])
+        kv[b:b + n] = inp["kv"][a:a + n]
+        zc[b:b + n] = inp["z_cached"][a:a + n]
+    alt["kv"], alt["z_cached"] = kv, zc
+    _, o3, z3, _ = run_gpu(alt)
+    assert torch.equal(o1.nan_to_num(7.0), o3.nan_to_num(7.0))
+    assert torch.equal(z1, z3)
+
+
+def test_poisoned_cache_inside_protected_rows():
+    """NaN in the cached state of rows of A never reaches the output (overwrite, not add)."""
+    cfg = SMALL_CONFIGS[1]
+    say("case poisoned cache %s" % cfg["name"])
+    inp = make_inputs(cfg, "cuda")
+    plan, o1, z1, _ = run_gpu(inp)
+    A = torch.as_tensor(plan.protected().astype(np.int64), device="cuda")
+    pois = dict(inp)
+    pois["z_cached"] = inp["z_cached"].clone()
+    pois["z_cached"][A] = float("nan")   # identity pool: pool row = request row
+    _, o2, z2, _ = run_gpu(pois)
+    assert torch.isfinite(z2.float()).all()
+    assert torch.equal(z1, z2)
+    plan.close()
+
+
+def test_exact_cache_identity():
+    """Cached Local state = the library's own fresh Local state on every row -> the replaced
+    state equals the all-rows recomputation (the projected-state sum is then exact)."""
+    cfg = dict(SMALL_CONFIGS[1], name="flash_small_all_rows")
+    say("case exact cache identity")
+    inp = make_inputs(cfg, "cuda")
+    full_cfg = dict(cfg, tail_rows=inp["T"])      # every row protected
+    full_inp = dict(inp, cfg=full_cfg)
+    _, _, z_full, _ = run_gpu(full_inp)
+    local = torch.as_tensor(np.nonzero(inp["head_is_global"] == 0)[0], device="cuda")
+    zc = z_full[:, local].contiguous()            # pool row = request row
+    inp2 = dict(inp, z_cached=zc)
+    _, _, z, _ = run_gpu(inp2)
+    ref_err = O.rel_err_rows(z.double().cpu().numpy(), z_full.double().cpu().numpy())
+    assert ref_err.max() <= 1e-6
+
+
+def test_standalone_lse_merge():
+    """segmla_lse_merge of per-key-range partials (computed here in fp64 on disjoint key
+    ranges) equals the oracle's dense attention over all keys."""
+    from segmented_attention_amd import segmla as S
+    cfg = CONFIGS[0]
+    say("case standalone lse merge")
+    inp = make_inputs(cfg, "cpu")
+    oi = oracle_inputs(inp)
+    g = O.geometry(oi["kinds"], oi["lens"], oi["offsets"], oi["pool_rows"], oi["n_pool"])
+    keys = O.relocated_keys(oi["latent"], g, cfg["d_nope"], cfg["d_rope"], cfg["rope_base"])
+    rows = np.array([0, 1, 5, 63, 64, 65, 150, 273])
+    q = oi["q"][rows][:, 0]                              # head 0
+    bounds = [0, 7, 64, 65, 200, 274]
+    ns = len(bounds) - 1
+    d = keys.shape[1]
+    po = np.zeros((ns, len(rows), d))
+    pm = np.zeros((ns, len(rows), 2))
+    for s in range(ns):
+        for i, t in enumerate(rows):
+            lo, hi = bounds[s], min(bounds[s + 1], t + 1)
+            if lo >= hi:
+                pm[s, i] = (-np.inf, 0.0)
+                continue
+            sc = q[i] @ keys[lo:hi].T
+            m = sc.max()
+            e = np.exp(sc - m)
+            pm[s, i] = (m, e.sum())
+            po[s, i] = e @ keys[lo:hi]
+    ref_o, ref_l = O.attend_rows(q[:, None], rows, keys, 1.0, d)
+    dev = "cuda"
+    out = torch.empty((len(rows), d), dtype=torch.float32, device=dev)
+    lse = torch.empty(len(rows), dtype=torch.float32, device=dev)
+    S.segmla_lse_merge(torch.tensor(po, dtype=torch.float32, device=dev),
+                       torch.tensor(pm, dtype=torch.float32, device=dev), out, lse)
+    torch.cuda.synchronize()
+    err = O.rel_err_rows(out.double().cpu().numpy(), ref_o[:, 0])
+    assert err.max() <= 1e-5
+    assert np.abs(lse.double().cpu().numpy() - ref_l[:, 0]).max() <= 1e-5
+    # a vector that saw no key at all
+    po0 = torch.zeros((2, 1, 8), device=dev)
+    pm0 = torch.tensor([[[-np.inf, 0.0]], [[-np.inf, 0.0]]], dtype=torch.float32, device=dev)
+    o0 = torch.full((1, 8), 5.0, device=dev)
+    l0 = torch.zeros(1, device=dev)
+    S.segmla_lse_merge(po0, pm0, o0, l0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, torch.zeros_like(o0)) and l0.item() == float("-inf")
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sample_rows(inp, A, rng, n_a=6, n_na=6, n_new=3):
+    lens, offs, kinds = inp["lens"], inp["offsets"], inp["kinds"]
+    T = inp["T"]
+    rows = {0, T - 1}
+    for i in rng.choice(len(lens), min(4, len(lens)), replace=False):
+        rows.add(int(offs[i]))
+        rows.add(int(offs[i] + lens[i] - 1))
+    new = [int(o + j) for o, n, k in zip(offs, lens, kinds) if k == 2 for j in range(n)]
+    rows.update(rng.choice(new, min(n_new, len(new)), replace=False).tolist())
+    rows.update(rng.choice(A, n_a, replace=False).tolist())
+    na = np.setdiff1d(np.arange(T), A)
+    if len(na):
+        rows.update(rng.choice(na, min(n_na, len(na)), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_parity_full_size_sampled(idx):
+    """Full workload sizes in the launch configuration the bench times: geometry and A
+    bit-exact on every row, outputs on sampled rows against the oracle."""
+    cfg = CONFIGS[idx]
+    say("case full-size %s" % cfg["name"])
+    inp = make_inputs(cfg, "cuda")
+    plan, out, z, lse = run_gpu(inp)
+    oi = oracle_inputs(inp, lazy=True)
+    g = O.geometry(oi["kinds"], oi["lens"], oi["offsets"], oi["pool_rows"], oi["n_pool"])
+    prot = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                            (), oi["scores"])
+    seg, pool_row = plan.geometry()
+    np.testing.assert_array_equal(seg, g["seg_of_row"])
+    np.testing.assert_array_equal(pool_row, g["pool_of_row"])
+    np.testing.assert_array_equal(plan.protected(), prot["A"])
+    rows = _sample_rows(inp, prot["A"], np.random.default_rng(idx))
+    ref = O.layer_forward(oi, rows=rows)
+    e = compare(cfg, ref, out, z, lse, None, rows=rows)
+    say("  %d sampled rows, max rel err O %.2e Z %.2e (tol %.0e)" % ((len(rows),) + e + (tol_of(cfg),)))
+    plan.close()
