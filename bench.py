@@ -119,18 +119,20 @@ def cpu_baseline(cfg_name, budget_s=20.0):
     in_a = np.zeros(T, bool)
     in_a[A] = True
     rng = np.random.default_rng(123)
-    # sample: rows spread over the request, protected and unprotected alike
+    # sample: rows spread uniformly over the request, protected and unprotected alike; the
+    # row count is calibrated so that the timed oracle run takes about `budget_s`
     cand = rng.permutation(T)
     n_g, n_l = len(cfg["global_heads"]), cfg["n_heads"] - len(cfg["global_heads"])
-    rows, est = [], 0.0
-    for t in cand[:4]:  # calibrate: time a few rows first
-        rows.append(int(t))
     t0 = time.perf_counter()
-    O.layer_forward(d, rows=rows)
-    first = time.perf_counter() - t0
-    per_row = first / len(rows)
-    n_more = int(max(0, budget_s - first) / max(per_row, 1e-3))
-    rows = sorted(int(t) for t in cand[:4 + n_more])
+    O.layer_forward(d, rows=[int(t) for t in cand[:4]])
+    t4 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.layer_forward(d, rows=[int(t) for t in cand[:36]])
+    t36 = time.perf_counter() - t0
+    per_row = max((t36 - t4) / 32.0, 1e-4)
+    fixed = max(t4 - 4 * per_row, 0.0)
+    n_rows = int(min(T, max(36, (budget_s - fixed) / per_row)))
+    rows = sorted(int(t) for t in cand[:n_rows])
     t0 = time.perf_counter()
     O.layer_forward(d, rows=rows)
     secs = time.perf_counter() - t0
