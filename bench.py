@@ -161,6 +161,9 @@ def main():
     ap.add_argument("--secondary", default="long_128k_bf16")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every GPU box has one "
@@ -169,6 +172,11 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.calib_copy_mib > 0:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = src.clone()
+        torch.cuda.synchronize()
+        del src, dst
     main_res = measure(args.workload, args.steps, args.warmup)
     sec = None
     if not args.no_secondary and args.secondary:

@@ -24,7 +24,7 @@ enum : uint8_t { kFlagForced = 1, kFlagCand = 2, kFlagIndexer = 4 };
 // streams. Stream F: rows of A with every head, flattened (a * H + h). Stream G: rows
 // outside A with the Global heads only (a * HG + g). Each stream is cut into tiles of
 // kTileQ consecutive qvecs; tiles [0, nF) are F tiles, [nF, nF + nG) are G tiles.
-constexpr int kTileQ = 64;
+constexpr int kTileQ = 128;
 
 struct TileMap {
   const int32_t* alist;   // [nA] rows of A, ascending

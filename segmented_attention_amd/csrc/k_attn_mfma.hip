@@ -2,11 +2,12 @@
 // the packed 512 + 64 latent (RedKnot-MLA paper: relocation paragraph, Eq. 5, and the fused
 // consumer paragraph; DeepSeek-V4 latent shape).
 //
-// Workgroup = 4 wavefronts (one per SIMD) = one tile of 64 query vectors (row, head); every
+// Workgroup = 8 wavefronts (two per SIMD) = one tile of 128 query vectors (row, head); every
 // query vector shares the same latent rows, so one 64-key tile of the canonical latent is
-// staged once in LDS and read by all four waves. Per wave: 16 query vectors (one per lane column of the
-// 16x16x32 MFMA), the query kept in VGPRs as the B operand (18 steps of 32 features) and
-// the output accumulator O^T [576 features x 16 query vectors] in 36 16x16 accumulators.
+// staged once in LDS and read by all eight waves. Per wave: 16 query vectors (one per lane
+// column of the 16x16x32 MFMA), the query kept in VGPRs as the B operand (18 steps of 32
+// features) and the output accumulator O^T [576 features x 16 query vectors] in 36 16x16
+// accumulators.
 //
 // Per segment i with keys visible from the tile: the query's RoPE part is rotated by
 // -rot_i (fp32 from an fp64-built table, rounded to bf16), S^T = K Q^T is computed against
@@ -19,10 +20,12 @@
 // per-segment (max, sum, partial output) statistics; key-range splits write their partials
 // for the standalone merge.
 //
-// LDS tile layout: 64 key rows x 72 16-byte chunks, chunk c of row r stored at
-// r*72 + (c ^ x(r)). With 64 banks (16 chunk slots per 256 bytes) the 16 rows a 16-lane
-// group reads for the QK^T operand land in 16 distinct slots, and the 8 rows x 2 chunks a
-// 32-lane half reads for the transposed PV operand do too.
+// LDS tile layout (72 KB): a nope region of 64 rows x 64 16-byte chunks (chunk c of row r at
+// r*64 + (c ^ fn(r))) followed by a RoPE region of 64 rows x 8 chunks (chunk c of row r at
+// r*8 + (c ^ fr(r))). With 64 banks (16 chunk slots per 256 bytes), the 16 consecutive rows a
+// 16-lane group reads for the QK^T operand and the 8 rows x 2 chunks a 32-lane half reads for
+// the transposed PV operand each land in 16 distinct slots. Each nope row is one
+// global->LDS instruction (64 lanes x 16 bytes), so the loader needs no per-chunk addresses.
 #include <cmath>
 #include "internal.h"
 
@@ -40,24 +43,48 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 576, kDN = 512;
 constexpr int kKT = 64;                          // keys per LDS tile
-constexpr int kRowChunks = kD / 8;               // 72
-constexpr int kTileChunks = kKT * kRowChunks;    // 4608
-constexpr int kTileBytes = kTileChunks * 16;     // 73728
-constexpr int kWaves = 4;
+constexpr int kRowBytes = kD * 2;                // 1152 bytes per bf16 latent row
+constexpr int kNRow = 1024;                      // LDS bytes per row, nope region
+constexpr int kRRow = 128;                       // LDS bytes per row, RoPE region
+constexpr int kRBase = kKT * kNRow;              // 65536
+constexpr int kTileBytes = kKT * (kNRow + kRRow);  // 73728
+constexpr int kWaves = 8;
+// per-lane slots for the segment-rotated RoPE query fragments (2 x 16 bytes per lane)
+constexpr int kQRBase = 2 * kTileBytes;          // 147456
+constexpr int kQRBytes = kWaves * 2 * 64 * 16;   // 16384
+constexpr int kLdsBytes = kQRBase + kQRBytes;    // 163840 = all of a CU's LDS
 constexpr int kThreads = 64 * kWaves;            // 512
-constexpr int kLoadsPerThread = kTileChunks / kThreads;  // 18
+static_assert(kWaves * 16 == kTileQ, "one 16-vector MFMA column block per wave");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;        // log2 units
 
-__device__ __forceinline__ int swz(int r) {
-  return ((r >> 4) & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2);
+__device__ __forceinline__ int bitof(int r, int k) { return (r >> k) & 1; }
+// nope-region swizzle: a bijection of row bits 0..3 onto the chunk-slot bits
+__device__ __forceinline__ int fn(int r) {
+  return bitof(r, 3) | (bitof(r, 0) << 1) | (bitof(r, 1) << 2) | (bitof(r, 2) << 3);
 }
-__device__ __forceinline__ int phys_chunk(int r, int c) { return r * kRowChunks + (c ^ swz(r)); }
+// RoPE-region swizzle (row bit 0 already selects the half of the 256-byte bank line)
+__device__ __forceinline__ int fr(int r) {
+  return bitof(r, 3) | (bitof(r, 1) << 1) | (bitof(r, 2) << 2);
+}
 
 __device__ __forceinline__ int wave_max_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
+}
+// max / sum over the 4 lanes {l, l^16, l^32, l^48} (the lanes holding one query vector)
+__device__ __forceinline__ float max4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
@@ -81,32 +108,37 @@ struct TileIt {
   int pos0;  // request position of row j0
 };
 
-// Stage one bf16 tile of up to 64 latent rows with direct global->LDS 16-byte loads. Rows
-// past nval repeat the last in-range row (finite data; their scores are masked).
-__device__ __forceinline__ void load_tile_bf16(char* buf, const __bf16* kv, int64_t row0, int nval,
-                                               int wave, int lane) {
+// Stage one bf16 tile of up to 64 latent rows with direct global->LDS 16-byte loads: one
+// instruction per nope row (wave w takes rows w, w+8, ...) and one for 8 RoPE rows per wave.
+// Rows past nval repeat the last in-range row (finite data; their scores are masked).
+__device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, int nval, int wave,
+                                               int lane) {
+  int lane16 = lane * 16;
+  asm volatile("" : "+v"(lane16));  // keep the per-row XORs in the loop (no hoisted copies)
 #pragma unroll
-  for (int n = 0; n < kLoadsPerThread; ++n) {
-    const int blk = n * kWaves + wave;     // 64 consecutive physical chunks per wave instruction
-    const int p = blk * 64 + lane;
-    const int r = p / kRowChunks;
-    const int c = (p - r * kRowChunks) ^ swz(r);
+  for (int n = 0; n < kKT / kWaves; ++n) {
+    const int r = wave + kWaves * n;
     const int rr = min(r, nval - 1);
-    const __bf16* src = kv + (row0 + rr) * (int64_t)kD + 8 * c;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + blk * 64 * 16), 16, 0, 0);
+    const char* src = tile_src + rr * kRowBytes + (lane16 ^ (fn(r) << 4));
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + r * kNRow), 16, 0, 0);
   }
+  const int r = 8 * wave + (lane >> 3);
+  const int rr = min(r, nval - 1);
+  const char* src = tile_src + rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4);
+  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + kRBase + wave * 1024), 16, 0, 0);
 }
 
 // Stage one E4M3 tile: codes * block scale -> bf16, RoPE dims copied, written in the same
-// swizzled layout as the bf16 tile.
+// layout as the bf16 tile.
 __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, const float* scales,
                                                const __bf16* rope, int64_t row0, int nval, int tid) {
-#pragma unroll 2
-  for (int n = 0; n < kLoadsPerThread; ++n) {
+#pragma unroll 3
+  for (int n = 0; n < kKT * 72 / kThreads; ++n) {
     const int idx = n * kThreads + tid;    // logical (row, chunk)
-    const int r = idx / kRowChunks, c = idx - r * kRowChunks;
+    const int r = idx / 72, c = idx - r * 72;
     const int64_t row = row0 + min(r, nval - 1);
     uint4 v;
+    int dst;
     if (c < kDN / 8) {
       const uint2 raw = *(const uint2*)(codes + row * kDN + 8 * c);
       const float sc = scales[row * (kDN / 128) + (c >> 4)];
@@ -116,10 +148,12 @@ __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) y[4 + k] = (__bf16)(e4m3_to_f32((raw.y >> (8 * k)) & 255u) * sc);
       v = *(const uint4*)y;
+      dst = r * kNRow + ((c ^ fn(r)) << 4);
     } else {
       v = *(const uint4*)(rope + row * 64 + 8 * (c - kDN / 8));
+      dst = kRBase + r * kRRow + (((c - kDN / 8) ^ fr(r)) << 4);
     }
-    *(uint4*)(buf + phys_chunk(r, c) * 16) = v;
+    *(uint4*)(buf + dst) = v;
   }
 }
 
@@ -128,8 +162,10 @@ __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, 
 template <bool VROPE, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int s_tmax[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the per-wave row maxima use the RoPE-query slots before any fragment is written there
+  int* s_tmax = (int*)(lds + kQRBase);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
   const int rank = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
   const int tile = a.work[rank];
@@ -152,37 +188,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 
   const float qk_scale = a.sigma * kLog2e;
   const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t : 0) * a.map.H + h) * kD;
-  // B operand of S^T = K Q^T: lane holds Q[qvec col][32 s + 8 g + 0..7]
-  bf16x8 qf[18];
+  // B operand of S^T = K Q^T: lane holds Q[qvec col][32 s + 8 g + 0..7]; the two RoPE
+  // steps (s = 16, 17) are rotated per segment and kept in this lane's LDS slots
+  bf16x8 qf[16];
+  char* const qslot = lds + kQRBase + wave * 2048 + lane * 16;
 #pragma unroll
-  for (int s = 0; s < 18; ++s) {
+  for (int s = 0; s < 16; ++s) {
     uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
     if (!valid) v = make_uint4(0, 0, 0, 0);
     qf[s] = *(bf16x8*)&v;
-  }
-  // per-lane LDS byte offsets (within a tile buffer, first 32-key block)
-  int kaddr_base[2], kaddr_flip[2];
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) {
-    const int krow = 8 * ((lane >> 2) & 3) + 4 * tau + (lane & 3);
-    const int x = swz(krow);
-    kaddr_base[tau] = (krow * kRowChunks + (g ^ (x & 3))) * 16;
-    kaddr_flip[tau] = ((x >> 2) & 1) * 64;  // s ^ x2 = s + x2 (s even), s - x2 (s odd)
-  }
-  int vaddr_base[4];
-  {
-    const int j = lane & 15;
-    const int r0 = 8 * g + (j >> 2);
-    const int x = swz(r0);
-    const int xp = (x >> 1) & 3, cofs = ((j & 3) >> 1) ^ (x & 1);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) vaddr_base[b] = (r0 * kRowChunks + 2 * (b ^ xp) + cofs) * 16 + 8 * (j & 1);
   }
   constexpr int NF = VROPE ? 36 : 32;  // 16-feature tiles of O^T
   floatx4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+
+  // Per-lane LDS byte offsets (first 32-key block, tile buffer 0).
+  // QK^T A operand, tile tau: row 16 tau + col, chunk 4 s + g. For s < 16 the swizzled
+  // chunk is 4 (s ^ (fn>>2)) + (g ^ (fn&3)): base qb[s & 3] + 256 (s >> 2); tau adds 16 rows.
+  int qb[4];
+  {
+    const int f = fn(col);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) qb[b] = (col * 64 + 4 * (b ^ (f >> 2)) + (g ^ (f & 3))) * 16;
+  }
+  const int qr0 = kRBase + (col * 8 + ((g) ^ fr(col))) * 16;      // s = 16
+  const int qr1 = kRBase + (col * 8 + ((4 + g) ^ fr(col))) * 16;  // s = 17
+  // PV A operand (V^T via transposing reads): source lane (g, j) supplies row 4 g + j/4
+  // (second read: +16 rows) and features 16 f + 4 (j%4) .. +3 -> chunk 2 f + cofs, half j&1.
+  const int pr = 4 * g + (col >> 2);
+  const int pcofs = (col & 3) >> 1;
+  const int pfn = fn(pr);
+  const int pb = (pr * 64 + (pcofs ^ (pfn & 1))) * 16 + 8 * (col & 1);
+  const int pfh = pfn >> 1;
+  const int pfr = fr(pr);
+  const int prb = kRBase + pr * 128 + 8 * (col & 1);
 
   // tile iterator over the key range [k_lo, k_hi), segment-aligned
   TileIt cur;
@@ -218,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     if constexpr (FP8)
       load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, row0, c.nval, tid);
     else
-      load_tile_bf16(buf, (const __bf16*)a.kv, row0, c.nval, wave, lane);
+      load_tile_bf16(buf, (const char*)a.kv + row0 * kRowBytes, c.nval, wave, lane);
   };
 
   const int half_r = a.d_rope / 2;  // 32
@@ -260,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
           y[2 * p] = (__bf16)(x0 * cs.x + x1 * cs.y);
           y[2 * p + 1] = (__bf16)(-x0 * cs.y + x1 * cs.x);
         }
-        qf[s] = y;
+        *(bf16x8*)(qslot + (s - 16) * 1024) = y;
       }
       prev_seg = cur.seg;
     }
@@ -270,42 +311,49 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
       const int pos_b = cur.pos0 + 32 * kb;
       if (32 * kb >= cur.nval || pos_b > t_wmax) continue;  // uniform per wave
-      // S^T for 32 keys as two 16-key tiles; tile tau row m reads key 8 (m/4) + 4 tau + m%4
-      // so lane (g, col) ends up with keys 8 g + 0..7 in k-slot order of the PV B operand.
+      const char* kbuf = buf + kb * 32 * kNRow;          // nope rows of this 32-key block
+      const char* rbuf = buf + kb * 32 * kRRow;          // RoPE rows (offset by kRBase)
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- S^T = K Q^T for keys 16 tau + m (two 16x16 tiles, one accumulation chain each)
+      const bf16x8 qr16 = *(const bf16x8*)qslot;
+      const bf16x8 qr17 = *(const bf16x8*)(qslot + 1024);
       floatx4 sacc[2];
-      sacc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      sacc[1] = sacc[0];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        // chunk 4 s + g of row krow sits at krow*72 + 4 (s ^ x2) + (g ^ (x & 3)), x = swz(krow):
-        // an even/odd base plus an immediate 64-byte step per s
-        const char* kb_even = buf + kaddr_base[tau] + 32 * kb * kRowChunks * 16;
-        const char* kb_odd = kb_even - kaddr_flip[tau];
-        kb_even += kaddr_flip[tau];
+        const char* kt = kbuf + tau * 16 * kNRow;
+        const char* rt = rbuf + tau * 16 * kRRow;
+        auto kaddr = [&](int s) -> const char* {
+          return s < 16 ? kt + qb[s & 3] + 256 * (s >> 2) : rt + (s == 16 ? qr0 : qr1);
+        };
+        floatx4 acc_s = floatx4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 ka = *(const bf16x8*)kaddr(0);
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
-          const char* p = ((s & 1) ? kb_odd : kb_even) + 64 * s;
-          const bf16x8 kf = *(const bf16x8*)p;
-          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[tau], 0, 0, 0);
+          bf16x8 na = ka;
+          if (s + 1 < 18) na = *(const bf16x8*)kaddr(s + 1);
+          const bf16x8 qv = s < 16 ? qf[s] : (s == 16 ? qr16 : qr17);
+          acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv, acc_s, 0, 0, 0);
+          ka = na;
+        }
+        sacc[tau] = acc_s;
+      }
+      floatx4 s0 = sacc[0], s1 = sacc[1];
+      __builtin_amdgcn_sched_barrier(0);
+      // lane (g, col): value (tau, i) = key 16 tau + 4 g + i of this block, query vector col
+      const bool need_mask = (pos_b + 31 > t) || (32 * kb + 32 > cur.nval);
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
+          if (pos_b + k0 > t || 32 * kb + k0 >= cur.nval) s0[i] = -INFINITY;
+          if (pos_b + k1 > t || 32 * kb + k1 >= cur.nval) s1[i] = -INFINITY;
         }
       }
-      // this lane: value (tau, i) = key 8 g + 4 tau + i of the 32-key block, qvec col
-      const bool need_mask = (pos_b + 31 > t) || (32 * kb + 32 > cur.nval);
-      float x[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kp = 8 * g + e;
-        float v = sacc[e >> 2][e & 3] * qk_scale;
-        if (need_mask && (pos_b + kp > t || 32 * kb + kp >= cur.nval)) v = -INFINITY;
-        x[e] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * qk_scale;
+      mx = max4(mx);
       const float m_new = fmaxf(m_run, mx);
-      const bool grow = m_new > m_run + kRescaleThreshold;
-      if (__ballot(grow) != 0ull) {  // wave-uniform rescale
+      if (__ballot(m_new > m_run + kRescaleThreshold) != 0ull) {  // wave-uniform rescale
         const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
@@ -316,26 +364,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       bf16x8 pf;
       float lsum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(x[e] - m_use);
-        lsum += p;
-        pf[e] = (__bf16)p;
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = exp2f(s0[i] * qk_scale - m_use);
+        const float p1 = exp2f(s1[i] * qk_scale - m_use);
+        lsum += p0 + p1;
+        pf[i] = (__bf16)p0;
+        pf[4 + i] = (__bf16)p1;
       }
       l_run += lsum;
-      // O^T += V^T P^T: A operand = V^T (16 features x 32 keys) by transposing reads; source
-      // lane j of group g supplies key 8 g + j/4 (+4) and features 16 f + 4 (j%4) .. +3.
-      // chunk 2 f + cofs of row r0 sits at r0*72 + 2 (f ^ x') + (cofs ^ x0), x' = (x>>1)&3:
-      // four bases (f mod 4) plus an immediate 128-byte step per 4 f; row r0 + 4 has the same x
-      const char* vb = buf + 32 * kb * kRowChunks * 16;
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- O^T += V^T P^T (A operand by two transposing reads: keys 4 g + 0..3, 16 + 4 g + 0..3)
+      const char* vbuf = buf + kb * 32 * kNRow;
+      int vx = pfh;
+      asm volatile("" : "+v"(vx));  // addresses computed per use, not hoisted into registers
+      auto vaddr = [&](int f) -> const char* {
+        if (f < 32) return vbuf + pb + ((f ^ vx) << 5);
+        const int c2 = 2 * (f - 32) + pcofs;
+        return rbuf + prb + ((c2 ^ pfr) << 4);
+      };
+      auto vtau1 = [&](int f) { return f < 32 ? 16 * kNRow : 16 * kRRow; };
+      bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(0));
+      bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(0) + vtau1(0)));
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const char* p = vb + vaddr_base[f & 3] + 128 * (f >> 2);
-        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(p + 4 * kRowChunks * 16));
-        const bf16x8 vt = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        bf16x4 nlo = vlo, nhi = vhi;
+        if (f + 1 < NF) {
+          nlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f + 1));
+          nhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f + 1) + vtau1(f + 1)));
+        }
+        const bf16x8 vt = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
         acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pf, acc[f], 0, 0, 0);
+        vlo = nlo;
+        vhi = nhi;
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (!has_next) break;
     cur = nxt;
@@ -354,8 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
         acc[f][i + 1] = x * cs.y + y * cs.x;
       }
   }
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum4(l_run);
   const int d_v = a.d_v;
   if (a.n_split > 1) {
     const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
@@ -387,7 +448,7 @@ namespace {
 template <bool VROPE, bool FP8>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
   static bool attr_set = false;
-  const int lds = 2 * kTileBytes;
+  const int lds = kLdsBytes;
   if (!attr_set) {
     hipError_t r = hipFuncSetAttribute((const void*)k_attn_mfma<VROPE, FP8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
