@@ -26,6 +26,22 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
+def attn_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "attn_mfma_flash32k_traffic.md")
+    src = os.path.join(ROOT, "segmented_attention_amd", "csrc", "k_attn_mfma.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof) if ": " in line and
+                      line.split(": ", 1)[0] in ("kernel_source_sha256", "attn_traffic_bytes_per_launch"))
+        if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(open(src, "rb").read()).hexdigest():
+            return None
+        return int(fields["attn_traffic_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -212,7 +228,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": attn_traffic() if r["cfg"]["name"] == "flash_32k_bf16" else None},
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                   for k, v in cpu.items() if k != "seconds"},
     }
