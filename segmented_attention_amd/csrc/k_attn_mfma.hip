@@ -3,11 +3,12 @@
 // consumer paragraph; DeepSeek-V4 latent shape).
 //
 // Workgroup = 8 wavefronts (two per SIMD) = one tile of 128 query vectors (row, head); every
-// query vector shares the same latent rows, so one 64-key tile of the canonical latent is
-// staged once in LDS and read by all eight waves. Per wave: 16 query vectors (one per lane
-// column of the 16x16x32 MFMA), the query kept in VGPRs as the B operand (18 steps of 32
-// features) and the output accumulator O^T [576 features x 16 query vectors] in 36 16x16
-// accumulators.
+// query vector shares the same latent rows, so each 32-key tile of the canonical latent is
+// staged once in LDS (a ring of three, loaded two tiles ahead) and read by all eight waves.
+// Per wave: 16 query vectors (one per lane column of the 16x16x32 MFMA). The query is the
+// MFMA B operand in 18 steps of 32 features: steps 0..11 stay in VGPRs, steps 12..17 live in
+// per-lane LDS slots (the last two hold the segment-rotated RoPE part). The output
+// accumulator O^T [576 features x 16 query vectors] is 36 16x16 fp32 accumulators.
 //
 // Per segment i with keys visible from the tile: the query's RoPE part is rotated by
 // -rot_i (fp32 from an fp64-built table, rounded to bf16), S^T = K Q^T is computed against
@@ -20,8 +21,8 @@
 // per-segment (max, sum, partial output) statistics; key-range splits write their partials
 // for the standalone merge.
 //
-// LDS tile layout (72 KB): a nope region of 64 rows x 64 16-byte chunks (chunk c of row r at
-// r*64 + (c ^ fn(r))) followed by a RoPE region of 64 rows x 8 chunks (chunk c of row r at
+// LDS tile layout (36 KB): a nope region of 32 rows x 64 16-byte chunks (chunk c of row r at
+// r*64 + (c ^ fn(r))) followed by a RoPE region of 32 rows x 8 chunks (chunk c of row r at
 // r*8 + (c ^ fr(r))). With 64 banks (16 chunk slots per 256 bytes), the 16 consecutive rows a
 // 16-lane group reads for the QK^T operand and the 8 rows x 2 chunks a 32-lane half reads for
 // the transposed PV operand each land in 16 distinct slots. Each nope row is one
@@ -40,24 +41,39 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+// The segment table is read-only for the whole launch: reading it through the constant
+// address space lets the compiler use scalar loads (no vector-memory round trip, and no
+// wait on the vector-memory counter that also tracks the tile prefetch).
+typedef const __attribute__((address_space(4))) SegDesc cseg_t;
 
 constexpr int kD = 576, kDN = 512;
-constexpr int kKT = 64;                          // keys per LDS tile
+constexpr int kKT = 32;                          // keys per LDS tile
+constexpr int kNBuf = 3;                         // LDS tile ring
 constexpr int kRowBytes = kD * 2;                // 1152 bytes per bf16 latent row
 constexpr int kNRow = 1024;                      // LDS bytes per row, nope region
 constexpr int kRRow = 128;                       // LDS bytes per row, RoPE region
-constexpr int kRBase = kKT * kNRow;              // 65536
-constexpr int kTileBytes = kKT * (kNRow + kRRow);  // 73728
+constexpr int kRBase = kKT * kNRow;              // 32768
+constexpr int kTileBytes = kKT * (kNRow + kRRow);  // 36864
 constexpr int kWaves = 8;
-// per-lane slots for the segment-rotated RoPE query fragments (2 x 16 bytes per lane)
-constexpr int kQRBase = 2 * kTileBytes;          // 147456
-constexpr int kQRBytes = kWaves * 2 * 64 * 16;   // 16384
-constexpr int kLdsBytes = kQRBase + kQRBytes;    // 163840 = all of a CU's LDS
 constexpr int kThreads = 64 * kWaves;            // 512
+// per-lane LDS slots for query steps kQReg..17 (16 bytes per lane per step)
+constexpr int kQReg = 12;                        // query steps kept in VGPRs
+constexpr int kQSlotStep = kThreads * 16;        // 8192 bytes per step
+constexpr int kQRBase = kNBuf * kTileBytes;      // 110592
+constexpr int kLdsBytes = kQRBase + (18 - kQReg) * kQSlotStep;  // 159744
 static_assert(kWaves * 16 == kTileQ, "one 16-vector MFMA column block per wave");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;        // log2 units
+#ifndef SEGMLA_QK_DEPTH
+#define SEGMLA_QK_DEPTH 2
+#endif
+#ifndef SEGMLA_PV_DEPTH
+#define SEGMLA_PV_DEPTH 3
+#endif
+constexpr int kQkDepth = SEGMLA_QK_DEPTH;        // K fragments in flight ahead of their MFMA
+constexpr int kPvDepth = SEGMLA_PV_DEPTH;        // V^T fragment pairs in flight
 
 __device__ __forceinline__ int bitof(int r, int k) { return (r >> k) & 1; }
 // nope-region swizzle: a bijection of row bits 0..3 onto the chunk-slot bits
@@ -102,39 +118,56 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 }
 
 struct TileIt {
-  int seg;   // segment index
-  int j0;    // first canonical row of the tile inside the segment
-  int nval;  // rows of the tile that are in range (1..64)
-  int pos0;  // request position of row j0
+  int seg;      // segment index
+  int j0;       // first canonical row of the tile inside the segment
+  int nval;     // rows of the tile that are in range (1..kKT)
+  int pos0;     // request position of row j0
+  int j_end;    // end of the segment's rows inside the key range
+  int64_t row0; // latent-pool row of row j0
 };
 
-// Stage one bf16 tile of up to 64 latent rows with direct global->LDS 16-byte loads: one
-// instruction per nope row (wave w takes rows w, w+8, ...) and one for 8 RoPE rows per wave.
-// Rows past nval repeat the last in-range row (finite data; their scores are masked).
+// One 64-lane global->LDS copy of 16 bytes per lane: lane L's bytes from sbase + voff land
+// at LDS byte address lds + 16 L. Issued from inline assembly so that the compiler does not
+// see an LDS write in flight: it would otherwise wait for the whole prefetch before every
+// later LDS read. The consumer orders it explicitly (s_waitcnt vmcnt, then a barrier).
+// M0 needs one wait state after the SALU write before the load reads it.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
+
+// Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte loads: one
+// instruction per nope row (wave w takes rows w, w+8, w+16, w+24) and, for waves 0..3, one
+// for 8 RoPE rows. Rows past nval repeat the last in-range row (finite; scores masked).
 __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, int nval, int wave,
                                                int lane) {
-  int lane16 = lane * 16;
-  asm volatile("" : "+v"(lane16));  // keep the per-row XORs in the loop (no hoisted copies)
+  const uint32_t base = lds_addr(buf);
 #pragma unroll
   for (int n = 0; n < kKT / kWaves; ++n) {
     const int r = wave + kWaves * n;
     const int rr = min(r, nval - 1);
-    const char* src = tile_src + rr * kRowBytes + (lane16 ^ (fn(r) << 4));
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + r * kNRow), 16, 0, 0);
+    dma16(tile_src + rr * kRowBytes, (lane * 16) ^ (fn(r) << 4), base + r * kNRow);
   }
-  const int r = 8 * wave + (lane >> 3);
-  const int rr = min(r, nval - 1);
-  const char* src = tile_src + rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4);
-  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(buf + kRBase + wave * 1024), 16, 0, 0);
+  if (wave < kKT / 8) {
+    const int r = 8 * wave + (lane >> 3);
+    const int rr = min(r, nval - 1);
+    dma16(tile_src, rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
+  }
 }
 
 // Stage one E4M3 tile: codes * block scale -> bf16, RoPE dims copied, written in the same
 // layout as the bf16 tile.
 __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, const float* scales,
                                                const __bf16* rope, int64_t row0, int nval, int tid) {
-#pragma unroll 3
-  for (int n = 0; n < kKT * 72 / kThreads; ++n) {
+#pragma unroll
+  for (int n = 0; n < (kKT * 72 + kThreads - 1) / kThreads; ++n) {
     const int idx = n * kThreads + tid;    // logical (row, chunk)
+    if (idx >= kKT * 72) break;
     const int r = idx / 72, c = idx - r * 72;
     const int64_t row = row0 + min(r, nval - 1);
     uint4 v;
@@ -162,8 +195,7 @@ __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, 
 template <bool VROPE, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  // the per-wave row maxima use the RoPE-query slots before any fragment is written there
-  int* s_tmax = (int*)(lds + kQRBase);
+  __shared__ int s_tmax[kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
@@ -179,6 +211,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   int t_max = s_tmax[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) t_max = max(t_max, s_tmax[w]);
+  t_max = __builtin_amdgcn_readfirstlane(t_max);
+  cseg_t* const sg = (cseg_t*)a.seg;
   int k_lo = 0, k_hi = t_max + 1;
   if (a.n_split > 1) {
     k_lo = split * a.split_keys;
@@ -188,23 +222,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 
   const float qk_scale = a.sigma * kLog2e;
   const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t : 0) * a.map.H + h) * kD;
-  // B operand of S^T = K Q^T: lane holds Q[qvec col][32 s + 8 g + 0..7]; the two RoPE
-  // steps (s = 16, 17) are rotated per segment and kept in this lane's LDS slots
-  bf16x8 qf[16];
-  char* const qslot = lds + kQRBase + wave * 2048 + lane * 16;
+  // B operand of S^T = K Q^T: lane holds Q[qvec col][32 s + 8 g + 0..7]
+  bf16x8 qf[kQReg];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
+  for (int s = 0; s < kQReg; ++s) {
     uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
     if (!valid) v = make_uint4(0, 0, 0, 0);
     qf[s] = *(bf16x8*)&v;
+  }
+  char* const qslot = lds + kQRBase + tid * 16;  // + (s - kQReg) * kQSlotStep
+#pragma unroll
+  for (int s = kQReg; s < 16; ++s) {
+    uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
+    if (!valid) v = make_uint4(0, 0, 0, 0);
+    *(uint4*)(qslot + (s - kQReg) * kQSlotStep) = v;
   }
   constexpr int NF = VROPE ? 36 : 32;  // 16-feature tiles of O^T
   floatx4 acc[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const int half_r = a.d_rope / 2;  // 32
 
-  // Per-lane LDS byte offsets (first 32-key block, tile buffer 0).
+  // Per-lane LDS byte offsets within a tile buffer.
   // QK^T A operand, tile tau: row 16 tau + col, chunk 4 s + g. For s < 16 the swizzled
   // chunk is 4 (s ^ (fn>>2)) + (g ^ (fn&3)): base qb[s & 3] + 256 (s >> 2); tau adds 16 rows.
   int qb[4];
@@ -225,197 +265,231 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   const int pfr = fr(pr);
   const int prb = kRBase + pr * 128 + 8 * (col & 1);
 
-  // tile iterator over the key range [k_lo, k_hi), segment-aligned
-  TileIt cur;
-  {
-    cur.seg = seg_of(a.seg, a.n_seg, k_lo);
-    const SegDesc sd = a.seg[cur.seg];
-    cur.j0 = k_lo - sd.offset;
-    cur.nval = min(kKT, min(sd.len, k_hi - sd.offset) - cur.j0);
-    cur.pos0 = sd.offset + cur.j0;
-  }
+  // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
+  auto first_tile = [&](TileIt& c) {
+    int lo = 0, hi = a.n_seg - 1;  // last segment starting at or before k_lo
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sg[mid].offset <= k_lo) lo = mid; else hi = mid - 1;
+    }
+    c.seg = lo;
+    const int off = sg[lo].offset, len = sg[lo].len;
+    c.j0 = k_lo - off;
+    c.j_end = min(len, k_hi - off);
+    c.nval = min(kKT, c.j_end - c.j0);
+    c.pos0 = k_lo;
+    c.row0 = sg[lo].pool_row + c.j0;
+  };
   auto advance = [&](const TileIt& c, TileIt& nx) -> bool {
-    const SegDesc sd = a.seg[c.seg];
-    const int j_end = min(sd.len, k_hi - sd.offset);
-    if (c.j0 + kKT < j_end) {
-      nx.seg = c.seg;
+    if (c.j0 + kKT < c.j_end) {
+      nx = c;
       nx.j0 = c.j0 + kKT;
-      nx.nval = min(kKT, j_end - nx.j0);
-      nx.pos0 = sd.offset + nx.j0;
+      nx.nval = min(kKT, c.j_end - nx.j0);
+      nx.pos0 = c.pos0 + kKT;
+      nx.row0 = c.row0 + kKT;
       return true;
     }
     if (c.seg + 1 >= a.n_seg) return false;
-    const SegDesc sn = a.seg[c.seg + 1];
-    if (sn.offset >= k_hi) return false;
+    const int off = sg[c.seg + 1].offset;
+    if (off >= k_hi) return false;
     nx.seg = c.seg + 1;
     nx.j0 = 0;
-    nx.nval = min(kKT, min(sn.len, k_hi - sn.offset));
-    nx.pos0 = sn.offset;
+    nx.j_end = min(sg[c.seg + 1].len, k_hi - off);
+    nx.nval = min(kKT, nx.j_end);
+    nx.pos0 = off;
+    nx.row0 = sg[c.seg + 1].pool_row;
     return true;
   };
   auto issue = [&](const TileIt& c, int b) {
     char* buf = lds + b * kTileBytes;
-    const int64_t row0 = a.seg[c.seg].pool_row + c.j0;
     if constexpr (FP8)
-      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, row0, c.nval, tid);
+      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, tid);
     else
-      load_tile_bf16(buf, (const char*)a.kv + row0 * kRowBytes, c.nval, wave, lane);
+      load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave, lane);
   };
-
-  const int half_r = a.d_rope / 2;  // 32
-  issue(cur, 0);
-  int prev_seg = -1;
-  for (int it = 0;; ++it) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    TileIt nxt;
-    const bool has_next = advance(cur, nxt);
-    if (has_next) issue(nxt, (it + 1) & 1);
-    if (cur.seg != prev_seg) {
-      if (VROPE && prev_seg >= 0) {
-        // move the accumulated output from segment prev_seg's RoPE frame to cur.seg's:
-        // lane holds features 16 f + 4 g + i, pairs (i, i+1) for even i
+  // q^r <- R(-rot_i) q^r from the stored query, into the slots of steps 16, 17
+  auto rotate_q = [&](int seg) {
 #pragma unroll
-        for (int f = 32; f < NF; ++f)
+    for (int s = 16; s < 18; ++s) {
+      uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
+      if (!valid) v = make_uint4(0, 0, 0, 0);
+      const bf16x8 x = *(bf16x8*)&v;
+      bf16x8 y;
 #pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const int k = 8 * (f - 32) + 2 * g + (i >> 1);
-            const float2 cs = a.stepcs[prev_seg * half_r + k];
-            const float x = acc[f][i], y = acc[f][i + 1];
-            acc[f][i] = x * cs.x - y * cs.y;
-            acc[f][i + 1] = x * cs.y + y * cs.x;
-          }
+      for (int p = 0; p < 4; ++p) {
+        const int k = 16 * (s - 16) + 4 * g + p;
+        const float2 cs = a.segcs[seg * half_r + k];
+        const float x0 = bf2f(x[2 * p]), x1 = bf2f(x[2 * p + 1]);
+        y[2 * p] = (__bf16)(x0 * cs.x + x1 * cs.y);
+        y[2 * p + 1] = (__bf16)(-x0 * cs.y + x1 * cs.x);
       }
-      // q^r <- R(-rot_i) q^r, from the stored query (features 512 + 32 (s-16) + 8 g + 0..7)
-#pragma unroll
-      for (int s = 16; s < 18; ++s) {
-        uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
-        if (!valid) v = make_uint4(0, 0, 0, 0);
-        const bf16x8 x = *(bf16x8*)&v;
-        bf16x8 y;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int k = 16 * (s - 16) + 4 * g + p;
-          const float2 cs = a.segcs[cur.seg * half_r + k];
-          const float x0 = bf2f(x[2 * p]), x1 = bf2f(x[2 * p + 1]);
-          y[2 * p] = (__bf16)(x0 * cs.x + x1 * cs.y);
-          y[2 * p + 1] = (__bf16)(-x0 * cs.y + x1 * cs.x);
-        }
-        *(bf16x8*)(qslot + (s - 16) * 1024) = y;
-      }
-      prev_seg = cur.seg;
+      *(bf16x8*)(qslot + (s - kQReg) * kQSlotStep) = y;
     }
-
-    const char* buf = lds + (it & 1) * kTileBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int pos_b = cur.pos0 + 32 * kb;
-      if (32 * kb >= cur.nval || pos_b > t_wmax) continue;  // uniform per wave
-      const char* kbuf = buf + kb * 32 * kNRow;          // nope rows of this 32-key block
-      const char* rbuf = buf + kb * 32 * kRRow;          // RoPE rows (offset by kRBase)
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- S^T = K Q^T for keys 16 tau + m (two 16x16 tiles, one accumulation chain each)
-      const bf16x8 qr16 = *(const bf16x8*)qslot;
-      const bf16x8 qr17 = *(const bf16x8*)(qslot + 1024);
-      floatx4 sacc[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const char* kt = kbuf + tau * 16 * kNRow;
-        const char* rt = rbuf + tau * 16 * kRRow;
-        auto kaddr = [&](int s) -> const char* {
-          return s < 16 ? kt + qb[s & 3] + 256 * (s >> 2) : rt + (s == 16 ? qr0 : qr1);
-        };
-        floatx4 acc_s = floatx4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 ka = *(const bf16x8*)kaddr(0);
-#pragma unroll
-        for (int s = 0; s < 18; ++s) {
-          bf16x8 na = ka;
-          if (s + 1 < 18) na = *(const bf16x8*)kaddr(s + 1);
-          const bf16x8 qv = s < 16 ? qf[s] : (s == 16 ? qr16 : qr17);
-          acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv, acc_s, 0, 0, 0);
-          ka = na;
-        }
-        sacc[tau] = acc_s;
-      }
-      floatx4 s0 = sacc[0], s1 = sacc[1];
-      __builtin_amdgcn_sched_barrier(0);
-      // lane (g, col): value (tau, i) = key 16 tau + 4 g + i of this block, query vector col
-      const bool need_mask = (pos_b + 31 > t) || (32 * kb + 32 > cur.nval);
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
-          if (pos_b + k0 > t || 32 * kb + k0 >= cur.nval) s0[i] = -INFINITY;
-          if (pos_b + k1 > t || 32 * kb + k1 >= cur.nval) s1[i] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                       fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * qk_scale;
-      mx = max4(mx);
-      const float m_new = fmaxf(m_run, mx);
-      if (__ballot(m_new > m_run + kRescaleThreshold) != 0ull) {  // wave-uniform rescale
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      bf16x8 pf;
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = exp2f(s0[i] * qk_scale - m_use);
-        const float p1 = exp2f(s1[i] * qk_scale - m_use);
-        lsum += p0 + p1;
-        pf[i] = (__bf16)p0;
-        pf[4 + i] = (__bf16)p1;
-      }
-      l_run += lsum;
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- O^T += V^T P^T (A operand by two transposing reads: keys 4 g + 0..3, 16 + 4 g + 0..3)
-      const char* vbuf = buf + kb * 32 * kNRow;
-      int vx = pfh;
-      asm volatile("" : "+v"(vx));  // addresses computed per use, not hoisted into registers
-      auto vaddr = [&](int f) -> const char* {
-        if (f < 32) return vbuf + pb + ((f ^ vx) << 5);
-        const int c2 = 2 * (f - 32) + pcofs;
-        return rbuf + prb + ((c2 ^ pfr) << 4);
-      };
-      auto vtau1 = [&](int f) { return f < 32 ? 16 * kNRow : 16 * kRRow; };
-      bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(0));
-      bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(0) + vtau1(0)));
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        bf16x4 nlo = vlo, nhi = vhi;
-        if (f + 1 < NF) {
-          nlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f + 1));
-          nhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f + 1) + vtau1(f + 1)));
-        }
-        const bf16x8 vt = {vlo[0], vlo[1], vlo[2], vlo[3], vhi[0], vhi[1], vhi[2], vhi[3]};
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pf, acc[f], 0, 0, 0);
-        vlo = nlo;
-        vhi = nhi;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (!has_next) break;
-    cur = nxt;
-  }
-
-  // restore the request phase of the RoPE part: R(+rot_last)
-  if (VROPE && prev_seg >= 0) {
+  };
+  auto frame_step = [&](int seg, const float2* table) {  // acc^r <- R(angle of table[seg]) acc^r
 #pragma unroll
     for (int f = 32; f < NF; ++f)
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         const int k = 8 * (f - 32) + 2 * g + (i >> 1);
-        const float2 cs = a.segcs[prev_seg * half_r + k];
+        const float2 cs = table[seg * half_r + k];
         const float x = acc[f][i], y = acc[f][i + 1];
         acc[f][i] = x * cs.x - y * cs.y;
         acc[f][i + 1] = x * cs.y + y * cs.x;
       }
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight
+  TileIt w0, w1, w2;
+  first_tile(w0);
+  bool v1 = advance(w0, w1);
+  issue(w0, 0);
+  if (v1) issue(w1, 1);
+  rotate_q(w0.seg);
+  int cb = 0;  // buffer of tile b
+  for (int b = 0;; ++b) {
+    // tile b resident (tile b+1 may still be in flight); every wave is done with tile b-1,
+    // whose buffer receives tile b+2
+    // (a wave has kKT/kWaves nope-row copies per tile in flight, plus one RoPE copy for the
+    // first kKT/8 waves; younger loads only make the wait stricter)
+    if (!FP8 && v1) {
+      if (wave < kKT / 8) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kKT / kWaves + 1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kKT / kWaves) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    const bool v2 = v1 && advance(w1, w2);
+    if (v2) issue(w2, cb == 0 ? 2 : cb - 1);
+    const char* buf = lds + cb * kTileBytes;
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- S^T = K Q^T for keys 16 tau + m (two 16x16 tiles, one accumulation chain each):
+    // 36 MFMAs alternating the tiles, K fragments read kQkDepth steps ahead (the issue order
+    // is pinned with scheduling groups so the reads stay ahead of their MFMAs)
+    floatx4 sacc[2];
+    {
+      auto kaddr = [&](int k) -> const char* {   // step k: tau = k & 1, s = k >> 1
+        const int tau = k & 1, s = k >> 1;
+        return s < 16 ? buf + qb[s & 3] + 256 * (s >> 2) + tau * 16 * kNRow
+                      : buf + (s == 16 ? qr0 : qr1) + tau * 16 * kRRow;
+      };
+      // query steps s >= kQReg come from the per-lane slots, read alongside the K fragment of
+      // step 2 s (kQkDepth steps ahead of its first use)
+      auto qread = [&](int k) { return (k & 1) == 0 && (k >> 1) >= kQReg; };
+      sacc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sacc[1] = sacc[0];
+      bf16x8 ring[kQkDepth], qring[2];
+#pragma unroll
+      for (int k = 0; k < kQkDepth; ++k) {
+        ring[k] = *(const bf16x8*)kaddr(k);
+        if (qread(k)) qring[(k >> 1) & 1] = *(const bf16x8*)(qslot + ((k >> 1) - kQReg) * kQSlotStep);
+      }
+#pragma unroll
+      for (int k = 0; k < 36; ++k) {
+        const bf16x8 kf = ring[k % kQkDepth];
+        const int s = k >> 1;
+        const bf16x8 qv = s < kQReg ? qf[s < kQReg ? s : 0] : qring[s & 1];
+        if (k + kQkDepth < 36) {
+          const int kn = k + kQkDepth;
+          ring[k % kQkDepth] = *(const bf16x8*)kaddr(kn);
+          if (qread(kn)) qring[(kn >> 1) & 1] = *(const bf16x8*)(qslot + ((kn >> 1) - kQReg) * kQSlotStep);
+        }
+        sacc[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv, sacc[k & 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth, 0);  // first reads (no query step yet)
+#pragma unroll
+      for (int k = 0; k < 36 - kQkDepth; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (qread(k + kQkDepth)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K + Q reads
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // K read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kQkDepth, 0);
+    }
+    floatx4 s0 = sacc[0], s1 = sacc[1];
+    __builtin_amdgcn_sched_barrier(0);
+    // lane (g, col): value (tau, i) = key 16 tau + 4 g + i of this tile, query vector col
+    const bool need_mask = (w0.pos0 + 31 > t) || (w0.nval < kKT);
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
+        if (w0.pos0 + k0 > t || k0 >= w0.nval) s0[i] = -INFINITY;
+        if (w0.pos0 + k1 > t || k1 >= w0.nval) s1[i] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * qk_scale;
+    mx = max4(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__ballot(m_new > m_run + kRescaleThreshold) != 0ull) {  // wave-uniform rescale
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) acc[f] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pf;
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // v_exp_f32 directly: results below 2^-126 flush to zero, irrelevant for probabilities
+      const float p0 = __builtin_amdgcn_exp2f(s0[i] * qk_scale - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(s1[i] * qk_scale - m_use);
+      lsum += p0 + p1;
+      pf[i] = (__bf16)p0;
+      pf[4 + i] = (__bf16)p1;
+    }
+    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T (A operand by two transposing reads: keys 4 g + 0..3, 16 + 4 g + 0..3)
+    {
+      int vx = pfh;
+      asm volatile("" : "+v"(vx));  // addresses computed per use, not hoisted into registers
+      auto vaddr = [&](int f) -> const char* {
+        if (f < 32) return buf + pb + ((f ^ vx) << 5);
+        const int c2 = 2 * (f - 32) + pcofs;
+        return buf + prb + ((c2 ^ pfr) << 4);
+      };
+      auto vtau1 = [&](int f) { return f < 32 ? 16 * kNRow : 16 * kRRow; };
+      bf16x4 lo[kPvDepth], hi[kPvDepth];
+#pragma unroll
+      for (int f = 0; f < kPvDepth; ++f) {
+        lo[f] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f));
+        hi[f] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f) + vtau1(f)));
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int r = f % kPvDepth;
+        const bf16x8 vt = {lo[r][0], lo[r][1], lo[r][2], lo[r][3], hi[r][0], hi[r][1], hi[r][2], hi[r][3]};
+        if (f + kPvDepth < NF) {
+          lo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f + kPvDepth));
+          hi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f + kPvDepth) + vtau1(f + kPvDepth)));
+        }
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pf, acc[f], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvDepth, 1);
+#pragma unroll
+      for (int f = 0; f < NF - kPvDepth; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPvDepth, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!v1) break;
+    if (w1.seg != w0.seg) {  // next tile starts a new segment
+      if (VROPE) frame_step(w0.seg, a.stepcs);
+      rotate_q(w1.seg);
+    }
+    w0 = w1;
+    w1 = w2;
+    v1 = v2;
+    cb = cb == kNBuf - 1 ? 0 : cb + 1;
   }
+
+  // restore the request phase of the RoPE part: R(+rot_last)
+  if (VROPE) frame_step(w0.seg, a.segcs);
   const float l_tot = sum4(l_run);
   const int d_v = a.d_v;
   if (a.n_split > 1) {
