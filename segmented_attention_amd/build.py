@@ -19,6 +19,10 @@ ARCH = "gfx950"
 SOURCES = ["segmla_host.hip", "k_plan.hip", "k_attn_f32.hip", "k_attn_mfma.hip", "k_merge.hip",
            "k_epilogue.hip"]
 
+# The attention kernel keeps the score MFMAs in VGPR form (its nope output accumulators live
+# in AGPRs, written by inline assembly), so it selects the VGPR MFMA form explicitly.
+SOURCE_FLAGS = {"k_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
@@ -26,7 +30,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE,
 
 def _compile(src, extra):
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -2,13 +2,15 @@
 // the packed 512 + 64 latent (RedKnot-MLA paper: relocation paragraph, Eq. 5, and the fused
 // consumer paragraph; DeepSeek-V4 latent shape).
 //
-// Workgroup = 8 wavefronts (two per SIMD) = one tile of 128 query vectors (row, head); every
-// query vector shares the same latent rows, so each 32-key tile of the canonical latent is
-// staged once in LDS (a ring of three, loaded two tiles ahead) and read by all eight waves.
-// Per wave: 16 query vectors (one per lane column of the 16x16x32 MFMA). The query is the
-// MFMA B operand in 18 steps of 32 features: steps 0..11 stay in VGPRs, steps 12..17 live in
-// per-lane LDS slots (the last two hold the segment-rotated RoPE part). The output
-// accumulator O^T [576 features x 16 query vectors] is 36 16x16 fp32 accumulators.
+// Workgroup = 4 wavefronts (one per SIMD, each with the whole 512-entry register file) = one
+// tile of 128 query vectors (row, head). Every query vector of the tile shares the same
+// latent rows, so each 32-key tile of the canonical latent is staged once in LDS (a ring of
+// three buffers) and read by all four waves. Per wave: 32 query vectors, one per lane column
+// of the 32x32x16 MFMA, so every K or V^T fragment read from LDS feeds a 32-wide product
+// (32 flops per LDS byte). The query is the MFMA B operand in 36 steps of 16 features: steps
+// 0..kQReg-1 stay in registers, the rest (including the four segment-rotated RoPE steps)
+// live in per-lane LDS slots. The output accumulator O^T [576 features x 32 query vectors]
+// is 18 32x32 fp32 accumulators.
 //
 // Per segment i with keys visible from the tile: the query's RoPE part is rotated by
 // -rot_i (fp32 from an fp64-built table, rounded to bf16), S^T = K Q^T is computed against
@@ -21,12 +23,22 @@
 // per-segment (max, sum, partial output) statistics; key-range splits write their partials
 // for the standalone merge.
 //
+// Register files: the 16 nope output tiles (256 values per lane) fill the AGPRs; their MFMAs
+// are issued from inline assembly with AGPR accumulators, everything else (query, scores,
+// RoPE output tiles) stays in VGPRs with the compiler's MFMAs in VGPR form. Hazards of the
+// assembly MFMAs are covered by hand: two wait states before each (operands written by the
+// vector ALU), twelve before the accumulators are read back after the loop.
+//
+// The key loop is software pipelined: while the softmax of tile i runs on the vector ALU,
+// the matrix core computes S^T of tile i+1; then O^T += V^T P^T for tile i. A wave therefore
+// holds two key tiles in LDS, and a third is in flight.
+//
 // LDS tile layout (36 KB): a nope region of 32 rows x 64 16-byte chunks (chunk c of row r at
 // r*64 + (c ^ fn(r))) followed by a RoPE region of 32 rows x 8 chunks (chunk c of row r at
-// r*8 + (c ^ fr(r))). With 64 banks (16 chunk slots per 256 bytes), the 16 consecutive rows a
-// 16-lane group reads for the QK^T operand and the 8 rows x 2 chunks a 32-lane half reads for
-// the transposed PV operand each land in 16 distinct slots. Each nope row is one
-// global->LDS instruction (64 lanes x 16 bytes), so the loader needs no per-chunk addresses.
+// r*8 + (c ^ fr(r))). With 64 banks (16 chunk slots per 256 bytes): the K operand read (16
+// consecutive rows, one chunk each, per 16 lanes) and the transposing V^T read (4 rows x 4
+// chunks per 32 lanes) both land in 16 distinct slots. Each nope row is one global->LDS
+// instruction (64 lanes x 16 bytes), so the loader needs no per-chunk addresses.
 #include <cmath>
 #include "internal.h"
 
@@ -38,9 +50,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 // The segment table is read-only for the whole launch: reading it through the constant
 // address space lets the compiler use scalar loads (no vector-memory round trip, and no
@@ -55,55 +66,92 @@ constexpr int kNRow = 1024;                      // LDS bytes per row, nope regi
 constexpr int kRRow = 128;                       // LDS bytes per row, RoPE region
 constexpr int kRBase = kKT * kNRow;              // 32768
 constexpr int kTileBytes = kKT * (kNRow + kRRow);  // 36864
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;            // 512
-// per-lane LDS slots for query steps kQReg..17 (16 bytes per lane per step)
-constexpr int kQReg = 12;                        // query steps kept in VGPRs
-constexpr int kQSlotStep = kThreads * 16;        // 8192 bytes per step
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;            // 256
+constexpr int kQSteps = kD / 16;                 // 36 query steps of 16 features
+#ifndef SEGMLA_QREG
+#define SEGMLA_QREG 24
+#endif
+constexpr int kQReg = SEGMLA_QREG;               // query steps kept in registers
+constexpr int kQSlotStep = kThreads * 16;        // 4096 bytes per step
 constexpr int kQRBase = kNBuf * kTileBytes;      // 110592
-constexpr int kLdsBytes = kQRBase + (18 - kQReg) * kQSlotStep;  // 159744
-static_assert(kWaves * 16 == kTileQ, "one 16-vector MFMA column block per wave");
+constexpr int kLdsBytes = kQRBase + (kQSteps - kQReg) * kQSlotStep;
+constexpr int kLoads = kKT / kWaves + 1;         // global->LDS copies per wave per tile
+static_assert(kWaves * 32 == kTileQ, "one 32-vector MFMA column block per wave");
+static_assert(kKT / 8 == kWaves, "one RoPE copy (8 rows) per wave");
+static_assert(kQReg <= 32, "the RoPE query steps live in LDS slots");
+static_assert(kLdsBytes + 64 <= 160 * 1024, "LDS budget");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;        // log2 units
 #ifndef SEGMLA_QK_DEPTH
-#define SEGMLA_QK_DEPTH 2
+#define SEGMLA_QK_DEPTH 3
 #endif
 #ifndef SEGMLA_PV_DEPTH
-#define SEGMLA_PV_DEPTH 3
+#define SEGMLA_PV_DEPTH 4
 #endif
 constexpr int kQkDepth = SEGMLA_QK_DEPTH;        // K fragments in flight ahead of their MFMA
-constexpr int kPvDepth = SEGMLA_PV_DEPTH;        // V^T fragment pairs in flight
+constexpr int kPvDepth = SEGMLA_PV_DEPTH;        // V^T fragments in flight
 
-__device__ __forceinline__ int bitof(int r, int k) { return (r >> k) & 1; }
-// nope-region swizzle: a bijection of row bits 0..3 onto the chunk-slot bits
-__device__ __forceinline__ int fn(int r) {
-  return bitof(r, 3) | (bitof(r, 0) << 1) | (bitof(r, 1) << 2) | (bitof(r, 2) << 3);
-}
-// RoPE-region swizzle (row bit 0 already selects the half of the 256-byte bank line)
-__device__ __forceinline__ int fr(int r) {
-  return bitof(r, 3) | (bitof(r, 1) << 1) | (bitof(r, 2) << 2);
-}
+// nope-region swizzle: a bijection on row bits 0..3 whose top two bits follow row bits 0..1
+__device__ __forceinline__ int fn(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// RoPE-region swizzle, a bijection on row bits 1..3 (row bit 0 selects the half of the
+// 256-byte bank line) whose top bit follows row bit 1
+__device__ __forceinline__ int fr(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ int wave_max_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
 }
-// max / sum over the 4 lanes {l, l^16, l^32, l^48} (the lanes holding one query vector)
-__device__ __forceinline__ float max4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// max / sum over the lanes l and l ^ 32 (the two lanes holding one query vector): the swap
+// returns (own, partner) in the low half and (partner, own) in the high half
+__device__ __forceinline__ float pair_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
-__device__ __forceinline__ float sum4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+__device__ __forceinline__ float pair_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+// Nope output tiles live in AGPRs ("a" constraints). Inside the key loop only inline
+// assembly touches them, so the register allocator keeps them there; vector-ALU work on them
+// goes through single-register operands.
+
+// acc += A B (32x32x16 bf16, fp32 accumulation); the s_nop gives the two wait states an
+// operand written by the vector ALU needs before the MFMA reads it
+__device__ __forceinline__ void mfma_agpr(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// acc *= alpha, register by register through one VGPR; the leading s_nops give the twelve
+// wait states an MFMA result needs before it is read
+__device__ __forceinline__ void rescale_agpr(floatx16& acc, float alpha) {
+  float e[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) e[i] = acc[i];
+  float tmp;
+#define SEGMLA_RS1(n) "v_accvgpr_read_b32 %16, %" #n "\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %" #n ", %16\n\t"
+  asm volatile("s_nop 7\n\ts_nop 3\n\t" SEGMLA_RS1(0) SEGMLA_RS1(1) SEGMLA_RS1(2) SEGMLA_RS1(3) SEGMLA_RS1(4)
+               SEGMLA_RS1(5) SEGMLA_RS1(6) SEGMLA_RS1(7) SEGMLA_RS1(8) SEGMLA_RS1(9) SEGMLA_RS1(10)
+               SEGMLA_RS1(11) SEGMLA_RS1(12) SEGMLA_RS1(13) SEGMLA_RS1(14) SEGMLA_RS1(15)
+               : "+a"(e[0]), "+a"(e[1]), "+a"(e[2]), "+a"(e[3]), "+a"(e[4]), "+a"(e[5]), "+a"(e[6]),
+                 "+a"(e[7]), "+a"(e[8]), "+a"(e[9]), "+a"(e[10]), "+a"(e[11]), "+a"(e[12]),
+                 "+a"(e[13]), "+a"(e[14]), "+a"(e[15]), "=&v"(tmp)
+               : "v"(alpha));
+#undef SEGMLA_RS1
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = e[i];
+}
+
+// twelve wait states after the last MFMA on the tiles, before they are read back
+__device__ __forceinline__ void settle_agpr(floatx16* acc) {
+  asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int f = 0; f < 16; ++f) asm volatile("" : "+a"(acc[f]));
+}
 
 // OCP E4M3 (float8_e4m3fn) decoding from the format: bias 7, subnormals m * 2^-9,
 // S.1111.111 = NaN, no infinity.
@@ -141,23 +189,25 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(const lds_char*)p;
 }
 
-// Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte loads: one
-// instruction per nope row (wave w takes rows w, w+8, w+16, w+24) and, for waves 0..3, one
-// for 8 RoPE rows. Rows past nval repeat the last in-range row (finite; scores masked).
-__device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, int nval, int wave,
-                                               int lane) {
+// Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte copies: one
+// per nope row (wave w takes rows w, w+4, ..., w+28) and one for 8 RoPE rows (rows 8w..8w+7).
+// Rows past nval repeat the last in-range row (finite; their scores are masked).
+__device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, int nval, int wave) {
   const uint32_t base = lds_addr(buf);
+  // lane id recomputed here (volatile, so not hoisted): per-lane offsets live only as long as
+  // the copies that use them, and are never spilled (a spill reload would wait on vmcnt, which
+  // also counts these copies)
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
 #pragma unroll
   for (int n = 0; n < kKT / kWaves; ++n) {
     const int r = wave + kWaves * n;
     const int rr = min(r, nval - 1);
     dma16(tile_src + rr * kRowBytes, (lane * 16) ^ (fn(r) << 4), base + r * kNRow);
   }
-  if (wave < kKT / 8) {
-    const int r = 8 * wave + (lane >> 3);
-    const int rr = min(r, nval - 1);
-    dma16(tile_src, rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
-  }
+  const int r = 8 * wave + (lane >> 3);
+  const int rr = min(r, nval - 1);
+  dma16(tile_src, rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
 }
 
 // Stage one E4M3 tile: codes * block scale -> bf16, RoPE dims copied, written in the same
@@ -165,9 +215,8 @@ __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, 
 __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, const float* scales,
                                                const __bf16* rope, int64_t row0, int nval, int tid) {
 #pragma unroll
-  for (int n = 0; n < (kKT * 72 + kThreads - 1) / kThreads; ++n) {
+  for (int n = 0; n < kKT * 72 / kThreads; ++n) {
     const int idx = n * kThreads + tid;    // logical (row, chunk)
-    if (idx >= kKT * 72) break;
     const int r = idx / 72, c = idx - r * 72;
     const int64_t row = row0 + min(r, nval - 1);
     uint4 v;
@@ -189,6 +238,7 @@ __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, 
     *(uint4*)(buf + dst) = v;
   }
 }
+static_assert(kKT * 72 % kThreads == 0, "whole E4M3 loader passes");
 
 }  // namespace
 
@@ -198,19 +248,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   __shared__ int s_tmax[kWaves];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, g = lane >> 4;
+  const int col = lane & 31, hf = lane >> 5;
   const int rank = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
   const int tile = a.work[rank];
   if (tile < 0 || tile >= a.map.nF + a.map.nG) return;  // uniform; the work list is a permutation
   int t = -1, h = 0;
-  const bool valid = tile_qvec(a.map, tile, wave * 16 + col, t, h);
+  const bool valid = tile_qvec(a.map, tile, wave * 32 + col, t, h);
   if (!valid) t = -1;
   const int t_wmax = wave_max_i(t);
   if (lane == 0) s_tmax[wave] = t_wmax;
   __syncthreads();
-  int t_max = s_tmax[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) t_max = max(t_max, s_tmax[w]);
+  int t_max = max(max(s_tmax[0], s_tmax[1]), max(s_tmax[2], s_tmax[3]));
   t_max = __builtin_amdgcn_readfirstlane(t_max);
   cseg_t* const sg = (cseg_t*)a.seg;
   int k_lo = 0, k_hi = t_max + 1;
@@ -222,48 +270,55 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 
   const float qk_scale = a.sigma * kLog2e;
   const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t : 0) * a.map.H + h) * kD;
-  // B operand of S^T = K Q^T: lane holds Q[qvec col][32 s + 8 g + 0..7]
+  // B operand of S^T = K Q^T, step s: lane holds Q[qvec col][16 s + 8 hf + 0..7]
   bf16x8 qf[kQReg];
 #pragma unroll
   for (int s = 0; s < kQReg; ++s) {
-    uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
+    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
     if (!valid) v = make_uint4(0, 0, 0, 0);
     qf[s] = *(bf16x8*)&v;
   }
   char* const qslot = lds + kQRBase + tid * 16;  // + (s - kQReg) * kQSlotStep
 #pragma unroll
-  for (int s = kQReg; s < 16; ++s) {
-    uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
+  for (int s = kQReg; s < 32; ++s) {
+    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
     if (!valid) v = make_uint4(0, 0, 0, 0);
     *(uint4*)(qslot + (s - kQReg) * kQSlotStep) = v;
   }
-  constexpr int NF = VROPE ? 36 : 32;  // 16-feature tiles of O^T
-  floatx4 acc[NF];
+  constexpr int NF = VROPE ? 18 : 16;  // 32-feature tiles of O^T
+  constexpr int NR = NF - 16;          // RoPE output tiles (VGPRs)
+  floatx16 acc[16], accr[NR > 0 ? NR : 1];  // nope tiles in AGPRs, RoPE tiles in VGPRs
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < 16; ++f)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[f][i] = 0.f;
+#pragma unroll
+  for (int f = 0; f < NR; ++f)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accr[f][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const int half_r = a.d_rope / 2;  // 32
 
-  // Per-lane LDS byte offsets within a tile buffer.
-  // QK^T A operand, tile tau: row 16 tau + col, chunk 4 s + g. For s < 16 the swizzled
-  // chunk is 4 (s ^ (fn>>2)) + (g ^ (fn&3)): base qb[s & 3] + 256 (s >> 2); tau adds 16 rows.
-  int qb[4];
-  {
-    const int f = fn(col);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) qb[b] = (col * 64 + 4 * (b ^ (f >> 2)) + (g ^ (f & 3))) * 16;
-  }
-  const int qr0 = kRBase + (col * 8 + ((g) ^ fr(col))) * 16;      // s = 16
-  const int qr1 = kRBase + (col * 8 + ((4 + g) ^ fr(col))) * 16;  // s = 17
-  // PV A operand (V^T via transposing reads): source lane (g, j) supplies row 4 g + j/4
-  // (second read: +16 rows) and features 16 f + 4 (j%4) .. +3 -> chunk 2 f + cofs, half j&1.
-  const int pr = 4 * g + (col >> 2);
-  const int pcofs = (col & 3) >> 1;
-  const int pfn = fn(pr);
-  const int pb = (pr * 64 + (pcofs ^ (pfn & 1))) * 16 + 8 * (col & 1);
-  const int pfh = pfn >> 1;
-  const int pfr = fr(pr);
-  const int prb = kRBase + pr * 128 + 8 * (col & 1);
+  // ---- per-lane LDS offsets inside a tile buffer
+  // K operand, step s (nope): row col, chunk 2 s + hf -> 2 s ^ (fn & 14) | (hf ^ (fn & 1))
+  const int fcol = fn(col), rcol = fr(col);
+  const int kbase = col * kNRow + 16 * (hf ^ (fcol & 1));
+  const int ksw0 = 16 * (fcol & 14);
+  // K operand, RoPE step 32 + j: row col, RoPE chunk 2 j + hf
+  const int krbase = kRBase + col * kRRow + 16 * (hf ^ (rcol & 1));
+  const int krsw0 = 16 * (rcol & 6);
+  // V^T operand (transposing reads): 16-lane group G, source lane j supplies key row
+  // 16 u + 4 (G >> 1) + (j >> 2) (+ 8 for the second read) and features
+  // 32 f + 16 (G & 1) + 4 (j & 3) .. + 3, i.e. chunk 4 f + cl, half j & 1.
+  const int G = lane >> 4, jj = lane & 15;
+  const int cl = 2 * (G & 1) + ((jj & 3) >> 1);
+  const int vrow = 4 * (G >> 1) + (jj >> 2);
+  const int vb0 = vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1));
+  const int vb1 = vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2));
+  const int vsw0 = 64 * (jj >> 2);
+  const int vr0 = kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1));
+  const int vr1 = kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2));
+  const int vrsw0 = 64 * ((jj >> 3) & 1);
 
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
   auto first_tile = [&](TileIt& c) {
@@ -305,19 +360,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     if constexpr (FP8)
       load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, tid);
     else
-      load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave, lane);
+      load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave);
   };
-  // q^r <- R(-rot_i) q^r from the stored query, into the slots of steps 16, 17
+  // q^r <- R(-rot_i) q^r from the stored query, into the slots of steps 32..35
   auto rotate_q = [&](int seg) {
 #pragma unroll
-    for (int s = 16; s < 18; ++s) {
-      uint4 v = *(const uint4*)(qrow + 32 * s + 8 * g);
+    for (int s = 32; s < 36; ++s) {
+      uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
       if (!valid) v = make_uint4(0, 0, 0, 0);
       const bf16x8 x = *(bf16x8*)&v;
       bf16x8 y;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int k = 16 * (s - 16) + 4 * g + p;
+        const int k = 8 * (s - 32) + 4 * hf + p;
         const float2 cs = a.segcs[seg * half_r + k];
         const float x0 = bf2f(x[2 * p]), x1 = bf2f(x[2 * p + 1]);
         y[2 * p] = (__bf16)(x0 * cs.x + x1 * cs.y);
@@ -326,180 +381,208 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       *(bf16x8*)(qslot + (s - kQReg) * kQSlotStep) = y;
     }
   };
-  auto frame_step = [&](int seg, const float2* table) {  // acc^r <- R(angle of table[seg]) acc^r
+  // acc^r <- R(angle of table[seg]) acc^r; O^T tile f, register i: feature
+  // 32 f + 8 (i >> 2) + 4 hf + (i & 3), so registers i, i + 1 (i even) hold one RoPE pair
+  auto frame_step = [&](int seg, const float2* table) {
 #pragma unroll
-    for (int f = 32; f < NF; ++f)
+    for (int f = 0; f < NR; ++f)
 #pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const int k = 8 * (f - 32) + 2 * g + (i >> 1);
+      for (int i = 0; i < 16; i += 2) {
+        const int k = 16 * f + 4 * (i >> 2) + 2 * hf + ((i & 3) >> 1);
         const float2 cs = table[seg * half_r + k];
-        const float x = acc[f][i], y = acc[f][i + 1];
-        acc[f][i] = x * cs.x - y * cs.y;
-        acc[f][i + 1] = x * cs.y + y * cs.x;
+        const float x = accr[f][i], y = accr[f][i + 1];
+        accr[f][i] = x * cs.x - y * cs.y;
+        accr[f][i + 1] = x * cs.y + y * cs.x;
       }
   };
 
-  // ---- prologue: tiles 0 and 1 in flight
+  // S^T of one tile (buffer nb) into sacc. With softmax work (sm != nullptr), that work is
+  // interleaved with the MFMAs: the matrix core computes the next tile's scores while the
+  // vector ALU finishes the current tile's probabilities.
+  auto qk_reads = [&](const char* buf, int ksw, int krsw, int k, bf16x8& kf) {
+    if (k < 32) {
+      const int s8 = k >> 3, sl = k & 7;
+      kf = *(const bf16x8*)(buf + kbase + ((32 * sl) ^ ksw) + 256 * s8);
+    } else {
+      kf = *(const bf16x8*)(buf + krbase + ((32 * (k - 32)) ^ krsw));
+    }
+  };
+
+  floatx16 S;
+  // S^T of one tile (buffer buf) into sacc, one MFMA per 16-feature step; the K fragment of
+  // step k + kQkDepth is read before the MFMA of step k, and hook(k) places a slice of
+  // vector-ALU work after it (program order is issue order: each step ends in a fence)
+  auto qk_tile = [&](const char* buf, floatx16& sacc, auto&& hook) {
+    int ksw = ksw0, krsw = krsw0;
+    asm volatile("" : "+v"(ksw), "+v"(krsw));  // addresses computed per use, not hoisted
+    bf16x8 ring[kQkDepth], qring[kQkDepth];
+#pragma unroll
+    for (int k = 0; k < kQkDepth; ++k) {
+      qk_reads(buf, ksw, krsw, k, ring[k]);
+      if (k >= kQReg) qring[k] = *(const bf16x8*)(qslot + (k - kQReg) * kQSlotStep);
+    }
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) {
+      const bf16x8 kf = ring[k % kQkDepth];
+      const bf16x8 qv = k < kQReg ? qf[k < kQReg ? k : 0] : qring[k % kQkDepth];
+      if (k + kQkDepth < kQSteps) {
+        const int kn = k + kQkDepth;
+        qk_reads(buf, ksw, krsw, kn, ring[k % kQkDepth]);
+        if (kn >= kQReg) qring[k % kQkDepth] = *(const bf16x8*)(qslot + (kn - kQReg) * kQSlotStep);
+      }
+      if (k == 0) {
+        const floatx16 zero = {};
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, zero, 0, 0, 0);
+      } else {
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, sacc, 0, 0, 0);
+      }
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 in flight, scores of tile 0
   TileIt w0, w1, w2;
   first_tile(w0);
   bool v1 = advance(w0, w1);
   issue(w0, 0);
   if (v1) issue(w1, 1);
   rotate_q(w0.seg);
-  int cb = 0;  // buffer of tile b
-  for (int b = 0;; ++b) {
-    // tile b resident (tile b+1 may still be in flight); every wave is done with tile b-1,
-    // whose buffer receives tile b+2
-    // (a wave has kKT/kWaves nope-row copies per tile in flight, plus one RoPE copy for the
-    // first kKT/8 waves; younger loads only make the wait stricter)
-    if (!FP8 && v1) {
-      if (wave < kKT / 8) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kKT / kWaves + 1) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kKT / kWaves) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+  if (!FP8 && v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk_tile(lds, S, [](int) {});
+  __builtin_amdgcn_sched_barrier(0);
+  int cb = 0;  // buffer of tile i
+  for (;;) {
+    // S = raw scores of tile i (w0, buffer cb). Tile i+1 (w1) becomes resident; every wave
+    // is done with tile i-1, whose buffer receives tile i+2.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    const int nb = cb == kNBuf - 1 ? 0 : cb + 1;
+    const int fb = nb == kNBuf - 1 ? 0 : nb + 1;
     const bool v2 = v1 && advance(w1, w2);
-    if (v2) issue(w2, cb == 0 ? 2 : cb - 1);
-    const char* buf = lds + cb * kTileBytes;
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- S^T = K Q^T for keys 16 tau + m (two 16x16 tiles, one accumulation chain each):
-    // 36 MFMAs alternating the tiles, K fragments read kQkDepth steps ahead (the issue order
-    // is pinned with scheduling groups so the reads stay ahead of their MFMAs)
-    floatx4 sacc[2];
-    {
-      auto kaddr = [&](int k) -> const char* {   // step k: tau = k & 1, s = k >> 1
-        const int tau = k & 1, s = k >> 1;
-        return s < 16 ? buf + qb[s & 3] + 256 * (s >> 2) + tau * 16 * kNRow
-                      : buf + (s == 16 ? qr0 : qr1) + tau * 16 * kRRow;
-      };
-      // query steps s >= kQReg come from the per-lane slots, read alongside the K fragment of
-      // step 2 s (kQkDepth steps ahead of its first use)
-      auto qread = [&](int k) { return (k & 1) == 0 && (k >> 1) >= kQReg; };
-      sacc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      sacc[1] = sacc[0];
-      bf16x8 ring[kQkDepth], qring[2];
+    if (v2) issue(w2, fb);
+    if (v1 && w1.seg != w0.seg) rotate_q(w1.seg);
+    // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
+    if (__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT)) != 0ull) {
 #pragma unroll
-      for (int k = 0; k < kQkDepth; ++k) {
-        ring[k] = *(const bf16x8*)kaddr(k);
-        if (qread(k)) qring[(k >> 1) & 1] = *(const bf16x8*)(qslot + ((k >> 1) - kQReg) * kQSlotStep);
+      for (int i = 0; i < 16; ++i) {
+        const int k = 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (w0.pos0 + k > t || k >= w0.nval) S[i] = -INFINITY;
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // softmax of tile i (online, log2 domain, lazy rescale), in slices that ride along the
+    // MFMAs of the next tile's scores: partial maxima, the running-max update, then one
+    // probability per step
+    bf16x8 pf[2];
+    float alpha = 1.f, m_use = 0.f, lsum = 0.f;
+    float pmx[4];
+    bool resc = false;
+    auto softmax_step = [&](int k) {
+      if (k < 4) {
+        pmx[k] = fmaxf(fmaxf(S[4 * k], S[4 * k + 1]), fmaxf(S[4 * k + 2], S[4 * k + 3]));
+      } else if (k == 4) {
+        const float mx = pair_max(fmaxf(fmaxf(pmx[0], pmx[1]), fmaxf(pmx[2], pmx[3])) * qk_scale);
+        const float m_new = fmaxf(m_run, mx);
+        // wave-uniform decision, taken without a branch
+        resc = __ballot(m_new > m_run + kRescaleThreshold) != 0ull;
+        const float a_new = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        alpha = resc ? a_new : 1.f;
+        m_run = resc ? m_new : m_run;
+        m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      } else if (k < 21) {
+        const int i = k - 5;
+        // v_exp_f32 directly: results below 2^-126 flush to zero, irrelevant for probabilities
+        const float p = __builtin_amdgcn_exp2f(S[i] * qk_scale - m_use);
+        lsum += p;
+        pf[i >> 3][i & 7] = (__bf16)p;
+      } else if (k == 21) {
+        l_run = l_run * alpha + lsum;
+      }
+    };
+    floatx16 Sn;
+    if (v1) {
+      qk_tile(lds + nb * kTileBytes, Sn, softmax_step);
+    } else {
 #pragma unroll
-      for (int k = 0; k < 36; ++k) {
-        const bf16x8 kf = ring[k % kQkDepth];
-        const int s = k >> 1;
-        const bf16x8 qv = s < kQReg ? qf[s < kQReg ? s : 0] : qring[s & 1];
-        if (k + kQkDepth < 36) {
-          const int kn = k + kQkDepth;
-          ring[k % kQkDepth] = *(const bf16x8*)kaddr(kn);
-          if (qread(kn)) qring[(kn >> 1) & 1] = *(const bf16x8*)(qslot + ((kn >> 1) - kQReg) * kQSlotStep);
+      for (int k = 0; k < 22; ++k) softmax_step(k);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (resc) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) rescale_agpr(acc[f], alpha);
+#pragma unroll
+      for (int f = 0; f < NR; ++f) accr[f] *= alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- O^T += V^T P^T for tile i: 2 key steps x NF feature tiles
+    {
+      const char* buf = lds + cb * kTileBytes;
+      int vsw = vsw0, vrsw = vrsw0;
+      asm volatile("" : "+v"(vsw), "+v"(vrsw));  // addresses computed per use, not hoisted
+      auto vread = [&](int n, bf16x4& lo, bf16x4& hi) {  // n = u * NF + f
+        const int u = n / NF, f = n % NF;
+        if (f < 16) {
+          const int f4 = f >> 2, fl = f & 3;
+          const char* p = buf + ((64 * fl) ^ vsw) + 256 * f4 + 16384 * u;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vb0));
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vb1 + 8192));
+        } else {
+          const char* p = buf + ((64 * (f - 16)) ^ vrsw) + 2048 * u;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vr0));
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vr1 + 1024));
         }
-        sacc[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv, sacc[k & 1], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, kQkDepth, 0);  // first reads (no query step yet)
-#pragma unroll
-      for (int k = 0; k < 36 - kQkDepth; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (qread(k + kQkDepth)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K + Q reads
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // K read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kQkDepth, 0);
-    }
-    floatx4 s0 = sacc[0], s1 = sacc[1];
-    __builtin_amdgcn_sched_barrier(0);
-    // lane (g, col): value (tau, i) = key 16 tau + 4 g + i of this tile, query vector col
-    const bool need_mask = (w0.pos0 + 31 > t) || (w0.nval < kKT);
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k0 = 4 * g + i, k1 = 16 + 4 * g + i;
-        if (w0.pos0 + k0 > t || k0 >= w0.nval) s0[i] = -INFINITY;
-        if (w0.pos0 + k1 > t || k1 >= w0.nval) s1[i] = -INFINITY;
-      }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * qk_scale;
-    mx = max4(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new > m_run + kRescaleThreshold) != 0ull) {  // wave-uniform rescale
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acc[f] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 pf;
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // v_exp_f32 directly: results below 2^-126 flush to zero, irrelevant for probabilities
-      const float p0 = __builtin_amdgcn_exp2f(s0[i] * qk_scale - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(s1[i] * qk_scale - m_use);
-      lsum += p0 + p1;
-      pf[i] = (__bf16)p0;
-      pf[4 + i] = (__bf16)p1;
-    }
-    l_run += lsum;
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O^T += V^T P^T (A operand by two transposing reads: keys 4 g + 0..3, 16 + 4 g + 0..3)
-    {
-      int vx = pfh;
-      asm volatile("" : "+v"(vx));  // addresses computed per use, not hoisted into registers
-      auto vaddr = [&](int f) -> const char* {
-        if (f < 32) return buf + pb + ((f ^ vx) << 5);
-        const int c2 = 2 * (f - 32) + pcofs;
-        return buf + prb + ((c2 ^ pfr) << 4);
       };
-      auto vtau1 = [&](int f) { return f < 32 ? 16 * kNRow : 16 * kRRow; };
       bf16x4 lo[kPvDepth], hi[kPvDepth];
 #pragma unroll
-      for (int f = 0; f < kPvDepth; ++f) {
-        lo[f] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f));
-        hi[f] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f) + vtau1(f)));
-      }
+      for (int n = 0; n < kPvDepth; ++n) vread(n, lo[n], hi[n]);
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int r = f % kPvDepth;
+      for (int n = 0; n < 2 * NF; ++n) {
+        const int r = n % kPvDepth;
         const bf16x8 vt = {lo[r][0], lo[r][1], lo[r][2], lo[r][3], hi[r][0], hi[r][1], hi[r][2], hi[r][3]};
-        if (f + kPvDepth < NF) {
-          lo[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vaddr(f + kPvDepth));
-          hi[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vaddr(f + kPvDepth) + vtau1(f + kPvDepth)));
-        }
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pf, acc[f], 0, 0, 0);
+        if (n + kPvDepth < 2 * NF) vread(n + kPvDepth, lo[r], hi[r]);
+        const int f = n % NF;
+        // (program order is issue order: the assembly MFMAs are ordered with the LDS reads)
+        if (f < 16) mfma_agpr(acc[f], vt, pf[n / NF]);
+        else accr[f - 16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[n / NF], accr[f - 16], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvDepth, 1);
-#pragma unroll
-      for (int f = 0; f < NF - kPvDepth; ++f) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kPvDepth, 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (!v1) break;
-    if (w1.seg != w0.seg) {  // next tile starts a new segment
-      if (VROPE) frame_step(w0.seg, a.stepcs);
-      rotate_q(w1.seg);
-    }
+    if (VROPE && w1.seg != w0.seg) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
+    S = Sn;
     w0 = w1;
     w1 = w2;
     v1 = v2;
-    cb = cb == kNBuf - 1 ? 0 : cb + 1;
+    cb = nb;
   }
 
+  settle_agpr(acc);
+  // whole-tile copies to VGPRs for the stores (element reads of a pinned AGPR tuple are not
+  // something the compiler can copy)
+  auto tile_vgpr = [&](int f) -> floatx16 {
+    floatx16 x = f < 16 ? acc[f < 16 ? f : 0] : accr[f < 16 ? 0 : f - 16];
+    asm volatile("" : "+v"(x));
+    return x;
+  };
   // restore the request phase of the RoPE part: R(+rot_last)
   if (VROPE) frame_step(w0.seg, a.segcs);
-  const float l_tot = sum4(l_run);
+  const float l_tot = pair_sum(l_run);
   const int d_v = a.d_v;
   if (a.n_split > 1) {
     const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
-    const int64_t v = (int64_t)tile * kTileQ + wave * 16 + col;
+    const int64_t v = (int64_t)tile * kTileQ + wave * 32 + col;
     float* po = a.part_o + ((int64_t)split * nvec + v) * d_v;
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      *(float4*)(po + 16 * f + 4 * g) = make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
-    if (g == 0) {
+    for (int f = 0; f < NF; ++f) {
+      const floatx16 x = tile_vgpr(f);
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *(float4*)(po + 32 * f + 8 * (i >> 2) + 4 * hf) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+    if (hf == 0) {
       float* pm = a.part_ml + ((int64_t)split * nvec + v) * 2;
       pm[0] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
       pm[1] = l_tot;
@@ -511,11 +594,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   __bf16* o = (__bf16*)a.out + ((int64_t)t * a.map.H + h) * d_v;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    bf16x4 y = {(__bf16)(acc[f][0] * inv), (__bf16)(acc[f][1] * inv), (__bf16)(acc[f][2] * inv),
-                (__bf16)(acc[f][3] * inv)};
-    *(bf16x4*)(o + 16 * f + 4 * g) = y;
+    const floatx16 x = tile_vgpr(f);
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      bf16x4 y = {(__bf16)(x[i] * inv), (__bf16)(x[i + 1] * inv), (__bf16)(x[i + 2] * inv),
+                  (__bf16)(x[i + 3] * inv)};
+      *(bf16x4*)(o + 32 * f + 8 * (i >> 2) + 4 * hf) = y;
+    }
   }
-  if (a.lse && g == 0) a.lse[(int64_t)t * a.map.H + h] = (m_run + log2f(l_tot)) * kLn2;
+  if (a.lse && hf == 0) a.lse[(int64_t)t * a.map.H + h] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 namespace {
