@@ -41,6 +41,7 @@
 // instruction (64 lanes x 16 bytes), so the loader needs no per-chunk addresses.
 #include <cmath>
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace segmla {
 
@@ -52,7 +53,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) char lds_char;
 // The segment table is read-only for the whole launch: reading it through the constant
 // address space lets the compiler use scalar loads (no vector-memory round trip, and no
 // wait on the vector-memory counter that also tracks the tile prefetch).
@@ -92,12 +92,6 @@ constexpr float kRescaleThreshold = 8.0f;        // log2 units
 #endif
 constexpr int kQkDepth = SEGMLA_QK_DEPTH;        // K fragments in flight ahead of their MFMA
 constexpr int kPvDepth = SEGMLA_PV_DEPTH;        // V^T fragments in flight
-
-// nope-region swizzle: a bijection on row bits 0..3 whose top two bits follow row bits 0..1
-__device__ __forceinline__ int fn(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-// RoPE-region swizzle, a bijection on row bits 1..3 (row bit 0 selects the half of the
-// 256-byte bank line) whose top bit follows row bit 1
-__device__ __forceinline__ int fr(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ int wave_max_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -174,31 +168,14 @@ struct TileIt {
   int64_t row0; // latent-pool row of row j0
 };
 
-// One 64-lane global->LDS copy of 16 bytes per lane: lane L's bytes from sbase + voff land
-// at LDS byte address lds + 16 L. Issued from inline assembly so that the compiler does not
-// see an LDS write in flight: it would otherwise wait for the whole prefetch before every
-// later LDS read. The consumer orders it explicitly (s_waitcnt vmcnt, then a barrier).
-// M0 needs one wait state after the SALU write before the load reads it.
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
-
 // Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte copies: one
 // per nope row (wave w takes rows w, w+4, ..., w+28) and one for 8 RoPE rows (rows 8w..8w+7).
 // Rows past nval repeat the last in-range row (finite; their scores are masked).
 __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, int nval, int wave) {
   const uint32_t base = lds_addr(buf);
-  // lane id recomputed here (volatile, so not hoisted): per-lane offsets live only as long as
-  // the copies that use them, and are never spilled (a spill reload would wait on vmcnt, which
-  // also counts these copies)
-  int lane;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  // lane id recomputed here: per-lane offsets live only as long as the copies that use them,
+  // and are never spilled (a spill reload would wait on vmcnt, which also counts these copies)
+  const int lane = lane_id();
 #pragma unroll
   for (int n = 0; n < kKT / kWaves; ++n) {
     const int r = wave + kWaves * n;
@@ -214,8 +191,8 @@ __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, 
 // layout as the bf16 tile.
 __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, const float* scales,
                                                const __bf16* rope, int64_t row0, int nval, int tid) {
-#pragma unroll
-  for (int n = 0; n < kKT * 72 / kThreads; ++n) {
+#pragma unroll 1
+  for (int n = 0; n < kKT * 72 / kThreads; ++n) {  // rolled: its registers stay few
     const int idx = n * kThreads + tid;    // logical (row, chunk)
     const int r = idx / 72, c = idx - r * 72;
     const int64_t row = row0 + min(r, nval - 1);
@@ -321,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   const int vrsw0 = 64 * ((jj >> 3) & 1);
 
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
-  auto first_tile = [&](TileIt& c) {
+  auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
     int lo = 0, hi = a.n_seg - 1;  // last segment starting at or before k_lo
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -335,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     c.pos0 = k_lo;
     c.row0 = sg[lo].pool_row + c.j0;
   };
-  auto advance = [&](const TileIt& c, TileIt& nx) -> bool {
+  auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) -> bool {
     if (c.j0 + kKT < c.j_end) {
       nx = c;
       nx.j0 = c.j0 + kKT;
@@ -355,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     nx.row0 = sg[c.seg + 1].pool_row;
     return true;
   };
-  auto issue = [&](const TileIt& c, int b) {
+  auto issue = [&](const TileIt& c, int b) __attribute__((always_inline)) {
     char* buf = lds + b * kTileBytes;
     if constexpr (FP8)
       load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, tid);
@@ -363,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave);
   };
   // q^r <- R(-rot_i) q^r from the stored query, into the slots of steps 32..35
-  auto rotate_q = [&](int seg) {
+  auto rotate_q = [&](int seg) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 32; s < 36; ++s) {
       uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
@@ -383,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   };
   // acc^r <- R(angle of table[seg]) acc^r; O^T tile f, register i: feature
   // 32 f + 8 (i >> 2) + 4 hf + (i & 3), so registers i, i + 1 (i even) hold one RoPE pair
-  auto frame_step = [&](int seg, const float2* table) {
+  auto frame_step = [&](int seg, const float2* table) __attribute__((always_inline)) {
 #pragma unroll
     for (int f = 0; f < NR; ++f)
 #pragma unroll
@@ -399,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // S^T of one tile (buffer nb) into sacc. With softmax work (sm != nullptr), that work is
   // interleaved with the MFMAs: the matrix core computes the next tile's scores while the
   // vector ALU finishes the current tile's probabilities.
-  auto qk_reads = [&](const char* buf, int ksw, int krsw, int k, bf16x8& kf) {
+  auto qk_reads = [&](const char* buf, int ksw, int krsw, int k, bf16x8& kf) __attribute__((always_inline)) {
     if (k < 32) {
       const int s8 = k >> 3, sl = k & 7;
       kf = *(const bf16x8*)(buf + kbase + ((32 * sl) ^ ksw) + 256 * s8);
@@ -412,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // S^T of one tile (buffer buf) into sacc, one MFMA per 16-feature step; the K fragment of
   // step k + kQkDepth is read before the MFMA of step k, and hook(k) places a slice of
   // vector-ALU work after it (program order is issue order: each step ends in a fence)
-  auto qk_tile = [&](const char* buf, floatx16& sacc, auto&& hook) {
+  auto qk_tile = [&](const char* buf, floatx16& sacc, auto&& hook) __attribute__((always_inline)) {
     int ksw = ksw0, krsw = krsw0;
     asm volatile("" : "+v"(ksw), "+v"(krsw));  // addresses computed per use, not hoisted
     bf16x8 ring[kQkDepth], qring[kQkDepth];
@@ -480,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     float alpha = 1.f, m_use = 0.f, lsum = 0.f;
     float pmx[4];
     bool resc = false;
-    auto softmax_step = [&](int k) {
+    auto softmax_step = [&](int k) __attribute__((always_inline)) {
       if (k < 4) {
         pmx[k] = fmaxf(fmaxf(S[4 * k], S[4 * k + 1]), fmaxf(S[4 * k + 2], S[4 * k + 3]));
       } else if (k == 4) {
@@ -522,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       const char* buf = lds + cb * kTileBytes;
       int vsw = vsw0, vrsw = vrsw0;
       asm volatile("" : "+v"(vsw), "+v"(vrsw));  // addresses computed per use, not hoisted
-      auto vread = [&](int n, bf16x4& lo, bf16x4& hi) {  // n = u * NF + f
+      auto vread = [&](int n, bf16x4& lo, bf16x4& hi) __attribute__((always_inline)) {  // n = u * NF + f
         const int u = n / NF, f = n % NF;
         if (f < 16) {
           const int f4 = f >> 2, fl = f & 3;
@@ -562,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   settle_agpr(acc);
   // whole-tile copies to VGPRs for the stores (element reads of a pinned AGPR tuple are not
   // something the compiler can copy)
-  auto tile_vgpr = [&](int f) -> floatx16 {
+  auto tile_vgpr = [&](int f) __attribute__((always_inline)) -> floatx16 {
     floatx16 x = f < 16 ? acc[f < 16 ? f : 0] : accr[f < 16 ? 0 : f - 16];
     asm volatile("" : "+v"(x));
     return x;

@@ -4,6 +4,7 @@
 // head's slice of the bias-free first output projection. On rows outside A the Local heads'
 // slots receive the cached contribution Zc[pool_row(t)] unchanged: replaced, never added to.
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace segmla {
 
@@ -69,89 +70,165 @@ __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
 }
 
 // ------------------------------------------------------------------------ bf16 path
-// Workgroup = (head, 64 rows of its list) x all d_state columns. U (64 x d_v, RoPE part
-// de-rotated in fp32, rounded to bf16) is staged in LDS with a 16-byte row pad so the
-// MFMA A-operand reads of 32 rows hit distinct banks; W_h fragments stream from global
-// (the slice is shared by all row tiles of the head and stays in L2). 4 waves, each owns
-// d_state/4 columns; MFMA 32x32x16 bf16 with fp32 accumulation.
-constexpr int kEpiRows = 64;
-constexpr int kEpiDv = 576;
-constexpr int kEpiChunks = kEpiDv / 8;       // 16-byte chunks per U row
-constexpr int kEpiStride = kEpiChunks + 1;   // padded row stride in chunks
+// Workgroup = (head h, 128 rows of its list) x all d_state columns, 4 waves (one per SIMD).
+// U (128 x d_v) is staged in LDS in the packed-latent tile layout (lds_tile.h) by
+// global->LDS copies, one per nope row and one per 8 RoPE rows, all in flight at once; the
+// RoPE part is then de-rotated in place by R(-t) (fp32, rounded to bf16). The product is
+// computed transposed, Z^T = W_h U^T, with MFMA 32x32x16 bf16 (fp32 accumulation): the A
+// operand (W_h rows) streams from L2 with a two-step register prefetch, the B operand (U^T,
+// 16 consecutive rows x one chunk per 16 lanes: conflict-free) comes from LDS. Wave w owns the
+// 32-column blocks w, w + 4, ..., four at a time (4 x 4 accumulators of 16 values = the 256
+// AGPRs). A lane's accumulator holds 4 consecutive columns of one row, stored as one 8-byte
+// write.
+constexpr int kEpiRows = 128;
+constexpr int kEpiNRow = 1024;                    // LDS bytes per row, nope region
+constexpr int kEpiRBase = kEpiRows * kEpiNRow;    // RoPE region (128 rows x 128 bytes)
+constexpr int kEpiRowIds = kEpiRBase + kEpiRows * 128;  // request row of each tile row
+constexpr int kEpiLds = kEpiRowIds + kEpiRows * 4;      // 147968 bytes
+constexpr int kEpiPf = 2;                         // W prefetch depth in k-steps (divides d_v / 16)
 
 __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
-  extern __shared__ __attribute__((aligned(16))) uint4 lds_u[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __attribute__((aligned(16))) char lds_u[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   EpiTile et = epi_tile(e, blockIdx.x, kEpiRows);
   const int h = et.h;
   const int n_here = min(kEpiRows, et.n_rows - et.r0);
-  const int d_v = e.d_v, chunks = d_v / 8, half_r = e.d_rope / 2;
+  const int d_v = e.d_v, half_r = e.d_rope / 2;
+  const bool rope = e.v_has_rope != 0;  // d_v = 576 (else 512: nope only)
+  const int64_t hstride = (int64_t)d_v * 2;
+  const char* outb = (const char*)e.out + (int64_t)h * hstride;
+  // request rows of the tile first (rows past n_here repeat the last row: finite data, outputs
+  // not stored), so that no vector load is waited for while copies are in flight
+  int* const row_id = (int*)(lds_u + kEpiRowIds);
+  if (tid < kEpiRows) row_id[tid] = epi_row(et, et.r0 + min(tid, n_here - 1));
+  __syncthreads();
   // stage U
-  for (int i = tid; i < kEpiRows * chunks; i += 256) {
-    const int r = i / chunks, c = i - r * chunks;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < n_here) {
-      const int t = epi_row(et, et.r0 + r);
-      const __bf16* src = (const __bf16*)e.out + ((int64_t)t * e.H + h) * d_v + 8 * c;
-      v = *(const uint4*)src;
-      if (e.v_has_rope && 8 * c >= e.d_nope) {
-        const __bf16* x = (const __bf16*)&v;
-        __bf16 y[8];
-        const int k0 = (8 * c - e.d_nope) / 2;
-        for (int p = 0; p < 4; ++p) {
-          float2 cs = e.rowcs[(int64_t)t * half_r + k0 + p];
-          float a0 = (float)(x[2 * p]), a1 = (float)(x[2 * p + 1]);
-          y[2 * p] = (__bf16)(a0 * cs.x + a1 * cs.y);
-          y[2 * p + 1] = (__bf16)(-a0 * cs.y + a1 * cs.x);
-        }
-        v = *(const uint4*)y;
+  {
+    const uint32_t base = lds_addr(lds_u);
+    const int lane = lane_id();
+    for (int n = 0; n < kEpiRows / 4; ++n) {
+      const int r = wave + 4 * n;
+      const int t = __builtin_amdgcn_readfirstlane(row_id[r]);
+      dma16(outb + (int64_t)t * e.H * hstride, (lane * 16) ^ (fn(r) << 4), base + r * kEpiNRow);
+    }
+    if (rope) {
+      for (int m = 0; m < kEpiRows / 32; ++m) {  // 8 RoPE rows per copy
+        const int q = wave + 4 * m;
+        const int r = 8 * q + (lane >> 3);
+        const int t = row_id[r];
+        dma16_v(outb + (int64_t)t * e.H * hstride + kEpiNRow + (((lane & 7) ^ fr(r)) << 4),
+                base + kEpiRBase + q * 1024);
       }
     }
-    lds_u[r * kEpiStride + c] = v;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  const int cols_per_wave = e.d_state / 4;      // multiple of 16 (d_state % 64 == 0)
-  const int col0 = wave * cols_per_wave;
+  if (rope) {  // u^r <- R(-t) O^r in place: 128 rows x 8 chunks, 4 chunks per thread
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int idx = n * 256 + tid, r = idx >> 3, c = idx & 7;
+      const int t = row_id[r];
+      char* p = lds_u + kEpiRBase + r * 128 + ((c ^ fr(r)) << 4);
+      uint4 v = *(const uint4*)p;
+      const __bf16* x = (const __bf16*)&v;
+      __bf16 y[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 cs = e.rowcs[(int64_t)t * half_r + 4 * c + k];
+        const float a0 = (float)(x[2 * k]), a1 = (float)(x[2 * k + 1]);
+        y[2 * k] = (__bf16)(a0 * cs.x + a1 * cs.y);
+        y[2 * k + 1] = (__bf16)(-a0 * cs.y + a1 * cs.x);
+      }
+      *(uint4*)p = *(const uint4*)y;
+    }
+    __syncthreads();
+  }
+  const int lane = tid & 63;
   const __bf16* w = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
   const int ksteps = d_v / 16;
-  for (int cb = 0; cb < cols_per_wave; cb += 64) {  // 64 columns x 64 rows per pass
-    floatx16_t acc[2][2];
-    for (int i = 0; i < 2; ++i)
-      for (int j = 0; j < 2; ++j)
-        for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
-    const int ncol = min(64, cols_per_wave - cb);
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int chunk = 2 * ks + (lane >> 5);
-      bf16x8_t af[2], bfr[2];
-      for (int i = 0; i < 2; ++i) {
-        uint4 v = lds_u[(32 * i + (lane & 31)) * kEpiStride + chunk];
-        af[i] = *(bf16x8_t*)&v;
-      }
-      for (int j = 0; j < 2; ++j) {
-        const int cw = cb + 32 * j + (lane & 31);  // column within this wave's share
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (cw < cols_per_wave) v = *(const uint4*)(w + (int64_t)(col0 + cw) * d_v + 8 * chunk);
-        bfr[j] = *(bf16x8_t*)&v;
-      }
-      for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  const int nblk = e.d_state / 32;      // 32-column blocks (d_state % 64 == 0)
+  const int col = lane & 31, hf = lane >> 5;
+  // B operand (U^T, 16 features x 32 rows): lane holds U[row 32 i + col][16 ks + 8 hf .. + 7],
+  // nope chunk 2 ks + hf at (2 ks ^ (fn & 14)) | (hf ^ (fn & 1)); RoPE step 32 + j: chunk 2 j + hf
+  const int fc = fn(col), rc = fr(col);
+  const char* ubn = lds_u + col * kEpiNRow + 16 * (hf ^ (fc & 1));
+  const int usw = 16 * (fc & 14);
+  const char* ubr = lds_u + kEpiRBase + col * 128 + 16 * (hf ^ (rc & 1));
+  const int ursw = 16 * (rc & 6);
+  int rows_t[4];                        // request row of each of the lane's 4 output rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * i + col;
+    rows_t[i] = r < n_here ? row_id[r] : -1;
+  }
+  for (int b0 = wave; b0 < nblk; b0 += 16) {  // up to 4 of this wave's blocks: b0, b0+4, ..
+    int nb = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nb += (b0 + 4 * j < nblk) ? 1 : 0;
+    floatx16_t acc[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc[j][i][k] = 0.f;
+    // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7]
+    const __bf16* wr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read a valid row
+      wr[j] = w + (int64_t)(32 * blk + col) * d_v + 8 * hf;
     }
-    // C layout: lane holds column lane%32, rows 8*(k/4) + 4*(lane/32) + k%4
-    for (int i = 0; i < 2; ++i)
-      for (int j = 0; j < 2; ++j) {
-        if (32 * j >= ncol) continue;
-        const int cw = cb + 32 * j + (lane & 31);
-        const int col = col0 + cw;
-        for (int k = 0; k < 16; ++k) {
-          const int r = 32 * i + 8 * (k / 4) + 4 * (lane >> 5) + (k % 4);
-          if (r < n_here && cw < cols_per_wave) {
-            const int t = epi_row(et, et.r0 + r);
-            __bf16* z = (__bf16*)e.z + ((int64_t)t * e.H + h) * e.d_state;
-            z[col] = (__bf16)(acc[i][j][k]);
-          }
+    bf16x8_t wf[kEpiPf][4];
+#pragma unroll
+    for (int s = 0; s < kEpiPf; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + 16 * s);
+    // k-steps in pairs so the prefetch slot is a compile-time index (ksteps is even)
+    for (int ks0 = 0; ks0 < ksteps; ks0 += kEpiPf) {
+#pragma unroll
+      for (int slot = 0; slot < kEpiPf; ++slot) {
+        const int ks = ks0 + slot;
+        bf16x8_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = wf[slot][j];
+        if (ks + kEpiPf < ksteps) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8_t*)(wr[j] + 16 * (ks + kEpiPf));
+        }
+        bf16x8_t u[4];
+        const char* up = ks < 32 ? ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3)
+                                 : ubr + ((32 * (ks - 32)) ^ ursw);
+        const int rstep = ks < 32 ? 32 * kEpiNRow : 32 * 128;  // 32 rows further
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * rstep);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], u[i], acc[j][i], 0, 0, 0);
+      }
+    }
+    // C[m][n] = Z^T[column][row]: lane holds row 32 i + col and columns
+    // 32 blk + 8 (k >> 2) + 4 hf + (k & 3)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j >= nb) continue;
+      const int cbase = 32 * (b0 + 4 * j) + 4 * hf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (rows_t[i] < 0) continue;
+        __bf16* z = (__bf16*)e.z + ((int64_t)rows_t[i] * e.H + h) * e.d_state + cbase;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          const bf16x4_t y = {(__bf16)acc[j][i][4 * g], (__bf16)acc[j][i][4 * g + 1],
+                              (__bf16)acc[j][i][4 * g + 2], (__bf16)acc[j][i][4 * g + 3]};
+          *(bf16x4_t*)(z + 8 * g) = y;
         }
       }
+    }
   }
 }
 
@@ -181,7 +258,7 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
   } else {
     const int64_t blocks = (int64_t)e.HG * ((e.T + kEpiRows - 1) / kEpiRows) +
                            (int64_t)e.HL * ((e.nA + kEpiRows - 1) / kEpiRows);
-    const size_t lds = sizeof(uint4) * kEpiRows * kEpiStride;
+    const size_t lds = kEpiLds;
     static bool attr_set = false;
     if (!attr_set) {
       hipError_t r = hipFuncSetAttribute((const void*)k_project_bf16,
