@@ -147,17 +147,6 @@ __device__ __forceinline__ void settle_agpr(floatx16* acc) {
   for (int f = 0; f < 16; ++f) asm volatile("" : "+a"(acc[f]));
 }
 
-// OCP E4M3 (float8_e4m3fn) decoding from the format: bias 7, subnormals m * 2^-9,
-// S.1111.111 = NaN, no infinity.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 15u && m == 7u) return __int_as_float(0x7fc00000);
-  if (e == 0u) {
-    const float v = (float)m * 0.001953125f;  // m * 2^-9
-    return s ? -v : v;
-  }
-  return __int_as_float(s | ((e + 120u) << 23) | (m << 20));
-}
 
 struct TileIt {
   int seg;      // segment index
@@ -187,35 +176,72 @@ __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, 
   dma16(tile_src, rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
 }
 
-// Stage one E4M3 tile: codes * block scale -> bf16, RoPE dims copied, written in the same
-// layout as the bf16 tile.
+// E4M3 tiles are staged raw inside their own bf16 buffer and converted in place once per
+// tile: the codes (32 rows x 512 bytes) sit where nope rows 16..31 will go, the block scales
+// (32 rows x 4 fp32) in the last KB below them, and the RoPE rows (bf16) are copied straight
+// to their final place in the RoPE region.
+constexpr int kRawCodes = 16 * kNRow;          // 16384
+constexpr int kRawScales = kRawCodes - 1024;   // 15360
+// Copies of wave `wave`: code row pairs wave + 4 m (m = 0..3, 64 lanes = 2 rows x 512 bytes),
+// its 8 RoPE rows, and (wave 0) the scales of all 32 rows (lanes 32..63 write a duplicate).
 __device__ __forceinline__ void load_tile_e4m3(char* buf, const uint8_t* codes, const float* scales,
-                                               const __bf16* rope, int64_t row0, int nval, int tid) {
-#pragma unroll 1
-  for (int n = 0; n < kKT * 72 / kThreads; ++n) {  // rolled: its registers stay few
-    const int idx = n * kThreads + tid;    // logical (row, chunk)
-    const int r = idx / 72, c = idx - r * 72;
-    const int64_t row = row0 + min(r, nval - 1);
-    uint4 v;
-    int dst;
-    if (c < kDN / 8) {
-      const uint2 raw = *(const uint2*)(codes + row * kDN + 8 * c);
-      const float sc = scales[row * (kDN / 128) + (c >> 4)];
-      __bf16 y[8];
+                                               const __bf16* rope, int64_t row0, int nval, int wave) {
+  const uint32_t base = lds_addr(buf);
+  const int lane = lane_id();
+  const char* cbase = (const char*)codes + row0 * kDN;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) y[k] = (__bf16)(e4m3_to_f32((raw.x >> (8 * k)) & 255u) * sc);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) y[4 + k] = (__bf16)(e4m3_to_f32((raw.y >> (8 * k)) & 255u) * sc);
-      v = *(const uint4*)y;
-      dst = r * kNRow + ((c ^ fn(r)) << 4);
-    } else {
-      v = *(const uint4*)(rope + row * 64 + 8 * (c - kDN / 8));
-      dst = kRBase + r * kRRow + (((c - kDN / 8) ^ fr(r)) << 4);
-    }
-    *(uint4*)(buf + dst) = v;
+  for (int m = 0; m < kKT / 2 / kWaves; ++m) {
+    const int pr = wave + kWaves * m;
+    const int rr = min(2 * pr + (lane >> 5), nval - 1);
+    dma16(cbase, rr * kDN + 16 * (lane & 31), base + kRawCodes + pr * 1024);
+  }
+  const int r = 8 * wave + (lane >> 3);
+  const int rr = min(r, nval - 1);
+  dma16((const char*)rope + row0 * 128, rr * 128 + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
+  if (wave == 0) {
+    const int rs = min(lane & 31, nval - 1);
+    dma16((const char*)scales + row0 * 16, rs * 16, base + kRawScales);
   }
 }
-static_assert(kKT * 72 % kThreads == 0, "whole E4M3 loader passes");
+static_assert(kKT / 2 % kWaves == 0, "whole code-row pairs per wave");
+
+// In-place conversion of a staged E4M3 tile to the bf16 tile layout, by all threads: each
+// takes 4 chunks of 16 codes (row r, codes 16 j .. 16 j + 15, block scale j / 8), reads them
+// all, waits for every thread to have read, then writes 2 bf16 chunks per code chunk.
+// Hardware conversion of packed E4M3 pairs to fp32, times the block scale, rounded to bf16.
+__device__ __forceinline__ void convert_tile_e4m3(char* buf, int wave) {
+  const int tid = wave * 64 + lane_id();  // recomputed here: no offsets kept live across the loop
+  uint4 raw[4];
+  float sc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int c = tid + kThreads * n, r = c >> 5, j = c & 31;
+    raw[n] = *(const uint4*)(buf + kRawCodes + r * kDN + 16 * j);
+    sc[n] = *(const float*)(buf + kRawScales + r * 16 + 4 * (j >> 3));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int c = tid + kThreads * n, r = c >> 5, j = c & 31;
+    const uint32_t wds[4] = {raw[n].x, raw[n].y, raw[n].z, raw[n].w};
+    bf16x8 y[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      typedef float f2 __attribute__((ext_vector_type(2)));
+      const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wds[q], false);
+      const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(wds[q], true);
+      y[q >> 1][4 * (q & 1) + 0] = (__bf16)(lo[0] * sc[n]);
+      y[q >> 1][4 * (q & 1) + 1] = (__bf16)(lo[1] * sc[n]);
+      y[q >> 1][4 * (q & 1) + 2] = (__bf16)(hi[0] * sc[n]);
+      y[q >> 1][4 * (q & 1) + 3] = (__bf16)(hi[1] * sc[n]);
+    }
+    const int f = fn(r);
+    *(bf16x8*)(buf + r * kNRow + (((2 * j) ^ f) << 4)) = y[0];
+    *(bf16x8*)(buf + r * kNRow + (((2 * j + 1) ^ f) << 4)) = y[1];
+  }
+  __syncthreads();
+}
+static_assert(kKT * (kDN / 16) == 4 * kThreads, "4 code chunks per thread");
 
 }  // namespace
 
@@ -335,7 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   auto issue = [&](const TileIt& c, int b) __attribute__((always_inline)) {
     char* buf = lds + b * kTileBytes;
     if constexpr (FP8)
-      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, tid);
+      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, wave);
     else
       load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave);
   };
@@ -428,6 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   if (!FP8 && v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (FP8) convert_tile_e4m3(lds, wave);
   qk_tile(lds, S, [](int) {});
   __builtin_amdgcn_sched_barrier(0);
   int cb = 0;  // buffer of tile i
@@ -439,6 +466,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     const int nb = cb == kNBuf - 1 ? 0 : cb + 1;
     const int fb = nb == kNBuf - 1 ? 0 : nb + 1;
     const bool v2 = v1 && advance(w1, w2);
+    if constexpr (FP8) {  // tile i+1 arrived raw: convert it in place
+      if (v1) convert_tile_e4m3(lds + nb * kTileBytes, wave);
+    }
     if (v2) issue(w2, fb);
     if (v1 && w1.seg != w0.seg) rotate_q(w1.seg);
     // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
