@@ -91,6 +91,10 @@ SMALL_CONFIGS = [
     _cfg("flash_small_vnope_bf16", None, "bf16", 64, 512, 64, 512,
          [("prefix", 17), ("doc", 150), ("doc", 99), ("new", 11)],
          edge_rows=16, tail_rows=40, budget_permille=150, seed=15, v_has_rope=0),
+    # E4M3 latent with nope-only values, ragged segment lengths (partial key tiles)
+    _cfg("pro_small_vnope_fp8", None, "bf16", 128, 512, 64, 512,
+         [("prefix", 9), ("doc", 77), ("doc", 33), ("doc", 150), ("new", 13)],
+         edge_rows=8, tail_rows=24, budget_permille=200, seed=16, kv_dtype="e4m3", v_has_rope=0),
 ]
 
 
