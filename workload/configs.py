@@ -72,6 +72,11 @@ CONFIGS = [
 # The 32K-tail variant of the Flash-like layer (labelled, not one of the five).
 FLASH_TAIL32K = dict(CONFIGS[1], name="flash_32k_tail32k_bf16", index=None, tail_rows=32768)
 
+# The Global-head work of the 128K layer alone: its 8 Global heads over every request row,
+# the same segments and protected-row rule (the 128K throughput target is stated on this part).
+LONG_128K_GLOBAL = dict(CONFIGS[2], name="long_128k_global_bf16", index=None, n_heads=8,
+                        global_heads=list(range(8)))
+
 SMALL_CONFIGS = [
     _cfg("tiny_fp32_ragged", None, "f32", 8, 64, 16, 64,
          [("prefix", 5), ("doc", 1), ("doc", 70), ("doc", 3), ("doc", 129), ("new", 9)],
@@ -99,7 +104,7 @@ SMALL_CONFIGS = [
 
 
 def config_by_name(name):
-    for c in CONFIGS + SMALL_CONFIGS + [FLASH_TAIL32K]:
+    for c in CONFIGS + SMALL_CONFIGS + [FLASH_TAIL32K, LONG_128K_GLOBAL]:
         if c["name"] == name:
             return c
     raise KeyError(name)
