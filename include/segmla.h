@@ -171,7 +171,10 @@ segmla_status segmla_plan_rows(const segmla_plan *plan, int64_t *n_rows, int64_t
  * 256-byte aligned): segment descriptors and RoPE tables (fp64-built), the row maps,
  * the protected set A and the ordered work list. indexer_score: device uint32 [T],
  * required iff the budget needs Indexer rows, else may be NULL. The workspace must
- * stay allocated and unmodified while the plan is used. */
+ * stay allocated and unmodified while the plan is used. It also holds forward scratch
+ * (key-range split partials; with bf16 io, a copy of W in the projection's operand
+ * order, H * d_state * d_v * 2 bytes), so forwards of one plan must not overlap: run them
+ * in order on one stream. */
 segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t workspace_bytes,
                                 const uint32_t *indexer_score, void *stream);
 

@@ -113,6 +113,7 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_spl
 struct EpiArgs {
   const void* out;        // [T][H][d_v] merged head outputs
   const void* w;          // [H][d_state][d_v]
+  void* wt;               // W in the projection's MFMA operand order (bf16; see k_w_tile)
   const void* z_cached;   // [n_pool][HL][d_state]
   void* z;                // [T][H][d_state]
   const float2* rowcs;    // [T][d_rope/2]

@@ -70,6 +70,23 @@ __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
 }
 
 // ------------------------------------------------------------------------ bf16 path
+// W_h in the projection's A-operand order: for head h, k-step ks (16 features) and 32-column
+// block b, the 64 lanes' fragments (lane (c, hf) = W[32 b + c][16 ks + 8 hf .. + 7]) are 1 KB
+// contiguous, so every operand load of the projection is one contiguous 1 KB read.
+// Wt[((h * KS + ks) * NB + b) * 64 + lane] (16-byte chunks), one chunk per thread, read in
+// W's own order (coalesced) and written to its operand slot.
+__global__ __launch_bounds__(256) void k_w_tile(EpiArgs e) {
+  const int ks_n = e.d_v / 16, nb = e.d_state / 32, cpr = e.d_v / 8;  // chunks per W row
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;         // W chunk (h, row, k8)
+  if (c >= (int64_t)e.H * e.d_state * cpr) return;
+  const int k8 = (int)(c % cpr);
+  const int64_t hr = c / cpr;
+  const int row = (int)(hr % e.d_state), h = (int)(hr / e.d_state);
+  const int ks = k8 >> 1, lane = ((k8 & 1) << 5) | (row & 31), b = row >> 5;
+  const uint4 v = ((const uint4*)e.w)[c];
+  ((uint4*)e.wt)[(((int64_t)h * ks_n + ks) * nb + b) * 64 + lane] = v;
+}
+
 // Workgroup = (head h, 128 rows of its list) x all d_state columns, 4 waves (one per SIMD).
 // U (128 x d_v) is staged in LDS in the packed-latent tile layout (lds_tile.h) by
 // global->LDS copies, one per nope row and one per 8 RoPE rows, all in flight at once; the
@@ -145,7 +162,9 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
     __syncthreads();
   }
   const int lane = tid & 63;
-  const __bf16* w = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
+  const int nblk_all = e.d_state / 32;
+  const __bf16* wt = (const __bf16*)e.wt + (int64_t)h * (d_v / 16) * nblk_all * 64 * 8;
+  const int64_t wstep = (int64_t)nblk_all * 64 * 8;  // elements per k-step
   const int ksteps = d_v / 16;
   const int nblk = e.d_state / 32;      // 32-column blocks (d_state % 64 == 0)
   const int col = lane & 31, hf = lane >> 5;
@@ -173,18 +192,19 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[j][i][k] = 0.f;
-    // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7]
+    // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7],
+    // read from the operand-ordered copy (1 KB contiguous per wave and k-step)
     const __bf16* wr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read a valid row
-      wr[j] = w + (int64_t)(32 * blk + col) * d_v + 8 * hf;
+      const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read valid data
+      wr[j] = wt + ((int64_t)blk * 64 + lane) * 8;
     }
     bf16x8_t wf[kEpiPf][4];
 #pragma unroll
     for (int s = 0; s < kEpiPf; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + 16 * s);
+      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + wstep * s);
     // k-steps in pairs so the prefetch slot is a compile-time index (ksteps is even)
     for (int ks0 = 0; ks0 < ksteps; ks0 += kEpiPf) {
 #pragma unroll
@@ -195,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
         for (int j = 0; j < 4; ++j) a[j] = wf[slot][j];
         if (ks + kEpiPf < ksteps) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8_t*)(wr[j] + 16 * (ks + kEpiPf));
+          for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8_t*)(wr[j] + wstep * (ks + kEpiPf));
         }
         bf16x8_t u[4];
         const char* up = ks < 32 ? ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3)
@@ -266,8 +286,11 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
       if (r != hipSuccess) return r;
       attr_set = true;
     }
-    if (blocks > 0)
+    if (blocks > 0) {
+      const int64_t chunks = (int64_t)e.H * e.d_state * e.d_v / 8;
+      hipLaunchKernelGGL(k_w_tile, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, e);
       hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)blocks), dim3(256), lds, stream, e);
+    }
     if (e.HL > 0 && e.nNA > 0)
       hipLaunchKernelGGL(k_restore_copy<uint4>, dim3(e.nNA), dim3(256), 0, stream, e,
                          e.d_state * 2 / 16);

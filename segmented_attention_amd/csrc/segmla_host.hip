@@ -32,7 +32,7 @@ struct segmla_plan {
   // workspace layout (byte offsets, 256-aligned)
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
-         o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0,
+         o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
          ws_bytes = 0;
   // profiling (events on the caller's stream)
   bool prof = false, fwd_pending = false, build_pending = false;
@@ -277,6 +277,8 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
     p->o_part_o = take(sizeof(float) * (size_t)p->n_split * nvec * p->d_v);
     p->o_part_ml = take(sizeof(float) * 2 * (size_t)p->n_split * nvec);
   }
+  if (p->io_dtype == SEGMLA_BF16)  // forward scratch: W in the projection's operand order
+    p->o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
   p->ws_bytes = o;
   *out_plan = p;
   return SEGMLA_OK;
@@ -394,6 +396,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   EpiArgs ep;
   ep.out = t->out;
   ep.w = t->w;
+  ep.wt = p->io_dtype == SEGMLA_BF16 ? p->at<void>(p->o_wt) : nullptr;
   ep.z_cached = t->z_cached;
   ep.z = t->z;
   ep.rowcs = p->at<float2>(p->o_rowcs);
