@@ -6,12 +6,13 @@ geometry and RoPE tables, protected row set, work list) followed by the forward
 row-replacement epilogue). The default workload is the Flash-like 32K layer
 (64 heads, 56 Local / 8 Global, 512 + 64 latent, 8 x 4096 documents after a 256-row
 prefix, 128 question rows, 10 % Local budget); the 128K layer is measured as a
-secondary figure, and its 8 Global heads alone (every row, the part the throughput target
-is stated on) as the "target" figure. Throughput is algorithmic attention TFLOP/s,
+secondary figure, its 8 Global heads alone (every row, the part the throughput target is
+stated on) as the "target" figure, and the Pro-like 64K layer with the E4M3 latent as the
+"fp8" figure. Throughput is algorithmic attention TFLOP/s,
 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
-                [--no-target] [--no-cpu-baseline]
+                [--no-target] [--no-fp8] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -180,6 +181,8 @@ def main():
     ap.add_argument("--target", default="long_128k_global_bf16",
                     help="workload of the stated throughput target (the 128K layer's Global heads)")
     ap.add_argument("--no-target", action="store_true")
+    ap.add_argument("--fp8", default="pro_64k_fp8", help="E4M3-latent workload reported alongside")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel "
@@ -204,6 +207,9 @@ def main():
     tgt = None
     if not args.no_target and args.target:
         tgt = measure(args.target, max(2, args.steps // 3), 1)
+    f8 = None
+    if not args.no_fp8 and args.fp8:
+        f8 = measure(args.fp8, 2, 1)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
 
     r = main_res
@@ -254,6 +260,16 @@ def main():
             "attention_ms": round(tgt["attn_ms"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(tgt["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "target_frac_bf16_peak": 0.5,
+        }
+    if f8 is not None:
+        line["fp8"] = {
+            "workload": f8["cfg"]["name"], "rows": f8["T"], "heads": f8["cfg"]["n_heads"],
+            "latent": "e4m3 (1x128 blocks, fp32 scales) + bf16 rope", "protected_rows": f8["n_protected"],
+            "tflops": round(f8["tflops"], 3), "us_per_layer": round(f8["wall_s"] * 1e6, 1),
+            "attention_tflops": round(f8["attn_tflops"], 3),
+            "attention_frac_bf16_peak": round(f8["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": {"attention": round(f8["attn_ms"], 3), "epilogue": round(f8["epi_ms"], 3),
+                         "plan_build": round(f8["build_ms"], 3)},
         }
     print(json.dumps(line), flush=True)
 
