@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     c.row0 = sg[lo].pool_row + c.j0;
   };
   auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) -> bool {
-    if (c.j0 + kKT < c.j_end) {
+    if (__builtin_expect(c.j0 + kKT < c.j_end, 1)) {
       nx = c;
       nx.j0 = c.j0 + kKT;
       nx.nval = min(kKT, c.j_end - nx.j0);
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
         const int k = 16 * f + 4 * (i >> 2) + 2 * hf + ((i & 3) >> 1);
         const float2 cs = table[seg * half_r + k];
         const float x = accr[f][i], y = accr[f][i + 1];
-        accr[f][i] = x * cs.x - y * cs.y;
-        accr[f][i + 1] = x * cs.y + y * cs.x;
+        accr[f][i] = fmaf(x, cs.x, -(y * cs.y));  // explicit contraction: fixed rounding
+        accr[f][i + 1] = fmaf(x, cs.y, y * cs.x);
       }
   };
 
@@ -469,10 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     if constexpr (FP8) {  // tile i+1 arrived raw: convert it in place
       if (v1) convert_tile_e4m3(lds + nb * kTileBytes, wave);
     }
-    if (v2) issue(w2, fb);
-    if (v1 && w1.seg != w0.seg) rotate_q(w1.seg);
+    if (__builtin_expect(v2, 1)) issue(w2, fb);
+    if (__builtin_expect(v1 && w1.seg != w0.seg, 0)) rotate_q(w1.seg);
     // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
-    if (__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT)) != 0ull) {
+    if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT)) != 0ull, 0)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int k = 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -510,14 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       }
     };
     floatx16 Sn;
-    if (v1) {
+    if (__builtin_expect(v1, 1)) {
       qk_tile(lds + nb * kTileBytes, Sn, softmax_step);
     } else {
 #pragma unroll
       for (int k = 0; k < 22; ++k) softmax_step(k);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (resc) {
+    if (__builtin_expect(resc, 0)) {
 #pragma unroll
       for (int f = 0; f < 16; ++f) rescale_agpr(acc[f], alpha);
 #pragma unroll
@@ -557,8 +557,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (!v1) break;
-    if (VROPE && w1.seg != w0.seg) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
+    if (__builtin_expect(!v1, 0)) break;
+    if (__builtin_expect(VROPE && w1.seg != w0.seg, 0)) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
     S = Sn;
     w0 = w1;
     w1 = w2;
