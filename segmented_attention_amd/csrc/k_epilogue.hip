@@ -102,7 +102,8 @@ constexpr int kEpiNRow = 1024;                    // LDS bytes per row, nope reg
 constexpr int kEpiRBase = kEpiRows * kEpiNRow;    // RoPE region (128 rows x 128 bytes)
 constexpr int kEpiRowIds = kEpiRBase + kEpiRows * 128;  // request row of each tile row
 constexpr int kEpiLds = kEpiRowIds + kEpiRows * 4;      // 147968 bytes
-constexpr int kEpiPf = 2;                         // W prefetch depth in k-steps (divides d_v / 16)
+constexpr int kEpiPf = 4;                         // W ring slots, in k-steps (even, divides 32)
+static_assert(32 % kEpiPf == 0 && kEpiPf % 2 == 0, "ring slots are compile-time: kEpiPf divides the 32 nope k-steps");
 
 __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
   extern __shared__ __attribute__((aligned(16))) char lds_u[];
@@ -200,35 +201,51 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
       const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read valid data
       wr[j] = wt + ((int64_t)blk * 64 + lane) * 8;
     }
+    // W fragments: a ring of kEpiPf k-steps; the loads for k-step ks + kEpiPf - 1 (clamped to
+    // the last k-step: no branch, so the wait counts stay exact) are issued at the start of
+    // k-step ks, giving each load kEpiPf - 1 k-steps (16 MFMAs each) to arrive. U fragments are
+    // read one k-step ahead. The 32 nope k-steps and the 4 RoPE k-steps run as separate loops,
+    // so each address form is fixed at compile time.
     bf16x8_t wf[kEpiPf][4];
 #pragma unroll
-    for (int s = 0; s < kEpiPf; ++s)
+    for (int s = 0; s < kEpiPf - 1; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + wstep * s);
-    // k-steps in pairs so the prefetch slot is a compile-time index (ksteps is even)
-    for (int ks0 = 0; ks0 < ksteps; ks0 += kEpiPf) {
+      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + wstep * min(s, ksteps - 1));
+    auto u_nope = [&](int ks, bf16x8_t* u) __attribute__((always_inline)) {  // ks < 32
+      const char* up = ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3);
 #pragma unroll
-      for (int slot = 0; slot < kEpiPf; ++slot) {
-        const int ks = ks0 + slot;
-        bf16x8_t a[4];
+      for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * kEpiNRow);
+    };
+    auto u_rope = [&](int j, bf16x8_t* u) __attribute__((always_inline)) {  // k-step 32 + j
+      const char* up = ubr + ((32 * j) ^ ursw);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = wf[slot][j];
-        if (ks + kEpiPf < ksteps) {
+      for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * 128);
+    };
+    bf16x8_t ur[2][4];
+    auto kstep = [&](int ks, int slot, auto&& read_next) __attribute__((always_inline)) {
+      const int kp = min(ks + kEpiPf - 1, ksteps - 1);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) wf[slot][j] = *(const bf16x8_t*)(wr[j] + wstep * (ks + kEpiPf));
-        }
-        bf16x8_t u[4];
-        const char* up = ks < 32 ? ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3)
-                                 : ubr + ((32 * (ks - 32)) ^ ursw);
-        const int rstep = ks < 32 ? 32 * kEpiNRow : 32 * 128;  // 32 rows further
+      for (int j = 0; j < 4; ++j) wf[(slot + kEpiPf - 1) % kEpiPf][j] = *(const bf16x8_t*)(wr[j] + wstep * kp);
+      read_next();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * rstep);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][j], ur[slot & 1][i], acc[j][i], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    u_nope(0, ur[0]);
+    for (int ks0 = 0; ks0 < 32; ks0 += kEpiPf) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], u[i], acc[j][i], 0, 0, 0);
-      }
+      for (int slot = 0; slot < kEpiPf; ++slot)
+        kstep(ks0 + slot, slot, [&] { u_nope(min(ks0 + slot + 1, 31), ur[(slot + 1) & 1]); });
+    }
+    if (rope) {  // k-steps 32..35 (ring slot (32 + j) % kEpiPf; kEpiPf is even)
+      u_rope(0, ur[0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kstep(32 + j, (32 + j) % kEpiPf, [&] { u_rope(min(j + 1, 3), ur[(j + 1) & 1]); });
     }
     // C[m][n] = Z^T[column][row]: lane holds row 32 i + col and columns
     // 32 blk + 8 (k >> 2) + 4 hf + (k & 3)
