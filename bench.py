@@ -16,6 +16,7 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-seco
 """
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -24,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "segmented-MLA attention TFLOP/s and µs/layer at 32K/128K ctx, 1 MI355X"
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 MFMA (the E4M3 path dequantizes to bf16 MFMA)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -84,9 +86,14 @@ def measure(cfg_name, steps, warmup):
     # kernel-level times from HIP events on the launch stream (separate profiled pass of
     # the same steps: the profiled forward waits for the previous one's events)
     S.segmla_profile_enable(plan.handle, True)
+    attn_steps, fwd_steps = [], []
+    prev = [0.0] * 4
     for _ in range(steps):
         step()
-    ms, n_fwd, n_build = S.segmla_profile_read(plan.handle)
+        ms, n_fwd, n_build = S.segmla_profile_read(plan.handle)  # cumulative; waits for the step
+        attn_steps.append(ms[0] - prev[0])
+        fwd_steps.append((ms[0] + ms[1] + ms[2]) - (prev[0] + prev[1] + prev[2]))
+        prev = list(ms)
     S.segmla_profile_enable(plan.handle, False)
     torch.cuda.synchronize()
     g_pairs, l_pairs = plan.pairs()
@@ -97,6 +104,8 @@ def measure(cfg_name, steps, warmup):
         cfg=cfg, T=T, n_protected=plan.n_protected, wall_s=wall, flops=flops,
         g_pairs=g_pairs, l_pairs=l_pairs,
         attn_ms=attn_ms, merge_ms=ms[1] / max(1, n_fwd), epi_ms=ms[2] / max(1, n_fwd),
+        attn_ms_median=statistics.median(attn_steps), attn_ms_min=min(attn_steps),
+        fwd_ms_median=statistics.median(fwd_steps), fwd_ms_min=min(fwd_steps),
         build_ms=ms[3] / max(1, n_build),
         attn_tflops=flops / (attn_ms * 1e-3) / 1e12,
         tflops=flops / wall / 1e12,
@@ -161,12 +170,21 @@ def cpu_baseline(cfg_name, budget_s=20.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu_model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     del inp
     torch.cuda.empty_cache()
     return dict(value=flops / secs / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample="%d of %d request rows of %s (uniform random, seed 123; Global heads on each, "
                        "Local heads on the %d sampled rows in A), fp64 numpy incl. key re-rotation "
-                       "of all rows; %.1f s" % (len(rows), T, cfg_name, int(in_a[rows].sum()), secs),
+                       "of all rows; %.1f s on %d threads of %s"
+                       % (len(rows), T, cfg_name, int(in_a[rows].sum()), secs, int(threads), cpu_model),
                 seconds=secs)
 
 
@@ -238,6 +256,10 @@ def main():
             "tflops_576_512_convention": round(r["tflops_576_512"], 3),
             "stage_ms": {"attention": round(r["attn_ms"], 4), "split_merge": round(r["merge_ms"], 4),
                          "epilogue": round(r["epi_ms"], 4), "plan_build": round(r["build_ms"], 4)},
+            "event_ms_per_forward": {"attention_median": round(r["attn_ms_median"], 4),
+                                     "attention_min": round(r["attn_ms_min"], 4),
+                                     "forward_median": round(r["fwd_ms_median"], 4),
+                                     "forward_min": round(r["fwd_ms_min"], 4)},
         },
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -257,7 +279,8 @@ def main():
     if tgt is not None:
         line["target"] = {
             "workload": tgt["cfg"]["name"], "rows": tgt["T"], "heads": tgt["cfg"]["n_heads"],
-            "attention_ms": round(tgt["attn_ms"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
+            "attention_ms": round(tgt["attn_ms"], 3), "attention_ms_median": round(tgt["attn_ms_median"], 3),
+            "attention_ms_min": round(tgt["attn_ms_min"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(tgt["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "target_frac_bf16_peak": 0.5,
         }
@@ -268,6 +291,7 @@ def main():
             "tflops": round(f8["tflops"], 3), "us_per_layer": round(f8["wall_s"] * 1e6, 1),
             "attention_tflops": round(f8["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(f8["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "attention_frac_fp8_peak": round(f8["attn_tflops"] / PEAK_FP8_TFLOPS, 4),
             "stage_ms": {"attention": round(f8["attn_ms"], 3), "epilogue": round(f8["epi_ms"], 3),
                          "plan_build": round(f8["build_ms"], 3)},
         }
