@@ -265,3 +265,44 @@ def test_parity_growing_scores(cfg, split, top, nope_only):
     e = compare(cfg, ref, out, z, lse, None)
     say("  max rel err O %.2e Z %.2e" % e)
     plan.close()
+
+
+# ------------------------------------------------------------------ protected rows under ties
+def _tie_scores(kind, T, seed):
+    """uint32 Indexer scores built so that the budget's threshold falls among equal scores."""
+    rng = np.random.default_rng([seed, 7])
+    if kind == "few_values":          # three distinct scores: the row order decides
+        return rng.integers(0, 3, T).astype(np.uint32)
+    if kind == "all_equal":
+        return np.full(T, 0x9E3779B9, dtype=np.uint32)
+    if kind == "coarse_top_byte":     # ties survive every radix pass (low 24 bits zero)
+        return (rng.integers(0, 16, T).astype(np.uint32) << np.uint32(24))
+    return rng.integers(0, 2**32, T, dtype=np.uint64).astype(np.uint32)
+
+
+@pytest.mark.parametrize("kind", ["few_values", "all_equal", "coarse_top_byte", "uniform"])
+@pytest.mark.parametrize("cfg", [c for c in SMALL_CONFIGS if c["budget_permille"] > 0] +
+                         [CONFIGS[1], CONFIGS[4]], ids=lambda c: c["name"])
+def test_protected_rows_with_ties(cfg, kind):
+    """Bit-exact protected set A against the oracle when many Indexer scores are equal: the
+    rows above the threshold, then the smallest rows among those equal to it. Only the plan
+    build runs (geometry-only plan, no attention)."""
+    from segmented_attention_amd.segmla import Plan
+    from workload import segment_table
+    from workload.gen import pool_placement
+    say("case protected rows %s scores=%s" % (cfg["name"], kind))
+    kinds, lens, offsets = segment_table(cfg)
+    T = int(lens.sum())
+    pool_rows, n_pool = pool_placement(lens, "identity", 0)
+    H = cfg["n_heads"]
+    hg = np.zeros(H, dtype=np.uint8)
+    hg[cfg["global_heads"]] = 1
+    scores = _tie_scores(kind, T, cfg["seed"])
+    plan = Plan(cfg, kinds, lens, offsets, pool_rows, n_pool, hg, 0, cfg.get("dirty_rows", ()))
+    plan.build(torch.from_numpy(scores.view(np.int32).copy()).cuda())  # uint32 bits as int32
+    got = plan.protected()
+    plan.close()
+    g = O.geometry(kinds, lens, offsets, pool_rows, n_pool)
+    ref = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
+                           cfg.get("dirty_rows", ()), scores.astype(np.uint64))["A"]
+    assert np.array_equal(np.asarray(got, dtype=np.int64), np.asarray(ref, dtype=np.int64))
