@@ -87,51 +87,103 @@ __global__ void k_protect_mark(const SegDesc* __restrict__ seg, const int32_t* _
 // score, ties to the smaller row. One workgroup: a 4-pass MSB-first radix select finds the
 // need-th largest score thr; rows above thr are taken, and among rows equal to thr the
 // smallest ones are taken in row order until `need` is reached.
+// Each pass reads four rows per thread and iteration (one 32-bit flag word, one 16-byte score
+// load) into per-wave histograms; the crossing bin is found by a parallel suffix sum over the
+// 256 bins. When every row equal to thr is taken (the usual case), the final marking is a
+// single sweep; otherwise an ordered pass takes the smallest rows among the equal ones.
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+__device__ __forceinline__ bool sel_eligible(uint32_t f) {
+  return (f & (kFlagCand | kFlagForced)) == kFlagCand;
+}
 __global__ __launch_bounds__(kSelThreads) void k_protect_select(uint8_t* __restrict__ flags,
                                                                 const uint32_t* __restrict__ score,
                                                                 int T, uint32_t need) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_mask, s_remaining;
-  __shared__ uint32_t wave_cnt[kSelThreads / 64];
-  const int tid = threadIdx.x;
-  if (tid == 0) { s_prefix = 0; s_mask = 0; s_remaining = need; }
+  __shared__ uint32_t hist[kSelWaves][256];
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t s_prefix, s_mask, s_remaining, s_eq;
+  __shared__ uint32_t wave_cnt[kSelWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) { s_prefix = 0; s_mask = 0; s_remaining = need; s_eq = 0; }
+  // vector path over rows [0, T4) when both arrays allow 4-row loads; scalar tail
+  const bool vec = ((uintptr_t)score & 15) == 0 && ((uintptr_t)flags & 3) == 0;
+  const int T4 = vec ? (T & ~3) : 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int t = tid; t < T; t += kSelThreads) {
-      if ((flags[t] & (kFlagCand | kFlagForced)) != kFlagCand) continue;
-      uint32_t s = score[t];
-      if ((s & mask) == prefix) atomicAdd(&hist[(s >> shift) & 255u], 1u);
+    uint32_t* const h = hist[wave];
+    auto count = [&](uint32_t f, uint32_t sc) {
+      if (sel_eligible(f) && (sc & mask) == prefix) atomicAdd(&h[(sc >> shift) & 255u], 1u);
+    };
+    for (int t = 4 * tid; t < T4; t += 4 * kSelThreads) {
+      const uint32_t f4 = *(const uint32_t*)(flags + t);
+      const uint4 s4 = *(const uint4*)(score + t);
+      count(f4 & 255u, s4.x);
+      count((f4 >> 8) & 255u, s4.y);
+      count((f4 >> 16) & 255u, s4.z);
+      count(f4 >> 24, s4.w);
+    }
+    for (int t = T4 + tid; t < T; t += kSelThreads) count(flags[t], score[t]);
+    __syncthreads();
+    // thread b < 256 owns bin b: its count, and the suffix sums incl(b) = sum over bins >= b
+    uint32_t c = 0, suf = 0;
+    if (tid < 256) {
+      for (int w = 0; w < kSelWaves; ++w) c += hist[w][tid];
+      suf = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o);
+        if (lane + o < 64) suf += v;
+      }
+      if (lane == 0) wtot[wave] = suf;
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t rem = s_remaining, cum = 0;
-      int bsel = 0;
-      for (int bin = 255; bin >= 0; --bin) {
-        if (cum + hist[bin] >= rem) { bsel = bin; break; }
-        cum += hist[bin];
+    if (tid < 256) {
+      uint32_t incl = suf;
+      for (int w = wave + 1; w < 4; ++w) incl += wtot[w];
+      const uint32_t excl = incl - c, rem = s_remaining;
+      // the highest bin whose inclusive suffix reaches rem; if even bin 0 does not (fewer
+      // eligible rows than rem), bin 0 with everything counted
+      const bool cross = incl >= rem && excl < rem;
+      const bool short_all = tid == 0 && incl < rem;
+      if (cross || short_all) {
+        s_prefix = prefix | ((uint32_t)tid << shift);
+        s_mask = mask | (255u << shift);
+        s_remaining = rem - (cross ? excl : incl);
+        s_eq = c;  // after the last pass: eligible rows whose score equals thr
       }
-      s_remaining = rem - cum;
-      s_prefix = prefix | ((uint32_t)bsel << shift);
-      s_mask = mask | (255u << shift);
     }
     __syncthreads();
   }
   const uint32_t thr = s_prefix;
   const uint32_t take_eq = s_remaining;  // rows with score == thr to take, smallest rows first
-  uint32_t taken = 0;                    // uniform across the workgroup
-  const int lane = tid & 63, wave = tid >> 6;
+  if (take_eq >= s_eq) {  // every eligible row with score >= thr is taken
+    for (int t = 4 * tid; t < T4; t += 4 * kSelThreads) {
+      const uint32_t f4 = *(const uint32_t*)(flags + t);
+      const uint4 s4 = *(const uint4*)(score + t);
+      const uint32_t sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      uint32_t add = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t f = (f4 >> (8 * k)) & 255u;
+        if (sel_eligible(f) && sv[k] >= thr) add |= (uint32_t)kFlagIndexer << (8 * k);
+      }
+      if (add) *(uint32_t*)(flags + t) = f4 | add;
+    }
+    for (int t = T4 + tid; t < T; t += kSelThreads)
+      if (sel_eligible(flags[t]) && score[t] >= thr) flags[t] |= kFlagIndexer;
+    return;
+  }
+  uint32_t taken = 0;  // uniform across the workgroup
   for (int base = 0; base < T; base += kSelThreads) {
     int t = base + tid;
     bool elig = false, eq = false;
-    uint32_t s = 0;
+    uint32_t sc = 0;
     if (t < T) {
-      elig = (flags[t] & (kFlagCand | kFlagForced)) == kFlagCand;
-      s = score[t];
-      eq = elig && s == thr;
+      elig = sel_eligible(flags[t]);
+      sc = score[t];
+      eq = elig && sc == thr;
     }
     uint64_t bal = __ballot(eq);
     uint32_t before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
@@ -139,11 +191,11 @@ __global__ __launch_bounds__(kSelThreads) void k_protect_select(uint8_t* __restr
     __syncthreads();
     uint32_t before = taken + before_in_wave;
     uint32_t blk_total = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
+    for (int w = 0; w < kSelWaves; ++w) {
       if (w < wave) before += wave_cnt[w];
       blk_total += wave_cnt[w];
     }
-    if (elig && (s > thr || (eq && before < take_eq))) flags[t] |= kFlagIndexer;
+    if (elig && (sc > thr || (eq && before < take_eq))) flags[t] |= kFlagIndexer;
     taken += blk_total;
     __syncthreads();
   }
