@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // 32 f + 8 (i >> 2) + 4 hf + (i & 3), so registers i, i + 1 (i even) hold one RoPE pair
   auto frame_step = [&](int seg, const float2* table) __attribute__((always_inline)) {
 #pragma unroll
-    for (int f = 0; f < NR; ++f)
+    for (int f = 0; f < NR; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const int k = 16 * f + 4 * (i >> 2) + 2 * hf + ((i & 3) >> 1);
@@ -397,6 +397,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
         accr[f][i] = fmaf(x, cs.x, -(y * cs.y));  // explicit contraction: fixed rounding
         accr[f][i + 1] = fmaf(x, cs.y, y * cs.x);
       }
+      asm volatile("" ::: "memory");  // one tile's table entries at a time (register peak)
+    }
   };
 
   // S^T of one tile (buffer nb) into sacc. With softmax work (sm != nullptr), that work is
@@ -458,8 +460,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   qk_tile(lds, S, [](int) {});
   __builtin_amdgcn_sched_barrier(0);
   int cb = 0;  // buffer of tile i
-  for (;;) {
-    // S = raw scores of tile i (w0, buffer cb). Tile i+1 (w1) becomes resident; every wave
+  // two iterations per trip, the score registers swapping roles (no copy of the next
+  // tile's scores into the current ones)
+  floatx16 Sn;
+  auto iteration = [&](floatx16& Sc, floatx16& Sx) __attribute__((always_inline)) -> bool {
+    // Sc = raw scores of tile i (w0, buffer cb). Tile i+1 (w1) becomes resident; every wave
     // is done with tile i-1, whose buffer receives tile i+2.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int k = 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (w0.pos0 + k > t || k >= w0.nval) S[i] = -INFINITY;
+        if (w0.pos0 + k > t || k >= w0.nval) Sc[i] = -INFINITY;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     bool resc = false;
     auto softmax_step = [&](int k) __attribute__((always_inline)) {
       if (k < 4) {
-        pmx[k] = fmaxf(fmaxf(S[4 * k], S[4 * k + 1]), fmaxf(S[4 * k + 2], S[4 * k + 3]));
+        pmx[k] = fmaxf(fmaxf(Sc[4 * k], Sc[4 * k + 1]), fmaxf(Sc[4 * k + 2], Sc[4 * k + 3]));
       } else if (k == 4) {
         const float mx = pair_max(fmaxf(fmaxf(pmx[0], pmx[1]), fmaxf(pmx[2], pmx[3])) * qk_scale);
         const float m_new = fmaxf(m_run, mx);
@@ -502,16 +507,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       } else if (k < 21) {
         const int i = k - 5;
         // v_exp_f32 directly: results below 2^-126 flush to zero, irrelevant for probabilities
-        const float p = __builtin_amdgcn_exp2f(S[i] * qk_scale - m_use);
+        const float p = __builtin_amdgcn_exp2f(Sc[i] * qk_scale - m_use);
         lsum += p;
         pf[i >> 3][i & 7] = (__bf16)p;
       } else if (k == 21) {
         l_run = l_run * alpha + lsum;
       }
     };
-    floatx16 Sn;
     if (__builtin_expect(v1, 1)) {
-      qk_tile(lds + nb * kTileBytes, Sn, softmax_step);
+      qk_tile(lds + nb * kTileBytes, Sx, softmax_step);
     } else {
 #pragma unroll
       for (int k = 0; k < 22; ++k) softmax_step(k);
@@ -557,15 +561,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (__builtin_expect(!v1, 0)) break;
+    if (__builtin_expect(!v1, 0)) return false;
     if (__builtin_expect(VROPE && w1.seg != w0.seg, 0)) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
-    S = Sn;
     w0 = w1;
     w1 = w2;
     v1 = v2;
     cb = nb;
+      return true;
+  };
+  for (;;) {
+    if (!iteration(S, Sn)) break;
+    if (!iteration(Sn, S)) break;
   }
-
   settle_agpr(acc);
   // whole-tile copies to VGPRs for the stores (element reads of a pinned AGPR tuple are not
   // something the compiler can copy)
