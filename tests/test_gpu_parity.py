@@ -12,6 +12,7 @@ import torch
 from oracle import segmla_oracle as O
 from tests.gpu_common import compare, oracle_inputs, run_gpu, say, tol_of
 from workload import CONFIGS, SMALL_CONFIGS, make_inputs
+from workload.configs import LONG_128K_GLOBAL, _cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +42,29 @@ def _full_case(cfg, pool="identity", split_keys=0):
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c["name"])
 def test_parity_small(cfg):
     _full_case(cfg)
+
+
+# degenerate requests: one row; no protected row at all (every Local-head row restored from the
+# cache); every head Global (no Local head, empty cached state)
+DEGENERATE = [
+    _cfg("single_row_bf16", None, "bf16", 64, 512, 64, 512, [("new", 1)],
+         edge_rows=0, tail_rows=0, budget_permille=0, seed=41),
+    _cfg("single_row_fp32", None, "f32", 8, 64, 16, 64, [("new", 1)],
+         edge_rows=0, tail_rows=0, budget_permille=0, seed=42),
+    _cfg("no_protected_bf16", None, "bf16", 64, 512, 64, 512,
+         [("prefix", 40), ("doc", 100), ("doc", 70)],
+         edge_rows=0, tail_rows=0, budget_permille=0, seed=43),
+    dict(_cfg("all_global_small_bf16", None, "bf16", 8, 512, 64, 512,
+              [("prefix", 24), ("doc", 90), ("doc", 60), ("new", 12)],
+              edge_rows=8, tail_rows=16, budget_permille=100, seed=44), global_heads=list(range(8))),
+]
+
+
+@pytest.mark.parametrize("cfg", DEGENERATE, ids=lambda c: c["name"])
+def test_parity_degenerate(cfg):
+    inp, _, _ = _full_case(cfg)
+    if cfg["name"] == "no_protected_bf16":
+        assert inp["T"] == 210
 
 
 @pytest.mark.parametrize("cfg,pool", [(CONFIGS[0], "shuffled"), (CONFIGS[0], "aliased"),
@@ -191,12 +215,16 @@ def _sample_rows(inp, A, rng, n_a=6, n_na=6, n_new=3):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+FULL = [CONFIGS[1], CONFIGS[2], CONFIGS[3], CONFIGS[4], LONG_128K_GLOBAL]
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+@pytest.mark.parametrize("idx", range(len(FULL)), ids=[c["name"] for c in FULL])
 def test_parity_full_size_sampled(idx):
-    """Full workload sizes in the launch configuration the bench times: geometry and A
-    bit-exact on every row, outputs on sampled rows against the oracle."""
-    cfg = CONFIGS[idx]
+    """Full workload sizes in the launch configuration the bench times (including the 128K
+    layer's Global heads alone, the bench's target workload): geometry and A bit-exact on every
+    row, outputs on sampled rows against the oracle."""
+    cfg = FULL[idx]
     say("case full-size %s" % cfg["name"])
     inp = make_inputs(cfg, "cuda")
     plan, out, z, lse = run_gpu(inp)
