@@ -31,7 +31,11 @@
 //
 // The key loop is software pipelined: while the softmax of tile i runs on the vector ALU,
 // the matrix core computes S^T of tile i+1; then O^T += V^T P^T for tile i. A wave therefore
-// holds two key tiles in LDS, and a third is in flight.
+// holds two key tiles in LDS, and a third is in flight. The loop body runs twice per trip with
+// the two score tiles swapping roles, and the rare per-tile work (query rotation and output
+// frame step at a segment change, masking of partial tiles, accumulator rescale) is marked
+// unlikely, so the common iteration runs straight through: with one wave per SIMD, every
+// taken branch is a fetch bubble in front of the matrix core.
 //
 // LDS tile layout (36 KB): a nope region of 32 rows x 64 16-byte chunks (chunk c of row r at
 // r*64 + (c ^ fn(r))) followed by a RoPE region of 32 rows x 8 chunks (chunk c of row r at
