@@ -35,7 +35,11 @@
 // the two score tiles swapping roles, and the rare per-tile work (query rotation and output
 // frame step at a segment change, masking of partial tiles, accumulator rescale) is marked
 // unlikely, so the common iteration runs straight through: with one wave per SIMD, every
-// taken branch is a fetch bubble in front of the matrix core.
+// taken branch is a fetch bubble in front of the matrix core. For the same reason every
+// instruction costs the wave an issue slot, and about four fit in the shadow of one score
+// MFMA next to its operand read: the softmax is cut into slices of that size, one per score
+// step (maxima, rescale test, one exponential per step, then one packed pair per step, the
+// row sum last).
 //
 // LDS tile layout (36 KB): a nope region of 32 rows x 64 16-byte chunks (chunk c of row r at
 // r*64 + (c ^ fn(r))) followed by a RoPE region of 32 rows x 8 chunks (chunk c of row r at
@@ -101,18 +105,29 @@ __device__ __forceinline__ int wave_max_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
 }
-// max / sum over the lanes l and l ^ 32 (the two lanes holding one query vector): the swap
-// returns (own, partner) in the low half and (partner, own) in the high half
-__device__ __forceinline__ float pair_max(float v) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-}
+// sum over the lanes l and l ^ 32 (the two lanes holding one query vector): the swap returns
+// (own, partner) in the low half and (partner, own) in the high half
 __device__ __forceinline__ float pair_sum(float v) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 __device__ __forceinline__ float bf2f(__bf16 x) { return (float)x; }
+
+// max(a, b, c) in one instruction (v_maximum3_f32). fmaxf on values the compiler cannot prove
+// canonical (such as MFMA results) costs two extra canonicalising instructions; the IEEE
+// maximum propagates NaN instead and needs none (scores are never NaN).
+__device__ __forceinline__ float max3r(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// Two probabilities rounded to bf16 (round to nearest even) and packed, low half first. A
+// volatile statement, so that it stays in the score step it is written in (a plain conversion
+// is sunk to the value product, after the last score step).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  uint32_t w;
+  asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(lo), "v"(hi));
+  return w;
+}
 
 // Nope output tiles live in AGPRs ("a" constraints). Inside the key loop only inline
 // assembly touches them, so the register allocator keeps them there; vector-ALU work on them
@@ -179,6 +194,40 @@ __device__ __forceinline__ void load_tile_bf16(char* buf, const char* tile_src, 
   const int rr = min(r, nval - 1);
   dma16(tile_src, rr * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), base + kRBase + wave * 1024);
 }
+
+// Full tiles (nval == kKT, every tile but a segment's last) with few instructions per copy:
+// with one wave per SIMD each instruction costs the wave an issue slot, and the clamped
+// per-row addressing above takes about twelve per row. Wave w copies nope rows r = w + 4 n:
+// fn(r) = 4 w + (n & 3), so lane L reads source bytes r * 1152 + 16 (L ^ fn(r)) =
+// (lw ^ 16 (n & 3)) + 4608 n with lw = 16 (L ^ 4 w) + 1152 w (1152 w has no bits below 128,
+// so adding it commutes with an xor of bits 4 and 5).
+// One row: M0 = lds + 4096 N, lane offset vb + 4608 N. The vector add is also the wait state
+// the copy needs after the M0 write.
+template <int N>
+__device__ __forceinline__ void dma16_row(const char* src, uint32_t vb, uint32_t lds) {
+  uint32_t t;
+  asm volatile("s_add_u32 m0, %2, %3\n\tv_add_u32 %0, %4, %1\n\tglobal_load_lds_dwordx4 %0, %5"
+               : "=&v"(t)
+               : "v"(vb), "s"(lds), "n"(N * kWaves * kNRow), "n"(N * kWaves * kRowBytes), "s"(src)
+               : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void load_tile_bf16_full(char* buf, const char* tile_src, int wave) {
+  const int lane = lane_id();
+  const uint32_t lb = lds_addr(buf) + wave * kNRow;
+  const uint32_t lw = (uint32_t)(((lane ^ (wave << 2)) << 4) + wave * kRowBytes);
+  const uint32_t vb1 = lw ^ 16, vb2 = lw ^ 32, vb3 = lw ^ 48;
+  dma16(tile_src, lw, lb);
+  dma16_row<1>(tile_src, vb1, lb);
+  dma16_row<2>(tile_src, vb2, lb);
+  dma16_row<3>(tile_src, vb3, lb);
+  dma16_row<4>(tile_src, lw, lb);
+  dma16_row<5>(tile_src, vb1, lb);
+  dma16_row<6>(tile_src, vb2, lb);
+  dma16_row<7>(tile_src, vb3, lb);
+  const int r = 8 * wave + (lane >> 3);
+  dma16(tile_src, r * kRowBytes + kNRow + (((lane & 7) ^ fr(r)) << 4), lds_addr(buf) + kRBase + wave * 1024);
+}
+static_assert(kKT / kWaves == 8 && kWaves == 4, "row n of wave w is w + 4 n, n = 0..7");
 
 // E4M3 tiles are staged raw inside their own bf16 buffer and converted in place once per
 // tile: the codes (32 rows x 512 bytes) sit where nope rows 16..31 will go, the block scales
@@ -303,7 +352,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   for (int f = 0; f < NR; ++f)
 #pragma unroll
     for (int i = 0; i < 16; ++i) accr[f][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max (log2 units), the shift the exponentials use (0 while no key is visible) and
+  // the threshold of the lazy rescale
+  float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, m_thr = -INFINITY;
   const int half_r = a.d_rope / 2;  // 32
 
   // ---- per-lane LDS offsets inside a tile buffer
@@ -366,6 +417,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     char* buf = lds + b * kTileBytes;
     if constexpr (FP8)
       load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, wave);
+    else if (__builtin_expect(c.nval == kKT, 1))
+      load_tile_bf16_full(buf, (const char*)a.kv + c.row0 * kRowBytes, wave);
     else
       load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave);
   };
@@ -490,40 +543,68 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // softmax of tile i (online, log2 domain, lazy rescale), in slices that ride along the
-    // MFMAs of the next tile's scores: partial maxima, the running-max update, then one
-    // probability per step
-    bf16x8 pf[2];
-    float alpha = 1.f, m_use = 0.f, lsum = 0.f;
-    float pmx[4];
+    // MFMAs of the next tile's scores, a few instructions per step: partial maxima, the pair
+    // maximum and the rescale test, the rescale itself (rare, out of line), one probability
+    // per step, then one packed pair and its two row-sum terms per step
+    constexpr int kSmSteps = 36;
+    uint32_t pw[8];
+    float alpha, lsum = 0.f, lsum2, mx = 0.f;  // alpha is set and read only when resc
+    float pmx[4], p[16];
     bool resc = false;
     auto softmax_step = [&](int k) __attribute__((always_inline)) {
       if (k < 4) {
-        pmx[k] = fmaxf(fmaxf(Sc[4 * k], Sc[4 * k + 1]), fmaxf(Sc[4 * k + 2], Sc[4 * k + 3]));
+        pmx[k] = max3r(max3r(Sc[4 * k], Sc[4 * k + 1], Sc[4 * k + 2]), Sc[4 * k + 3], Sc[4 * k + 3]);
       } else if (k == 4) {
-        const float mx = pair_max(fmaxf(fmaxf(pmx[0], pmx[1]), fmaxf(pmx[2], pmx[3])) * qk_scale);
-        const float m_new = fmaxf(m_run, mx);
-        // wave-uniform decision, taken without a branch
-        resc = __ballot(m_new > m_run + kRescaleThreshold) != 0ull;
-        const float a_new = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        alpha = resc ? a_new : 1.f;
-        m_run = resc ? m_new : m_run;
-        m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      } else if (k < 21) {
-        const int i = k - 5;
+        mx = max3r(max3r(pmx[0], pmx[1], pmx[2]), pmx[3], pmx[3]) * qk_scale;
+      } else if (k == 5) {
+        // the two lanes l, l ^ 32 hold one query vector
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = max3r(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        // wave-uniform: the running max moves only when some lane's grows by more than 8
+        resc = __ballot(mx > m_thr) != 0ull;
+      } else if (k == 6) {
+        if (__builtin_expect(resc, 0)) {
+          const float m_new = fmaxf(m_run, mx);
+          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          m_use = (m_run == -INFINITY) ? 0.f : m_run;
+          m_thr = m_run + kRescaleThreshold;
+          l_run *= alpha;
+        }
+      } else if (k < 7 + 16) {
+        const int i = k - 7;
         // v_exp_f32 directly: results below 2^-126 flush to zero, irrelevant for probabilities
-        const float p = __builtin_amdgcn_exp2f(Sc[i] * qk_scale - m_use);
-        lsum += p;
-        pf[i >> 3][i & 7] = (__bf16)p;
-      } else if (k == 21) {
-        l_run = l_run * alpha + lsum;
+        p[i] = __builtin_amdgcn_exp2f(fmaf(Sc[i], qk_scale, -m_use));
+      } else if (k < 7 + 16 + 8) {
+        const int j = k - 23;
+        pw[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+        lsum += p[2 * j];
+      } else if (k >= kSmSteps - 3) {  // the odd terms of the row sum, three per step
+        const int j = k - (kSmSteps - 3);
+        if (j == 0) {
+          lsum2 = p[1] + p[3];
+          lsum2 += p[5];
+        } else if (j == 1) {
+          lsum2 += p[7];
+          lsum2 += p[9];
+          lsum2 += p[11];
+        } else {
+          lsum2 += p[13];
+          lsum2 += p[15];
+          l_run += lsum + lsum2;
+        }
       }
     };
+    static_assert(kSmSteps <= kQSteps, "the softmax rides along the score steps");
     if (__builtin_expect(v1, 1)) {
       qk_tile(lds + nb * kTileBytes, Sx, softmax_step);
     } else {
 #pragma unroll
-      for (int k = 0; k < 22; ++k) softmax_step(k);
+      for (int k = 0; k < kSmSteps; ++k) softmax_step(k);
     }
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 pw0 = {pw[0], pw[1], pw[2], pw[3]}, pw1 = {pw[4], pw[5], pw[6], pw[7]};
+    const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pw0), __builtin_bit_cast(bf16x8, pw1)};
     __builtin_amdgcn_sched_barrier(0);
     if (__builtin_expect(resc, 0)) {
 #pragma unroll
