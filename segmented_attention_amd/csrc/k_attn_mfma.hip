@@ -26,8 +26,10 @@
 // Register files: the 16 nope output tiles (256 values per lane) fill the AGPRs; their MFMAs
 // are issued from inline assembly with AGPR accumulators, everything else (query, scores,
 // RoPE output tiles) stays in VGPRs with the compiler's MFMAs in VGPR form. Hazards of the
-// assembly MFMAs are covered by hand: two wait states before each (operands written by the
-// vector ALU), twelve before the accumulators are read back after the loop.
+// assembly MFMAs are covered by hand: two wait states before the first of each tile's value
+// product (operands written by the vector ALU; the others read LDS results only, which a CPU
+// test checks on the generated assembly), twelve before the accumulators are read back after
+// the loop.
 //
 // The key loop is software pipelined: while the softmax of tile i runs on the vector ALU,
 // the matrix core computes S^T of tile i+1; then O^T += V^T P^T for tile i. A wave therefore
@@ -61,6 +63,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 // The segment table is read-only for the whole launch: reading it through the constant
 // address space lets the compiler use scalar loads (no vector-memory round trip, and no
 // wait on the vector-memory counter that also tracks the tile prefetch).
@@ -88,7 +91,9 @@ constexpr int kLoads = kKT / kWaves + 1;         // global->LDS copies per wave 
 static_assert(kWaves * 32 == kTileQ, "one 32-vector MFMA column block per wave");
 static_assert(kKT / 8 == kWaves, "one RoPE copy (8 rows) per wave");
 static_assert(kQReg <= 32, "the RoPE query steps live in LDS slots");
-static_assert(kLdsBytes + 64 <= 160 * 1024, "LDS budget");
+constexpr int kLdsAlloc = kLdsBytes + 16;       // + the per-wave maxima of the prologue
+static_assert(kLdsAlloc <= 160 * 1024, "LDS budget");
+static_assert(kTileBytes % 256 == 0, "tile buffers keep address bits 0..7 free");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;        // log2 units
@@ -133,10 +138,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // assembly touches them, so the register allocator keeps them there; vector-ALU work on them
 // goes through single-register operands.
 
-// acc += A B (32x32x16 bf16, fp32 accumulation); the s_nop gives the two wait states an
-// operand written by the vector ALU needs before the MFMA reads it
+// acc += A B (32x32x16 bf16, fp32 accumulation). With kWait, an s_nop gives the two wait
+// states an operand written by the vector ALU needs before the MFMA reads it. Without it,
+// the caller's operands come from LDS reads and earlier MFMAs only; a CPU test checks on the
+// generated assembly that no vector-ALU write of an operand falls within two wait states.
+template <bool kWait>
 __device__ __forceinline__ void mfma_agpr(floatx16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (kWait)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // acc *= alpha, register by register through one VGPR; the leading s_nops give the twelve
@@ -300,8 +311,10 @@ static_assert(kKT * (kDN / 16) == 4 * kThreads, "4 code chunks per thread");
 
 template <bool VROPE, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int s_tmax[kWaves];
+  // The kernel has no static LDS, so the dynamic area, and with it every tile buffer, starts
+  // on a 256-byte boundary: the operand addresses below rely on it.
+  extern __shared__ __attribute__((aligned(256))) char lds[];
+  int* const s_tmax = (int*)(lds + kLdsBytes);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
@@ -357,26 +370,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, m_thr = -INFINITY;
   const int half_r = a.d_rope / 2;  // 32
 
-  // ---- per-lane LDS offsets inside a tile buffer
+  // ---- per-lane LDS offsets inside a tile buffer. Each is a base B plus a swizzle term X ^ C,
+  // where C is a per-step constant and B has no bits where X and C live; with the buffer
+  // start on a 256-byte boundary, buffer + B + (X ^ C) = (buffer + (B | X)) ^ C, one XOR per
+  // read (the remaining per-step term goes into the instruction's offset field).
   // K operand, step s (nope): row col, chunk 2 s + hf -> 2 s ^ (fn & 14) | (hf ^ (fn & 1))
   const int fcol = fn(col), rcol = fr(col);
-  const int kbase = col * kNRow + 16 * (hf ^ (fcol & 1));
-  const int ksw0 = 16 * (fcol & 14);
+  const int kx0 = (col * kNRow + 16 * (hf ^ (fcol & 1))) | (16 * (fcol & 14));  // C = 32 (s & 7)
   // K operand, RoPE step 32 + j: row col, RoPE chunk 2 j + hf
-  const int krbase = kRBase + col * kRRow + 16 * (hf ^ (rcol & 1));
-  const int krsw0 = 16 * (rcol & 6);
+  const int krx0 = (kRBase + col * kRRow + 16 * (hf ^ (rcol & 1))) | (16 * (rcol & 6));  // C = 32 j
   // V^T operand (transposing reads): 16-lane group G, source lane j supplies key row
   // 16 u + 4 (G >> 1) + (j >> 2) (+ 8 for the second read) and features
-  // 32 f + 16 (G & 1) + 4 (j & 3) .. + 3, i.e. chunk 4 f + cl, half j & 1.
+  // 32 f + 16 (G & 1) + 4 (j & 3) .. + 3, i.e. chunk 4 f + cl, half j & 1. C = 64 (f & 3).
   const int G = lane >> 4, jj = lane & 15;
   const int cl = 2 * (G & 1) + ((jj & 3) >> 1);
   const int vrow = 4 * (G >> 1) + (jj >> 2);
-  const int vb0 = vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1));
-  const int vb1 = vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2));
-  const int vsw0 = 64 * (jj >> 2);
-  const int vr0 = kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1));
-  const int vr1 = kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2));
-  const int vrsw0 = 64 * ((jj >> 3) & 1);
+  const int vx0 = (vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1))) | (64 * (jj >> 2));
+  const int vx1 = (vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2))) | (64 * (jj >> 2));
+  // RoPE features (f = 16, 17): C = 64 (f - 16)
+  const int vrx0 = (kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1))) | (64 * ((jj >> 3) & 1));
+  const int vrx1 = (kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2))) | (64 * ((jj >> 3) & 1));
 
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
   auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
@@ -461,12 +474,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // S^T of one tile (buffer nb) into sacc. With softmax work (sm != nullptr), that work is
   // interleaved with the MFMAs: the matrix core computes the next tile's scores while the
   // vector ALU finishes the current tile's probabilities.
-  auto qk_reads = [&](const char* buf, int ksw, int krsw, int k, bf16x8& kf) __attribute__((always_inline)) {
+  auto qk_reads = [&](uint32_t kt, uint32_t krt, int k, bf16x8& kf) __attribute__((always_inline)) {
     if (k < 32) {
       const int s8 = k >> 3, sl = k & 7;
-      kf = *(const bf16x8*)(buf + kbase + ((32 * sl) ^ ksw) + 256 * s8);
+      kf = *(const lds_bf16x8*)(size_t)((kt ^ (32 * sl)) + 256 * s8);
     } else {
-      kf = *(const bf16x8*)(buf + krbase + ((32 * (k - 32)) ^ krsw));
+      kf = *(const lds_bf16x8*)(size_t)(krt ^ (32 * (k - 32)));
     }
   };
 
@@ -475,12 +488,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // step k + kQkDepth is read before the MFMA of step k, and hook(k) places a slice of
   // vector-ALU work after it (program order is issue order: each step ends in a fence)
   auto qk_tile = [&](const char* buf, floatx16& sacc, auto&& hook) __attribute__((always_inline)) {
-    int ksw = ksw0, krsw = krsw0;
-    asm volatile("" : "+v"(ksw), "+v"(krsw));  // addresses computed per use, not hoisted
+    // per-tile bases, opaque to the compiler: the per-step XORs stay XORs of this value (no
+    // per-step addresses precomputed and held across the loop)
+    uint32_t kt = lds_addr(buf) + kx0, krt = lds_addr(buf) + krx0;
+    asm volatile("" : "+v"(kt), "+v"(krt));
     bf16x8 ring[kQkDepth], qring[kQkDepth];
 #pragma unroll
     for (int k = 0; k < kQkDepth; ++k) {
-      qk_reads(buf, ksw, krsw, k, ring[k]);
+      qk_reads(kt, krt, k, ring[k]);
       if (k >= kQReg) qring[k] = *(const bf16x8*)(qslot + (k - kQReg) * kQSlotStep);
     }
 #pragma unroll
@@ -489,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       const bf16x8 qv = k < kQReg ? qf[k < kQReg ? k : 0] : qring[k % kQkDepth];
       if (k + kQkDepth < kQSteps) {
         const int kn = k + kQkDepth;
-        qk_reads(buf, ksw, krsw, kn, ring[k % kQkDepth]);
+        qk_reads(kt, krt, kn, ring[k % kQkDepth]);
         if (kn >= kQReg) qring[k % kQkDepth] = *(const bf16x8*)(qslot + (kn - kQReg) * kQSlotStep);
       }
       if (k == 0) {
@@ -615,20 +630,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // ---- O^T += V^T P^T for tile i: 2 key steps x NF feature tiles
     {
-      const char* buf = lds + cb * kTileBytes;
-      int vsw = vsw0, vrsw = vrsw0;
-      asm volatile("" : "+v"(vsw), "+v"(vrsw));  // addresses computed per use, not hoisted
+      const uint32_t bb = lds_addr(lds + cb * kTileBytes);
+      uint32_t vt0 = bb + vx0, vt1 = bb + vx1, vrt0 = bb + vrx0, vrt1 = bb + vrx1;
+      asm volatile("" : "+v"(vt0), "+v"(vt1), "+v"(vrt0), "+v"(vrt1));  // as kt above
+      auto tr = [](uint32_t addr) __attribute__((always_inline)) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)addr);
+      };
       auto vread = [&](int n, bf16x4& lo, bf16x4& hi) __attribute__((always_inline)) {  // n = u * NF + f
         const int u = n / NF, f = n % NF;
         if (f < 16) {
           const int f4 = f >> 2, fl = f & 3;
-          const char* p = buf + ((64 * fl) ^ vsw) + 256 * f4 + 16384 * u;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vb0));
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vb1 + 8192));
+          lo = tr((vt0 ^ (64 * fl)) + 256 * f4 + 16384 * u);
+          hi = tr((vt1 ^ (64 * fl)) + 8192 + 256 * f4 + 16384 * u);
         } else {
-          const char* p = buf + ((64 * (f - 16)) ^ vrsw) + 2048 * u;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vr0));
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + vr1 + 1024));
+          lo = tr((vrt0 ^ (64 * (f - 16))) + 2048 * u);
+          hi = tr((vrt1 ^ (64 * (f - 16))) + 1024 + 2048 * u);
         }
       };
       bf16x4 lo[kPvDepth], hi[kPvDepth];
@@ -641,7 +657,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
         if (n + kPvDepth < 2 * NF) vread(n + kPvDepth, lo[r], hi[r]);
         const int f = n % NF;
         // (program order is issue order: the assembly MFMAs are ordered with the LDS reads)
-        if (f < 16) mfma_agpr(acc[f], vt, pf[n / NF]);
+        if (f < 16) {
+          // the first follows the probabilities' conversion and the rescale; the others
+          // follow LDS reads
+          if (n == 0) mfma_agpr<true>(acc[f], vt, pf[n / NF]);
+          else mfma_agpr<false>(acc[f], vt, pf[n / NF]);
+        }
         else accr[f - 16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[n / NF], accr[f - 16], 0, 0, 0);
       }
     }
@@ -708,7 +729,7 @@ namespace {
 template <bool VROPE, bool FP8>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
   static bool attr_set = false;
-  const int lds = kLdsBytes;
+  const int lds = kLdsAlloc;
   if (!attr_set) {
     hipError_t r = hipFuncSetAttribute((const void*)k_attn_mfma<VROPE, FP8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);

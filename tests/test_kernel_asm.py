@@ -7,6 +7,10 @@ produce (CPU only: hipcc cross-compiles).
 * The nope output accumulators live in AGPRs written by inline-assembly MFMAs. Each attention
   kernel's descriptor must reserve the AGPRs it uses (next_free_vgpr - accum_offset), and the
   kernels make no calls (a callee would make the compiler save and restore live AGPRs).
+* An MFMA must not read a register that the vector ALU wrote less than two wait states
+  before. The compiler keeps this for its own MFMAs; the inline-assembly MFMAs without their
+  own s_nop rely on their operands coming from LDS reads, which is checked here instruction
+  by instruction.
 """
 import os
 import re
@@ -117,3 +121,92 @@ def test_copy_kernels_keep_m0_free(tmp_path):
             bad = _compiler_m0_uses(lines)
             assert not bad, (fname, bad[:3])
     assert checked >= 5, checked  # four attention instantiations + the projection
+
+
+_REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+))")
+
+
+def _regs(text):
+    """Set of ('v'|'a', index) named by an operand list."""
+    out = set()
+    for m in _REG.finditer(text):
+        kind = m.group(1)
+        lo = int(m.group(2) if m.group(2) is not None else m.group(4))
+        hi = int(m.group(3) if m.group(3) is not None else m.group(4))
+        out.update((kind, r) for r in range(lo, hi + 1))
+    return out
+
+
+def _valu_mfma_hazards(lines, window=2):
+    """Inline-assembly MFMAs (AGPR accumulators) issued without an s_nop of their own, where
+    a vector-ALU instruction within `window` wait states before names one of the MFMA's
+    registers (conservative: any register operand of the VALU instruction counts as written).
+    A label inside the window counts as a hazard (another path may reach the MFMA)."""
+    bad, prev = [], []  # prev: (kind, wait_states, mnemonic, operands) most recent last
+    in_asm, asm_first = False, False
+    for line in lines:
+        t = line.strip()
+        if ";;#ASMSTART" in t:
+            in_asm, asm_first = True, True
+            continue
+        if ";;#ASMEND" in t:
+            in_asm = False
+            continue
+        if t.startswith(".LBB") or t.startswith("; %bb."):
+            prev.append(("label", 1, "", ""))
+            continue
+        code = t.split(";")[0].strip()
+        if not code or code.startswith("."):
+            continue
+        mnem, _, ops = code.partition(" ")
+        if in_asm and mnem.startswith("v_mfma") and "a[" in ops and asm_first:
+            need, seen = window, 0
+            for kind, ws, pm, pops in reversed(prev):
+                if seen >= need:
+                    break
+                if kind == "label":
+                    bad.append(("label before", code))
+                    break
+                if pm.startswith("v_") and not pm.startswith("v_mfma") and _regs(pops) & _regs(ops):
+                    bad.append((pm + " " + pops, code))
+                    break
+                seen += ws
+        if in_asm:
+            asm_first = False
+        ws = 1
+        m = re.match(r"s_nop (\d+)", code)
+        if m:
+            ws = int(m.group(1)) + 1
+        prev.append(("insn", ws, mnem, ops))
+        if len(prev) > 16:
+            prev.pop(0)
+    return bad
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not found")
+def test_assembly_mfmas_without_nop_read_no_fresh_valu_result(tmp_path):
+    funcs = {k: v for k, v in _functions(_asm(tmp_path)).items() if "k_attn_mfma" in k}
+    assert len(funcs) == 4, sorted(funcs)
+    checked = 0
+    for fname, lines in funcs.items():
+        bad = _valu_mfma_hazards(lines)
+        assert not bad, (fname, bad[:3])
+        checked += sum(1 for l in lines if re.match(r"\s*v_mfma\S* a\[", l))
+    assert checked >= 4 * 16, checked
+
+
+def test_hazard_checker_flags_a_fresh_valu_write():
+    """The checker itself: a VALU write of an operand right before a nop-less MFMA is found,
+    the same write three instructions earlier is not."""
+    mf = ["\t;;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[72:75], v[68:71], a[0:15]", "\t;;#ASMEND"]
+    near = ["\tv_add_u32_e32 v73, s0, v94", "\ts_waitcnt lgkmcnt(2)"] + mf
+    far = ["\tv_add_u32_e32 v73, s0, v94", "\tds_read_b64_tr_b16 v[80:81], v95", "\ts_waitcnt lgkmcnt(2)"] + mf
+    other = ["\tv_add_u32_e32 v90, s0, v94", "\ts_waitcnt lgkmcnt(2)"] + mf
+    label = ["\tds_read_b64_tr_b16 v[80:81], v95", ".LBB1_5:", "\ts_waitcnt lgkmcnt(2)"] + mf
+    nop = ["\tv_add_u32_e32 v73, s0, v94", "\t;;#ASMSTART", "\ts_nop 1",
+           "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[72:75], v[68:71], a[0:15]", "\t;;#ASMEND"]
+    assert _valu_mfma_hazards(near)
+    assert not _valu_mfma_hazards(far)
+    assert not _valu_mfma_hazards(other)
+    assert _valu_mfma_hazards(label)
+    assert not _valu_mfma_hazards(nop)
