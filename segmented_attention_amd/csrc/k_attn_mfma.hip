@@ -33,8 +33,9 @@
 //
 // The key loop is software pipelined: while the softmax of tile i runs on the vector ALU,
 // the matrix core computes S^T of tile i+1; then O^T += V^T P^T for tile i. A wave therefore
-// holds two key tiles in LDS, and a third is in flight. The loop body runs twice per trip with
-// the two score tiles swapping roles, and the rare per-tile work (query rotation and output
+// holds two key tiles in LDS, and a third is in flight. The loop body runs six times per trip
+// (three tile buffers, two score tiles), so buffers and roles are fixed per copy, and the rare
+// per-tile work (query rotation and output
 // frame step at a segment change, masking of partial tiles, accumulator rescale) is marked
 // unlikely, so the common iteration runs straight through: with one wave per SIMD, every
 // taken branch is a fetch bubble in front of the matrix core. For the same reason every
@@ -178,13 +179,19 @@ __device__ __forceinline__ void settle_agpr(floatx16* acc) {
 }
 
 
-struct TileIt {
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
+struct TileIt {  // assigned field by field: a whole-struct copy between the rotating roles
+                 // made the compiler keep descriptors in private memory
+  int v;        // the tile exists (the key range is not exhausted)
   int seg;      // segment index
-  int j0;       // first canonical row of the tile inside the segment
   int nval;     // rows of the tile that are in range (1..kKT)
-  int pos0;     // request position of row j0
-  int j_end;    // end of the segment's rows inside the key range
-  int64_t row0; // latent-pool row of row j0
+  int pos0;     // request position of the tile's first row
+  int pend;     // end (exclusive) of the segment's positions inside the key range
+  int64_t row0; // latent-pool row of the tile's first row
 };
 
 // Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte copies: one
@@ -400,29 +407,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     }
     c.seg = lo;
     const int off = sg[lo].offset, len = sg[lo].len;
-    c.j0 = k_lo - off;
-    c.j_end = min(len, k_hi - off);
-    c.nval = min(kKT, c.j_end - c.j0);
     c.pos0 = k_lo;
-    c.row0 = sg[lo].pool_row + c.j0;
+    c.pend = min(off + len, k_hi);
+    c.nval = min(kKT, c.pend - k_lo);
+    c.row0 = sg[lo].pool_row + (k_lo - off);
   };
   auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) -> bool {
-    if (__builtin_expect(c.j0 + kKT < c.j_end, 1)) {
-      nx = c;
-      nx.j0 = c.j0 + kKT;
-      nx.nval = min(kKT, c.j_end - nx.j0);
+    if (__builtin_expect(c.pos0 + kKT < c.pend, 1)) {
+      nx.seg = c.seg;
       nx.pos0 = c.pos0 + kKT;
+      nx.pend = c.pend;
+      nx.nval = min(kKT, c.pend - nx.pos0);
       nx.row0 = c.row0 + kKT;
       return true;
     }
     if (c.seg + 1 >= a.n_seg) return false;
-    const int off = sg[c.seg + 1].offset;
+    const int off = sg[c.seg + 1].offset;  // the segments are contiguous: off == c.pend
     if (off >= k_hi) return false;
     nx.seg = c.seg + 1;
-    nx.j0 = 0;
-    nx.j_end = min(sg[c.seg + 1].len, k_hi - off);
-    nx.nval = min(kKT, nx.j_end);
     nx.pos0 = off;
+    nx.pend = min(off + sg[c.seg + 1].len, k_hi);
+    nx.nval = min(kKT, nx.pend - off);
     nx.row0 = sg[c.seg + 1].pool_row;
     return true;
   };
@@ -519,30 +524,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   };
 
   // ---- prologue: tiles 0 and 1 in flight, scores of tile 0
-  TileIt w0, w1, w2;
-  first_tile(w0);
-  bool v1 = advance(w0, w1);
-  issue(w0, 0);
-  if (v1) issue(w1, 1);
-  rotate_q(w0.seg);
-  if (!FP8 && v1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
+  TileIt wa, wb, wc;
+  first_tile(wa);
+  wa.v = 1;
+  wb.v = advance(wa, wb);
+  issue(wa, 0);
+  if (wb.v) issue(wb, 1);
+  rotate_q(wa.seg);
+  if (!FP8 && wb.v) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if constexpr (FP8) convert_tile_e4m3(lds, wave);
   qk_tile(lds, S, [](int) {});
   __builtin_amdgcn_sched_barrier(0);
-  int cb = 0;  // buffer of tile i
-  // two iterations per trip, the score registers swapping roles (no copy of the next
-  // tile's scores into the current ones)
   floatx16 Sn;
-  auto iteration = [&](floatx16& Sc, floatx16& Sx) __attribute__((always_inline)) -> bool {
-    // Sc = raw scores of tile i (w0, buffer cb). Tile i+1 (w1) becomes resident; every wave
-    // is done with tile i-1, whose buffer receives tile i+2.
+  int fin_seg = 0;  // segment of the last tile
+  // One iteration per key tile i: tile i in buffer CB with descriptor w0 and raw scores Sc,
+  // tile i+1 (w1, buffer CB+1) gets its scores into Sx, tile i+2 (w2, buffer CB+2) is staged.
+  // The loop below is unrolled six times, so that the buffers (period 3), the descriptor
+  // roles (period 3) and the score registers (period 2) are all fixed per copy: no index
+  // arithmetic and no descriptor or score copies between iterations.
+  auto iteration = [&](auto cbc, floatx16& Sc, floatx16& Sx, const TileIt& w0, const TileIt& w1,
+                       TileIt& w2) __attribute__((always_inline)) -> bool {
+    constexpr int cb = decltype(cbc)::value;
+    constexpr int nb = (cb + 1) % kNBuf, fb = (cb + 2) % kNBuf;
+    // every wave is done with tile i-1, whose buffer (fb) receives tile i+2; tile i+1 is
+    // resident
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int nb = cb == kNBuf - 1 ? 0 : cb + 1;
-    const int fb = nb == kNBuf - 1 ? 0 : nb + 1;
-    const bool v2 = v1 && advance(w1, w2);
+    const bool v1 = w1.v;
+    w2.v = v1 && advance(w1, w2);
+    const bool v2 = w2.v;
     if constexpr (FP8) {  // tile i+1 arrived raw: convert it in place
       if (v1) convert_tile_e4m3(lds + nb * kTileBytes, wave);
     }
@@ -667,17 +679,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (__builtin_expect(!v1, 0)) return false;
+    if (__builtin_expect(!v1, 0)) {
+      fin_seg = w0.seg;
+      return false;
+    }
     if (__builtin_expect(VROPE && w1.seg != w0.seg, 0)) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
-    w0 = w1;
-    w1 = w2;
-    v1 = v2;
-    cb = nb;
-      return true;
+    return true;
   };
   for (;;) {
-    if (!iteration(S, Sn)) break;
-    if (!iteration(Sn, S)) break;
+    if (!iteration(IntC<0>{}, S, Sn, wa, wb, wc)) break;
+    if (!iteration(IntC<1>{}, Sn, S, wb, wc, wa)) break;
+    if (!iteration(IntC<2>{}, S, Sn, wc, wa, wb)) break;
+    if (!iteration(IntC<0>{}, Sn, S, wa, wb, wc)) break;
+    if (!iteration(IntC<1>{}, S, Sn, wb, wc, wa)) break;
+    if (!iteration(IntC<2>{}, Sn, S, wc, wa, wb)) break;
   }
   settle_agpr(acc);
   // whole-tile copies to VGPRs for the stores (element reads of a pinned AGPR tuple are not
@@ -688,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     return x;
   };
   // restore the request phase of the RoPE part: R(+rot_last)
-  if (VROPE) frame_step(w0.seg, a.segcs);
+  if (VROPE) frame_step(fin_seg, a.segcs);
   const float l_tot = pair_sum(l_run);
   const int d_v = a.d_v;
   if (a.n_split > 1) {

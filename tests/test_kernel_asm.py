@@ -86,7 +86,8 @@ def test_attention_kernel_asm_invariants(tmp_path):
     assert len(funcs) == 4, sorted(funcs)
 
     for fname, lines in funcs.items():
-        assert not any(re.search(r"\bs_(swappc|setpc|call)", l.split(";")[0]) for l in lines), fname
+        # no calls (s_setpc alone is also the far-jump form of a branch in a large kernel)
+        assert not any(re.search(r"\bs_(swappc|call)", l.split(";")[0]) for l in lines), fname
         in_asm = False
         for line in lines:
             if ";;#ASMSTART" in line:
