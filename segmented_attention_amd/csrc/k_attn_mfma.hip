@@ -191,7 +191,7 @@ struct TileIt {  // assigned field by field: a whole-struct copy between the rot
   int nval;     // rows of the tile that are in range (1..kKT)
   int pos0;     // request position of the tile's first row
   int pend;     // end (exclusive) of the segment's positions inside the key range
-  int64_t row0; // latent-pool row of the tile's first row
+  int64_t src;  // the tile's first row: bf16 latent, byte offset in the pool; E4M3, its row
 };
 
 // Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte copies: one
@@ -399,6 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   const int vrx1 = (kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2))) | (64 * ((jj >> 3) & 1));
 
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
+  constexpr int64_t kSrcStride = FP8 ? 1 : kRowBytes;  // TileIt::src units per latent row
   auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
     int lo = 0, hi = a.n_seg - 1;  // last segment starting at or before k_lo
     while (lo < hi) {
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     c.pos0 = k_lo;
     c.pend = min(off + len, k_hi);
     c.nval = min(kKT, c.pend - k_lo);
-    c.row0 = sg[lo].pool_row + (k_lo - off);
+    c.src = (sg[lo].pool_row + (k_lo - off)) * kSrcStride;
   };
   auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) -> bool {
     if (__builtin_expect(c.pos0 + kKT < c.pend, 1)) {
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       nx.pos0 = c.pos0 + kKT;
       nx.pend = c.pend;
       nx.nval = min(kKT, c.pend - nx.pos0);
-      nx.row0 = c.row0 + kKT;
+      nx.src = c.src + kKT * kSrcStride;
       return true;
     }
     if (c.seg + 1 >= a.n_seg) return false;
@@ -428,17 +429,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     nx.pos0 = off;
     nx.pend = min(off + sg[c.seg + 1].len, k_hi);
     nx.nval = min(kKT, nx.pend - off);
-    nx.row0 = sg[c.seg + 1].pool_row;
+    nx.src = sg[c.seg + 1].pool_row * kSrcStride;
     return true;
   };
   auto issue = [&](const TileIt& c, int b) __attribute__((always_inline)) {
     char* buf = lds + b * kTileBytes;
     if constexpr (FP8)
-      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.row0, c.nval, wave);
+      load_tile_e4m3(buf, (const uint8_t*)a.kv, a.kv_scale, (const __bf16*)a.kv_rope, c.src, c.nval, wave);
     else if (__builtin_expect(c.nval == kKT, 1))
-      load_tile_bf16_full(buf, (const char*)a.kv + c.row0 * kRowBytes, wave);
+      load_tile_bf16_full(buf, (const char*)a.kv + c.src, wave);
     else
-      load_tile_bf16(buf, (const char*)a.kv + c.row0 * kRowBytes, c.nval, wave);
+      load_tile_bf16(buf, (const char*)a.kv + c.src, c.nval, wave);
   };
   // q^r <- R(-rot_i) q^r from the stored query, into the slots of steps 32..35
   auto rotate_q = [&](int seg) __attribute__((always_inline)) {
