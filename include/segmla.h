@@ -127,19 +127,23 @@ typedef struct segmla_protect {
   const int32_t *dirty_rows; /* host [n_dirty], may be NULL when n_dirty = 0 */
 } segmla_protect;
 
-/* Device tensors of one forward, all row-major and caller-owned.
- *  q        [T][H][d_nope + d_rope] io_dtype, stored post-RoPE at request position t
+/* Device tensors of one forward, all row-major and caller-owned. A plan computes the
+ * request rows of its window [q_begin, q_end) (the whole request [0, T) for
+ * segmla_plan_create); q, out, z and lse hold those rows only, row t at index t - q_begin.
+ *  q        [q_end - q_begin][H][d_nope + d_rope] io_dtype, stored post-RoPE at request
+ *           position t
  *  kv       F32/BF16: [n_pool][d_nope + d_rope]; E4M3_B128: codes uint8 [n_pool][d_nope]
  *  kv_scale E4M3_B128 only: fp32 [n_pool][d_nope / 128], else NULL
  *  kv_rope  E4M3_B128 only: bf16 [n_pool][d_rope], else NULL
  *  w        [H][d_state][d_v] io_dtype, head h's slice of the first output projection
  *  z_cached [n_pool][H_L][d_state] io_dtype, cached projected contribution of the Local
  *           heads (in head order), indexed by latent-pool row; may be NULL when H_L = 0
- *  out      [T][H][d_v] io_dtype: merged head outputs in request phase; written for
- *           Global heads on every row and for Local heads on rows in A only
- *  z        [T][H][d_state] io_dtype: projected state, every (row, head) written
- *  lse      optional fp32 [T][H]: natural-log log-sum-exp of sigma*q.k for every computed
- *           (row, head); NULL to skip */
+ *  out      [q_end - q_begin][H][d_v] io_dtype: merged head outputs in request phase;
+ *           written for Global heads on every row and for Local heads on rows in A only
+ *  z        [q_end - q_begin][H][d_state] io_dtype: projected state, every (row, head)
+ *           written
+ *  lse      optional fp32 [q_end - q_begin][H]: natural-log log-sum-exp of sigma*q.k for
+ *           every computed (row, head); NULL to skip */
 typedef struct segmla_tensors {
   const void *q;
   const void *kv;
@@ -159,6 +163,18 @@ typedef struct segmla_plan segmla_plan;
 segmla_status segmla_plan_create(const segmla_geometry *geom, const segmla_layer *layer,
                                  const segmla_protect *prot, int64_t n_pool,
                                  segmla_plan **out_plan);
+
+/* The same for the window of request rows [q_begin, q_end) only: chunked prefill, or
+ * decode (a few new rows at the end of a long request). Every window row attends to its
+ * full causal context [0, t] over all segments (relocation paragraph: rotate, attend the
+ * stored latent in place, restore, merge), and the protected set A is the whole
+ * request's, so windows that cover the request in pieces give the rows of the whole-request
+ * forward. The latent pool must hold every row the window sees. Few window rows and a
+ * long context split the key axis (merged by the log-sum-exp merge). Host only;
+ * 0 <= q_begin < q_end <= T, else SEGMLA_E_SHAPE; q_end = -1 means T. */
+segmla_status segmla_plan_create_range(const segmla_geometry *geom, const segmla_layer *layer,
+                                       const segmla_protect *prot, int64_t n_pool,
+                                       int64_t q_begin, int64_t q_end, segmla_plan **out_plan);
 
 /* Device workspace bytes segmla_plan_build needs (host only). */
 segmla_status segmla_plan_workspace_bytes(const segmla_plan *plan, size_t *bytes);
@@ -206,8 +222,8 @@ segmla_status segmla_lse_merge(const float *partial_o, const float *partial_ml, 
                                float *lse, void *stream);
 
 /* Number of (row, head, key) triples the forward computes, by role: out[0] Global
- * heads (every row), out[1] Local heads (rows in A). Needs a built plan; copies the
- * device-side sum over A and synchronizes `stream`. */
+ * heads (every window row), out[1] Local heads (window rows in A). Needs a built plan;
+ * copies the device-side sum over A and synchronizes `stream`. */
 segmla_status segmla_plan_pairs(const segmla_plan *plan, double out[2], void *stream);
 
 /* The analytic ledger, namespaces kept apart (RedKnot-MLA paper, namespaces

@@ -331,6 +331,16 @@ def flops_pairs(T, A, n_global, n_local):
     return g, l_
 
 
+def flops_pairs_window(q0, q1, A, n_global, n_local):
+    """(Global, Local) counts of computed (row, head, key) triples when only the request rows
+    [q0, q1) are computed: each such row t sees t + 1 keys; Local heads only on rows of A."""
+    A = np.asarray(A, dtype=np.int64)
+    g = n_global * (q1 * (q1 + 1) - q0 * (q0 + 1)) // 2
+    inw = A[(A >= q0) & (A < q1)]
+    l_ = n_local * int(np.sum(inw + 1))
+    return g, l_
+
+
 def rel_err_rows(x, ref):
     """Per-(row, head) relative L2 error ||x - ref|| / ||ref|| over the channel axis."""
     x = np.asarray(x, dtype=np.float64)

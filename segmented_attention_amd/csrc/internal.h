@@ -26,42 +26,53 @@ enum : uint8_t { kFlagForced = 1, kFlagCand = 2, kFlagIndexer = 4 };
 // kTileQ consecutive qvecs; tiles [0, nF) are F tiles, [nF, nF + nG) are G tiles.
 constexpr int kTileQ = 128;
 
+// The computed rows are a window [q0, q1) of the request (all of it for a whole prefill).
+// Its rows of A are alist[rng[0], rng[1]) and its other rows nalist[rng[2], rng[3]): both lists
+// cover the whole request in ascending order, so a window is a contiguous range of each. The
+// range ends depend on which rows the Indexer picked, so they live in device memory (written
+// by the plan build); nF and nG are sized for the largest share the window can have, and the
+// tiles past the actual end are empty.
 struct TileMap {
   const int32_t* alist;   // [nA] rows of A, ascending
   const int32_t* nalist;  // [T - nA] rows outside A, ascending
   const int32_t* ghead;   // [HG] Global head ids
-  int32_t nA, nNA, H, HG, nF, nG;
+  const int32_t* rng;     // device {a_lo, a_hi, na_lo, na_hi}
+  int32_t H, HG, nF, nG;
 };
 
 __device__ __forceinline__ bool tile_qvec(const TileMap& m, int tile, int qi, int& t, int& h) {
   if (tile < m.nF) {
+    const int a0 = m.rng[0], na = m.rng[1] - a0;
     int64_t f = (int64_t)tile * kTileQ + qi;
-    if (f >= (int64_t)m.nA * m.H) return false;
+    if (f >= (int64_t)na * m.H) return false;
     int a = (int)(f / m.H);
     h = (int)(f - (int64_t)a * m.H);
-    t = m.alist[a];
+    t = m.alist[a0 + a];
   } else {
+    const int b0 = m.rng[2], nb = m.rng[3] - b0;
     int64_t f = (int64_t)(tile - m.nF) * kTileQ + qi;
-    if (f >= (int64_t)m.nNA * m.HG) return false;
+    if (f >= (int64_t)nb * m.HG) return false;
     int a = (int)(f / m.HG);
     h = m.ghead[(int)(f - (int64_t)a * m.HG)];
-    t = m.nalist[a];
+    t = m.nalist[b0 + a];
   }
   return true;
 }
 
-// Largest request row among a tile's qvecs (lists are ascending).
+// Largest request row among a tile's qvecs (lists are ascending); -1 for an empty tile.
 __device__ __forceinline__ int tile_max_row(const TileMap& m, int tile) {
   if (tile < m.nF) {
-    int64_t last = (int64_t)tile * kTileQ + kTileQ - 1;
-    int64_t cap = (int64_t)m.nA * m.H - 1;
-    if (last > cap) last = cap;
-    return m.alist[(int)(last / m.H)];
+    const int a0 = m.rng[0], na = m.rng[1] - a0;
+    const int64_t first = (int64_t)tile * kTileQ, cap = (int64_t)na * m.H - 1;
+    if (first > cap) return -1;
+    const int64_t last = first + kTileQ - 1 < cap ? first + kTileQ - 1 : cap;
+    return m.alist[a0 + (int)(last / m.H)];
   }
-  int64_t last = (int64_t)(tile - m.nF) * kTileQ + kTileQ - 1;
-  int64_t cap = (int64_t)m.nNA * m.HG - 1;
-  if (last > cap) last = cap;
-  return m.nalist[(int)(last / m.HG)];
+  const int b0 = m.rng[2], nb = m.rng[3] - b0;
+  const int64_t first = (int64_t)(tile - m.nF) * kTileQ, cap = (int64_t)nb * m.HG - 1;
+  if (first > cap) return -1;
+  const int64_t last = first + kTileQ - 1 < cap ? first + kTileQ - 1 : cap;
+  return m.nalist[b0 + (int)(last / m.HG)];
 }
 
 // Index of the segment containing request row `row` (segments contiguous from 0).
@@ -76,12 +87,12 @@ __device__ __forceinline__ int seg_of(const SegDesc* seg, int n_seg, int row) {
 
 // Arguments of the attention kernels (one struct so every variant shares the launch code).
 struct AttnArgs {
-  const void* q;          // [T][H][d_qk] io dtype
+  const void* q;          // [q1 - q0][H][d_qk] io dtype (row t at t - q0)
   const void* kv;         // latent pool (f32 / bf16 rows, or E4M3 codes)
   const float* kv_scale;  // E4M3: [n_pool][d_nope/128]
   const void* kv_rope;    // E4M3: [n_pool][d_rope] bf16
-  void* out;              // [T][H][d_v] io dtype (unsplit)
-  float* lse;             // [T][H] or null (unsplit)
+  void* out;              // [q1 - q0][H][d_v] io dtype (unsplit)
+  float* lse;             // [q1 - q0][H] or null (unsplit)
   float* part_o;          // [n_split][nTiles*kTileQ][d_v] (split)
   float* part_ml;         // [n_split][nTiles*kTileQ][2] (split)
   const SegDesc* seg;
@@ -90,6 +101,7 @@ struct AttnArgs {
   const int32_t* work;    // [nF + nG] tile ids in decreasing cost order
   TileMap map;
   int32_t n_seg, T, d_nope, d_rope, d_v;
+  int32_t q0;             // first computed row: q, out and lse rows are t - q0
   int32_t n_split, split_keys;
   float sigma;            // softmax scale
 };
@@ -103,7 +115,7 @@ hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_r
                           const uint32_t* score, int64_t need, uint8_t* flags,
                           uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,
                           int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
-                          hipStream_t stream);
+                          int q0, int q1, int32_t* rng, hipStream_t stream);
 hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
 hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream);
@@ -111,19 +123,22 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_spl
                             int d, void* out, int out_dtype, float* lse, hipStream_t stream);
 
 struct EpiArgs {
-  const void* out;        // [T][H][d_v] merged head outputs
+  const void* out;        // [nq][H][d_v] merged head outputs (row t at t - q0)
   const void* w;          // [H][d_state][d_v]
   void* wt;               // W in the projection's MFMA operand order (bf16; see k_w_tile)
   const void* z_cached;   // [n_pool][HL][d_state]
-  void* z;                // [T][H][d_state]
+  void* z;                // [nq][H][d_state] (row t at t - q0)
   const float2* rowcs;    // [T][d_rope/2]
   const int32_t* alist;
   const int32_t* nalist;
+  const int32_t* rng;     // device {a_lo, a_hi, na_lo, na_hi} (see TileMap)
   const int32_t* ghead;   // [HG]
   const int32_t* lhead;   // [HL]
   const int32_t* seg_of_row;
   const SegDesc* seg;
-  int32_t T, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;
+  // window [q0, q0 + nq); nA, nNA: the largest number of its rows inside / outside A (grid
+  // sizes; the actual numbers are in rng)
+  int32_t q0, nq, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;
 };
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
 

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     if (k_lo > tile_max_row(a.map, tile)) return;  // this split is not read by the merge
     k_hi = min(k_hi, k_lo + S);
   }
-  const float* q = (const float*)a.q + ((int64_t)t * a.map.H + h) * d_qk;
+  const float* q = (const float*)a.q + ((int64_t)(t - a.q0) * a.map.H + h) * d_qk;
   for (int d = lane; d < d_qk; d += 64) q0[d] = q[d];
   const float* kv = (const float*)a.kv;
 
@@ -136,13 +136,13 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
     return;
   }
   const float inv = 1.f / l;
-  float* o = (float*)a.out + ((int64_t)t * a.map.H + h) * d_v;
+  float* o = (float*)a.out + ((int64_t)(t - a.q0) * a.map.H + h) * d_v;
   for (int r = 0; r < kMaxPairsPerLane; ++r) {
     int d0 = 2 * (lane + 64 * r);
     if (d0 < d_v) o[d0] = acc[2 * r] * inv;
     if (d0 + 1 < d_v) o[d0 + 1] = acc[2 * r + 1] * inv;
   }
-  if (a.lse && lane == 0) a.lse[(int64_t)t * a.map.H + h] = m + logf(l);
+  if (a.lse && lane == 0) a.lse[(int64_t)(t - a.q0) * a.map.H + h] = m + logf(l);
 }
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   if (k_lo >= k_hi) return;  // uniform over the workgroup
 
   const float qk_scale = a.sigma * kLog2e;
-  const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t : 0) * a.map.H + h) * kD;
+  const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t - a.q0 : 0) * a.map.H + h) * kD;
   // B operand of S^T = K Q^T, step s: lane holds Q[qvec col][16 s + 8 hf + 0..7]
   bf16x8 qf[kQReg];
 #pragma unroll
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   }
   if (!valid) return;
   const float inv = 1.f / l_tot;
-  __bf16* o = (__bf16*)a.out + ((int64_t)t * a.map.H + h) * d_v;
+  __bf16* o = (__bf16*)a.out + ((int64_t)(t - a.q0) * a.map.H + h) * d_v;
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const floatx16 x = tile_vgpr(f);
@@ -738,7 +738,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       *(bf16x4*)(o + 32 * f + 8 * (i >> 2) + 4 * hf) = y;
     }
   }
-  if (a.lse && hf == 0) a.lse[(int64_t)t * a.map.H + h] = (m_run + log2f(l_tot)) * kLn2;
+  if (a.lse && hf == 0) a.lse[(int64_t)(t - a.q0) * a.map.H + h] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 namespace {

@@ -11,32 +11,36 @@ namespace segmla {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-// Row t of head h's list: Global heads walk every request row, Local heads walk A.
+// Row i of head h's list: Global heads walk every row of the window [q0, q0 + nq), Local
+// heads its rows of A (alist[rng[0], rng[1])). Local tiles are laid out for the largest
+// possible count (e.nA); tiles past the actual count are empty (n_rows <= r0).
 struct EpiTile {
-  int h, r0, n_rows;
-  const int32_t* rows;  // null = identity (row index = request row)
+  int h, r0, n_rows, q0;
+  const int32_t* rows;  // null = the window's rows in order (request row q0 + i)
 };
 
 __device__ __forceinline__ EpiTile epi_tile(const EpiArgs& e, int b, int rows_per_tile) {
   EpiTile et;
-  const int tg = (e.T + rows_per_tile - 1) / rows_per_tile;
+  et.q0 = e.q0;
+  const int tg = (e.nq + rows_per_tile - 1) / rows_per_tile;
   if (b < e.HG * tg) {
     et.h = e.ghead[b / tg];
     et.r0 = (b % tg) * rows_per_tile;
-    et.n_rows = e.T;
+    et.n_rows = e.nq;
     et.rows = nullptr;
   } else {
     b -= e.HG * tg;
     const int ta = (e.nA + rows_per_tile - 1) / rows_per_tile;
     et.h = e.lhead[b / ta];
     et.r0 = (b % ta) * rows_per_tile;
-    et.n_rows = e.nA;
-    et.rows = e.alist;
+    et.n_rows = e.rng[1] - e.rng[0];
+    et.rows = e.alist + e.rng[0];
   }
   return et;
 }
 
-__device__ __forceinline__ int epi_row(const EpiTile& et, int i) { return et.rows ? et.rows[i] : i; }
+// request row of list entry i
+__device__ __forceinline__ int epi_row(const EpiTile& et, int i) { return et.rows ? et.rows[i] : et.q0 + i; }
 
 // ------------------------------------------------------------------------ fp32 path
 // One wavefront per (row, head): u staged in LDS, each lane produces d_state/64 outputs.
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
   EpiTile et = epi_tile(e, blockIdx.x, 1);
   if (et.r0 >= et.n_rows) return;
   const int t = epi_row(et, et.r0), h = et.h;
-  const float* o = (const float*)e.out + ((int64_t)t * e.H + h) * e.d_v;
+  const float* o = (const float*)e.out + ((int64_t)(t - e.q0) * e.H + h) * e.d_v;
   for (int d = lane; d < e.d_v; d += 64) u[d] = o[d];
   __syncthreads();
   if (e.v_has_rope) {
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
   }
   __syncthreads();
   const float* w = (const float*)e.w + (int64_t)h * e.d_state * e.d_v;
-  float* z = (float*)e.z + ((int64_t)t * e.H + h) * e.d_state;
+  float* z = (float*)e.z + ((int64_t)(t - e.q0) * e.H + h) * e.d_state;
   for (int c = lane; c < e.d_state; c += 64) {
     const float* wr = w + (int64_t)c * e.d_v;
     float acc = 0.f;
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
   EpiTile et = epi_tile(e, blockIdx.x, kEpiRows);
   const int h = et.h;
   const int n_here = min(kEpiRows, et.n_rows - et.r0);
+  if (n_here <= 0) return;  // uniform: a Local tile past the window's rows of A
   const int d_v = e.d_v, half_r = e.d_rope / 2;
   const bool rope = e.v_has_rope != 0;  // d_v = 576 (else 512: nope only)
   const int64_t hstride = (int64_t)d_v * 2;
@@ -128,14 +133,14 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
     for (int n = 0; n < kEpiRows / 4; ++n) {
       const int r = wave + 4 * n;
       const int t = __builtin_amdgcn_readfirstlane(row_id[r]);
-      dma16(outb + (int64_t)t * e.H * hstride, (lane * 16) ^ (fn(r) << 4), base + r * kEpiNRow);
+      dma16(outb + (int64_t)(t - e.q0) * e.H * hstride, (lane * 16) ^ (fn(r) << 4), base + r * kEpiNRow);
     }
     if (rope) {
       for (int m = 0; m < kEpiRows / 32; ++m) {  // 8 RoPE rows per copy
         const int q = wave + 4 * m;
         const int r = 8 * q + (lane >> 3);
         const int t = row_id[r];
-        dma16_v(outb + (int64_t)t * e.H * hstride + kEpiNRow + (((lane & 7) ^ fr(r)) << 4),
+        dma16_v(outb + (int64_t)(t - e.q0) * e.H * hstride + kEpiNRow + (((lane & 7) ^ fr(r)) << 4),
                 base + kEpiRBase + q * 1024);
       }
     }
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (rows_t[i] < 0) continue;
-        __bf16* z = (__bf16*)e.z + ((int64_t)rows_t[i] * e.H + h) * e.d_state + cbase;
+        __bf16* z = (__bf16*)e.z + ((int64_t)(rows_t[i] - e.q0) * e.H + h) * e.d_state + cbase;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -271,13 +276,16 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 
 // ------------------------------------------------------------------- restore copy
 // Local heads on rows outside A: Z[t][lhead[l]] = Zc[pool_row(t)][l], copied bit for bit.
+// One block per window row outside A (nalist[rng[2], rng[3])); the grid is laid out for the
+// largest possible count.
 template <typename V>
 __global__ __launch_bounds__(256) void k_restore_copy(EpiArgs e, int vec_per_head) {
-  const int t = e.nalist[blockIdx.x];
+  if ((int)blockIdx.x >= e.rng[3] - e.rng[2]) return;
+  const int t = e.nalist[e.rng[2] + blockIdx.x];
   const SegDesc sd = e.seg[e.seg_of_row[t]];
   const int64_t prow = sd.pool_row + (t - sd.offset);
   const V* src = (const V*)e.z_cached + prow * (int64_t)e.HL * vec_per_head;
-  V* dst = (V*)e.z + (int64_t)t * e.H * vec_per_head;
+  V* dst = (V*)e.z + (int64_t)(t - e.q0) * e.H * vec_per_head;
   const int n = e.HL * vec_per_head;
   for (int i = threadIdx.x; i < n; i += 256) {
     const int l = i / vec_per_head, c = i - l * vec_per_head;
@@ -287,13 +295,13 @@ __global__ __launch_bounds__(256) void k_restore_copy(EpiArgs e, int vec_per_hea
 
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
   if (io_dtype == 0) {
-    const int64_t blocks = (int64_t)e.HG * e.T + (int64_t)e.HL * e.nA;
+    const int64_t blocks = (int64_t)e.HG * e.nq + (int64_t)e.HL * e.nA;
     if (blocks > 0)
       hipLaunchKernelGGL(k_project_f32, dim3((unsigned)blocks), dim3(64), 0, stream, e);
     if (e.HL > 0 && e.nNA > 0)
       hipLaunchKernelGGL(k_restore_copy<float>, dim3(e.nNA), dim3(256), 0, stream, e, e.d_state);
   } else {
-    const int64_t blocks = (int64_t)e.HG * ((e.T + kEpiRows - 1) / kEpiRows) +
+    const int64_t blocks = (int64_t)e.HG * ((e.nq + kEpiRows - 1) / kEpiRows) +
                            (int64_t)e.HL * ((e.nA + kEpiRows - 1) / kEpiRows);
     const size_t lds = kEpiLds;
     static bool attr_set = false;

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_merge_tiles(AttnArgs a) {
   int t, h;
   if (!tile_qvec(a.map, tile, qi, t, h)) return;
   const int n_valid = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);
-  const int64_t o = (int64_t)t * a.map.H + h;
+  const int64_t o = (int64_t)(t - a.q0) * a.map.H + h;
   merge_vec(a.part_o, a.part_ml, n_valid, nvec, v, a.d_v, (OutT*)a.out + o * a.d_v,
             a.lse ? a.lse + o : nullptr, lane);
 }

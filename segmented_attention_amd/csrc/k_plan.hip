@@ -206,14 +206,17 @@ constexpr int kScanBlock = 1024;
 
 __device__ __forceinline__ bool in_a(uint8_t f) { return (f & (kFlagForced | kFlagIndexer)) != 0; }
 
+// Per block of rows: how many are in A, and the sum of t + 1 over its rows of A inside the
+// computed window [q0, q1) (the Local heads' key count there).
 __global__ __launch_bounds__(kScanBlock) void k_count_a(const uint8_t* __restrict__ flags, int T,
+                                                        int q0, int q1,
                                                         int32_t* __restrict__ blk_count,
                                                         uint64_t* __restrict__ blk_sum) {
   __shared__ uint32_t c[kScanBlock / 64];
   __shared__ uint64_t sm[kScanBlock / 64];
   int t = blockIdx.x * kScanBlock + threadIdx.x;
   bool a = t < T && in_a(flags[t]);
-  uint64_t v = a ? (uint64_t)t + 1 : 0;
+  uint64_t v = (a && t >= q0 && t < q1) ? (uint64_t)t + 1 : 0;
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   uint64_t bal = __ballot(a);
   if ((threadIdx.x & 63) == 0) { c[threadIdx.x >> 6] = __popcll(bal); sm[threadIdx.x >> 6] = v; }
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kScanBlock) void k_count_a(const uint8_t* __restric
   }
 }
 
-// Exclusive scan of the per-block counts (in place) and the total of sum(t + 1) over A.
+// Exclusive scan of the per-block counts (in place) and the total of the window sums.
 __global__ __launch_bounds__(1024) void k_scan_counts(int32_t* __restrict__ blk_count,
                                                       const uint64_t* __restrict__ blk_sum,
                                                       int n_blk, uint64_t* __restrict__ sum_a) {
@@ -258,10 +261,14 @@ __global__ __launch_bounds__(1024) void k_scan_counts(int32_t* __restrict__ blk_
   }
 }
 
+// Scatter of the rows of A and of the other rows into their ascending lists. The window
+// [q0, q1) is the range alist[rng[0], rng[1]) and nalist[rng[2], rng[3]): the ranks of q0 and
+// q1 in the two lists, written by the threads of rows q0 and q1 (q1 = T: the last row).
 __global__ __launch_bounds__(kScanBlock) void k_scatter_a(const uint8_t* __restrict__ flags, int T,
                                                           const int32_t* __restrict__ blk_off,
                                                           int32_t* __restrict__ alist,
-                                                          int32_t* __restrict__ nalist, int nA) {
+                                                          int32_t* __restrict__ nalist, int nA,
+                                                          int q0, int q1, int32_t* __restrict__ rng) {
   __shared__ uint32_t c[kScanBlock / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int t = blockIdx.x * kScanBlock + threadIdx.x;
@@ -274,6 +281,18 @@ __global__ __launch_bounds__(kScanBlock) void k_scatter_a(const uint8_t* __restr
   for (int w = 0; w < wave; ++w) before += c[w];
   if (valid) {
     int32_t off = blk_off[blockIdx.x];
+    const int32_t a_before = off + (int32_t)before;  // rows of A before row t
+    if (t == q0) {
+      rng[0] = a_before;
+      rng[2] = t - a_before;
+    }
+    if (t == q1) {
+      rng[1] = a_before;
+      rng[3] = t - a_before;
+    } else if (q1 == T && t == T - 1) {
+      rng[1] = a_before + (a ? 1 : 0);
+      rng[3] = T - rng[1];
+    }
     // the host sized both lists from the same rule; the bounds only guard the workspace
     if (a) {
       if (off + (int)before < nA) alist[off + before] = t;
@@ -290,7 +309,7 @@ hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_r
                           const uint32_t* score, int64_t need, uint8_t* flags,
                           uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,
                           int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
-                          hipStream_t stream) {
+                          int q0, int q1, int32_t* rng, hipStream_t stream) {
   (void)n_seg;
   (void)sel_state;
   int blocks = (T + 255) / 256;
@@ -300,40 +319,54 @@ hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_r
   if (need > 0)
     hipLaunchKernelGGL(k_protect_select, dim3(1), dim3(kSelThreads), 0, stream, flags, score, T,
                        (uint32_t)need);
-  hipLaunchKernelGGL(k_count_a, dim3(n_blk), dim3(kScanBlock), 0, stream, flags, T, blk_count,
-                     blk_sum);
+  hipLaunchKernelGGL(k_count_a, dim3(n_blk), dim3(kScanBlock), 0, stream, flags, T, q0, q1,
+                     blk_count, blk_sum);
   hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, stream, blk_count, blk_sum, n_blk,
                      sum_a);
   hipLaunchKernelGGL(k_scatter_a, dim3(n_blk), dim3(kScanBlock), 0, stream, flags, T, blk_count,
-                     alist, nalist, n_a);
+                     alist, nalist, n_a, q0, q1, rng);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------ work list
 // Tiles sorted by decreasing largest row (their key count), F and G tiles interleaved by a
 // merge-by-rank: each tile's rank = its position in its own descending list plus the number
-// of tiles of the other list that sort before it (equal costs: F tiles first).
+// of tiles of the other list that sort before it (equal costs: F tiles first). Only the first
+// nF_act / nG_act tiles of each stream hold rows (a row window can fill less than the host's
+// sizing); the empty ones take the last ranks, so `work` stays a permutation of all tiles.
 __global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
-  int n = m.nF + m.nG;
+  const int n = m.nF + m.nG;
+  const int nF_act = (int)(((int64_t)(m.rng[1] - m.rng[0]) * m.H + kTileQ - 1) / kTileQ);
+  const int nG_act = (int)(((int64_t)(m.rng[3] - m.rng[2]) * m.HG + kTileQ - 1) / kTileQ);
+  const int n_act = nF_act + nG_act;
   for (int tile = blockIdx.x * blockDim.x + threadIdx.x; tile < n; tile += gridDim.x * blockDim.x) {
-    int c = tile_max_row(m, tile);
     int rank;
     if (tile < m.nF) {
-      // G tiles with cost > c: nG - (#G tiles with cost <= c)
-      int lo = 0, hi = m.nG;  // first G index with cost > c
-      while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (tile_max_row(m, m.nF + mid) > c) hi = mid; else lo = mid + 1;
+      if (tile >= nF_act) {
+        rank = n_act + (tile - nF_act);
+      } else {
+        const int c = tile_max_row(m, tile);
+        // G tiles with cost > c: nG_act - (#G tiles with cost <= c)
+        int lo = 0, hi = nG_act;  // first G index with cost > c
+        while (lo < hi) {
+          int mid = (lo + hi) >> 1;
+          if (tile_max_row(m, m.nF + mid) > c) hi = mid; else lo = mid + 1;
+        }
+        rank = (nF_act - 1 - tile) + (nG_act - lo);
       }
-      rank = (m.nF - 1 - tile) + (m.nG - lo);
     } else {
-      int k = tile - m.nF;
-      int lo = 0, hi = m.nF;  // first F index with cost >= c
-      while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (tile_max_row(m, mid) >= c) hi = mid; else lo = mid + 1;
+      const int k = tile - m.nF;
+      if (k >= nG_act) {
+        rank = n_act + (m.nF - nF_act) + (k - nG_act);
+      } else {
+        const int c = tile_max_row(m, tile);
+        int lo = 0, hi = nF_act;  // first F index with cost >= c
+        while (lo < hi) {
+          int mid = (lo + hi) >> 1;
+          if (tile_max_row(m, mid) >= c) hi = mid; else lo = mid + 1;
+        }
+        rank = (nG_act - 1 - k) + (nF_act - lo);
       }
-      rank = (m.nG - 1 - k) + (m.nF - lo);
     }
     work[rank] = tile;
   }

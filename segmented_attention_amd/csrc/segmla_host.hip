@@ -15,6 +15,7 @@ struct segmla_plan {
   // geometry
   int32_t n_seg = 0;
   int32_t T = 0;
+  int32_t q0 = 0, q1 = 0;  // computed window of request rows [q0, q1)
   int64_t n_pool = 0;
   std::vector<SegDesc> segs;
   // layer
@@ -33,7 +34,9 @@ struct segmla_plan {
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
-         ws_bytes = 0;
+         o_rng = 0, ws_bytes = 0;
+  // largest number of window rows inside / outside A (the Indexer picks decide the actual)
+  int64_t nA_w = 0, nNA_w = 0;
   // profiling (events on the caller's stream)
   bool prof = false, fwd_pending = false, build_pending = false;
   hipEvent_t ev[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
@@ -144,6 +147,12 @@ const char* segmla_status_string(int32_t s) {
 segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer* layer,
                                  const segmla_protect* prot, int64_t n_pool,
                                  segmla_plan** out_plan) {
+  return segmla_plan_create_range(geom, layer, prot, n_pool, 0, -1, out_plan);
+}
+
+segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla_layer* layer,
+                                       const segmla_protect* prot, int64_t n_pool,
+                                       int64_t q_begin, int64_t q_end, segmla_plan** out_plan) {
   if (!geom || !layer || !prot || !out_plan) return SEGMLA_E_NULL;
   segmla_status st = check_layer(layer);
   if (st != SEGMLA_OK) return st;
@@ -151,6 +160,8 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
   st = check_geometry(geom, n_pool, &T64);
   if (st != SEGMLA_OK) return st;
   const int32_t T = (int32_t)T64;
+  if (q_end == -1) q_end = T;
+  if (q_begin < 0 || q_end <= q_begin || q_end > T) return SEGMLA_E_SHAPE;
   if (prot->edge_rows < 0 || prot->tail_rows < 0 || prot->budget_permille < 0 ||
       prot->budget_permille > 1000 || prot->n_dirty < 0)
     return SEGMLA_E_PROTECT;
@@ -162,6 +173,8 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
   if (!p) return SEGMLA_E_UNSUPPORTED;
   p->n_seg = geom->n_seg;
   p->T = T;
+  p->q0 = (int32_t)q_begin;
+  p->q1 = (int32_t)q_end;
   p->n_pool = n_pool;
   p->segs.resize(geom->n_seg);
   for (int i = 0; i < geom->n_seg; ++i) {
@@ -227,25 +240,31 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
     p->nA = nf + p->need;
   }
 
-  // Work decomposition: qvec tiles of stream F (rows of A x all heads) and stream G (other
-  // rows x Global heads), optionally split along the key axis.
-  const int64_t qF = p->nA * p->H, qG = ((int64_t)T - p->nA) * p->HG;
+  // Work decomposition: qvec tiles of stream F (window rows of A x all heads) and stream G
+  // (other window rows x Global heads), optionally split along the key axis. For a window
+  // smaller than the request, the split between the streams depends on the Indexer picks:
+  // both are sized for their largest share.
+  const int64_t L = (int64_t)p->q1 - p->q0;
+  p->nA_w = std::min<int64_t>(p->nA, L);
+  p->nNA_w = std::min<int64_t>((int64_t)T - p->nA, L);
+  const int64_t qF = p->nA_w * p->H, qG = p->nNA_w * p->HG;
   const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
   if (nF + nG > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
   p->nF = (int32_t)nF;
   p->nG = (int32_t)nG;
   const int64_t n_tiles = nF + nG;
   int32_t sk = layer->split_keys;
+  const int32_t keys = p->q1;  // the window's rows see keys [0, q1) at most
   if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
     sk = -1;
-    if (n_tiles > 0 && n_tiles < 2 * kNumCU && T > 2048) {
-      int64_t want = std::min<int64_t>((4 * kNumCU + n_tiles - 1) / n_tiles, (T + 1023) / 1024);
-      if (want > 1) sk = (int32_t)((((T + want - 1) / want) + 63) / 64 * 64);
+    if (n_tiles > 0 && n_tiles < 2 * kNumCU && keys > 2048) {
+      int64_t want = std::min<int64_t>((4 * kNumCU + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
+      if (want > 1) sk = (int32_t)((((keys + want - 1) / want) + 63) / 64 * 64);
     }
   }
-  if (sk > 0 && sk < T) {
+  if (sk > 0 && sk < keys) {
     p->split_keys = sk;
-    p->n_split = (int32_t)((T + sk - 1) / sk);
+    p->n_split = (int32_t)((keys + sk - 1) / sk);
   } else {
     p->split_keys = 0;
     p->n_split = 1;
@@ -271,6 +290,7 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
   p->o_blk_sum = take(sizeof(uint64_t) * p->n_blk);
   p->o_sum_a = take(sizeof(uint64_t));
   p->o_sel = take(sizeof(uint32_t) * 4);
+  p->o_rng = take(sizeof(int32_t) * 4);
   p->o_work = take(sizeof(int32_t) * (size_t)n_tiles);
   if (p->n_split > 1) {
     const size_t nvec = (size_t)n_tiles * kTileQ;
@@ -302,8 +322,7 @@ static TileMap tile_map(const segmla_plan* p) {
   m.alist = p->at<int32_t>(p->o_alist);
   m.nalist = p->at<int32_t>(p->o_nalist);
   m.ghead = p->at<int32_t>(p->o_ghead);
-  m.nA = (int32_t)p->nA;
-  m.nNA = p->T - (int32_t)p->nA;
+  m.rng = p->at<int32_t>(p->o_rng);
   m.H = p->H;
   m.HG = p->HG;
   m.nF = p->nF;
@@ -341,7 +360,7 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
                      indexer_score, p->need, p->at<uint8_t>(p->o_flags), p->at<uint32_t>(p->o_sel),
                      p->at<int32_t>(p->o_blk_count), p->at<uint64_t>(p->o_blk_sum), p->n_blk,
                      p->at<int32_t>(p->o_alist), p->at<int32_t>(p->o_nalist), (int)p->nA,
-                     p->at<uint64_t>(p->o_sum_a), s);
+                     p->at<uint64_t>(p->o_sum_a), p->q0, p->q1, p->at<int32_t>(p->o_rng), s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
   e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
@@ -379,6 +398,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   a.d_nope = p->d_nope;
   a.d_rope = p->d_rope;
   a.d_v = p->d_v;
+  a.q0 = p->q0;
   a.n_split = p->n_split;
   a.split_keys = p->split_keys;
   a.sigma = p->sigma;
@@ -402,16 +422,18 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   ep.rowcs = p->at<float2>(p->o_rowcs);
   ep.alist = p->at<int32_t>(p->o_alist);
   ep.nalist = p->at<int32_t>(p->o_nalist);
+  ep.rng = p->at<int32_t>(p->o_rng);
   ep.ghead = p->at<int32_t>(p->o_ghead);
   ep.lhead = p->at<int32_t>(p->o_lhead);
   ep.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
   ep.seg = p->at<SegDesc>(p->o_seg);
-  ep.T = p->T;
+  ep.q0 = p->q0;
+  ep.nq = p->q1 - p->q0;
   ep.H = p->H;
   ep.HG = p->HG;
   ep.HL = p->HL;
-  ep.nA = (int32_t)p->nA;
-  ep.nNA = p->T - (int32_t)p->nA;
+  ep.nA = (int32_t)p->nA_w;
+  ep.nNA = (int32_t)p->nNA_w;
   ep.d_nope = p->d_nope;
   ep.d_rope = p->d_rope;
   ep.d_v = p->d_v;
@@ -495,8 +517,8 @@ segmla_status segmla_plan_pairs(const segmla_plan* p, double out[2], void* strea
           hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return SEGMLA_E_HIP;
-  const double T = (double)p->T;
-  out[0] = (double)p->HG * T * (T + 1.0) / 2.0;
+  const double q0 = (double)p->q0, q1 = (double)p->q1;  // window rows t see t + 1 keys
+  out[0] = (double)p->HG * (q1 * (q1 + 1.0) - q0 * (q0 + 1.0)) / 2.0;
   out[1] = (double)p->HL * (double)sum_a;
   return SEGMLA_OK;
 }

@@ -25,6 +25,7 @@ EXPORTED = [
     "segmla_forward", "segmla_copy_protected", "segmla_copy_geometry", "segmla_lse_merge",
     "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
     "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
+    "segmla_plan_create_range",
 ]
 
 
@@ -75,6 +76,9 @@ def lib():
         sig = {
             "segmla_plan_create": (i32, [ctypes.POINTER(Geometry), ctypes.POINTER(Layer),
                                          ctypes.POINTER(Protect), i64, ctypes.POINTER(P)]),
+            "segmla_plan_create_range": (i32, [ctypes.POINTER(Geometry), ctypes.POINTER(Layer),
+                                               ctypes.POINTER(Protect), i64, i64, i64,
+                                               ctypes.POINTER(P)]),
             "segmla_plan_workspace_bytes": (i32, [P, ctypes.POINTER(ctypes.c_size_t)]),
             "segmla_plan_rows": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
             "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
@@ -139,8 +143,9 @@ def segmla_status_string(status):
 def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is_global, d_nope,
                        d_rope, d_state, v_has_rope=1, rope_base=10000.0, softmax_scale=1.0,
                        kv_dtype=SEGMLA_BF16, io_dtype=SEGMLA_BF16, split_keys=0, edge_rows=0,
-                       tail_rows=0, budget_permille=0, dirty_rows=()):
-    """Validate and size a plan; returns (plan handle, keepalive) -- see Plan for lifetime."""
+                       tail_rows=0, budget_permille=0, dirty_rows=(), q_range=None):
+    """Validate and size a plan; returns the plan handle. q_range = (q_begin, q_end): a plan
+    for that window of request rows (segmla_plan_create_range); None: the whole request."""
     keep = dict(kind=_arr(kinds, np.uint8), len=_arr(lens, np.int32), offset=_arr(offsets, np.int64),
                 pool=_arr(pool_rows, np.int64), glob=_arr(head_is_global, np.uint8),
                 dirty=_arr(list(dirty_rows), np.int32))
@@ -155,8 +160,13 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                  keep["dirty"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(keep["dirty"])
                  else None)
     h = ctypes.c_void_p()
-    _check(lib().segmla_plan_create(ctypes.byref(g), ctypes.byref(L), ctypes.byref(pr), int(n_pool),
-                                    ctypes.byref(h)), "segmla_plan_create")
+    if q_range is None:
+        _check(lib().segmla_plan_create(ctypes.byref(g), ctypes.byref(L), ctypes.byref(pr),
+                                        int(n_pool), ctypes.byref(h)), "segmla_plan_create")
+    else:
+        _check(lib().segmla_plan_create_range(ctypes.byref(g), ctypes.byref(L), ctypes.byref(pr),
+                                              int(n_pool), int(q_range[0]), int(q_range[1]),
+                                              ctypes.byref(h)), "segmla_plan_create_range")
     return h
 
 
@@ -250,15 +260,17 @@ class Plan:
     """A plan plus its device workspace (torch uint8 tensor on the current GPU)."""
 
     def __init__(self, cfg, kinds, lens, offsets, pool_rows, n_pool, head_is_global, split_keys=0,
-                 dirty_rows=()):
+                 dirty_rows=(), q_range=None):
         d_v = cfg["d_nope"] + cfg["d_rope"] if cfg["v_has_rope"] else cfg["d_nope"]
         self.cfg, self.d_v = cfg, d_v
         self.handle = segmla_plan_create(
             kinds, lens, offsets, pool_rows, n_pool, cfg["n_heads"], head_is_global, cfg["d_nope"],
             cfg["d_rope"], cfg["d_state"], cfg["v_has_rope"], cfg["rope_base"], cfg["softmax_scale"],
             _DT[cfg["kv_dtype"]], _DT[cfg["dtype"]], split_keys, cfg["edge_rows"], cfg["tail_rows"],
-            cfg["budget_permille"], dirty_rows)
+            cfg["budget_permille"], dirty_rows, q_range)
         self.T, self.n_protected = segmla_plan_rows(self.handle)
+        # computed window: q, out, z and lse hold rows q0 .. q1 - 1
+        self.q0, self.q1 = (0, self.T) if q_range is None else (int(q_range[0]), int(q_range[1]))
         self.workspace = None
 
     def build(self, scores=None, stream=None):
@@ -269,7 +281,12 @@ class Plan:
         segmla_plan_build(self.handle, self.workspace, scores, stream)
 
     def forward(self, inp, out, z, lse=None, stream=None):
-        segmla_forward(self.handle, inp["q"], inp["kv"], inp["w"], out, z, inp.get("z_cached"),
+        """out, z, lse: the window's rows. inp["q"] may hold the whole request (its window
+        rows are passed, a view) or the window only."""
+        q = inp["q"]
+        if q.shape[0] != self.q1 - self.q0:
+            q = q[self.q0:self.q1]
+        segmla_forward(self.handle, q, inp["kv"], inp["w"], out, z, inp.get("z_cached"),
                        inp.get("kv_scale"), inp.get("kv_rope"), lse, stream)
 
     def protected(self):
@@ -293,6 +310,7 @@ class Plan:
             pass
 
     @classmethod
-    def for_inputs(cls, inp, split_keys=0):
+    def for_inputs(cls, inp, split_keys=0, q_range=None):
         return cls(inp["cfg"], inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"],
-                   inp["n_pool"], inp["head_is_global"], split_keys, inp["cfg"].get("dirty_rows", ()))
+                   inp["n_pool"], inp["head_is_global"], split_keys, inp["cfg"].get("dirty_rows", ()),
+                   q_range)

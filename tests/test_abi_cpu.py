@@ -89,6 +89,27 @@ def test_plan_rows_match_oracle(L, cfg):
         S.segmla_plan_destroy(p)
 
 
+def test_range_errors(L):
+    """Row windows: 0 <= q_begin < q_end <= T (q_end = -1: T); |A| stays the request's."""
+    cfg = SMALL_CONFIGS[1]
+    kinds, lens, offsets = segment_table(cfg)
+    T = int(lens.sum())
+    full = _create(cfg)
+    try:
+        T0, nA0 = S.segmla_plan_rows(full)
+    finally:
+        S.segmla_plan_destroy(full)
+    for rng in [(0, T), (0, -1), (0, 1), (T - 1, T), (37, 300)]:
+        p = _create(cfg, q_range=rng)
+        try:
+            assert S.segmla_plan_rows(p) == (T0, nA0)
+            assert S.segmla_plan_workspace_bytes(p) > 0
+        finally:
+            S.segmla_plan_destroy(p)
+    for rng in [(-1, 5), (5, 5), (6, 5), (0, T + 1), (T, T + 1)]:
+        assert _status(cfg, q_range=rng) == S.SEGMLA_E_SHAPE, rng
+
+
 def test_geometry_errors(L):
     cfg = SMALL_CONFIGS[1]
     kinds, lens, offsets = segment_table(cfg)

@@ -1,0 +1,104 @@
+"""GPU parity of row-window plans (segmla_plan_create_range): chunked prefill and decode.
+
+A window plan computes the request rows [q_begin, q_end) with their full causal context over
+all segments, and the whole request's protected set A. Without a key split every (row, head)
+result depends only on that row's own keys, so windows that cover the request in pieces must
+give the whole-request forward's rows bit for bit. Every window must also match the fp64 oracle
+on its rows, including decode windows (a few rows at the end of a long request, where the
+library splits the key axis and merges the partials).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import segmla_oracle as O
+from segmented_attention_amd.segmla import Plan
+from tests.gpu_common import compare, oracle_inputs, run_gpu, say
+from workload import CONFIGS, SMALL_CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_window(inp, q0, q1, split_keys=0):
+    cfg = inp["cfg"]
+    H, L = cfg["n_heads"], q1 - q0
+    plan = Plan.for_inputs(inp, split_keys, q_range=(q0, q1))
+    plan.build(inp["scores"])
+    dt = inp["q"].dtype
+    out = torch.full((L, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+    z = torch.full((L, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+    lse = torch.full((L, H), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(inp, out, z, lse)
+    torch.cuda.synchronize()
+    return plan, out, z, lse
+
+
+def _bits(x):
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+
+def _check_pairs(plan, inp, A, q0, q1):
+    cfg = inp["cfg"]
+    hg = len(cfg["global_heads"])
+    assert plan.pairs() == O.flops_pairs_window(q0, q1, A, hg, cfg["n_heads"] - hg)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_CONFIGS[0], SMALL_CONFIGS[1], SMALL_CONFIGS[3],
+                                 SMALL_CONFIGS[4], SMALL_CONFIGS[5]], ids=lambda c: c["name"])
+def test_windows_compose_to_whole_request_bitwise(cfg):
+    say("case windows %s" % cfg["name"])
+    inp = make_inputs(cfg, "cuda")
+    T = inp["T"]
+    plan, out, z, lse = run_gpu(inp, -1)  # never split: per-row results are order independent
+    A = plan.protected()
+    plan.close()
+    rng = np.random.default_rng(cfg["seed"])
+    cuts = sorted(set(rng.integers(2, T - 1, 5).tolist()) | {1, T - 1})  # 1-row windows at both ends
+    edges = [0] + cuts + [T]
+    for q0, q1 in zip(edges[:-1], edges[1:]):
+        say("  window [%d, %d)" % (q0, q1))
+        p, o, zz, ls = _run_window(inp, q0, q1, -1)
+        np.testing.assert_array_equal(p.protected(), A)  # A stays the whole request's
+        _check_pairs(p, inp, A, q0, q1)
+        p.close()
+        assert torch.equal(_bits(o), _bits(out[q0:q1])), "out differs from the whole request's rows"
+        assert torch.equal(_bits(zz), _bits(z[q0:q1])), "z differs from the whole request's rows"
+        assert torch.equal(_bits(ls), _bits(lse[q0:q1])), "lse differs from the whole request's rows"
+
+
+@pytest.mark.parametrize("cfg,q0,q1", [(SMALL_CONFIGS[1], 300, 700), (SMALL_CONFIGS[1], 0, 1),
+                                       (SMALL_CONFIGS[0], 80, 81), (SMALL_CONFIGS[4], 200, 530),
+                                       (SMALL_CONFIGS[6], 100, 282)],
+                         ids=lambda x: x["name"] if isinstance(x, dict) else str(x))
+def test_window_parity_with_oracle(cfg, q0, q1):
+    """A window in the middle of the request (crossing segment boundaries) against the oracle,
+    with the library's own choice of key split."""
+    say("case window %s [%d, %d)" % (cfg["name"], q0, q1))
+    inp = make_inputs(cfg, "cuda")
+    plan, out, z, lse = _run_window(inp, q0, q1)
+    ref = O.layer_forward(oracle_inputs(inp), rows=np.arange(q0, q1))
+    _check_pairs(plan, inp, ref["A"], q0, q1)
+    plan.close()
+    e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
+    say("  max rel err O %.2e Z %.2e" % e)
+
+
+@pytest.mark.parametrize("where", ["last_row", "last_4_rows", "doc_interior_row", "doc_start_row"])
+def test_decode_windows_32k(where):
+    """Decode-shaped windows on the 32K layer: one or a few rows against 33K keys, so the key
+    axis is split over many workgroups and merged."""
+    cfg = CONFIGS[1]
+    inp = make_inputs(cfg, "cuda")
+    T = inp["T"]
+    offs = np.asarray(inp["offsets"])
+    q0, q1 = {"last_row": (T - 1, T), "last_4_rows": (T - 4, T),
+              "doc_interior_row": (int(offs[3]) + 1000, int(offs[3]) + 1001),
+              "doc_start_row": (int(offs[5]), int(offs[5]) + 1)}[where]
+    say("case decode %s [%d, %d)" % (where, q0, q1))
+    plan, out, z, lse = _run_window(inp, q0, q1)
+    oi = oracle_inputs(inp, lazy=True)
+    ref = O.layer_forward(oi, rows=np.arange(q0, q1))
+    _check_pairs(plan, inp, ref["A"], q0, q1)
+    plan.close()
+    e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
+    say("  max rel err O %.2e Z %.2e" % e)

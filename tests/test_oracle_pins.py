@@ -65,6 +65,28 @@ def test_tiny_worked_example():
     assert (gp, lp) == (37675, 82908)
 
 
+def test_window_pair_counts():
+    """Pairs of a row window: brute-force count of (row, head, key) triples on the tiny layer,
+    the whole request as one window, and windows covering it in pieces summing to the whole."""
+    cfg = CONFIGS[0]
+    g = _geom(cfg)
+    T = g["T"]
+    A = O.protected_rows(g, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"])["A"]
+    in_a = np.zeros(T, bool)
+    in_a[A] = True
+    assert O.flops_pairs_window(0, T, A, 1, 7) == O.flops_pairs(T, A, 1, 7)
+    for q0, q1 in [(0, 1), (5, 9), (100, 274), (273, 274), (17, 200)]:
+        bg = bl = 0
+        for t in range(q0, q1):
+            for key in range(t + 1):  # causal: keys 0..t
+                bg += 1
+                bl += 7 * in_a[t]
+        assert O.flops_pairs_window(q0, q1, A, 1, 7) == (bg, bl)
+    cuts = [0, 3, 66, 67, 150, 266, T]
+    parts = [O.flops_pairs_window(a, b, A, 1, 7) for a, b in zip(cuts[:-1], cuts[1:])]
+    assert tuple(map(sum, zip(*parts))) == O.flops_pairs(T, A, 1, 7)
+
+
 @pytest.mark.parametrize("idx,expect", [(1, (2432, 999, 3431)), (2, (38784, 0, 38784)),
                                         (4, (4224, 12416, 16640))])
 def test_workload_protected_sizes(idx, expect):
