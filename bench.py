@@ -8,11 +8,13 @@ row-replacement epilogue). The default workload is the Flash-like 32K layer
 prefix, 128 question rows, 10 % Local budget); the 128K layer is measured as a
 secondary figure, its 8 Global heads alone (every row, the part the throughput target is
 stated on) as the "target" figure, and the Pro-like 64K layer with the E4M3 latent as the
-"fp8" figure. Throughput is algorithmic attention TFLOP/s,
-2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the step time.
+"fp8" figure. A row-window plan of the 128K layer's last row (decode: one new row against
+131,584 keys) is the "decode" figure, against the HBM roofline. Throughput is algorithmic
+attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the
+step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
-                [--no-target] [--no-fp8] [--no-cpu-baseline]
+                [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N]
 """
 import argparse
 import json
@@ -56,7 +58,41 @@ def flops_per_pair(cfg):
     return 2.0 * (d_qk + d_v)
 
 
-def measure(cfg_name, steps, warmup):
+def measure_window(inp, cfg, n_rows, steps, warmup):
+    """Decode-shaped forward: a plan for the last n_rows request rows only (their full
+    causal context over every segment), built once; HIP-event times per forward. The
+    algorithmic bytes are the latent rows the window sees plus its q and out."""
+    import torch
+    from segmented_attention_amd import segmla as S
+
+    T, H = inp["T"], cfg["n_heads"]
+    q0 = T - n_rows
+    dt = inp["q"].dtype
+    out = torch.empty((n_rows, H, inp["d_v"]), dtype=dt, device="cuda")
+    z = torch.empty((n_rows, H, cfg["d_state"]), dtype=dt, device="cuda")
+    plan = S.Plan.for_inputs(inp, q_range=(q0, T))
+    plan.build(inp["scores"])
+    for _ in range(warmup):
+        plan.forward(inp, out, z)
+    torch.cuda.synchronize()
+    S.segmla_profile_enable(plan.handle, True)
+    for _ in range(steps):
+        plan.forward(inp, out, z)
+    ms, n_fwd, _ = S.segmla_profile_read(plan.handle)
+    S.segmla_profile_enable(plan.handle, False)
+    torch.cuda.synchronize()
+    plan.close()
+    n = max(1, n_fwd)
+    attn_us, merge_us, epi_us = (1e3 * ms[i] / n for i in range(3))
+    d_qk = cfg["d_nope"] + cfg["d_rope"]
+    row_bytes = d_qk * 2 if cfg["kv_dtype"] == "bf16" else cfg["d_nope"] + 4 * (cfg["d_nope"] // 128) + 2 * cfg["d_rope"]
+    nbytes = T * row_bytes + n_rows * H * (d_qk + inp["d_v"]) * 2
+    gbps = nbytes / ((attn_us + merge_us) * 1e-6) / 1e9
+    return dict(rows=n_rows, keys=T, attention_us=attn_us, merge_us=merge_us, epilogue_us=epi_us,
+                bytes=nbytes, gbps=gbps)
+
+
+def measure(cfg_name, steps, warmup, decode_rows=0):
     import torch
     from segmented_attention_amd import segmla as S
     from workload import config_by_name, make_inputs
@@ -112,6 +148,9 @@ def measure(cfg_name, steps, warmup):
         tflops_576_512=(2.0 * (576 + 512)) * (g_pairs + l_pairs) / wall / 1e12,
     )
     plan.close()
+    if decode_rows > 0:
+        log("workload %s: decode window of the last %d row(s)" % (cfg_name, decode_rows))
+        res["decode"] = measure_window(inp, cfg, decode_rows, 20, 3)
     del inp, out, z
     torch.cuda.empty_cache()
     return res
@@ -202,6 +241,8 @@ def main():
     ap.add_argument("--fp8", default="pro_64k_fp8", help="E4M3-latent workload reported alongside")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-rows", type=int, default=1,
+                    help="decode window (last rows of the secondary workload) reported alongside; 0: none")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -221,7 +262,7 @@ def main():
     main_res = measure(args.workload, args.steps, args.warmup)
     sec = None
     if not args.no_secondary and args.secondary:
-        sec = measure(args.secondary, max(2, args.steps // 3), 1)
+        sec = measure(args.secondary, max(2, args.steps // 3), 1, decode_rows=args.decode_rows)
     tgt = None
     if not args.no_target and args.target:
         tgt = measure(args.target, max(2, args.steps // 3), 1)
@@ -275,6 +316,16 @@ def main():
             "attention_frac_bf16_peak": round(sec["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "stage_ms": {"attention": round(sec["attn_ms"], 3), "epilogue": round(sec["epi_ms"], 3),
                          "plan_build": round(sec["build_ms"], 3)},
+        }
+    if sec is not None and "decode" in sec:
+        d = sec["decode"]
+        line["decode"] = {
+            "workload": sec["cfg"]["name"], "window_rows": d["rows"], "keys": d["keys"],
+            "attention_us": round(d["attention_us"], 2), "split_merge_us": round(d["merge_us"], 2),
+            "epilogue_us": round(d["epilogue_us"], 2),
+            "roofline": {"bound": "hbm", "achieved": round(d["gbps"], 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(d["gbps"] / PEAK_HBM_GBS, 4),
+                         "bytes": int(d["bytes"]), "over": "attention + split merge"},
         }
     if tgt is not None:
         line["target"] = {

@@ -78,7 +78,9 @@ def test_parity_pool_placement(cfg, pool):
 
 @pytest.mark.parametrize("cfg,split", [(CONFIGS[0], 64), (SMALL_CONFIGS[0], 64),
                                        (SMALL_CONFIGS[1], 256), (SMALL_CONFIGS[3], 192),
-                                       (SMALL_CONFIGS[4], 128)],
+                                       (SMALL_CONFIGS[4], 128),
+                                       # 17 splits: the workgroup-per-vector merge
+                                       (SMALL_CONFIGS[2], 64)],
                          ids=lambda x: x["name"] if isinstance(x, dict) else str(x))
 def test_parity_split_keys(cfg, split):
     """Key-range splits + log-sum-exp merge give the same result as one pass."""
