@@ -130,6 +130,8 @@ typedef struct segmla_protect {
 /* Device tensors of one forward, all row-major and caller-owned. A plan computes the
  * request rows of its window [q_begin, q_end) (the whole request [0, T) for
  * segmla_plan_create); q, out, z and lse hold those rows only, row t at index t - q_begin.
+ * Every pointer is 16-byte aligned (the kernels move 16-byte vectors), else
+ * segmla_forward returns SEGMLA_E_SHAPE.
  *  q        [q_end - q_begin][H][d_nope + d_rope] io_dtype, stored post-RoPE at request
  *           position t
  *  kv       F32/BF16: [n_pool][d_nope + d_rope]; E4M3_B128: codes uint8 [n_pool][d_nope]

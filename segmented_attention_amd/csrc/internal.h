@@ -96,6 +96,7 @@ struct AttnArgs {
   float* part_o;          // [n_split][nTiles*kTileQ][d_v] (split)
   float* part_ml;         // [n_split][nTiles*kTileQ][2] (split)
   const SegDesc* seg;
+  const int32_t* seg_of_row;  // [T] segment of each request row
   const float2* segcs;    // [n_seg][d_rope/2] cos/sin(rot_i * theta_k)
   const float2* stepcs;   // [n_seg][d_rope/2] cos/sin((rot_i - rot_{i+1}) * theta_k)
   const int32_t* work;    // [nF + nG] tile ids in decreasing cost order

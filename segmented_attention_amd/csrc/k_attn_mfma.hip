@@ -346,21 +346,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 
   const float qk_scale = a.sigma * kLog2e;
   const __bf16* qrow = (const __bf16*)a.q + ((int64_t)(valid ? t - a.q0 : 0) * a.map.H + h) * kD;
-  // B operand of S^T = K Q^T, step s: lane holds Q[qvec col][16 s + 8 hf + 0..7]
+  // B operand of S^T = K Q^T, step s: lane holds Q[qvec col][16 s + 8 hf + 0..7]; steps below
+  // kQReg in registers, the others in per-thread LDS slots (loaded in the prologue)
   bf16x8 qf[kQReg];
-#pragma unroll
-  for (int s = 0; s < kQReg; ++s) {
-    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
-    if (!valid) v = make_uint4(0, 0, 0, 0);
-    qf[s] = *(bf16x8*)&v;
-  }
   char* const qslot = lds + kQRBase + tid * 16;  // + (s - kQReg) * kQSlotStep
-#pragma unroll
-  for (int s = kQReg; s < 32; ++s) {
-    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
-    if (!valid) v = make_uint4(0, 0, 0, 0);
-    *(uint4*)(qslot + (s - kQReg) * kQSlotStep) = v;
-  }
   constexpr int NF = VROPE ? 18 : 16;  // 32-feature tiles of O^T
   constexpr int NR = NF - 16;          // RoPE output tiles (VGPRs)
   floatx16 acc[16], accr[NR > 0 ? NR : 1];  // nope tiles in AGPRs, RoPE tiles in VGPRs
@@ -401,11 +390,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
   constexpr int64_t kSrcStride = FP8 ? 1 : kRowBytes;  // TileIt::src units per latent row
   auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
-    int lo = 0, hi = a.n_seg - 1;  // last segment starting at or before k_lo
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sg[mid].offset <= k_lo) lo = mid; else hi = mid - 1;
-    }
+    const int lo = a.seg_of_row[k_lo];  // k_lo < k_hi <= T
     c.seg = lo;
     const int off = sg[lo].offset, len = sg[lo].len;
     c.pos0 = k_lo;
@@ -524,13 +509,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, scores of tile 0
+  // ---- prologue: tiles 0 and 1 in flight, then the query (its loads overlap the copies),
+  // scores of tile 0
   TileIt wa, wb, wc;
   first_tile(wa);
   wa.v = 1;
   wb.v = advance(wa, wb);
   issue(wa, 0);
   if (wb.v) issue(wb, 1);
+#pragma unroll
+  for (int s = 0; s < kQReg; ++s) {
+    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
+    if (!valid) v = make_uint4(0, 0, 0, 0);
+    qf[s] = *(bf16x8*)&v;
+  }
+#pragma unroll
+  for (int s = kQReg; s < 32; ++s) {
+    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
+    if (!valid) v = make_uint4(0, 0, 0, 0);
+    *(uint4*)(qslot + (s - kQReg) * kQSlotStep) = v;
+  }
   rotate_q(wa.seg);
   if (!FP8 && wb.v) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoads) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -707,7 +705,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   if (VROPE) frame_step(fin_seg, a.segcs);
   const float l_tot = pair_sum(l_run);
   const int d_v = a.d_v;
-  if (a.n_split > 1) {
+  if (a.n_split > 1) {  // partials of the tile's real vectors only: the merge reads no other
+    if (!valid) return;
     const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
     const int64_t v = (int64_t)tile * kTileQ + wave * 32 + col;
     float* po = a.part_o + ((int64_t)split * nvec + v) * d_v;

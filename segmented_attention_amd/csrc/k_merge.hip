@@ -34,52 +34,6 @@ __device__ __forceinline__ void merge_vec(const float* __restrict__ part_o,
   }
   if (lse_dst && lane == 0) *lse_dst = den > 0.f ? M + logf(den) : -INFINITY;
 }
-// The same merge of one vector by a whole workgroup, for many splits (decode: a few rows
-// against a long context): wave w takes splits w, w + 4, ...; each lane accumulates all of its
-// channels (lane + 64 k) for a split at once, so that those loads are in flight together; the
-// waves' partial sums meet in LDS. d <= 64 * kWideCh.
-constexpr int kWideCh = 9;
-template <typename OutT>
-__device__ __forceinline__ void merge_vec_wide(const float* __restrict__ part_o,
-                                               const float* __restrict__ part_ml, int n_split,
-                                               int64_t n_vec, int64_t v, int d,
-                                               OutT* __restrict__ dst, float* __restrict__ lse_dst) {
-  __shared__ float red[4], dens[4];
-  __shared__ float accs[4][64 * kWideCh];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float m = -INFINITY;
-  for (int s = tid; s < n_split; s += 256) m = fmaxf(m, part_ml[((int64_t)s * n_vec + v) * 2]);
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (lane == 0) red[wave] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float den = 0.f, acc[kWideCh];
-#pragma unroll
-  for (int k = 0; k < kWideCh; ++k) acc[k] = 0.f;
-#pragma unroll 2
-  for (int s = wave; s < n_split; s += 4) {
-    const float* ml = part_ml + ((int64_t)s * n_vec + v) * 2;
-    const float ms = ml[0];
-    if (ms == -INFINITY) continue;  // the split saw no key of this vector
-    const float w = expf(ms - M);
-    den += w * ml[1];
-    const float* o = part_o + ((int64_t)s * n_vec + v) * d;
-#pragma unroll
-    for (int k = 0; k < kWideCh; ++k) {
-      const int c = lane + 64 * k;
-      if (c < d) acc[k] += w * o[c];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kWideCh; ++k) accs[wave][lane + 64 * k] = acc[k];
-  if (lane == 0) dens[wave] = den;
-  __syncthreads();
-  const float dt = dens[0] + dens[1] + dens[2] + dens[3];
-  const float inv = dt > 0.f ? 1.f / dt : 0.f;
-  for (int c = tid; c < d; c += 256)
-    store(dst + c, (accs[0][c] + accs[1][c] + accs[2][c] + accs[3][c]) * inv);
-  if (lse_dst && tid == 0) *lse_dst = dt > 0.f ? M + logf(dt) : -INFINITY;
-}
 }  // namespace
 
 template <typename OutT>
@@ -93,7 +47,10 @@ __global__ __launch_bounds__(256) void k_lse_merge(const float* __restrict__ par
   merge_vec(part_o, part_ml, n_split, n_vec, v, d, out + v * d, lse ? lse + v : nullptr, lane);
 }
 
-constexpr int kWideMergeSplits = 16;  // from this many splits on, a workgroup per vector
+constexpr int kWideMergeSplits = 16;   // from this many splits on, the wide merge
+constexpr int kWideMaxSplits = 4096;   // its LDS weight table
+constexpr int kWideChunk = 256;        // channels per workgroup (4 per lane)
+constexpr int kWideBatch = 16;         // splits whose loads a lane has in flight at once
 
 // Forward's merge: vector v = tile * kTileQ + qi goes to out[t][h]; only the splits the
 // attention wrote (split start <= the tile's largest row) are read.
@@ -112,18 +69,91 @@ __global__ __launch_bounds__(256) void k_merge_tiles(AttnArgs a) {
             a.lse ? a.lse + o : nullptr, lane);
 }
 
-// One workgroup per vector (merge_vec_wide), for many splits.
+// The same merge for many splits (decode: a few rows against a long context), laid out for
+// bandwidth: workgroup = (vector, 256 channels). The split weights e^(m_s - M) are computed
+// once into LDS; then wave w sums splits w, w + 4, ... with each lane holding 4 channels and
+// kWideBatch splits' loads in flight per batch, no branch between them (a split that saw no
+// key of the vector has weight 0 and a zero partial). The four waves' sums meet in LDS.
+__device__ __forceinline__ void store4(float* p, float4 v) { *(float4*)p = v; }
+__device__ __forceinline__ void store4(__bf16* p, float4 v) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 y = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+  *(bf16x4*)p = y;
+}
+__device__ __forceinline__ void fma4(float4& acc, float w, const float4& x) {
+  acc.x = fmaf(w, x.x, acc.x);
+  acc.y = fmaf(w, x.y, acc.y);
+  acc.z = fmaf(w, x.z, acc.z);
+  acc.w = fmaf(w, x.w, acc.w);
+}
+
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
+  __shared__ float sw[kWideMaxSplits];
+  __shared__ float red[4], dens[4];
+  __shared__ float4 accs[3][64];
+  const int nchunk = (a.d_v + kWideChunk - 1) / kWideChunk;
   const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
-  const int64_t v = blockIdx.x;
+  const int64_t v = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
   const int tile = (int)(v / kTileQ), qi = (int)(v % kTileQ);
   int t, h;
   if (!tile_qvec(a.map, tile, qi, t, h)) return;  // uniform over the workgroup
-  const int n_valid = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);
+  const int n = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float m = -INFINITY;
+  for (int s = tid; s < n; s += 256) {
+    const float ms = a.part_ml[((int64_t)s * nvec + v) * 2];
+    sw[s] = ms;
+    m = fmaxf(m, ms);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float den = 0.f;
+  for (int s = tid; s < n; s += 256) {  // the same entries this thread wrote above
+    const float ms = sw[s];
+    const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+    sw[s] = w;
+    den += w * a.part_ml[((int64_t)s * nvec + v) * 2 + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+  if (lane == 0) dens[wave] = den;
+  __syncthreads();
+  const int c = chunk * kWideChunk + 4 * lane;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < a.d_v) {
+    const int64_t sstride = nvec * a.d_v;
+    const float* po = a.part_o + v * a.d_v + c;
+    for (int s = wave; s < n; s += 4 * kWideBatch) {
+      float4 x[kWideBatch];
+#pragma unroll
+      for (int k = 0; k < kWideBatch; ++k) {  // past the last split: reread split s, weight 0
+        const int sk = s + 4 * k < n ? s + 4 * k : s;
+        x[k] = *(const float4*)(po + (int64_t)sk * sstride);
+      }
+#pragma unroll
+      for (int k = 0; k < kWideBatch; ++k) fma4(acc, s + 4 * k < n ? sw[s + 4 * k] : 0.f, x[k]);
+    }
+  }
+  if (wave > 0) accs[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+  const float dt = dens[0] + dens[1] + dens[2] + dens[3];
+  const float inv = dt > 0.f ? 1.f / dt : 0.f;
   const int64_t o = (int64_t)(t - a.q0) * a.map.H + h;
-  merge_vec_wide(a.part_o, a.part_ml, n_valid, nvec, v, a.d_v, (OutT*)a.out + o * a.d_v,
-                 a.lse ? a.lse + o : nullptr);
+  if (c < a.d_v) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      acc.x += accs[w][lane].x;
+      acc.y += accs[w][lane].y;
+      acc.z += accs[w][lane].z;
+      acc.w += accs[w][lane].w;
+    }
+    store4((OutT*)a.out + o * a.d_v + c, make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv));
+  }
+  if (a.lse && chunk == 0 && lane == 0) a.lse[o] = dt > 0.f ? M + logf(dt) : -INFINITY;
 }
 
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
@@ -141,12 +171,13 @@ hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_spl
 
 hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream) {
   const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
-  if (a.n_split >= kWideMergeSplits && a.d_v <= 64 * kWideCh) {
-    if (nvec > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (a.n_split >= kWideMergeSplits && a.n_split <= kWideMaxSplits && a.d_v % 4 == 0) {
+    const int64_t blocks = nvec * ((a.d_v + kWideChunk - 1) / kWideChunk);
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
     if (io_dtype == 0)
-      hipLaunchKernelGGL(k_merge_tiles_wide<float>, dim3((unsigned)nvec), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(k_merge_tiles_wide<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_merge_tiles_wide<__bf16>, dim3((unsigned)nvec), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(k_merge_tiles_wide<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t blocks = (nvec + 3) / 4;

@@ -223,14 +223,17 @@ segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla
     }
     for (int32_t r : p->dirty) forced[r] = 1;
     for (int64_t t = std::max<int64_t>(0, (int64_t)T - p->tail_rows); t < T; ++t) forced[t] = 1;
-    int64_t nf = 0, nc = 0, nfc = 0;
+    int64_t nf = 0, nc = 0, nfc = 0, nf_w = 0, nc_w = 0;  // _w: window rows; nc_w: not forced
     for (const SegDesc& d : p->segs) {
       bool cand = d.kind != SEGMLA_SEG_NEW;
       for (int j = 0; j < d.len; ++j) {
-        bool f = forced[d.offset + j] != 0;
+        const int64_t t = d.offset + j;
+        bool f = forced[t] != 0, in_w = t >= p->q0 && t < p->q1;
         nf += f;
         nc += cand;
         nfc += (f && cand);
+        nf_w += (f && in_w);
+        nc_w += (!f && cand && in_w);
       }
     }
     p->n_forced = nf;
@@ -238,15 +241,16 @@ segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla
     p->K = ((int64_t)p->budget_permille * nc + 999) / 1000;
     p->need = std::max<int64_t>(0, p->K - nfc);
     p->nA = nf + p->need;
+    // Window rows of A: all its forced rows, plus at most min(need, nc_w) Indexer picks.
+    const int64_t L = (int64_t)p->q1 - p->q0;
+    p->nA_w = std::min<int64_t>(nf_w + std::min(p->need, nc_w), L);
+    p->nNA_w = L - nf_w;
   }
 
   // Work decomposition: qvec tiles of stream F (window rows of A x all heads) and stream G
   // (other window rows x Global heads), optionally split along the key axis. For a window
   // smaller than the request, the split between the streams depends on the Indexer picks:
-  // both are sized for their largest share.
-  const int64_t L = (int64_t)p->q1 - p->q0;
-  p->nA_w = std::min<int64_t>(p->nA, L);
-  p->nNA_w = std::min<int64_t>((int64_t)T - p->nA, L);
+  // both are sized for their largest share (above).
   const int64_t qF = p->nA_w * p->H, qG = p->nNA_w * p->HG;
   const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
   if (nF + nG > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
@@ -258,7 +262,11 @@ segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla
   if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
     sk = -1;
     if (n_tiles > 0 && n_tiles < 2 * kNumCU && keys > 2048) {
+      // about four workgroups per CU, each with at least 1024 keys; where that leaves CUs idle
+      // (decode: one or two tiles), one workgroup per CU, each with at least 256 keys
       int64_t want = std::min<int64_t>((4 * kNumCU + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
+      if (want * n_tiles < kNumCU)
+        want = std::min<int64_t>((kNumCU + n_tiles - 1) / n_tiles, (keys + 255) / 256);
       if (want > 1) sk = (int32_t)((((keys + want - 1) / want) + 63) / 64 * 64);
     }
   }
@@ -378,6 +386,9 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   if (!t->q || !t->kv || !t->w || !t->out || !t->z) return SEGMLA_E_NULL;
   if (p->HL > 0 && !t->z_cached) return SEGMLA_E_NULL;
   if (p->kv_dtype == SEGMLA_E4M3_B128 && (!t->kv_scale || !t->kv_rope)) return SEGMLA_E_NULL;
+  for (const void* ptr : {t->q, t->kv, (const void*)t->kv_scale, t->kv_rope, t->w, t->z_cached,
+                          (const void*)t->out, (const void*)t->z, (const void*)t->lse})
+    if ((uintptr_t)ptr % 16 != 0) return SEGMLA_E_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   AttnArgs a;
   a.q = t->q;
@@ -389,6 +400,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   a.part_o = p->n_split > 1 ? p->at<float>(p->o_part_o) : nullptr;
   a.part_ml = p->n_split > 1 ? p->at<float>(p->o_part_ml) : nullptr;
   a.seg = p->at<SegDesc>(p->o_seg);
+  a.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
   a.segcs = p->at<float2>(p->o_segcs);
   a.stepcs = p->at<float2>(p->o_stepcs);
   a.work = p->at<int32_t>(p->o_work);
