@@ -15,7 +15,7 @@ attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, di
 step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
-                [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N]
+                [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N] [--decode-only]
 """
 import argparse
 import json
@@ -94,6 +94,17 @@ def measure_window(inp, cfg, n_rows, steps, warmup):
     gbps = nbytes / (fwd_us * 1e-6) / 1e9
     return dict(rows=n_rows, keys=T, attention_us=attn_us, merge_us=merge_us, epilogue_us=epi_us,
                 forward_us=fwd_us, bytes=nbytes, gbps=gbps)
+
+
+def decode_json(name, d):
+    return {
+        "workload": name, "window_rows": d["rows"], "keys": d["keys"],
+        "attention_us": round(d["attention_us"], 2), "split_merge_us": round(d["merge_us"], 2),
+        "epilogue_us": round(d["epilogue_us"], 2), "forward_us": round(d["forward_us"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(d["gbps"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(d["gbps"] / PEAK_HBM_GBS, 4),
+                     "bytes": int(d["bytes"]), "over": "whole forward"},
+    }
 
 
 def measure(cfg_name, steps, warmup, decode_rows=0):
@@ -247,6 +258,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-rows", type=int, default=1,
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode window of the secondary workload (for kernel "
+                         "traces of the decode path) and print its figures")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -263,6 +277,15 @@ def main():
         dst = src.clone()
         torch.cuda.synchronize()
         del src, dst
+    if args.decode_only:
+        from workload import config_by_name, make_inputs
+        cfg = config_by_name(args.secondary)
+        log("workload %s: generating inputs" % cfg["name"])
+        inp = make_inputs(cfg, "cuda")
+        log("workload %s: decode window of the last %d row(s)" % (cfg["name"], args.decode_rows))
+        d = measure_window(inp, cfg, args.decode_rows, args.steps, args.warmup)
+        print(json.dumps({"decode": decode_json(cfg["name"], d)}), flush=True)
+        return
     main_res = measure(args.workload, args.steps, args.warmup)
     sec = None
     if not args.no_secondary and args.secondary:
@@ -322,15 +345,7 @@ def main():
                          "plan_build": round(sec["build_ms"], 3)},
         }
     if sec is not None and "decode" in sec:
-        d = sec["decode"]
-        line["decode"] = {
-            "workload": sec["cfg"]["name"], "window_rows": d["rows"], "keys": d["keys"],
-            "attention_us": round(d["attention_us"], 2), "split_merge_us": round(d["merge_us"], 2),
-            "epilogue_us": round(d["epilogue_us"], 2), "forward_us": round(d["forward_us"], 2),
-            "roofline": {"bound": "hbm", "achieved": round(d["gbps"], 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(d["gbps"] / PEAK_HBM_GBS, 4),
-                         "bytes": int(d["bytes"]), "over": "whole forward"},
-        }
+        line["decode"] = decode_json(sec["cfg"]["name"], sec["decode"])
     if tgt is not None:
         line["target"] = {
             "workload": tgt["cfg"]["name"], "rows": tgt["T"], "heads": tgt["cfg"]["n_heads"],
