@@ -10,12 +10,14 @@ secondary figure, its 8 Global heads alone (every row, the part the throughput t
 stated on) as the "target" figure, and the Pro-like 64K layer with the E4M3 latent as the
 "fp8" figure. A row-window plan of the 128K layer's last row (decode: one new row against
 131,584 keys) is the "decode" figure, its whole forward against the HBM roofline (latent
-rows, W, and the row's q, out and z moved once). Throughput is algorithmic
+rows, W, and the row's q, out and z moved once). The main workload over a paged latent pool
+(64-row pages in shuffled order) is the "paged" figure. Throughput is algorithmic
 attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the
 step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                 [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N] [--decode-only]
+                [--paged-rows P]
 """
 import argparse
 import json
@@ -107,14 +109,14 @@ def decode_json(name, d):
     }
 
 
-def measure(cfg_name, steps, warmup, decode_rows=0):
+def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
     import torch
     from segmented_attention_amd import segmla as S
     from workload import config_by_name, make_inputs
 
     cfg = config_by_name(cfg_name)
-    log("workload %s: generating inputs" % cfg_name)
-    inp = make_inputs(cfg, "cuda")
+    log("workload %s: generating inputs (pool %s)" % (cfg_name, pool))
+    inp = make_inputs(cfg, "cuda", pool=pool)
     T, H = inp["T"], cfg["n_heads"]
     dt = inp["q"].dtype
     out = torch.empty((T, H, inp["d_v"]), dtype=dt, device="cuda")
@@ -258,6 +260,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-rows", type=int, default=1,
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
+    ap.add_argument("--paged-rows", type=int, default=64,
+                    help="also time the main workload over a paged latent pool of this many rows "
+                         "per page; 0: none")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode window of the secondary workload (for kernel "
                          "traces of the decode path) and print its figures")
@@ -296,6 +301,9 @@ def main():
     f8 = None
     if not args.no_fp8 and args.fp8:
         f8 = measure(args.fp8, 2, 1)
+    pg = None
+    if args.paged_rows > 0:
+        pg = measure(args.workload, max(2, args.steps // 2), 1, pool="paged:%d" % args.paged_rows)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
 
     r = main_res
@@ -353,6 +361,14 @@ def main():
             "attention_ms_min": round(tgt["attn_ms_min"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(tgt["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "target_frac_bf16_peak": 0.5,
+        }
+    if pg is not None:
+        line["paged"] = {
+            "workload": pg["cfg"]["name"], "page_rows": args.paged_rows,
+            "layout": "shuffled pages, equal-length documents sharing pages",
+            "attention_ms": round(pg["attn_ms"], 3), "attention_tflops": round(pg["attn_tflops"], 3),
+            "attention_frac_bf16_peak": round(pg["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "us_per_layer": round(pg["wall_s"] * 1e6, 1),
         }
     if f8 is not None:
         line["fp8"] = {

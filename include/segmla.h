@@ -178,6 +178,31 @@ segmla_status segmla_plan_create_range(const segmla_geometry *geom, const segmla
                                        const segmla_protect *prot, int64_t n_pool,
                                        int64_t q_begin, int64_t q_end, segmla_plan **out_plan);
 
+/* Paged latent pool (RedKnot-MLA paper, relocation and fused-consumer paragraphs: each cached
+ * segment is paged in once and attended in place). The pool is cut into pages of page_rows
+ * rows; page g holds pool rows [g * page_rows, (g + 1) * page_rows). Segment i's rows sit on
+ * ceil(len[i] / page_rows) pages listed in order at page_table[page_start[i] ...]: row j of
+ * segment i is pool row page_table[page_start[i] + j / page_rows] * page_rows + j % page_rows,
+ * and the same row of the cached projected state z_cached. Pages may be shared between
+ * segments (the same cached document placed twice). Host memory, read only during plan
+ * creation. Requirements (else SEGMLA_E_GEOMETRY): page_rows >= 1; page_table and page_start
+ * non-NULL (else SEGMLA_E_NULL); 0 <= page_start[i] and page_start[i] + ceil(len[i] /
+ * page_rows) <= n_entries; every pool row a segment uses lies in [0, n_pool). Pages of a
+ * multiple of 32 rows keep every 32-key tile of the attention whole. */
+typedef struct segmla_pages {
+  int32_t page_rows;
+  int64_t n_entries;          /* entries of page_table */
+  const int64_t *page_start;  /* [n_seg] */
+  const int64_t *page_table;  /* [n_entries] page indices */
+} segmla_pages;
+
+/* segmla_plan_create_range over a paged latent pool: geom->pool_row is ignored (may be
+ * NULL); `pages` places every segment's rows. Everything else as segmla_plan_create_range. */
+segmla_status segmla_plan_create_paged(const segmla_geometry *geom, const segmla_pages *pages,
+                                       const segmla_layer *layer, const segmla_protect *prot,
+                                       int64_t n_pool, int64_t q_begin, int64_t q_end,
+                                       segmla_plan **out_plan);
+
 /* Device workspace bytes segmla_plan_build needs (host only). */
 segmla_status segmla_plan_workspace_bytes(const segmla_plan *plan, size_t *bytes);
 

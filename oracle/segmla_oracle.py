@@ -50,8 +50,13 @@ SEG_PREFIX, SEG_DOC, SEG_NEW = 0, 1, 2
 
 
 # --------------------------------------------------------------------------- geometry
-def geometry(kinds, lens, offsets, pool_rows, n_pool):
+def geometry(kinds, lens, offsets, pool_rows, n_pool, pages=None):
     """Integer layout of a request (segment list in request order).
+
+    The pool is either contiguous per segment (segment i at pool rows pool_rows[i] + j) or,
+    with `pages` = dict(page_rows, page_start, page_table), paged: row j of segment i sits on
+    page page_table[page_start[i] + j // page_rows] at offset j % page_rows (RedKnot-MLA
+    paper, fused-consumer paragraph: each cached segment paged in once, attended in place).
 
     Returns dict(T, seg_of_row, canon, pool_of_row, relocated, stored_pos_base).
     A document is relocated when it sits at a nonzero offset (RedKnot-MLA
@@ -73,12 +78,23 @@ def geometry(kinds, lens, offsets, pool_rows, n_pool):
         raise ValueError("segments must be contiguous from request position 0")
     if np.any((kinds < 0) | (kinds > 2)):
         raise ValueError("unknown segment kind")
-    if np.any(pool_rows < 0) or np.any(pool_rows + lens > n_pool):
-        raise ValueError("segment pool range out of bounds")
     T = int(offsets[-1] + lens[-1])
     seg_of_row = np.repeat(np.arange(n, dtype=np.int64), lens)
     canon = np.arange(T, dtype=np.int64) - offsets[seg_of_row]
-    pool_of_row = pool_rows[seg_of_row] + canon
+    if pages is None:
+        if np.any(pool_rows < 0) or np.any(pool_rows + lens > n_pool):
+            raise ValueError("segment pool range out of bounds")
+        pool_of_row = pool_rows[seg_of_row] + canon
+    else:
+        P = int(pages["page_rows"])
+        start = np.asarray(pages["page_start"], dtype=np.int64)
+        table = np.asarray(pages["page_table"], dtype=np.int64)
+        entry = start[seg_of_row] + canon // P
+        if P < 1 or np.any(entry < 0) or np.any(entry >= len(table)):
+            raise ValueError("page list out of bounds")
+        pool_of_row = table[entry] * P + canon % P
+        if np.any(pool_of_row < 0) or np.any(pool_of_row >= n_pool):
+            raise ValueError("paged pool row out of bounds")
     relocated = (kinds == SEG_DOC) & (offsets != 0)
     stored_pos_base = np.where(kinds == SEG_DOC, 0, offsets)
     return dict(T=T, n_seg=n, kinds=kinds, lens=lens, offsets=offsets, pool_rows=pool_rows,
@@ -241,7 +257,8 @@ def layer_forward(inp, rows=None, A_override=None, zc_override=None):
     base, sigma = cfg["rope_base"], cfg["softmax_scale"]
     v_rope = bool(cfg["v_has_rope"])
     d_v = d_nope + d_rope if v_rope else d_nope
-    geom = geometry(inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"], inp["n_pool"])
+    geom = geometry(inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"], inp["n_pool"],
+                    inp.get("pages"))
     prot = protected_rows(geom, cfg["edge_rows"], cfg["tail_rows"], cfg["budget_permille"],
                           cfg.get("dirty_rows", ()), inp.get("scores"))
     A = prot["A"] if A_override is None else np.asarray(A_override, dtype=np.int64)

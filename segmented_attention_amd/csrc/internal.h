@@ -5,7 +5,10 @@
 
 namespace segmla {
 
-// Device segment descriptor (one per segment, 32 bytes).
+// Device segment descriptor (32 bytes). The attention and the row map walk physical runs:
+// stretches of one segment's rows that are contiguous in the latent pool (the whole segment
+// for an unpaged pool). A run carries its segment's phase shift, kind and relocation flag,
+// and the segment's index as `frame`; the protected-row marking reads the segments.
 struct SegDesc {
   int64_t pool_row;  // first latent-pool row
   int32_t offset;    // Delta_i: request position of the segment's first row
@@ -14,7 +17,7 @@ struct SegDesc {
                      // canonical 0..n-1), 0 for prefix/new rows (stored at request positions)
   int32_t kind;      // segmla_seg_kind
   int32_t relocated; // document at a nonzero offset
-  int32_t pad;
+  int32_t frame;     // index of the segment (a run's RoPE frame is its segment's)
 };
 
 // Row flag bits written by the protected-row builder.
@@ -111,7 +114,7 @@ struct AttnArgs {
 hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, double base,
                            int32_t* seg_of_row, float2* segcs, float2* stepcs, float2* rowcs,
                            hipStream_t stream);
-hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_row, int T,
+hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_t* seg_of_row, int T,
                           int edge_rows, int tail_rows, const int32_t* dirty, int n_dirty,
                           const uint32_t* score, int64_t need, uint8_t* flags,
                           uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,

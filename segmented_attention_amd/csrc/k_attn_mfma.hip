@@ -558,7 +558,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       if (v1) convert_tile_e4m3(lds + nb * kTileBytes, wave);
     }
     if (__builtin_expect(v2, 1)) issue(w2, fb);
-    if (__builtin_expect(v1 && w1.seg != w0.seg, 0)) rotate_q(w1.seg);
+    if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
+      rotate_q(w1.seg);
     // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
     if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT)) != 0ull, 0)) {
 #pragma unroll
@@ -682,7 +683,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       fin_seg = w0.seg;
       return false;
     }
-    if (__builtin_expect(VROPE && w1.seg != w0.seg, 0)) frame_step(w0.seg, a.stepcs);  // next tile starts a new segment
+    // next tile starts a new segment (a new run of the same segment keeps the frame)
+    if (__builtin_expect(VROPE && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
+      frame_step(w0.seg, a.stepcs);
     return true;
   };
   for (;;) {

@@ -62,12 +62,14 @@ hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, dou
 
 // ------------------------------------------------------------------ protected rows
 // Forced set F (new rows, dirty rows, edges of relocated documents, recent tail) and the
-// candidate flag (prefix and document rows).
-__global__ void k_protect_mark(const SegDesc* __restrict__ seg, const int32_t* __restrict__ seg_of_row,
-                               int T, int b, int tau, const int32_t* __restrict__ dirty, int n_dirty,
+// candidate flag (prefix and document rows). seg_of_row maps rows to runs; a run's frame is
+// its segment.
+__global__ void k_protect_mark(const SegDesc* __restrict__ seg, const SegDesc* __restrict__ runs,
+                               const int32_t* __restrict__ seg_of_row, int T, int b, int tau,
+                               const int32_t* __restrict__ dirty, int n_dirty,
                                uint8_t* __restrict__ flags) {
   for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
-    const SegDesc d = seg[seg_of_row[t]];
+    const SegDesc d = seg[runs[seg_of_row[t]].frame];
     int j = t - d.offset;
     bool forced = d.kind == 2 || (d.relocated && (j < b || j >= d.len - b)) || t >= T - tau;
     if (!forced && n_dirty > 0) {  // dirty rows are sorted and unique
@@ -304,17 +306,16 @@ __global__ __launch_bounds__(kScanBlock) void k_scatter_a(const uint8_t* __restr
   }
 }
 
-hipError_t launch_protect(const SegDesc* seg, int n_seg, const int32_t* seg_of_row, int T,
+hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_t* seg_of_row, int T,
                           int edge_rows, int tail_rows, const int32_t* dirty, int n_dirty,
                           const uint32_t* score, int64_t need, uint8_t* flags,
                           uint32_t* sel_state, int32_t* blk_count, uint64_t* blk_sum,
                           int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
                           int q0, int q1, int32_t* rng, hipStream_t stream) {
-  (void)n_seg;
   (void)sel_state;
   int blocks = (T + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_protect_mark, dim3(blocks), dim3(256), 0, stream, seg, seg_of_row, T,
+  hipLaunchKernelGGL(k_protect_mark, dim3(blocks), dim3(256), 0, stream, lseg, runs, seg_of_row, T,
                      edge_rows, tail_rows, dirty, n_dirty, flags);
   if (need > 0)
     hipLaunchKernelGGL(k_protect_select, dim3(1), dim3(kSelThreads), 0, stream, flags, score, T,

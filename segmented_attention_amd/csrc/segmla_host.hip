@@ -17,7 +17,12 @@ struct segmla_plan {
   int32_t T = 0;
   int32_t q0 = 0, q1 = 0;  // computed window of request rows [q0, q1)
   int64_t n_pool = 0;
-  std::vector<SegDesc> segs;
+  std::vector<SegDesc> segs;  // logical segments (kinds, edges, relocation)
+  // physical runs: maximal stretches of a segment's rows that are contiguous in the pool (one
+  // per segment for an unpaged pool); each carries its segment's phase shift and, as `frame`,
+  // its segment's index. The attention, the RoPE tables and the row map work on runs.
+  std::vector<SegDesc> runs;
+  int32_t n_run = 0;
   // layer
   int32_t H = 0, HG = 0, HL = 0, d_nope = 0, d_rope = 0, d_qk = 0, d_v = 0, d_state = 0;
   int32_t v_has_rope = 1, kv_dtype = 0, io_dtype = 0;
@@ -34,7 +39,7 @@ struct segmla_plan {
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
-         o_rng = 0, ws_bytes = 0;
+         o_rng = 0, o_lseg = 0, ws_bytes = 0;
   // largest number of window rows inside / outside A (the Indexer picks decide the actual)
   int64_t nA_w = 0, nNA_w = 0;
   // profiling (events on the caller's stream)
@@ -107,16 +112,30 @@ segmla_status check_layer(const segmla_layer* L) {
   return SEGMLA_OK;
 }
 
-segmla_status check_geometry(const segmla_geometry* G, int64_t n_pool, int64_t* T_out) {
-  if (!G->pool_row || !G->len || !G->offset || !G->kind) return SEGMLA_E_NULL;
+segmla_status check_geometry(const segmla_geometry* G, const segmla_pages* P, int64_t n_pool,
+                             int64_t* T_out) {
+  if ((!P && !G->pool_row) || !G->len || !G->offset || !G->kind) return SEGMLA_E_NULL;
   if (G->n_seg < 1 || n_pool < 1) return SEGMLA_E_GEOMETRY;
   int64_t pos = 0;
   for (int i = 0; i < G->n_seg; ++i) {
     if (G->len[i] < 1 || G->kind[i] > 2) return SEGMLA_E_GEOMETRY;
     if (G->offset[i] != pos) return SEGMLA_E_GEOMETRY;
-    if (G->pool_row[i] < 0 || G->pool_row[i] > n_pool - G->len[i]) return SEGMLA_E_GEOMETRY;
+    if (!P && (G->pool_row[i] < 0 || G->pool_row[i] > n_pool - G->len[i])) return SEGMLA_E_GEOMETRY;
     pos += G->len[i];
     if (pos >= ((int64_t)1 << 31)) return SEGMLA_E_GEOMETRY;
+  }
+  if (P) {  // every page a segment uses: listed, and its used rows inside the pool
+    if (!P->page_start || !P->page_table) return SEGMLA_E_NULL;
+    if (P->page_rows < 1 || P->n_entries < 0) return SEGMLA_E_GEOMETRY;
+    const int64_t pr = P->page_rows;
+    for (int i = 0; i < G->n_seg; ++i) {
+      const int64_t np = (G->len[i] + pr - 1) / pr, st = P->page_start[i];
+      if (st < 0 || st > P->n_entries - np) return SEGMLA_E_GEOMETRY;
+      for (int64_t k = 0; k < np; ++k) {
+        const int64_t rows = std::min<int64_t>(pr, G->len[i] - k * pr), g = P->page_table[st + k];
+        if (g < 0 || g > (n_pool - rows) / pr) return SEGMLA_E_GEOMETRY;
+      }
+    }
   }
   *T_out = pos;
   return SEGMLA_OK;
@@ -153,11 +172,19 @@ segmla_status segmla_plan_create(const segmla_geometry* geom, const segmla_layer
 segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla_layer* layer,
                                        const segmla_protect* prot, int64_t n_pool,
                                        int64_t q_begin, int64_t q_end, segmla_plan** out_plan) {
+  return segmla_plan_create_paged(geom, nullptr, layer, prot, n_pool, q_begin, q_end, out_plan);
+}
+
+// With pages = NULL the pool is unpaged (geom->pool_row places each segment).
+segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla_pages* pages,
+                                       const segmla_layer* layer, const segmla_protect* prot,
+                                       int64_t n_pool, int64_t q_begin, int64_t q_end,
+                                       segmla_plan** out_plan) {
   if (!geom || !layer || !prot || !out_plan) return SEGMLA_E_NULL;
   segmla_status st = check_layer(layer);
   if (st != SEGMLA_OK) return st;
   int64_t T64 = 0;
-  st = check_geometry(geom, n_pool, &T64);
+  st = check_geometry(geom, pages, n_pool, &T64);
   if (st != SEGMLA_OK) return st;
   const int32_t T = (int32_t)T64;
   if (q_end == -1) q_end = T;
@@ -179,14 +206,38 @@ segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla
   p->segs.resize(geom->n_seg);
   for (int i = 0; i < geom->n_seg; ++i) {
     SegDesc& d = p->segs[i];
-    d.pool_row = geom->pool_row[i];
+    d.pool_row = pages ? -1 : geom->pool_row[i];
     d.offset = (int32_t)geom->offset[i];
     d.len = geom->len[i];
     d.kind = geom->kind[i];
     d.relocated = (geom->kind[i] == SEGMLA_SEG_DOC && geom->offset[i] != 0) ? 1 : 0;
     d.rot = geom->kind[i] == SEGMLA_SEG_DOC ? d.offset : 0;
-    d.pad = 0;
+    d.frame = i;
   }
+  // runs: an unpaged segment is one run; a paged one is cut at every page boundary where the
+  // next page does not continue the pool rows
+  if (!pages) {
+    p->runs = p->segs;
+  } else {
+    const int64_t pr = pages->page_rows;
+    for (int i = 0; i < geom->n_seg; ++i) {
+      const SegDesc& d = p->segs[i];
+      for (int64_t k = 0; k * pr < d.len; ++k) {
+        const int64_t prow = pages->page_table[pages->page_start[i] + k] * pr;
+        const int32_t rows = (int32_t)std::min<int64_t>(pr, d.len - k * pr);
+        if (k > 0 && p->runs.back().pool_row + p->runs.back().len == prow) {
+          p->runs.back().len += rows;
+          continue;
+        }
+        SegDesc r = d;
+        r.pool_row = prow;
+        r.offset = d.offset + (int32_t)(k * pr);
+        r.len = rows;
+        p->runs.push_back(r);
+      }
+    }
+  }
+  p->n_run = (int32_t)p->runs.size();
   p->H = layer->n_heads;
   for (int h = 0; h < p->H; ++h) (layer->head_is_global[h] ? p->ghead : p->lhead).push_back(h);
   p->HG = (int32_t)p->ghead.size();
@@ -283,9 +334,10 @@ segmla_status segmla_plan_create_range(const segmla_geometry* geom, const segmla
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
   const size_t half = (size_t)p->d_rope / 2;
-  p->o_seg = take(sizeof(SegDesc) * p->n_seg);
-  p->o_segcs = take(sizeof(float2) * half * p->n_seg);
-  p->o_stepcs = take(sizeof(float2) * half * p->n_seg);
+  p->o_seg = take(sizeof(SegDesc) * p->n_run);
+  p->o_lseg = take(sizeof(SegDesc) * p->n_seg);
+  p->o_segcs = take(sizeof(float2) * half * p->n_run);
+  p->o_stepcs = take(sizeof(float2) * half * p->n_run);
   p->o_rowcs = take(sizeof(float2) * half * (size_t)T);
   p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
   p->o_flags = take((size_t)T);
@@ -354,16 +406,17 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
   auto up = [&](size_t off, const void* src, size_t bytes) {
     if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
   };
-  up(p->o_seg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
+  up(p->o_seg, p->runs.data(), sizeof(SegDesc) * p->runs.size());
+  up(p->o_lseg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
   up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
   up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
   up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
   if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_seg, p->T, p->d_rope, p->rope_base,
+  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->d_rope, p->rope_base,
                       p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
                       p->at<float2>(p->o_stepcs), p->at<float2>(p->o_rowcs), s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_protect(p->at<SegDesc>(p->o_seg), p->n_seg, p->at<int32_t>(p->o_seg_of_row), p->T,
+  e = launch_protect(p->at<SegDesc>(p->o_lseg), p->at<SegDesc>(p->o_seg), p->at<int32_t>(p->o_seg_of_row), p->T,
                      p->edge_rows, p->tail_rows, p->at<int32_t>(p->o_dirty), (int)p->dirty.size(),
                      indexer_score, p->need, p->at<uint8_t>(p->o_flags), p->at<uint32_t>(p->o_sel),
                      p->at<int32_t>(p->o_blk_count), p->at<uint64_t>(p->o_blk_sum), p->n_blk,
@@ -405,7 +458,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   a.stepcs = p->at<float2>(p->o_stepcs);
   a.work = p->at<int32_t>(p->o_work);
   a.map = tile_map(p);
-  a.n_seg = p->n_seg;
+  a.n_seg = p->n_run;
   a.T = p->T;
   a.d_nope = p->d_nope;
   a.d_rope = p->d_rope;
@@ -510,12 +563,12 @@ segmla_status segmla_copy_geometry(const segmla_plan* p, int32_t* seg_of_row, in
                             hipMemcpyDeviceToHost, s) != hipSuccess)
     return SEGMLA_E_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return SEGMLA_E_HIP;
-  if (pool_of_row) {
-    for (int32_t r = 0; r < p->T; ++r) {
-      int32_t i = dst[r];
-      if (i < 0 || i >= p->n_seg) { pool_of_row[r] = -1; continue; }
-      pool_of_row[r] = p->segs[i].pool_row + (r - p->segs[i].offset);
-    }
+  if (!dst) return SEGMLA_OK;
+  for (int32_t r = 0; r < p->T; ++r) {  // the device map holds runs
+    const int32_t i = dst[r];
+    const bool ok = i >= 0 && i < p->n_run;
+    if (pool_of_row) pool_of_row[r] = ok ? p->runs[i].pool_row + (r - p->runs[i].offset) : -1;
+    dst[r] = ok ? p->runs[i].frame : -1;
   }
   return SEGMLA_OK;
 }

@@ -25,7 +25,7 @@ EXPORTED = [
     "segmla_forward", "segmla_copy_protected", "segmla_copy_geometry", "segmla_lse_merge",
     "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
     "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
-    "segmla_plan_create_range",
+    "segmla_plan_create_range", "segmla_plan_create_paged",
 ]
 
 
@@ -33,6 +33,12 @@ class SegmlaError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
         super().__init__("%s: %s (status %d)" % (what, _status_string(status), status))
+
+
+class Pages(ctypes.Structure):
+    _fields_ = [("page_rows", ctypes.c_int32), ("n_entries", ctypes.c_int64),
+                ("page_start", ctypes.POINTER(ctypes.c_int64)),
+                ("page_table", ctypes.POINTER(ctypes.c_int64))]
 
 
 class Geometry(ctypes.Structure):
@@ -79,6 +85,9 @@ def lib():
             "segmla_plan_create_range": (i32, [ctypes.POINTER(Geometry), ctypes.POINTER(Layer),
                                                ctypes.POINTER(Protect), i64, i64, i64,
                                                ctypes.POINTER(P)]),
+            "segmla_plan_create_paged": (i32, [ctypes.POINTER(Geometry), ctypes.POINTER(Pages),
+                                               ctypes.POINTER(Layer), ctypes.POINTER(Protect), i64,
+                                               i64, i64, ctypes.POINTER(P)]),
             "segmla_plan_workspace_bytes": (i32, [P, ctypes.POINTER(ctypes.c_size_t)]),
             "segmla_plan_rows": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
             "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
@@ -143,9 +152,11 @@ def segmla_status_string(status):
 def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is_global, d_nope,
                        d_rope, d_state, v_has_rope=1, rope_base=10000.0, softmax_scale=1.0,
                        kv_dtype=SEGMLA_BF16, io_dtype=SEGMLA_BF16, split_keys=0, edge_rows=0,
-                       tail_rows=0, budget_permille=0, dirty_rows=(), q_range=None):
+                       tail_rows=0, budget_permille=0, dirty_rows=(), q_range=None, pages=None):
     """Validate and size a plan; returns the plan handle. q_range = (q_begin, q_end): a plan
-    for that window of request rows (segmla_plan_create_range); None: the whole request."""
+    for that window of request rows (segmla_plan_create_range); None: the whole request.
+    pages = dict(page_rows, page_start, page_table): a paged latent pool
+    (segmla_plan_create_paged; pool_rows is then ignored)."""
     keep = dict(kind=_arr(kinds, np.uint8), len=_arr(lens, np.int32), offset=_arr(offsets, np.int64),
                 pool=_arr(pool_rows, np.int64), glob=_arr(head_is_global, np.uint8),
                 dirty=_arr(list(dirty_rows), np.int32))
@@ -160,7 +171,17 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                  keep["dirty"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(keep["dirty"])
                  else None)
     h = ctypes.c_void_p()
-    if q_range is None:
+    if pages is not None:
+        keep["pstart"] = _arr(pages["page_start"], np.int64)
+        keep["ptable"] = _arr(pages["page_table"], np.int64)
+        pg = Pages(int(pages["page_rows"]), len(keep["ptable"]),
+                   keep["pstart"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                   keep["ptable"].ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+        q0, q1 = (0, -1) if q_range is None else (int(q_range[0]), int(q_range[1]))
+        _check(lib().segmla_plan_create_paged(ctypes.byref(g), ctypes.byref(pg), ctypes.byref(L),
+                                              ctypes.byref(pr), int(n_pool), q0, q1,
+                                              ctypes.byref(h)), "segmla_plan_create_paged")
+    elif q_range is None:
         _check(lib().segmla_plan_create(ctypes.byref(g), ctypes.byref(L), ctypes.byref(pr),
                                         int(n_pool), ctypes.byref(h)), "segmla_plan_create")
     else:
@@ -260,14 +281,14 @@ class Plan:
     """A plan plus its device workspace (torch uint8 tensor on the current GPU)."""
 
     def __init__(self, cfg, kinds, lens, offsets, pool_rows, n_pool, head_is_global, split_keys=0,
-                 dirty_rows=(), q_range=None):
+                 dirty_rows=(), q_range=None, pages=None):
         d_v = cfg["d_nope"] + cfg["d_rope"] if cfg["v_has_rope"] else cfg["d_nope"]
         self.cfg, self.d_v = cfg, d_v
         self.handle = segmla_plan_create(
             kinds, lens, offsets, pool_rows, n_pool, cfg["n_heads"], head_is_global, cfg["d_nope"],
             cfg["d_rope"], cfg["d_state"], cfg["v_has_rope"], cfg["rope_base"], cfg["softmax_scale"],
             _DT[cfg["kv_dtype"]], _DT[cfg["dtype"]], split_keys, cfg["edge_rows"], cfg["tail_rows"],
-            cfg["budget_permille"], dirty_rows, q_range)
+            cfg["budget_permille"], dirty_rows, q_range, pages)
         self.T, self.n_protected = segmla_plan_rows(self.handle)
         # computed window: q, out, z and lse hold rows q0 .. q1 - 1
         self.q0, self.q1 = (0, self.T) if q_range is None else (int(q_range[0]), int(q_range[1]))
@@ -313,4 +334,4 @@ class Plan:
     def for_inputs(cls, inp, split_keys=0, q_range=None):
         return cls(inp["cfg"], inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"],
                    inp["n_pool"], inp["head_is_global"], split_keys, inp["cfg"].get("dirty_rows", ()),
-                   q_range)
+                   q_range, inp.get("pages"))

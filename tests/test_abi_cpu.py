@@ -110,6 +110,50 @@ def test_range_errors(L):
         assert _status(cfg, q_range=rng) == S.SEGMLA_E_SHAPE, rng
 
 
+def test_paged_pool_errors(L):
+    """Paged pool: every page a segment uses must be listed and lie inside the pool; a valid
+    page list gives the same |A| and rows as the contiguous pool (A does not depend on where
+    the rows are stored)."""
+    from workload.gen import page_placement
+    cfg = SMALL_CONFIGS[1]
+    kinds, lens, offsets = segment_table(cfg)
+    full = _create(cfg)
+    try:
+        rows0 = S.segmla_plan_rows(full)
+    finally:
+        S.segmla_plan_destroy(full)
+    for P in (1, 32, 48, 64):
+        pages, n_pool, _ = page_placement(kinds, lens, P, 3)
+        p = _create(cfg, pages=pages, n_pool=n_pool, pool_rows=np.zeros(len(lens), np.int64))
+        try:
+            assert S.segmla_plan_rows(p) == rows0
+        finally:
+            S.segmla_plan_destroy(p)
+    pages, n_pool, _ = page_placement(kinds, lens, 64, 3)
+
+    def st(**pg):
+        d = dict(pages)
+        d.update(pg)
+        return _status(cfg, pages=d, n_pool=n_pool)
+    assert st() == S.SEGMLA_OK
+    assert st(page_rows=0) == S.SEGMLA_E_GEOMETRY
+    bad = pages["page_start"].copy()
+    bad[-1] = len(pages["page_table"])  # the last segment's pages past the list
+    assert st(page_start=bad) == S.SEGMLA_E_GEOMETRY
+    bad = pages["page_start"].copy()
+    bad[0] = -1
+    assert st(page_start=bad) == S.SEGMLA_E_GEOMETRY
+    tbl = pages["page_table"].copy()
+    tbl[0] = n_pool // 64  # one page past the pool
+    assert st(page_table=tbl) == S.SEGMLA_E_GEOMETRY
+    tbl[0] = -1
+    assert st(page_table=tbl) == S.SEGMLA_E_GEOMETRY
+    from workload.gen import pool_rows_of
+    last = int(pool_rows_of(lens, pages).max())  # the highest pool row any segment uses
+    assert _status(cfg, pages=pages, n_pool=last + 1) == S.SEGMLA_OK
+    assert _status(cfg, pages=pages, n_pool=last) == S.SEGMLA_E_GEOMETRY
+
+
 def test_geometry_errors(L):
     cfg = SMALL_CONFIGS[1]
     kinds, lens, offsets = segment_table(cfg)

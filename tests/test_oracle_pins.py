@@ -283,6 +283,14 @@ def _segmented_fp64(inp, rows, rng):
 
     kinds, lens, offs, pr = inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"]
     lat = inp["latent"]
+    pages = inp.get("pages")
+
+    def seg_rows(i, n):  # pool rows of segment i's first n rows
+        if pages is None:
+            return np.arange(pr[i], pr[i] + n)
+        P, j = pages["page_rows"], np.arange(n)
+        return pages["page_table"][pages["page_start"][i] + j // P] * P + j % P
+
     out = {}
     for t in rows:
         stats = []
@@ -291,7 +299,7 @@ def _segmented_fp64(inp, rows, rng):
                 break
             nvis = min(int(lens[i]), t - int(offs[i]) + 1)
             rot_i = float(offs[i]) if kinds[i] == 1 else 0.0
-            C = lat[pr[i]:pr[i] + nvis]
+            C = lat[seg_rows(i, nvis)]
             q = rot(inp["q"][t], -rot_i * theta)            # [H, d]
             s = sig * q @ C.T
             m = s.max(axis=1)
@@ -307,7 +315,8 @@ def _segmented_fp64(inp, rows, rng):
 
 
 @pytest.mark.parametrize("cfg,mode", [(CONFIGS[0], "identity"), (SMALL_CONFIGS[0], "shuffled"),
-                                      (SMALL_CONFIGS[0], "aliased")])
+                                      (SMALL_CONFIGS[0], "aliased"), (SMALL_CONFIGS[0], "paged:16"),
+                                      (CONFIGS[0], "paged:7")])
 def test_relocation_identity(cfg, mode):
     inp = _oracle_inputs(make_inputs(cfg, "cpu", pool=mode))
     T = inp["T"]
@@ -427,3 +436,34 @@ def test_e4m3_generator_roundtrip_error():
     sc = inp["kv_scale"].double().numpy()
     amax = np.abs(vals[:, :512]).reshape(-1, 4, 128).max(-1)
     np.testing.assert_allclose(amax, 448 * sc, rtol=2 ** -4)
+
+
+@pytest.mark.parametrize("page_rows", [1, 5, 32])
+def test_paged_pool_equals_contiguous(page_rows):
+    """The same latent rows and cached state placed on shuffled pages instead of contiguous
+    segment ranges: the oracle's results are identical (every row read through the page
+    list lands on the row it stands for; unused pages hold NaN)."""
+    from workload.gen import page_placement
+    cfg = SMALL_CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    pages, n_pool, _ = page_placement(inp["kinds"], inp["lens"], page_rows, 5, share_docs=False)
+    # the page list's pool row of every request row, written out here from the definition
+    P = page_rows
+    rows = []
+    for i, L in enumerate(inp["lens"]):
+        for j in range(int(L)):
+            rows.append(int(pages["page_table"][pages["page_start"][i] + j // P]) * P + j % P)
+    rows = np.asarray(rows)
+    assert len(np.unique(rows)) == inp["T"]
+    src = inp["pool_rows"][np.repeat(np.arange(len(inp["lens"])), inp["lens"])] + \
+        (np.arange(inp["T"]) - np.repeat(inp["offsets"], inp["lens"]))
+    paged = dict(inp)
+    paged["pages"], paged["n_pool"] = pages, n_pool
+    paged["latent"] = np.full((n_pool, inp["latent"].shape[1]), np.nan)
+    paged["latent"][rows] = inp["latent"][src]
+    paged["z_cached"] = np.full((n_pool,) + inp["z_cached"].shape[1:], np.nan)
+    paged["z_cached"][rows] = inp["z_cached"][src]
+    a, b = O.layer_forward(inp), O.layer_forward(paged)
+    np.testing.assert_array_equal(a["A"], b["A"])
+    for k in ("O", "Z", "lse"):
+        np.testing.assert_array_equal(a[k], b[k])

@@ -22,7 +22,7 @@ from .configs import segment_table
 
 SEG_PREFIX, SEG_DOC, SEG_NEW = 0, 1, 2
 
-TAG_Q, TAG_LAT, TAG_W, TAG_ZC, TAG_SCORE, TAG_POOL = 1, 2, 3, 4, 5, 7
+TAG_Q, TAG_LAT, TAG_W, TAG_ZC, TAG_SCORE, TAG_POOL, TAG_PAGES = 1, 2, 3, 4, 5, 7, 8
 CHUNK_ROWS = 2048
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -110,12 +110,61 @@ def pool_placement(lens, mode, seed):
     raise ValueError(mode)
 
 
+def page_placement(kinds, lens, page_rows, seed, share_docs=True):
+    """Paged pool: segment i's rows on ceil(len_i / page_rows) pages listed at
+    page_table[page_start[i] ...]. Pages come from a shuffled list of pages with unused ones
+    among them; every third segment takes consecutive pages instead (runs longer than a page);
+    a document as long as an earlier document shares that document's pages (the same cached
+    document placed twice). Returns (pages dict, n_pool, pool row of each segment's first row)."""
+    rng = np.random.default_rng([seed, TAG_PAGES])
+    n = len(lens)
+    npg = (np.asarray(lens, dtype=np.int64) + page_rows - 1) // page_rows
+    need = int(npg.sum())
+    n_shuf = need + need // 3 + 2
+    free = [int(g) for g in rng.permutation(n_shuf)]
+    next_block = n_shuf  # consecutive pages are taken past the shuffled ones
+    page_start = np.zeros(n, dtype=np.int64)
+    table, first_doc_of_len = [], {}
+    for i in range(n):
+        L = int(lens[i])
+        if share_docs and kinds[i] == 1 and L in first_doc_of_len:
+            page_start[i] = page_start[first_doc_of_len[L]]
+            continue
+        if kinds[i] == 1:
+            first_doc_of_len[L] = i
+        page_start[i] = len(table)
+        if i % 3 == 0:
+            table += list(range(next_block, next_block + int(npg[i])))
+            next_block += int(npg[i])
+        else:
+            table += [free.pop() for _ in range(int(npg[i]))]
+    table = np.asarray(table, dtype=np.int64)
+    first_rows = table[page_start] * page_rows
+    return dict(page_rows=page_rows, page_start=page_start, page_table=table), \
+        next_block * page_rows, first_rows
+
+
+def pool_rows_of(lens, pages):
+    """Pool row of every request row under a page placement (the pages' definition)."""
+    P = pages["page_rows"]
+    out = []
+    for i, L in enumerate(lens):
+        j = np.arange(int(L), dtype=np.int64)
+        out.append(pages["page_table"][pages["page_start"][i] + j // P] * P + j % P)
+    return np.concatenate(out)
+
+
 def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
-    """All inputs of one layer forward for workload `cfg` on `device`."""
+    """All inputs of one layer forward for workload `cfg` on `device`. pool: identity,
+    shuffled, aliased, or paged:<rows per page>."""
     kinds, lens, offsets = segment_table(cfg)
     T = int(np.sum(lens, dtype=np.int64))
     seed = cfg["seed"]
-    pool_rows, n_pool = pool_placement(lens, pool, seed)
+    pages = None
+    if pool.startswith("paged:"):
+        pages, n_pool, pool_rows = page_placement(kinds, lens, int(pool.split(":")[1]), seed)
+    else:
+        pool_rows, n_pool = pool_placement(lens, pool, seed)
     H = cfg["n_heads"]
     d_nope, d_rope = cfg["d_nope"], cfg["d_rope"]
     d_qk = d_nope + d_rope
@@ -126,12 +175,17 @@ def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
     io = _TORCH_DT[cfg["dtype"]]
 
     used = np.zeros(n_pool, dtype=bool)
-    for p, n in zip(pool_rows, lens):
-        used[p:p + n] = True
+    if pages is not None:
+        used[pool_rows_of(lens, pages)] = True
+    else:
+        for p, n in zip(pool_rows, lens):
+            used[p:p + n] = True
     unused = torch.from_numpy(~used).to(device)
 
     out = dict(cfg=cfg, kinds=kinds, lens=lens, offsets=offsets, pool_rows=pool_rows,
                n_pool=n_pool, T=T, head_is_global=head_is_global, n_local=n_local, d_v=d_v)
+    if pages is not None:
+        out["pages"] = pages
     out["q"] = randn_rows((T, H, d_qk), seed, TAG_Q, device, io, std=cfg["q_std"])
     lat = randn_rows((n_pool, d_qk), seed, TAG_LAT, device, torch.float32)
     if cfg["kv_dtype"] == "e4m3":
