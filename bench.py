@@ -11,13 +11,15 @@ stated on) as the "target" figure, and the Pro-like 64K layer with the E4M3 late
 "fp8" figure. A row-window plan of the 128K layer's last row (decode: one new row against
 131,584 keys) is the "decode" figure, its whole forward against the HBM roofline (latent
 rows, W, and the row's q, out and z moved once). The main workload over a paged latent pool
-(64-row pages in shuffled order) is the "paged" figure. Throughput is algorithmic
+(64-row pages in shuffled order) is the "paged" figure, and the main workload with its
+projected state in groups of 8 heads (z and the cache per group) the "grouped" figure.
+Throughput is algorithmic
 attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the
 step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                 [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N] [--decode-only]
-                [--paged-rows P]
+                [--paged-rows P] [--grouped NAME]
 """
 import argparse
 import json
@@ -120,7 +122,8 @@ def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
     T, H = inp["T"], cfg["n_heads"]
     dt = inp["q"].dtype
     out = torch.empty((T, H, inp["d_v"]), dtype=dt, device="cuda")
-    z = torch.empty((T, H, cfg["d_state"]), dtype=dt, device="cuda")
+    G = cfg.get("group_heads", 0)
+    z = torch.empty((T, H // G if G >= 2 else H, cfg["d_state"]), dtype=dt, device="cuda")
     plan = S.Plan.for_inputs(inp)
 
     def step():
@@ -260,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-rows", type=int, default=1,
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
+    ap.add_argument("--grouped", default="flash_32k_grouped_bf16",
+                    help="also time this grouped-state workload (z per group of heads); '' for none")
     ap.add_argument("--paged-rows", type=int, default=64,
                     help="also time the main workload over a paged latent pool of this many rows "
                          "per page; 0: none")
@@ -301,6 +306,9 @@ def main():
     f8 = None
     if not args.no_fp8 and args.fp8:
         f8 = measure(args.fp8, 2, 1)
+    gr = None
+    if args.grouped:
+        gr = measure(args.grouped, max(2, args.steps // 2), 1)
     pg = None
     if args.paged_rows > 0:
         pg = measure(args.workload, max(2, args.steps // 2), 1, pool="paged:%d" % args.paged_rows)
@@ -361,6 +369,12 @@ def main():
             "attention_ms_min": round(tgt["attn_ms_min"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(tgt["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "target_frac_bf16_peak": 0.5,
+        }
+    if gr is not None:
+        line["grouped"] = {
+            "workload": gr["cfg"]["name"], "group_heads": gr["cfg"]["group_heads"],
+            "epilogue_ms": round(gr["epi_ms"], 3), "epilogue_ms_per_head_state": round(r["epi_ms"], 3),
+            "attention_ms": round(gr["attn_ms"], 3), "us_per_layer": round(gr["wall_s"] * 1e6, 1),
         }
     if pg is not None:
         line["paged"] = {

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define SEGMLA_ABI_VERSION 1
+#define SEGMLA_ABI_VERSION 2
 
 typedef enum segmla_status {
   SEGMLA_OK = 0,
@@ -109,6 +109,13 @@ typedef struct segmla_layer {
                                     > 0 (a multiple of 64): each work item covers at most
                                     this many keys and split partials are merged by the
                                     log-sum-exp merge */
+  int32_t group_heads;           /* 0 or 1: per-head projected state (z and z_cached hold
+                                    one vector per head / per Local head); G >= 2, dividing
+                                    n_heads: grouped state (RedKnot-MLA paper, projected-
+                                    state paragraph, Eq. 3, z = z_L + z_G): heads gG .. gG+G-1
+                                    form group g, z holds one vector per group, the sum of
+                                    its heads' projections, and z_cached the group's cached
+                                    Local contribution (else SEGMLA_E_SHAPE) */
 } segmla_layer;
 
 /* Protected-row rule (RedKnot-MLA paper, protected-row paragraph, Eq. 6):
@@ -145,7 +152,11 @@ typedef struct segmla_protect {
  *  z        [q_end - q_begin][H][d_state] io_dtype: projected state, every (row, head)
  *           written
  *  lse      optional fp32 [q_end - q_begin][H]: natural-log log-sum-exp of sigma*q.k for
- *           every computed (row, head); NULL to skip */
+ *           every computed (row, head); NULL to skip
+ * With grouped state (group_heads = G >= 2, n_groups = H / G): z is
+ * [q_end - q_begin][n_groups][d_state] with z[t][g] = the sum over the group's Global heads of
+ * W_h u_h plus, on rows in A, the sum over its Local heads of W_h u_h, or else
+ * z_cached[pool_row(t)][g]; z_cached is [n_pool][n_groups][d_state] (may be NULL when H_L = 0). */
 typedef struct segmla_tensors {
   const void *q;
   const void *kv;

@@ -295,6 +295,45 @@ def layer_forward(inp, rows=None, A_override=None, zc_override=None):
     return dict(geom=geom, prot=prot, A=A, rows=rows, O=O, lse=lse, Z=Z, computed=computed)
 
 
+class _NoCache:
+    """Stand-in cached state whose every row is zero (used to take the computed heads alone)."""
+
+    def __init__(self, n_local, d_state):
+        self.row = np.zeros((n_local, d_state))
+
+    def __getitem__(self, i):
+        return self.row
+
+
+def layer_forward_grouped(inp, rows=None):
+    """Oracle of the grouped projected state (RedKnot-MLA paper, projected-state paragraph,
+    Eq. 3: z = z_L + z_G, with the producer retaining the projected Local contribution).
+
+    Heads gG .. gG+G-1 form group g (G = cfg["group_heads"]). For request row t:
+    z[t][g] = sum over the group's Global heads of W_h u_h(t)
+              + (t in A ? sum over its Local heads of W_h u_h(t) : z_cached[pool_row(t)][g]),
+    with z_cached [n_pool, n_groups, d_state] the cached Local contribution per group. O, lse
+    and A are those of layer_forward. Returns its dict with Z [n, n_groups, d_state].
+    """
+    cfg = inp["cfg"]
+    G = int(cfg["group_heads"])
+    gmask = np.asarray(inp["head_is_global"]).astype(bool)
+    H = len(gmask)
+    none = _NoCache(int((~gmask).sum()), cfg["d_state"])
+    res = layer_forward(inp, rows=rows, zc_override=none)  # Local heads outside A add 0
+    geom, A = res["geom"], res["A"]
+    in_A = np.zeros(geom["T"], dtype=bool)
+    in_A[A] = True
+    Zh = res["Z"]                                             # [n, H, d_state]
+    Zg = Zh.reshape(len(res["rows"]), H // G, G, -1).sum(axis=2)
+    Zc = inp["z_cached"]
+    for i, t in enumerate(res["rows"]):
+        if not in_A[t]:
+            Zg[i] += np.asarray(Zc[geom["pool_of_row"][t]], dtype=np.float64)
+    res["Z"] = Zg
+    return res
+
+
 # ---------------------------------------------------------------------------- ledger
 def head_row_ceiling(f_front, r, f_back, n_heads, n_local):
     """Logical head-row eligibility ceiling (RedKnot-MLA paper, profiles paragraph,

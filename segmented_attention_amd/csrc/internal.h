@@ -140,6 +140,11 @@ struct EpiArgs {
   const int32_t* lhead;   // [HL]
   const int32_t* seg_of_row;
   const SegDesc* seg;
+  // grouped state (G >= 2): group g's Global heads are grp_ghead[grp_gstart[g] ..
+  // grp_gstart[g + 1]); z and z_cached hold n_groups slots per row
+  const int32_t* grp_gstart;
+  const int32_t* grp_ghead;
+  int32_t G, n_groups;
   // window [q0, q0 + nq); nA, nNA: the largest number of its rows inside / outside A (grid
   // sizes; the actual numbers are in rng)
   int32_t q0, nq, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;

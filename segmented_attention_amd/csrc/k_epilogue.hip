@@ -11,17 +11,53 @@ namespace segmla {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-// Row i of head h's list: Global heads walk every row of the window [q0, q0 + nq), Local
-// heads its rows of A (alist[rng[0], rng[1])). Local tiles are laid out for the largest
-// possible count (e.nA); tiles past the actual count are empty (n_rows <= r0).
+// A tile is a run of rows of one list and an output slot. Per-head state: the slot is a
+// head; Global heads walk every row of the window [q0, q0 + nq), Local heads its rows of A
+// (alist[rng[0], rng[1])). Grouped state: the slot is a group; on its rows of A the tile sums
+// all of the group's heads, on its other rows (nalist[rng[2], rng[3])) the group's Global
+// heads plus the cached Local contribution. Lists of rows of A (or outside A) are laid out for
+// the largest possible count (e.nA, e.nNA); tiles past the actual count are empty
+// (n_rows <= r0).
 struct EpiTile {
   int h, r0, n_rows, q0;
-  const int32_t* rows;  // null = the window's rows in order (request row q0 + i)
+  const int32_t* rows;   // null = the window's rows in order (request row q0 + i)
+  int nh;                // heads summed into the slot
+  const int32_t* heads;  // null = heads h .. h + nh - 1
+  int slot;              // output slot: the head, or the group
+  bool add_cache;        // add z_cached[pool_row(t)][slot] (grouped state, rows outside A)
 };
 
 __device__ __forceinline__ EpiTile epi_tile(const EpiArgs& e, int b, int rows_per_tile) {
   EpiTile et;
   et.q0 = e.q0;
+  et.nh = 1;
+  et.heads = nullptr;
+  et.add_cache = false;
+  const int ta = (e.nA + rows_per_tile - 1) / rows_per_tile;
+  if (e.G >= 2) {
+    if (b < e.n_groups * ta) {
+      const int g = b / ta;
+      et.h = g * e.G;
+      et.nh = e.G;
+      et.slot = g;
+      et.r0 = (b % ta) * rows_per_tile;
+      et.n_rows = e.rng[1] - e.rng[0];
+      et.rows = e.alist + e.rng[0];
+    } else {
+      b -= e.n_groups * ta;
+      const int tn = (e.nNA + rows_per_tile - 1) / rows_per_tile;
+      const int g = b / tn;
+      et.h = 0;
+      et.heads = e.grp_ghead + e.grp_gstart[g];
+      et.nh = e.grp_gstart[g + 1] - e.grp_gstart[g];
+      et.slot = g;
+      et.add_cache = e.HL > 0;
+      et.r0 = (b % tn) * rows_per_tile;
+      et.n_rows = e.rng[3] - e.rng[2];
+      et.rows = e.nalist + e.rng[2];
+    }
+    return et;
+  }
   const int tg = (e.nq + rows_per_tile - 1) / rows_per_tile;
   if (b < e.HG * tg) {
     et.h = e.ghead[b / tg];
@@ -30,46 +66,72 @@ __device__ __forceinline__ EpiTile epi_tile(const EpiArgs& e, int b, int rows_pe
     et.rows = nullptr;
   } else {
     b -= e.HG * tg;
-    const int ta = (e.nA + rows_per_tile - 1) / rows_per_tile;
     et.h = e.lhead[b / ta];
     et.r0 = (b % ta) * rows_per_tile;
     et.n_rows = e.rng[1] - e.rng[0];
     et.rows = e.alist + e.rng[0];
   }
+  et.slot = et.h;
   return et;
 }
 
-// request row of list entry i
+// request row of list entry i; head j of the tile
 __device__ __forceinline__ int epi_row(const EpiTile& et, int i) { return et.rows ? et.rows[i] : et.q0 + i; }
+__device__ __forceinline__ int epi_head(const EpiTile& et, int j) { return et.heads ? et.heads[j] : et.h + j; }
+// output slots per row of z, and the pool row of request row t (the cached state's row)
+__device__ __forceinline__ int z_slots(const EpiArgs& e) { return e.G >= 2 ? e.n_groups : e.H; }
+__device__ __forceinline__ int64_t pool_row_of(const EpiArgs& e, int t) {
+  const SegDesc sd = e.seg[e.seg_of_row[t]];
+  return sd.pool_row + (t - sd.offset);
+}
 
 // ------------------------------------------------------------------------ fp32 path
-// One wavefront per (row, head): u staged in LDS, each lane produces d_state/64 outputs.
+// One wavefront per (row, slot): for each of the slot's heads u is staged in LDS and each
+// lane adds its d_state/64 outputs (per-head state: one head, so z = W_h u exactly).
+constexpr int kF32MaxCols = 16;  // d_state <= 64 * 16
 __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
   __shared__ float u[1024];
   const int lane = threadIdx.x;
   EpiTile et = epi_tile(e, blockIdx.x, 1);
   if (et.r0 >= et.n_rows) return;
-  const int t = epi_row(et, et.r0), h = et.h;
-  const float* o = (const float*)e.out + ((int64_t)(t - e.q0) * e.H + h) * e.d_v;
-  for (int d = lane; d < e.d_v; d += 64) u[d] = o[d];
-  __syncthreads();
-  if (e.v_has_rope) {
-    const int half_r = e.d_rope / 2;
-    for (int k = lane; k < half_r; k += 64) {  // u^r <- R(-t) O^r
-      float2 cs = e.rowcs[(int64_t)t * half_r + k];
-      float x = o[e.d_nope + 2 * k], y = o[e.d_nope + 2 * k + 1];
-      u[e.d_nope + 2 * k] = x * cs.x + y * cs.y;
-      u[e.d_nope + 2 * k + 1] = -x * cs.y + y * cs.x;
+  const int t = epi_row(et, et.r0);
+  float acc[kF32MaxCols];
+#pragma unroll
+  for (int k = 0; k < kF32MaxCols; ++k) acc[k] = 0.f;
+  for (int j = 0; j < et.nh; ++j) {
+    const int h = epi_head(et, j);
+    __syncthreads();  // the previous head's u is consumed
+    const float* o = (const float*)e.out + ((int64_t)(t - e.q0) * e.H + h) * e.d_v;
+    for (int d = lane; d < e.d_v; d += 64) u[d] = o[d];
+    __syncthreads();
+    if (e.v_has_rope) {
+      const int half_r = e.d_rope / 2;
+      for (int k = lane; k < half_r; k += 64) {  // u^r <- R(-t) O^r
+        float2 cs = e.rowcs[(int64_t)t * half_r + k];
+        float x = o[e.d_nope + 2 * k], y = o[e.d_nope + 2 * k + 1];
+        u[e.d_nope + 2 * k] = x * cs.x + y * cs.y;
+        u[e.d_nope + 2 * k + 1] = -x * cs.y + y * cs.x;
+      }
+    }
+    __syncthreads();
+    const float* w = (const float*)e.w + (int64_t)h * e.d_state * e.d_v;
+#pragma unroll
+    for (int k = 0; k < kF32MaxCols; ++k) {
+      const int c = lane + 64 * k;
+      if (c >= e.d_state) continue;
+      const float* wr = w + (int64_t)c * e.d_v;
+      float dot = 0.f;
+      for (int d = 0; d < e.d_v; ++d) dot = fmaf(wr[d], u[d], dot);
+      acc[k] += dot;
     }
   }
-  __syncthreads();
-  const float* w = (const float*)e.w + (int64_t)h * e.d_state * e.d_v;
-  float* z = (float*)e.z + ((int64_t)(t - e.q0) * e.H + h) * e.d_state;
-  for (int c = lane; c < e.d_state; c += 64) {
-    const float* wr = w + (int64_t)c * e.d_v;
-    float acc = 0.f;
-    for (int d = 0; d < e.d_v; ++d) acc = fmaf(wr[d], u[d], acc);
-    z[c] = acc;
+  const float* zc = et.add_cache
+      ? (const float*)e.z_cached + (pool_row_of(e, t) * z_slots(e) + et.slot) * e.d_state : nullptr;
+  float* z = (float*)e.z + ((int64_t)(t - e.q0) * z_slots(e) + et.slot) * e.d_state;
+#pragma unroll
+  for (int k = 0; k < kF32MaxCols; ++k) {
+    const int c = lane + 64 * k;
+    if (c < e.d_state) z[c] = zc ? acc[k] + zc[c] : acc[k];
   }
 }
 
@@ -109,25 +171,25 @@ constexpr int kEpiLds = kEpiRowIds + kEpiRows * 4;      // 147968 bytes
 constexpr int kEpiPf = 4;                         // W ring slots, in k-steps (even, divides 32)
 static_assert(32 % kEpiPf == 0 && kEpiPf % 2 == 0, "ring slots are compile-time: kEpiPf divides the 32 nope k-steps");
 
+template <bool GROUPED>
 __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
   extern __shared__ __attribute__((aligned(16))) char lds_u[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   EpiTile et = epi_tile(e, blockIdx.x, kEpiRows);
-  const int h = et.h;
   const int n_here = min(kEpiRows, et.n_rows - et.r0);
   if (n_here <= 0) return;  // uniform: a Local tile past the window's rows of A
   const int d_v = e.d_v, half_r = e.d_rope / 2;
   const bool rope = e.v_has_rope != 0;  // d_v = 576 (else 512: nope only)
   const int64_t hstride = (int64_t)d_v * 2;
-  const char* outb = (const char*)e.out + (int64_t)h * hstride;
   // request rows of the tile first (rows past n_here repeat the last row: finite data, outputs
   // not stored), so that no vector load is waited for while copies are in flight
   int* const row_id = (int*)(lds_u + kEpiRowIds);
   if (tid < kEpiRows) row_id[tid] = epi_row(et, et.r0 + min(tid, n_here - 1));
   __syncthreads();
-  // stage U
-  {
+  // stage U of head h (the tile's rows), then de-rotate its RoPE part
+  auto stage = [&](int h) __attribute__((always_inline)) {
+    const char* outb = (const char*)e.out + (int64_t)h * hstride;
     const uint32_t base = lds_addr(lds_u);
     const int lane = lane_id();
     for (int n = 0; n < kEpiRows / 4; ++n) {
@@ -145,31 +207,32 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-  if (rope) {  // u^r <- R(-t) O^r in place: 128 rows x 8 chunks, 4 chunks per thread
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int idx = n * 256 + tid, r = idx >> 3, c = idx & 7;
-      const int t = row_id[r];
-      char* p = lds_u + kEpiRBase + r * 128 + ((c ^ fr(r)) << 4);
-      uint4 v = *(const uint4*)p;
-      const __bf16* x = (const __bf16*)&v;
-      __bf16 y[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float2 cs = e.rowcs[(int64_t)t * half_r + 4 * c + k];
-        const float a0 = (float)(x[2 * k]), a1 = (float)(x[2 * k + 1]);
-        y[2 * k] = (__bf16)(a0 * cs.x + a1 * cs.y);
-        y[2 * k + 1] = (__bf16)(-a0 * cs.y + a1 * cs.x);
-      }
-      *(uint4*)p = *(const uint4*)y;
-    }
     __syncthreads();
-  }
+    if (rope) {  // u^r <- R(-t) O^r in place: 128 rows x 8 chunks, 4 chunks per thread
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int idx = n * 256 + tid, r = idx >> 3, c = idx & 7;
+        const int t = row_id[r];
+        char* p = lds_u + kEpiRBase + r * 128 + ((c ^ fr(r)) << 4);
+        uint4 v = *(const uint4*)p;
+        const __bf16* x = (const __bf16*)&v;
+        __bf16 y[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float2 cs = e.rowcs[(int64_t)t * half_r + 4 * c + k];
+          const float a0 = (float)(x[2 * k]), a1 = (float)(x[2 * k + 1]);
+          y[2 * k] = (__bf16)(a0 * cs.x + a1 * cs.y);
+          y[2 * k + 1] = (__bf16)(-a0 * cs.y + a1 * cs.x);
+        }
+        *(uint4*)p = *(const uint4*)y;
+      }
+      __syncthreads();
+    }
+  };
+  const int nh = GROUPED ? et.nh : 1;
+  if (nh > 0) stage(epi_head(et, 0));
   const int lane = tid & 63;
   const int nblk_all = e.d_state / 32;
-  const __bf16* wt = (const __bf16*)e.wt + (int64_t)h * (d_v / 16) * nblk_all * 64 * 8;
   const int64_t wstep = (int64_t)nblk_all * 64 * 8;  // elements per k-step
   const int ksteps = d_v / 16;
   const int nblk = e.d_state / 32;      // 32-column blocks (d_state % 64 == 0)
@@ -187,7 +250,10 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
     const int r = 32 * i + col;
     rows_t[i] = r < n_here ? row_id[r] : -1;
   }
-  for (int b0 = wave; b0 < nblk; b0 += 16) {  // up to 4 of this wave's blocks: b0, b0+4, ..
+  const int zs = z_slots(e);
+  // passes over the 32-column blocks, the same count on every wave (the staging of the next
+  // head inside a pass is a workgroup barrier); wave w takes blocks b0, b0 + 4, .. < b0 + 16
+  for (int b0 = wave; b0 - wave < nblk; b0 += 16) {
     int nb = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) nb += (b0 + 4 * j < nblk) ? 1 : 0;
@@ -198,62 +264,71 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[j][i][k] = 0.f;
-    // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7],
-    // read from the operand-ordered copy (1 KB contiguous per wave and k-step)
-    const __bf16* wr[4];
+    for (int hj = 0; hj < nh; ++hj) {
+      if (GROUPED && nh > 1 && (b0 > wave || hj > 0)) {  // U of the slot's next head
+        __syncthreads();
+        stage(epi_head(et, hj));
+      }
+      if (nb == 0) continue;
+      const __bf16* wt = (const __bf16*)e.wt + (int64_t)epi_head(et, hj) * (d_v / 16) * nblk_all * 64 * 8;
+      // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7],
+      // read from the operand-ordered copy (1 KB contiguous per wave and k-step)
+      const __bf16* wr[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read valid data
-      wr[j] = wt + ((int64_t)blk * 64 + lane) * 8;
-    }
-    // W fragments: a ring of kEpiPf k-steps; the loads for k-step ks + kEpiPf - 1 (clamped to
-    // the last k-step: no branch, so the wait counts stay exact) are issued at the start of
-    // k-step ks, giving each load kEpiPf - 1 k-steps (16 MFMAs each) to arrive. U fragments are
-    // read one k-step ahead. The 32 nope k-steps and the 4 RoPE k-steps run as separate loops,
-    // so each address form is fixed at compile time.
-    bf16x8_t wf[kEpiPf][4];
+      for (int j = 0; j < 4; ++j) {
+        const int blk = min(b0 + 4 * j, nblk - 1);  // clamp: unused blocks read valid data
+        wr[j] = wt + ((int64_t)blk * 64 + lane) * 8;
+      }
+      // W fragments: a ring of kEpiPf k-steps; the loads for k-step ks + kEpiPf - 1 (clamped to
+      // the last k-step: no branch, so the wait counts stay exact) are issued at the start of
+      // k-step ks, giving each load kEpiPf - 1 k-steps (16 MFMAs each) to arrive. U fragments are
+      // read one k-step ahead. The 32 nope k-steps and the 4 RoPE k-steps run as separate loops,
+      // so each address form is fixed at compile time.
+      bf16x8_t wf[kEpiPf][4];
 #pragma unroll
-    for (int s = 0; s < kEpiPf - 1; ++s)
+      for (int s = 0; s < kEpiPf - 1; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + wstep * min(s, ksteps - 1));
-    auto u_nope = [&](int ks, bf16x8_t* u) __attribute__((always_inline)) {  // ks < 32
-      const char* up = ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3);
+        for (int j = 0; j < 4; ++j) wf[s][j] = *(const bf16x8_t*)(wr[j] + wstep * min(s, ksteps - 1));
+      auto u_nope = [&](int ks, bf16x8_t* u) __attribute__((always_inline)) {  // ks < 32
+        const char* up = ubn + ((32 * (ks & 7)) ^ usw) + 256 * (ks >> 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * kEpiNRow);
-    };
-    auto u_rope = [&](int j, bf16x8_t* u) __attribute__((always_inline)) {  // k-step 32 + j
-      const char* up = ubr + ((32 * j) ^ ursw);
+        for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * kEpiNRow);
+      };
+      auto u_rope = [&](int j, bf16x8_t* u) __attribute__((always_inline)) {  // k-step 32 + j
+        const char* up = ubr + ((32 * j) ^ ursw);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * 128);
-    };
-    bf16x8_t ur[2][4];
-    auto kstep = [&](int ks, int slot, auto&& read_next) __attribute__((always_inline)) {
-      const int kp = min(ks + kEpiPf - 1, ksteps - 1);
+        for (int i = 0; i < 4; ++i) u[i] = *(const bf16x8_t*)(up + i * 32 * 128);
+      };
+      bf16x8_t ur[2][4];
+      auto kstep = [&](int ks, int slot, auto&& read_next) __attribute__((always_inline)) {
+        const int kp = min(ks + kEpiPf - 1, ksteps - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[(slot + kEpiPf - 1) % kEpiPf][j] = *(const bf16x8_t*)(wr[j] + wstep * kp);
-      read_next();
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) wf[(slot + kEpiPf - 1) % kEpiPf][j] = *(const bf16x8_t*)(wr[j] + wstep * kp);
+        read_next();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][j], ur[slot & 1][i], acc[j][i], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    u_nope(0, ur[0]);
-    for (int ks0 = 0; ks0 < 32; ks0 += kEpiPf) {
+          for (int i = 0; i < 4; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[slot][j], ur[slot & 1][i], acc[j][i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      u_nope(0, ur[0]);
+      for (int ks0 = 0; ks0 < 32; ks0 += kEpiPf) {
 #pragma unroll
-      for (int slot = 0; slot < kEpiPf; ++slot)
-        kstep(ks0 + slot, slot, [&] { u_nope(min(ks0 + slot + 1, 31), ur[(slot + 1) & 1]); });
-    }
-    if (rope) {  // k-steps 32..35 (ring slot (32 + j) % kEpiPf; kEpiPf is even)
-      u_rope(0, ur[0]);
+        for (int slot = 0; slot < kEpiPf; ++slot)
+          kstep(ks0 + slot, slot, [&] { u_nope(min(ks0 + slot + 1, 31), ur[(slot + 1) & 1]); });
+      }
+      if (rope) {  // k-steps 32..35 (ring slot (32 + j) % kEpiPf; kEpiPf is even)
+        u_rope(0, ur[0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        kstep(32 + j, (32 + j) % kEpiPf, [&] { u_rope(min(j + 1, 3), ur[(j + 1) & 1]); });
+        for (int j = 0; j < 4; ++j)
+          kstep(32 + j, (32 + j) % kEpiPf, [&] { u_rope(min(j + 1, 3), ur[(j + 1) & 1]); });
+      }
     }
     // C[m][n] = Z^T[column][row]: lane holds row 32 i + col and columns
     // 32 blk + 8 (k >> 2) + 4 hf + (k & 3)
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j >= nb) continue;
@@ -261,12 +336,19 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (rows_t[i] < 0) continue;
-        __bf16* z = (__bf16*)e.z + ((int64_t)(rows_t[i] - e.q0) * e.H + h) * e.d_state + cbase;
+        __bf16* z = (__bf16*)e.z + ((int64_t)(rows_t[i] - e.q0) * zs + et.slot) * e.d_state + cbase;
+        const __bf16* zc = nullptr;
+        if (GROUPED && et.add_cache)
+          zc = (const __bf16*)e.z_cached + (pool_row_of(e, rows_t[i]) * zs + et.slot) * e.d_state + cbase;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-          const bf16x4_t y = {(__bf16)acc[j][i][4 * g], (__bf16)acc[j][i][4 * g + 1],
-                              (__bf16)acc[j][i][4 * g + 2], (__bf16)acc[j][i][4 * g + 3]};
+          float v[4] = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]};
+          if (GROUPED && zc) {
+            const bf16x4_t c = *(const bf16x4_t*)(zc + 8 * g);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] += (float)c[k];
+          }
+          const bf16x4_t y = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
           *(bf16x4_t*)(z + 8 * g) = y;
         }
       }
@@ -397,36 +479,46 @@ __global__ __launch_bounds__(256) void k_restore_copy(EpiArgs e, int vec_per_hea
 }
 
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
+  const bool grouped = e.G >= 2;
+  // tiles of `rows` rows: per-head state: Global heads x window rows + Local heads x rows of A
+  // (the restore copy takes the Local heads' other rows); grouped: groups x (rows of A + the
+  // other rows)
+  auto n_tiles = [&](int rows) -> int64_t {
+    if (grouped)
+      return (int64_t)e.n_groups * ((e.nA + rows - 1) / rows + (e.nNA + rows - 1) / rows);
+    return (int64_t)e.HG * ((e.nq + rows - 1) / rows) + (int64_t)e.HL * ((e.nA + rows - 1) / rows);
+  };
   if (io_dtype == 0) {
-    const int64_t blocks = (int64_t)e.HG * e.nq + (int64_t)e.HL * e.nA;
+    const int64_t blocks = n_tiles(1);
     if (blocks > 0)
       hipLaunchKernelGGL(k_project_f32, dim3((unsigned)blocks), dim3(64), 0, stream, e);
-    if (e.HL > 0 && e.nNA > 0)
+    if (!grouped && e.HL > 0 && e.nNA > 0)
       hipLaunchKernelGGL(k_restore_copy<float>, dim3(e.nNA), dim3(256), 0, stream, e, e.d_state);
   } else {
-    const int64_t blocks = (int64_t)e.HG * ((e.nq + kEpiRows - 1) / kEpiRows) +
-                           (int64_t)e.HL * ((e.nA + kEpiRows - 1) / kEpiRows);
+    const int64_t blocks = n_tiles(kEpiRows);
     const size_t lds = kEpiLds;
     static bool attr_set = false;
     if (!attr_set) {
-      hipError_t r = hipFuncSetAttribute((const void*)k_project_bf16,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (r != hipSuccess) return r;
+      for (const void* k : {(const void*)k_project_bf16<false>, (const void*)k_project_bf16<true>}) {
+        hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (r != hipSuccess) return r;
+      }
       attr_set = true;
     }
-    const bool thin = e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
+    const bool thin = !grouped && e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
                       e.d_state % kThinCols == 0;
     if (blocks > 0 && thin) {  // one tile per head (nA <= nq <= kThinRows)
-      const int64_t tiles = (int64_t)e.HG * ((e.nq + kThinRows - 1) / kThinRows) +
-                            (int64_t)e.HL * ((e.nA + kThinRows - 1) / kThinRows);
-      hipLaunchKernelGGL(k_project_thin, dim3((unsigned)(tiles * (e.d_state / kThinCols))),
+      hipLaunchKernelGGL(k_project_thin, dim3((unsigned)(n_tiles(kThinRows) * (e.d_state / kThinCols))),
                          dim3(256), 0, stream, e);
     } else if (blocks > 0) {
       const int64_t chunks = (int64_t)e.H * e.d_state * e.d_v / 8;
       hipLaunchKernelGGL(k_w_tile, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, e);
-      hipLaunchKernelGGL(k_project_bf16, dim3((unsigned)blocks), dim3(256), lds, stream, e);
+      if (grouped)
+        hipLaunchKernelGGL(k_project_bf16<true>, dim3((unsigned)blocks), dim3(256), lds, stream, e);
+      else
+        hipLaunchKernelGGL(k_project_bf16<false>, dim3((unsigned)blocks), dim3(256), lds, stream, e);
     }
-    if (e.HL > 0 && e.nNA > 0)
+    if (!grouped && e.HL > 0 && e.nNA > 0)
       hipLaunchKernelGGL(k_restore_copy<uint4>, dim3(e.nNA), dim3(256), 0, stream, e,
                          e.d_state * 2 / 16);
   }

@@ -29,6 +29,8 @@ struct segmla_plan {
   double rope_base = 10000.0;
   float sigma = 1.f;
   std::vector<int32_t> ghead, lhead;
+  int32_t G = 1, n_groups = 0;             // grouped projected state when G >= 2
+  std::vector<int32_t> grp_gstart, grp_ghead;  // each group's Global heads (CSR)
   // protection
   int32_t edge_rows = 0, tail_rows = 0, budget_permille = 0;
   std::vector<int32_t> dirty;  // sorted, unique
@@ -39,7 +41,7 @@ struct segmla_plan {
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
-         o_rng = 0, o_lseg = 0, ws_bytes = 0;
+         o_rng = 0, o_lseg = 0, o_grp = 0, ws_bytes = 0;
   // largest number of window rows inside / outside A (the Indexer picks decide the actual)
   int64_t nA_w = 0, nNA_w = 0;
   // profiling (events on the caller's stream)
@@ -100,6 +102,8 @@ segmla_status check_layer(const segmla_layer* L) {
   if (!is_dtype(L->kv_dtype) || !is_dtype(L->io_dtype)) return SEGMLA_E_DTYPE;
   if (L->io_dtype == SEGMLA_E4M3_B128) return SEGMLA_E_DTYPE;
   if (L->split_keys < -1 || (L->split_keys > 0 && (L->split_keys % 64) != 0)) return SEGMLA_E_SHAPE;
+  if (L->group_heads < 0 || (L->group_heads >= 2 && L->n_heads % L->group_heads != 0))
+    return SEGMLA_E_SHAPE;
   const int d_qk = L->d_nope + L->d_rope;
   if (L->kv_dtype == SEGMLA_F32) {
     if (L->io_dtype != SEGMLA_F32) return SEGMLA_E_UNSUPPORTED;
@@ -242,6 +246,16 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   for (int h = 0; h < p->H; ++h) (layer->head_is_global[h] ? p->ghead : p->lhead).push_back(h);
   p->HG = (int32_t)p->ghead.size();
   p->HL = (int32_t)p->lhead.size();
+  if (layer->group_heads >= 2) {
+    p->G = layer->group_heads;
+    p->n_groups = p->H / p->G;
+    p->grp_gstart.push_back(0);
+    for (int g = 0; g < p->n_groups; ++g) {
+      for (int h = g * p->G; h < (g + 1) * p->G; ++h)
+        if (layer->head_is_global[h]) p->grp_ghead.push_back(h);
+      p->grp_gstart.push_back((int32_t)p->grp_ghead.size());
+    }
+  }
   p->d_nope = layer->d_nope;
   p->d_rope = layer->d_rope;
   p->d_qk = layer->d_nope + layer->d_rope;
@@ -344,6 +358,7 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
   p->o_ghead = take(sizeof(int32_t) * p->ghead.size());
   p->o_lhead = take(sizeof(int32_t) * p->lhead.size());
+  p->o_grp = take(sizeof(int32_t) * (p->grp_gstart.size() + p->grp_ghead.size()));
   p->o_alist = take(sizeof(int32_t) * (size_t)p->nA);
   p->o_nalist = take(sizeof(int32_t) * (size_t)(T - p->nA));
   p->o_blk_count = take(sizeof(int32_t) * p->n_blk);
@@ -411,6 +426,9 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
   up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
   up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
   up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
+  up(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
+  up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
+     sizeof(int32_t) * p->grp_ghead.size());
   if (e != hipSuccess) return SEGMLA_E_HIP;
   e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->d_rope, p->rope_base,
                       p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
@@ -504,6 +522,10 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   ep.d_v = p->d_v;
   ep.d_state = p->d_state;
   ep.v_has_rope = p->v_has_rope;
+  ep.G = p->G;
+  ep.n_groups = p->n_groups;
+  ep.grp_gstart = p->at<int32_t>(p->o_grp);
+  ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
   e = launch_epilogue(ep, p->io_dtype, s);
   if (e == hipSuccess && p->prof) {
     e = hipEventRecord(p->ev[3], s);

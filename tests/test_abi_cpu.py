@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert S.segmla_abi_version() == 1
+    assert S.segmla_abi_version() == 2
     for st in range(-9, 1):
         assert S.segmla_status_string(st) not in ("", "unknown status")
     assert S.segmla_status_string(-100) == "unknown status"

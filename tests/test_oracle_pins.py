@@ -467,3 +467,51 @@ def test_paged_pool_equals_contiguous(page_rows):
     np.testing.assert_array_equal(a["A"], b["A"])
     for k in ("O", "Z", "lse"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_grouped_state_is_the_group_sum_of_per_head_state():
+    """Grouped state (Eq. 3, z = z_L + z_G) against the per-head oracle: with the grouped cache
+    holding each group's sum of the per-head cached Local rows, the grouped z of every row is the
+    sum over the group's heads of the per-head z (computed heads on rows of A, Global heads plus
+    the cache elsewhere), for groups with and without a Global head."""
+    from workload.configs import GROUPED_CONFIGS
+    cfg = GROUPED_CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    G, H = cfg["group_heads"], cfg["n_heads"]
+    gmask = np.asarray(inp["head_is_global"]).astype(bool)
+    local = np.nonzero(~gmask)[0]
+    rng = np.random.default_rng(4)
+    zc_h = rng.standard_normal((inp["n_pool"], len(local), cfg["d_state"]))
+    zc_g = np.zeros((inp["n_pool"], H // G, cfg["d_state"]))
+    for li, h in enumerate(local):
+        zc_g[:, h // G] += zc_h[:, li]
+    per_head = O.layer_forward(dict(inp, z_cached=zc_h))
+    grouped = O.layer_forward_grouped(dict(inp, z_cached=zc_g))
+    np.testing.assert_array_equal(grouped["A"], per_head["A"])
+    ref = per_head["Z"].reshape(len(per_head["rows"]), H // G, G, -1).sum(axis=2)
+    np.testing.assert_allclose(grouped["Z"], ref, rtol=0, atol=1e-12)
+    assert not gmask[G:2 * G].any()  # the second group has no Global head
+    outside = np.setdiff1d(np.arange(inp["T"]), per_head["A"])
+    np.testing.assert_allclose(grouped["Z"][outside, 1], zc_g[grouped["geom"]["pool_of_row"][outside], 1],
+                               rtol=0, atol=0)
+
+
+def test_grouped_exact_cache_identity():
+    """When the cached Local contribution of every group equals the full recomputation's (the
+    cache was produced in the same context), the grouped state equals full recomputation on
+    every row, whatever A is (Eq. 4 as an exact linear identity)."""
+    from workload.configs import GROUPED_CONFIGS
+    cfg = GROUPED_CONFIGS[0]
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    G, H, T = cfg["group_heads"], cfg["n_heads"], inp["T"]
+    full = O.layer_forward(inp, A_override=np.arange(T))  # every head on every row
+    gmask = np.asarray(inp["head_is_global"]).astype(bool)
+    zc_g = np.full((inp["n_pool"], H // G, cfg["d_state"]), np.nan)
+    pool = full["geom"]["pool_of_row"]
+    for g in range(H // G):
+        heads = [h for h in range(g * G, (g + 1) * G) if not gmask[h]]
+        zc_g[pool, g] = full["Z"][:, heads].sum(axis=1)
+    grouped = O.layer_forward_grouped(dict(inp, z_cached=zc_g))
+    ref = full["Z"].reshape(T, H // G, G, -1).sum(axis=2)
+    assert len(grouped["A"]) < T
+    np.testing.assert_allclose(grouped["Z"], ref, rtol=0, atol=1e-12)

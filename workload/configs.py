@@ -103,8 +103,26 @@ SMALL_CONFIGS = [
 ]
 
 
+# Grouped projected state (z and the cache hold one vector per group of heads): the tiny layer
+# in groups of 4 (group 1 has no Global head: its rows outside A are the cache alone), and the
+# Flash-like and Pro-like layers in groups of 8 (one Global head each).
+GROUPED_CONFIGS = [
+    dict(_cfg("tiny_fp32_grouped", None, "f32", 8, 64, 16, 64,
+              [("prefix", 12), ("doc", 40), ("doc", 75), ("new", 6)],
+              edge_rows=8, tail_rows=16, budget_permille=200, seed=20), group_heads=4),
+    dict(_cfg("flash_small_grouped_bf16", None, "bf16", 64, 512, 64, 512,
+              [("prefix", 33), ("doc", 200), ("doc", 257), ("doc", 120), ("new", 21)],
+              edge_rows=16, tail_rows=48, budget_permille=150, seed=21), group_heads=8),
+    dict(_cfg("pro_small_grouped_fp8", None, "bf16", 128, 512, 64, 512,
+              [("prefix", 9), ("doc", 140), ("doc", 95), ("new", 13)],
+              edge_rows=8, tail_rows=24, budget_permille=250, seed=22, kv_dtype="e4m3"),
+         group_heads=8),
+    dict(CONFIGS[1], name="flash_32k_grouped_bf16", index=None, group_heads=8),
+]
+
+
 def config_by_name(name):
-    for c in CONFIGS + SMALL_CONFIGS + [FLASH_TAIL32K, LONG_128K_GLOBAL]:
+    for c in CONFIGS + SMALL_CONFIGS + GROUPED_CONFIGS + [FLASH_TAIL32K, LONG_128K_GLOBAL]:
         if c["name"] == name:
             return c
     raise KeyError(name)

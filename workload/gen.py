@@ -204,7 +204,9 @@ def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
     del lat
     out["w"] = randn_rows((H, cfg["d_state"], d_v), seed, TAG_W, device, io,
                           std=1.0 / np.sqrt(d_v))
-    out["z_cached"] = randn_rows((n_pool, n_local, cfg["d_state"]), seed, TAG_ZC, device, io)
+    G = cfg.get("group_heads", 0)
+    slots = H // G if G >= 2 else n_local  # grouped state: one cached vector per group
+    out["z_cached"] = randn_rows((n_pool, slots, cfg["d_state"]), seed, TAG_ZC, device, io)
     if with_scores:
         out["scores"] = uint32_scores(T, seed, device)
     return out
