@@ -251,9 +251,10 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
     rows_t[i] = r < n_here ? row_id[r] : -1;
   }
   const int zs = z_slots(e);
-  // passes over the 32-column blocks, the same count on every wave (the staging of the next
-  // head inside a pass is a workgroup barrier); wave w takes blocks b0, b0 + 4, .. < b0 + 16
-  for (int b0 = wave; b0 - wave < nblk; b0 += 16) {
+  // passes over the 32-column blocks: wave w takes blocks b0, b0 + 4, .. < b0 + 16. Grouped,
+  // every wave makes the same number of passes (staging the slot's next head is a workgroup
+  // barrier); per head, a wave with no block left stops.
+  for (int b0 = wave; GROUPED ? b0 - wave < nblk : b0 < nblk; b0 += 16) {
     int nb = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) nb += (b0 + 4 * j < nblk) ? 1 : 0;
@@ -270,7 +271,8 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
         stage(epi_head(et, hj));
       }
       if (nb == 0) continue;
-      const __bf16* wt = (const __bf16*)e.wt + (int64_t)epi_head(et, hj) * (d_v / 16) * nblk_all * 64 * 8;
+      const int hh = GROUPED ? epi_head(et, hj) : et.h;
+      const __bf16* wt = (const __bf16*)e.wt + (int64_t)hh * (d_v / 16) * nblk_all * 64 * 8;
       // A operand (W_h, 32 columns x 16 features): lane holds W[column][16 ks + 8 hf .. + 7],
       // read from the operand-ordered copy (1 KB contiguous per wave and k-step)
       const __bf16* wr[4];
@@ -336,7 +338,8 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (rows_t[i] < 0) continue;
-        __bf16* z = (__bf16*)e.z + ((int64_t)(rows_t[i] - e.q0) * zs + et.slot) * e.d_state + cbase;
+        __bf16* z = (__bf16*)e.z + ((int64_t)(rows_t[i] - e.q0) * (GROUPED ? zs : e.H) +
+                                    (GROUPED ? et.slot : et.h)) * e.d_state + cbase;
         const __bf16* zc = nullptr;
         if (GROUPED && et.add_cache)
           zc = (const __bf16*)e.z_cached + (pool_row_of(e, rows_t[i]) * zs + et.slot) * e.d_state + cbase;
