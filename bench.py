@@ -265,6 +265,9 @@ def main():
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
     ap.add_argument("--grouped", default="flash_32k_grouped_bf16",
                     help="also time this grouped-state workload (z per group of heads); '' for none")
+    ap.add_argument("--pool", default="identity",
+                    help="latent pool layout of the main workload: identity, shuffled, aliased or "
+                         "paged:<rows per page>")
     ap.add_argument("--paged-rows", type=int, default=64,
                     help="also time the main workload over a paged latent pool of this many rows "
                          "per page; 0: none")
@@ -296,7 +299,7 @@ def main():
         d = measure_window(inp, cfg, args.decode_rows, args.steps, args.warmup)
         print(json.dumps({"decode": decode_json(cfg["name"], d)}), flush=True)
         return
-    main_res = measure(args.workload, args.steps, args.warmup)
+    main_res = measure(args.workload, args.steps, args.warmup, pool=args.pool)
     sec = None
     if not args.no_secondary and args.secondary:
         sec = measure(args.secondary, max(2, args.steps // 3), 1, decode_rows=args.decode_rows)
@@ -332,6 +335,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": r["cfg"]["name"],
+            **({"pool": args.pool} if args.pool != "identity" else {}),
             "rows": r["T"], "heads": cfg["n_heads"], "global_heads": len(cfg["global_heads"]),
             "latent": "%d+%d" % (cfg["d_nope"], cfg["d_rope"]),
             "protected_rows": r["n_protected"],

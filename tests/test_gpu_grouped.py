@@ -97,3 +97,24 @@ def test_grouped_full_size_32k_sampled():
     np.testing.assert_array_equal(A, ref["A"])
     say("  %d rows, max rel err O %.2e Z %.2e" % ((len(rows),) + _check(cfg, ref, out[rows], z[rows],
                                                                           lse[rows], np.arange(len(rows)))))
+
+
+@pytest.mark.parametrize("q0,q1,split", [(0, None, 0), (250, 420, 128), (-1, None, 0)], ids=str)
+def test_grouped_paged_windows_compose(q0, q1, split):
+    """The features together: grouped state over a paged latent pool (48-row pages, documents
+    of equal length sharing pages), in row windows and with key splits."""
+    cfg = GROUPED_CONFIGS[1]
+    inp = make_inputs(cfg, "cuda", pool="paged:48")
+    T = inp["T"]
+    if q0 < 0:
+        q0 = T - 3
+    q1 = T if q1 is None else q1
+    say("case grouped paged %s [%d, %d) split=%d" % (cfg["name"], q0, q1, split))
+    plan, out, z, lse = _run(inp, split, q_range=(q0, q1))
+    oi = oracle_inputs(inp)
+    ref = O.layer_forward_grouped(oi, rows=np.arange(q0, q1))
+    np.testing.assert_array_equal(plan.protected(), ref["A"])
+    seg, pool_row = plan.geometry()
+    np.testing.assert_array_equal(pool_row, ref["geom"]["pool_of_row"])
+    plan.close()
+    say("  max rel err O %.2e Z %.2e" % _check(cfg, ref, out, z, lse, np.arange(q1 - q0)))
