@@ -74,8 +74,10 @@ def measure_window(inp, cfg, n_rows, steps, warmup):
     T, H = inp["T"], cfg["n_heads"]
     q0 = T - n_rows
     dt = inp["q"].dtype
+    G = cfg.get("group_heads", 0)
+    slots = H // G if G >= 2 else H  # z vectors per row (per head, or per group of heads)
     out = torch.empty((n_rows, H, inp["d_v"]), dtype=dt, device="cuda")
-    z = torch.empty((n_rows, H, cfg["d_state"]), dtype=dt, device="cuda")
+    z = torch.empty((n_rows, slots, cfg["d_state"]), dtype=dt, device="cuda")
     plan = S.Plan.for_inputs(inp, q_range=(q0, T))
     plan.build(inp["scores"])
     for _ in range(warmup):
@@ -93,7 +95,7 @@ def measure_window(inp, cfg, n_rows, steps, warmup):
     d_qk = cfg["d_nope"] + cfg["d_rope"]
     row_bytes = d_qk * 2 if cfg["kv_dtype"] == "bf16" else cfg["d_nope"] + 4 * (cfg["d_nope"] // 128) + 2 * cfg["d_rope"]
     w_bytes = H * cfg["d_state"] * inp["d_v"] * 2
-    nbytes = T * row_bytes + w_bytes + n_rows * H * (d_qk + inp["d_v"] + cfg["d_state"]) * 2
+    nbytes = T * row_bytes + w_bytes + n_rows * (H * (d_qk + inp["d_v"]) + slots * cfg["d_state"]) * 2
     fwd_us = attn_us + merge_us + epi_us
     gbps = nbytes / (fwd_us * 1e-6) / 1e9
     return dict(rows=n_rows, keys=T, attention_us=attn_us, merge_us=merge_us, epilogue_us=epi_us,

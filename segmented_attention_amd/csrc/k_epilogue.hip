@@ -362,7 +362,9 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 // ------------------------------------------------------------------------ thin path
 // Windows of at most kThinRows rows (decode): per head the projection is a product of W_h
 // with a few vectors, bound by reading W once, so W is read in its own layout (no
-// operand-order copy) and no matrix core is used. Workgroup = (head tile, 64 columns of Z).
+// operand-order copy) and no matrix core is used. Workgroup = (slot tile, 64 columns of Z);
+// a grouped slot sums its heads one after the other (u restaged per head) and adds the cached
+// group vector on rows outside A.
 // A team of 8 lanes takes one column: lane j reads the 16-byte chunks j, j + 8, ... of the
 // column's W row (each team step reads 128 contiguous bytes) and the team's partial sums meet
 // by lane shuffles. The u rows sit in LDS as fp32 holding the values the tile path
@@ -382,74 +384,84 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
   const int cb = blockIdx.x % ncb;
   const EpiTile et = epi_tile(e, blockIdx.x / ncb, kThinRows);
   const int n_here = min(kThinRows, et.n_rows - et.r0);
-  if (n_here <= 0) return;  // uniform: a Local tile past the window's rows of A
-  const int tid = threadIdx.x, h = et.h, d_v = e.d_v;
+  if (n_here <= 0) return;  // uniform: a tile past the window's rows of its list
+  const int tid = threadIdx.x, d_v = e.d_v;
   if (tid < kThinRows) row_id[tid] = epi_row(et, et.r0 + min(tid, n_here - 1));
-  __syncthreads();
-  {
-    const __bf16* outp = (const __bf16*)e.out;
-    const int n_pairs = d_v / 2, nope_pairs = e.d_nope / 2, half_r = e.d_rope / 2;
-    for (int i = tid; i < n_here * n_pairs; i += 256) {
-      const int r = i / n_pairs, k2 = i - r * n_pairs;
-      const int t = row_id[r];
-      const __bf16* o = outp + ((int64_t)(t - e.q0) * e.H + h) * d_v + 2 * k2;
-      float a0 = (float)o[0], a1 = (float)o[1];
-      if (k2 >= nope_pairs) {  // v carries the RoPE part (d_v > d_nope)
-        const float2 cs = e.rowcs[(int64_t)t * half_r + (k2 - nope_pairs)];
-        const float y0 = (float)(__bf16)(a0 * cs.x + a1 * cs.y);
-        const float y1 = (float)(__bf16)(-a0 * cs.y + a1 * cs.x);
-        a0 = y0;
-        a1 = y1;
-      }
-      us[r][2 * k2] = a0;
-      us[r][2 * k2 + 1] = a1;
-    }
-  }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, team = lane >> 3, j = lane & 7;
   const int nk = d_v / 64;
-  const __bf16* wh = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
-  uint4 wv[2][kThinMaxK];
+  float acc[2][kThinRows];
 #pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    const __bf16* wc = wh + (int64_t)(cb * kThinCols + wave * 16 + ps * 8 + team) * d_v + 8 * j;
+  for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-    for (int k = 0; k < kThinMaxK; ++k)
-      if (k < nk) wv[ps][k] = *(const uint4*)(wc + 64 * k);
-  }
-#pragma unroll
-  for (int ps = 0; ps < 2; ++ps) {
-    float acc[kThinRows];
-#pragma unroll
-    for (int r = 0; r < kThinRows; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int k = 0; k < kThinMaxK; ++k) {
-      if (k >= nk) continue;
-      const uint4 x = wv[ps][k];
-      const float w8[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
-                           bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
-#pragma unroll
-      for (int r = 0; r < kThinRows; ++r) {
-        if (r >= n_here) continue;
-        const float4 u0 = *(const float4*)&us[r][8 * (j + 8 * k)];
-        const float4 u1 = *(const float4*)&us[r][8 * (j + 8 * k) + 4];
-        float a = acc[r];
-        a = fmaf(w8[0], u0.x, a);
-        a = fmaf(w8[1], u0.y, a);
-        a = fmaf(w8[2], u0.z, a);
-        a = fmaf(w8[3], u0.w, a);
-        a = fmaf(w8[4], u1.x, a);
-        a = fmaf(w8[5], u1.y, a);
-        a = fmaf(w8[6], u1.z, a);
-        a = fmaf(w8[7], u1.w, a);
-        acc[r] = a;
+    for (int r = 0; r < kThinRows; ++r) acc[ps][r] = 0.f;
+  for (int hj = 0; hj < et.nh; ++hj) {  // the slot's heads (grouped state: the group's)
+    const int h = epi_head(et, hj);
+    if (hj > 0) __syncthreads();  // every wave is done with the previous head's u
+    {
+      const __bf16* outp = (const __bf16*)e.out;
+      const int n_pairs = d_v / 2, nope_pairs = e.d_nope / 2, half_r = e.d_rope / 2;
+      for (int i = tid; i < n_here * n_pairs; i += 256) {
+        const int r = i / n_pairs, k2 = i - r * n_pairs;
+        const int t = row_id[r];
+        const __bf16* o = outp + ((int64_t)(t - e.q0) * e.H + h) * d_v + 2 * k2;
+        float a0 = (float)o[0], a1 = (float)o[1];
+        if (k2 >= nope_pairs) {  // v carries the RoPE part (d_v > d_nope)
+          const float2 cs = e.rowcs[(int64_t)t * half_r + (k2 - nope_pairs)];
+          const float y0 = (float)(__bf16)(a0 * cs.x + a1 * cs.y);
+          const float y1 = (float)(__bf16)(-a0 * cs.y + a1 * cs.x);
+          a0 = y0;
+          a1 = y1;
+        }
+        us[r][2 * k2] = a0;
+        us[r][2 * k2 + 1] = a1;
       }
     }
+    __syncthreads();
+    const __bf16* wh = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
+    uint4 wv[2][kThinMaxK];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const __bf16* wc = wh + (int64_t)(cb * kThinCols + wave * 16 + ps * 8 + team) * d_v + 8 * j;
+#pragma unroll
+      for (int k = 0; k < kThinMaxK; ++k)
+        if (k < nk) wv[ps][k] = *(const uint4*)(wc + 64 * k);
+    }
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+      for (int k = 0; k < kThinMaxK; ++k) {
+        if (k >= nk) continue;
+        const uint4 x = wv[ps][k];
+        const float w8[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
+                             bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
+#pragma unroll
+        for (int r = 0; r < kThinRows; ++r) {
+          if (r >= n_here) continue;
+          const float4 u0 = *(const float4*)&us[r][8 * (j + 8 * k)];
+          const float4 u1 = *(const float4*)&us[r][8 * (j + 8 * k) + 4];
+          float a = acc[ps][r];
+          a = fmaf(w8[0], u0.x, a);
+          a = fmaf(w8[1], u0.y, a);
+          a = fmaf(w8[2], u0.z, a);
+          a = fmaf(w8[3], u0.w, a);
+          a = fmaf(w8[4], u1.x, a);
+          a = fmaf(w8[5], u1.y, a);
+          a = fmaf(w8[6], u1.z, a);
+          a = fmaf(w8[7], u1.w, a);
+          acc[ps][r] = a;
+        }
+      }
+    }
+  }
+  const int zs = z_slots(e);
+#pragma unroll
+  for (int ps = 0; ps < 2; ++ps) {
     // team sums; lane j of the team then stores row j
     float mine = 0.f;
 #pragma unroll
     for (int r = 0; r < kThinRows; ++r) {
-      float a = acc[r];
+      float a = acc[ps][r];
       a += __shfl_xor(a, 1);
       a += __shfl_xor(a, 2);
       a += __shfl_xor(a, 4);
@@ -457,7 +469,10 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
     }
     if (j < n_here) {
       const int col = cb * kThinCols + wave * 16 + ps * 8 + team;
-      ((__bf16*)e.z)[((int64_t)(row_id[j] - e.q0) * e.H + h) * e.d_state + col] = (__bf16)mine;
+      const int t = row_id[j];
+      if (et.add_cache)
+        mine += (float)((const __bf16*)e.z_cached)[(pool_row_of(e, t) * zs + et.slot) * e.d_state + col];
+      ((__bf16*)e.z)[((int64_t)(t - e.q0) * zs + et.slot) * e.d_state + col] = (__bf16)mine;
     }
   }
 }
@@ -508,9 +523,9 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
       }
       attr_set = true;
     }
-    const bool thin = !grouped && e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
+    const bool thin = e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
                       e.d_state % kThinCols == 0;
-    if (blocks > 0 && thin) {  // one tile per head (nA <= nq <= kThinRows)
+    if (blocks > 0 && thin) {  // one tile per slot and list (nA, nNA <= nq <= kThinRows)
       hipLaunchKernelGGL(k_project_thin, dim3((unsigned)(n_tiles(kThinRows) * (e.d_state / kThinCols))),
                          dim3(256), 0, stream, e);
     } else if (blocks > 0) {

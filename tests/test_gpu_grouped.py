@@ -118,3 +118,16 @@ def test_grouped_paged_windows_compose(q0, q1, split):
     np.testing.assert_array_equal(pool_row, ref["geom"]["pool_of_row"])
     plan.close()
     say("  max rel err O %.2e Z %.2e" % _check(cfg, ref, out, z, lse, np.arange(q1 - q0)))
+
+
+def test_grouped_decode_128k_last_row():
+    """The 128K layer's last row with grouped state: split keys, the wide merge and the
+    matrix-vector projection summing each group's heads."""
+    cfg = GROUPED_CONFIGS[4]
+    inp = make_inputs(cfg, "cuda")
+    T = inp["T"]
+    say("case grouped decode %s [%d, %d)" % (cfg["name"], T - 1, T))
+    plan, out, z, lse = _run(inp, q_range=(T - 1, T))
+    ref = O.layer_forward_grouped(oracle_inputs(inp, lazy=True), rows=np.arange(T - 1, T))
+    plan.close()
+    say("  max rel err O %.2e Z %.2e" % _check(cfg, ref, out, z, lse, np.arange(1)))

@@ -118,6 +118,7 @@ GROUPED_CONFIGS = [
               edge_rows=8, tail_rows=24, budget_permille=250, seed=22, kv_dtype="e4m3"),
          group_heads=8),
     dict(CONFIGS[1], name="flash_32k_grouped_bf16", index=None, group_heads=8),
+    dict(CONFIGS[2], name="long_128k_grouped_bf16", index=None, group_heads=8),
 ]
 
 
