@@ -145,6 +145,7 @@ struct EpiArgs {
   const int32_t* grp_gstart;
   const int32_t* grp_ghead;
   int32_t G, n_groups;
+  float* zpart;  // grouped windows of at most 8 rows: per-head fp32 projections [nq][H][d_state]
   // window [q0, q0 + nq); nA, nNA: the largest number of its rows inside / outside A (grid
   // sizes; the actual numbers are in rng)
   int32_t q0, nq, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;

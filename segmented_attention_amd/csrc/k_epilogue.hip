@@ -27,14 +27,17 @@ struct EpiTile {
   bool add_cache;        // add z_cached[pool_row(t)][slot] (grouped state, rows outside A)
 };
 
-__device__ __forceinline__ EpiTile epi_tile(const EpiArgs& e, int b, int rows_per_tile) {
+// grouped = false lays out per-head tiles whatever the state (the per-head fp32 projections
+// of a grouped decode window)
+__device__ __forceinline__ EpiTile epi_tile(const EpiArgs& e, int b, int rows_per_tile,
+                                            bool grouped) {
   EpiTile et;
   et.q0 = e.q0;
   et.nh = 1;
   et.heads = nullptr;
   et.add_cache = false;
   const int ta = (e.nA + rows_per_tile - 1) / rows_per_tile;
-  if (e.G >= 2) {
+  if (grouped) {
     if (b < e.n_groups * ta) {
       const int g = b / ta;
       et.h = g * e.G;
@@ -92,7 +95,7 @@ constexpr int kF32MaxCols = 16;  // d_state <= 64 * 16
 __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
   __shared__ float u[1024];
   const int lane = threadIdx.x;
-  EpiTile et = epi_tile(e, blockIdx.x, 1);
+  EpiTile et = epi_tile(e, blockIdx.x, 1, e.G >= 2);
   if (et.r0 >= et.n_rows) return;
   const int t = epi_row(et, et.r0);
   float acc[kF32MaxCols];
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
   extern __shared__ __attribute__((aligned(16))) char lds_u[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  EpiTile et = epi_tile(e, blockIdx.x, kEpiRows);
+  EpiTile et = epi_tile(e, blockIdx.x, kEpiRows, e.G >= 2);
   const int n_here = min(kEpiRows, et.n_rows - et.r0);
   if (n_here <= 0) return;  // uniform: a Local tile past the window's rows of A
   const int d_v = e.d_v, half_r = e.d_rope / 2;
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
   __shared__ int row_id[kThinRows];
   const int ncb = e.d_state / kThinCols;
   const int cb = blockIdx.x % ncb;
-  const EpiTile et = epi_tile(e, blockIdx.x / ncb, kThinRows);
+  const EpiTile et = epi_tile(e, blockIdx.x / ncb, kThinRows, e.G >= 2 && !e.zpart);
   const int n_here = min(kThinRows, et.n_rows - et.r0);
   if (n_here <= 0) return;  // uniform: a tile past the window's rows of its list
   const int tid = threadIdx.x, d_v = e.d_v;
@@ -470,10 +473,36 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
     if (j < n_here) {
       const int col = cb * kThinCols + wave * 16 + ps * 8 + team;
       const int t = row_id[j];
+      if (e.zpart) {  // per-head fp32 projection, summed per group by k_group_sum
+        e.zpart[((int64_t)(t - e.q0) * e.H + et.h) * e.d_state + col] = mine;
+        continue;
+      }
       if (et.add_cache)
         mine += (float)((const __bf16*)e.z_cached)[(pool_row_of(e, t) * zs + et.slot) * e.d_state + col];
       ((__bf16*)e.z)[((int64_t)(t - e.q0) * zs + et.slot) * e.d_state + col] = (__bf16)mine;
     }
+  }
+}
+
+// Grouped decode windows: z[t][g] = the group's computed heads' fp32 projections, summed in
+// head order, plus the cached group vector on rows outside A. Workgroup = (window row, group).
+__global__ __launch_bounds__(256) void k_group_sum(EpiArgs e) {
+  const int i = blockIdx.x / e.n_groups, g = blockIdx.x % e.n_groups;
+  const int t = e.q0 + i;
+  bool in_a = false;  // the window's rows of A: alist[rng[0], rng[1]), at most 8 of them
+  for (int k = e.rng[0]; k < e.rng[1]; ++k) in_a = in_a || e.alist[k] == t;
+  const int g0 = e.grp_gstart[g], g1 = e.grp_gstart[g + 1];
+  const __bf16* zc = (!in_a && e.HL > 0)
+      ? (const __bf16*)e.z_cached + (pool_row_of(e, t) * e.n_groups + g) * e.d_state : nullptr;
+  for (int c = threadIdx.x; c < e.d_state; c += 256) {
+    float acc = 0.f;
+    for (int h = g * e.G; h < (g + 1) * e.G; ++h) {
+      bool global = false;
+      for (int k = g0; k < g1; ++k) global = global || e.grp_ghead[k] == h;
+      if (global || in_a) acc += e.zpart[((int64_t)i * e.H + h) * e.d_state + c];
+    }
+    if (zc) acc += (float)zc[c];
+    ((__bf16*)e.z)[((int64_t)i * e.n_groups + g) * e.d_state + c] = (__bf16)acc;
   }
 }
 
@@ -525,7 +554,13 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
     }
     const bool thin = e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
                       e.d_state % kThinCols == 0;
-    if (blocks > 0 && thin) {  // one tile per slot and list (nA, nNA <= nq <= kThinRows)
+    if (blocks > 0 && thin && e.zpart) {  // grouped: per-head projections, then group sums
+      const int64_t tiles = (int64_t)e.HG * ((e.nq + kThinRows - 1) / kThinRows) +
+                            (int64_t)e.HL * ((e.nA + kThinRows - 1) / kThinRows);
+      hipLaunchKernelGGL(k_project_thin, dim3((unsigned)(tiles * (e.d_state / kThinCols))),
+                         dim3(256), 0, stream, e);
+      hipLaunchKernelGGL(k_group_sum, dim3((unsigned)(e.nq * e.n_groups)), dim3(256), 0, stream, e);
+    } else if (blocks > 0 && thin) {  // one tile per slot and list (nA, nNA <= nq <= kThinRows)
       hipLaunchKernelGGL(k_project_thin, dim3((unsigned)(n_tiles(kThinRows) * (e.d_state / kThinCols))),
                          dim3(256), 0, stream, e);
     } else if (blocks > 0) {

@@ -41,7 +41,7 @@ struct segmla_plan {
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
-         o_rng = 0, o_lseg = 0, o_grp = 0, ws_bytes = 0;
+         o_rng = 0, o_lseg = 0, o_grp = 0, o_zpart = 0, ws_bytes = 0;
   // largest number of window rows inside / outside A (the Indexer picks decide the actual)
   int64_t nA_w = 0, nNA_w = 0;
   // profiling (events on the caller's stream)
@@ -372,6 +372,9 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
     p->o_part_o = take(sizeof(float) * (size_t)p->n_split * nvec * p->d_v);
     p->o_part_ml = take(sizeof(float) * 2 * (size_t)p->n_split * nvec);
   }
+  // grouped state in a small window (decode): per-head fp32 projections, summed per group
+  if (p->io_dtype == SEGMLA_BF16 && p->G >= 2 && (int64_t)p->q1 - p->q0 <= 8)
+    p->o_zpart = take(sizeof(float) * (size_t)(p->q1 - p->q0) * p->H * p->d_state);
   if (p->io_dtype == SEGMLA_BF16)  // forward scratch: W in the projection's operand order
     p->o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
   p->ws_bytes = o;
@@ -526,6 +529,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   ep.n_groups = p->n_groups;
   ep.grp_gstart = p->at<int32_t>(p->o_grp);
   ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
+  ep.zpart = p->o_zpart ? p->at<float>(p->o_zpart) : nullptr;
   e = launch_epilogue(ep, p->io_dtype, s);
   if (e == hipSuccess && p->prof) {
     e = hipEventRecord(p->ev[3], s);
