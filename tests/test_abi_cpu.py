@@ -154,6 +154,25 @@ def test_paged_pool_errors(L):
     assert _status(cfg, pages=pages, n_pool=last) == S.SEGMLA_E_GEOMETRY
 
 
+def test_group_heads_errors(L):
+    """Grouped state: group_heads 0 or 1 is per head; G >= 2 must divide n_heads; negative is
+    an error. A valid grouping changes neither T nor |A|."""
+    cfg = SMALL_CONFIGS[1]  # 64 heads
+    base = _create(cfg)
+    try:
+        rows0 = S.segmla_plan_rows(base)
+    finally:
+        S.segmla_plan_destroy(base)
+    for G in (0, 1, 2, 8, 64):
+        p = _create(cfg, group_heads=G)
+        try:
+            assert S.segmla_plan_rows(p) == rows0
+        finally:
+            S.segmla_plan_destroy(p)
+    for G in (-1, 3, 7, 65):
+        assert _status(cfg, group_heads=G) == S.SEGMLA_E_SHAPE, G
+
+
 def test_geometry_errors(L):
     cfg = SMALL_CONFIGS[1]
     kinds, lens, offsets = segment_table(cfg)
