@@ -7,8 +7,9 @@ row-replacement epilogue). The default workload is the Flash-like 32K layer
 (64 heads, 56 Local / 8 Global, 512 + 64 latent, 8 x 4096 documents after a 256-row
 prefix, 128 question rows, 10 % Local budget); the 128K layer is measured as a
 secondary figure, its 8 Global heads alone (every row, the part the throughput target is
-stated on) as the "target" figure, and the Pro-like 64K layer with the E4M3 latent as the
-"fp8" figure. A row-window plan of the 128K layer's last row (decode: one new row against
+stated on) as the "target" figure, the Pro-like 64K layer with the E4M3 latent as the
+"fp8" figure, and the layer of 256 short documents (a 256-way merge per question row) as the
+"many_short" figure. A row-window plan of the 128K layer's last row (decode: one new row against
 131,584 keys) is the "decode" figure, its whole forward against the HBM roofline (latent
 rows, W, and the row's q, out and z moved once). The main workload over a paged latent pool
 (64-row pages in shuffled order) is the "paged" figure, and the main workload with its
@@ -18,8 +19,8 @@ attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, di
 step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
-                [--no-target] [--no-fp8] [--no-cpu-baseline] [--decode-rows N] [--decode-only]
-                [--paged-rows P] [--grouped NAME]
+                [--no-target] [--no-fp8] [--many-short NAME] [--no-cpu-baseline]
+                [--decode-rows N] [--decode-only] [--paged-rows P] [--grouped NAME]
 """
 import argparse
 import json
@@ -262,6 +263,9 @@ def main():
     ap.add_argument("--no-target", action="store_true")
     ap.add_argument("--fp8", default="pro_64k_fp8", help="E4M3-latent workload reported alongside")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--many-short", default="many_short_bf16",
+                    help="many-short-segments workload (256 documents, 256-way merge per row) "
+                         "reported alongside; '' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-rows", type=int, default=1,
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
@@ -302,15 +306,20 @@ def main():
         print(json.dumps({"decode": decode_json(cfg["name"], d)}), flush=True)
         return
     main_res = measure(args.workload, args.steps, args.warmup, pool=args.pool)
-    sec = None
-    if not args.no_secondary and args.secondary:
-        sec = measure(args.secondary, max(2, args.steps // 3), 1, decode_rows=args.decode_rows)
+    # the target figure comes before the long layers (a chip that has run them for seconds
+    # clocks lower) with at least 3 warm-up and 10 timed steps
     tgt = None
     if not args.no_target and args.target:
-        tgt = measure(args.target, max(2, args.steps // 3), 1)
+        tgt = measure(args.target, max(10, args.steps // 2), max(3, args.warmup))
+    sec = None
+    if not args.no_secondary and args.secondary:
+        sec = measure(args.secondary, max(3, args.steps // 4), 1, decode_rows=args.decode_rows)
     f8 = None
     if not args.no_fp8 and args.fp8:
-        f8 = measure(args.fp8, 2, 1)
+        f8 = measure(args.fp8, 10, 3)
+    msh = None
+    if args.many_short:
+        msh = measure(args.many_short, max(3, args.steps // 4), 1)
     gr = None
     if args.grouped:
         gr = measure(args.grouped, max(2, args.steps // 2), 1)
@@ -375,6 +384,16 @@ def main():
             "attention_ms_min": round(tgt["attn_ms_min"], 3), "attention_tflops": round(tgt["attn_tflops"], 3),
             "attention_frac_bf16_peak": round(tgt["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
             "target_frac_bf16_peak": 0.5,
+        }
+    if msh is not None:
+        line["many_short"] = {
+            "workload": msh["cfg"]["name"], "rows": msh["T"],
+            "segments": len(msh["cfg"]["segments"]), "protected_rows": msh["n_protected"],
+            "tflops": round(msh["tflops"], 3), "us_per_layer": round(msh["wall_s"] * 1e6, 1),
+            "attention_tflops": round(msh["attn_tflops"], 3),
+            "attention_frac_bf16_peak": round(msh["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": {"attention": round(msh["attn_ms"], 3), "split_merge": round(msh["merge_ms"], 3),
+                         "epilogue": round(msh["epi_ms"], 3), "plan_build": round(msh["build_ms"], 3)},
         }
     if gr is not None:
         line["grouped"] = {

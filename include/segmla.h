@@ -23,10 +23,14 @@
  *    All device work is enqueued on it with no hidden synchronization; only the
  *    segmla_copy_* calls synchronize that stream.
  *  - Errors: arguments are validated on the host before anything is enqueued; on
- *    any status other than SEGMLA_OK nothing has been written to caller memory and
- *    no work has been enqueued, so the caller chooses the fallback (there is never
- *    a silent one). SEGMLA_E_HIP reports a failed HIP call or launch; faults of
- *    enqueued kernels surface at the caller's next synchronization.
+ *    any status other than SEGMLA_OK and SEGMLA_E_HIP nothing has been written to
+ *    caller memory and no work has been enqueued, so the caller chooses the fallback
+ *    (there is never a silent one). SEGMLA_E_HIP reports a HIP call or launch that
+ *    failed after validation: work enqueued earlier in the same call may still run,
+ *    so after SEGMLA_E_HIP from segmla_plan_build the plan stays unbuilt (the
+ *    workspace contents are undefined) and after SEGMLA_E_HIP from segmla_forward
+ *    the outputs are undefined. Faults of enqueued kernels surface at the caller's
+ *    next synchronization.
  *  - Immutability: the latent pool, the cached projected state and the Indexer
  *    scores are read only.
  *  - Aliasing: segment pool ranges may alias (one document placed twice); outputs
@@ -171,8 +175,10 @@ typedef struct segmla_tensors {
 
 typedef struct segmla_plan segmla_plan;
 
-/* Validate geometry, roles and protection (host only, no HIP call) and size the
- * plan. n_pool = rows of the latent pool. On success *out_plan owns a new plan. */
+/* Validate geometry, roles and protection and size the plan (host only: nothing is
+ * enqueued; the one HIP call reads the current device's compute-unit count, which the
+ * key-range split spreads short work lists over, and 256 is assumed when no device is
+ * visible). n_pool = rows of the latent pool. On success *out_plan owns a new plan. */
 segmla_status segmla_plan_create(const segmla_geometry *geom, const segmla_layer *layer,
                                  const segmla_protect *prot, int64_t n_pool,
                                  segmla_plan **out_plan);
@@ -220,6 +226,27 @@ segmla_status segmla_plan_workspace_bytes(const segmla_plan *plan, size_t *bytes
 /* Host only, no synchronization: request rows T and |A|. |A| = |F| + need is fixed
  * by geometry and protection; only which Indexer rows are chosen needs the scores. */
 segmla_status segmla_plan_rows(const segmla_plan *plan, int64_t *n_rows, int64_t *n_protected);
+
+/* Shapes a forward of this plan reads and writes (host only, no synchronization), so that a
+ * binding can check caller tensors before passing raw pointers: in elements, q holds
+ * window_rows * n_heads * (d_nope + d_rope) io values, out window_rows * n_heads * d_v, z
+ * window_rows * z_slots * d_state, lse window_rows * n_heads (fp32), w n_heads * d_state *
+ * d_v, z_cached n_pool * zc_slots * d_state (io dtype); the latent n_pool rows (see
+ * segmla_tensors); indexer_score T values. z_slots = n_heads (per-head state) or the number
+ * of groups; zc_slots = the Local heads or the number of groups. */
+typedef struct segmla_plan_info {
+  int64_t T;               /* request rows */
+  int64_t q_begin, q_end;  /* computed window */
+  int64_t n_pool;          /* latent-pool rows the plan was validated against */
+  int64_t n_protected;     /* |A| */
+  int64_t workspace_bytes; /* as segmla_plan_workspace_bytes */
+  int32_t n_heads, n_global, n_local;
+  int32_t d_nope, d_rope, d_v, d_state;
+  int32_t z_slots, zc_slots;
+  int32_t kv_dtype, io_dtype;
+  int32_t n_split;         /* key-range splits of the attention (1: none) */
+} segmla_plan_info;
+segmla_status segmla_plan_get_info(const segmla_plan *plan, segmla_plan_info *info);
 
 /* Build the plan's device descriptors into `workspace` (>= segmla_plan_workspace_bytes,
  * 256-byte aligned): segment descriptors and RoPE tables (fp64-built), the row maps,

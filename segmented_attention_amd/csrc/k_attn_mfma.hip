@@ -746,14 +746,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 namespace {
 template <bool VROPE, bool FP8>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
-  static bool attr_set = false;
   const int lds = kLdsAlloc;
-  if (!attr_set) {
-    hipError_t r = hipFuncSetAttribute((const void*)k_attn_mfma<VROPE, FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (r != hipSuccess) return r;
-    attr_set = true;
-  }
+  // once per process and instantiation; a function-local static is initialized exactly once
+  // even when several host threads launch at the same time
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_attn_mfma<VROPE, FP8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
   const int64_t blocks = (int64_t)(a.map.nF + a.map.nG) * a.n_split;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((k_attn_mfma<VROPE, FP8>), dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);

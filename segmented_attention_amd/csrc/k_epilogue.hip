@@ -544,14 +544,15 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
   } else {
     const int64_t blocks = n_tiles(kEpiRows);
     const size_t lds = kEpiLds;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // once per process (thread-safe initialization of a function-local static)
+    static const hipError_t attr = [] {
       for (const void* k : {(const void*)k_project_bf16<false>, (const void*)k_project_bf16<true>}) {
-        hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t r = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kEpiLds);
         if (r != hipSuccess) return r;
       }
-      attr_set = true;
-    }
+      return hipSuccess;
+    }();
+    if (attr != hipSuccess) return attr;
     const bool thin = e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
                       e.d_state % kThinCols == 0;
     if (blocks > 0 && thin && e.zpart) {  // grouped: per-head projections, then group sums

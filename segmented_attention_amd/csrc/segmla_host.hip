@@ -37,6 +37,7 @@ struct segmla_plan {
   int64_t n_forced = 0, n_cand = 0, K = 0, need = 0, nA = 0;
   // work decomposition
   int32_t nF = 0, nG = 0, n_split = 1, split_keys = 0, n_blk = 0;
+  int32_t n_cu = 256;  // compute units of the device the plan was sized for
   // workspace layout (byte offsets, 256-aligned)
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
@@ -58,7 +59,18 @@ struct segmla_plan {
 
 namespace {
 
-constexpr int kNumCU = 256;
+// Compute units of the current device: the key-range split spreads short work lists over
+// them. A plan can be sized where no device is visible (validation on a host without a GPU);
+// it then assumes 256, the MI355X count, and clears the runtime's error state.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -137,7 +149,9 @@ segmla_status check_geometry(const segmla_geometry* G, const segmla_pages* P, in
       if (st < 0 || st > P->n_entries - np) return SEGMLA_E_GEOMETRY;
       for (int64_t k = 0; k < np; ++k) {
         const int64_t rows = std::min<int64_t>(pr, G->len[i] - k * pr), g = P->page_table[st + k];
-        if (g < 0 || g > (n_pool - rows) / pr) return SEGMLA_E_GEOMETRY;
+        // the page's used rows [g * pr, g * pr + rows) inside [0, n_pool), in int64 without
+        // overflow (no division: it would round a negative room up to page 0)
+        if (g < 0 || g > (INT64_MAX - rows) / pr || g * pr + rows > n_pool) return SEGMLA_E_GEOMETRY;
       }
     }
   }
@@ -324,14 +338,16 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   const int64_t n_tiles = nF + nG;
   int32_t sk = layer->split_keys;
   const int32_t keys = p->q1;  // the window's rows see keys [0, q1) at most
+  p->n_cu = device_cus();
+  const int64_t ncu = p->n_cu;
   if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
     sk = -1;
-    if (n_tiles > 0 && n_tiles < 2 * kNumCU && keys > 2048) {
+    if (n_tiles > 0 && n_tiles < 2 * ncu && keys > 2048) {
       // about four workgroups per CU, each with at least 1024 keys; where that leaves CUs idle
       // (decode: one or two tiles), one workgroup per CU, each with at least 256 keys
-      int64_t want = std::min<int64_t>((4 * kNumCU + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
-      if (want * n_tiles < kNumCU)
-        want = std::min<int64_t>((kNumCU + n_tiles - 1) / n_tiles, (keys + 255) / 256);
+      int64_t want = std::min<int64_t>((4 * ncu + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
+      if (want * n_tiles < ncu)
+        want = std::min<int64_t>((ncu + n_tiles - 1) / n_tiles, (keys + 255) / 256);
       if (want > 1) sk = (int32_t)((((keys + want - 1) / want) + 63) / 64 * 64);
     }
   }
@@ -392,6 +408,29 @@ segmla_status segmla_plan_rows(const segmla_plan* p, int64_t* n_rows, int64_t* n
   if (!p || !n_rows || !n_protected) return SEGMLA_E_NULL;
   *n_rows = p->T;
   *n_protected = p->nA;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_plan_get_info(const segmla_plan* p, segmla_plan_info* info) {
+  if (!p || !info) return SEGMLA_E_NULL;
+  info->T = p->T;
+  info->q_begin = p->q0;
+  info->q_end = p->q1;
+  info->n_pool = p->n_pool;
+  info->n_protected = p->nA;
+  info->workspace_bytes = (int64_t)p->ws_bytes;
+  info->n_heads = p->H;
+  info->n_global = p->HG;
+  info->n_local = p->HL;
+  info->d_nope = p->d_nope;
+  info->d_rope = p->d_rope;
+  info->d_v = p->d_v;
+  info->d_state = p->d_state;
+  info->z_slots = p->G >= 2 ? p->n_groups : p->H;
+  info->zc_slots = p->G >= 2 ? p->n_groups : p->HL;
+  info->kv_dtype = p->kv_dtype;
+  info->io_dtype = p->io_dtype;
+  info->n_split = p->n_split;
   return SEGMLA_OK;
 }
 

@@ -25,7 +25,7 @@ EXPORTED = [
     "segmla_forward", "segmla_copy_protected", "segmla_copy_geometry", "segmla_lse_merge",
     "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
     "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
-    "segmla_plan_create_range", "segmla_plan_create_paged",
+    "segmla_plan_create_range", "segmla_plan_create_paged", "segmla_plan_get_info",
 ]
 
 
@@ -68,6 +68,17 @@ class Tensors(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("q_begin", ctypes.c_int64), ("q_end", ctypes.c_int64),
+                ("n_pool", ctypes.c_int64), ("n_protected", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("n_heads", ctypes.c_int32),
+                ("n_global", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("z_slots", ctypes.c_int32),
+                ("zc_slots", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -91,6 +102,7 @@ def lib():
                                                i64, i64, ctypes.POINTER(P)]),
             "segmla_plan_workspace_bytes": (i32, [P, ctypes.POINTER(ctypes.c_size_t)]),
             "segmla_plan_rows": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+            "segmla_plan_get_info": (i32, [P, ctypes.POINTER(PlanInfo)]),
             "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
             "segmla_forward": (i32, [P, ctypes.POINTER(Tensors), P]),
             "segmla_copy_protected": (i32, [P, ctypes.POINTER(i32), i64, P]),
@@ -139,6 +151,41 @@ def _stream(stream):
 
 def _arr(a, dtype):
     return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def _torch_dtypes(code):
+    """torch dtypes a tensor of segmla_dtype `code` may have (E4M3 codes: bytes)."""
+    import torch
+    return {SEGMLA_F32: (torch.float32,), SEGMLA_BF16: (torch.bfloat16,),
+            SEGMLA_E4M3_B128: (torch.uint8, torch.float8_e4m3fn)}[code]
+
+
+def _check_tensors(specs):
+    """specs: (name, tensor, dtypes, numel, required). Raise ValueError unless every given
+    tensor is a contiguous GPU tensor of one of its dtypes with at least `numel` elements. The
+    C ABI sees only raw addresses, so this is the last place where a host tensor, a wrong dtype
+    or an undersized buffer can be caught before a kernel reads or writes past it. Types,
+    dtypes and sizes of all tensors are checked before any device."""
+    import torch
+    given = []
+    for name, t, dtypes, numel, required in specs:
+        if t is None:
+            if required:
+                raise ValueError("%s is required" % name)
+            continue
+        if not torch.is_tensor(t):
+            raise ValueError("%s must be a torch tensor, got %s" % (name, type(t).__name__))
+        if t.dtype not in dtypes:
+            raise ValueError("%s has dtype %s, expected %s"
+                             % (name, t.dtype, " or ".join(map(str, dtypes))))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.numel() < numel:
+            raise ValueError("%s holds %d elements, the plan needs %d" % (name, t.numel(), numel))
+        given.append((name, t))
+    for name, t in given:
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU, got device %s" % (name, t.device))
 
 
 # ------------------------------------------------------------------- C entry points
@@ -205,14 +252,50 @@ def segmla_plan_rows(plan):
     return int(T.value), int(nA.value)
 
 
+def segmla_plan_get_info(plan):
+    """The plan's shapes (segmla_plan_info) as a dict."""
+    info = PlanInfo()
+    _check(lib().segmla_plan_get_info(plan, ctypes.byref(info)), "segmla_plan_get_info")
+    return {name: int(getattr(info, name)) for name, _ in PlanInfo._fields_}
+
+
 def segmla_plan_build(plan, workspace, indexer_score=None, stream=None):
+    import torch
+    info = segmla_plan_get_info(plan)
+    _check_tensors([("workspace", workspace, (torch.uint8,), info["workspace_bytes"], True),
+                    ("indexer_score", indexer_score, (torch.int32, torch.uint32), info["T"], False)])
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().segmla_plan_build(plan, _ptr(workspace), nbytes, _ptr(indexer_score),
                                    _stream(stream)), "segmla_plan_build")
 
 
+def check_forward_tensors(info, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope=None,
+                          lse=None):
+    """Validate the tensors of one forward against a plan's shapes (segmla_plan_get_info)."""
+    import torch
+    io = _torch_dtypes(info["io_dtype"])
+    nq = info["q_end"] - info["q_begin"]
+    H, dn, dr, dv, ds = (info[k] for k in ("n_heads", "d_nope", "d_rope", "d_v", "d_state"))
+    n_pool = info["n_pool"]
+    specs = [("q", q, io, nq * H * (dn + dr), True)]
+    if info["kv_dtype"] == SEGMLA_E4M3_B128:
+        specs += [("kv", kv, _torch_dtypes(SEGMLA_E4M3_B128), n_pool * dn, True),
+                  ("kv_scale", kv_scale, (torch.float32,), n_pool * (dn // 128), True),
+                  ("kv_rope", kv_rope, (torch.bfloat16,), n_pool * dr, True)]
+    else:
+        specs += [("kv", kv, _torch_dtypes(info["kv_dtype"]), n_pool * (dn + dr), True)]
+    specs += [("w", w, io, H * ds * dv, True),
+              ("z_cached", z_cached, io, n_pool * info["zc_slots"] * ds, info["n_local"] > 0),
+              ("out", out, io, nq * H * dv, True),
+              ("z", z, io, nq * info["z_slots"] * ds, True),
+              ("lse", lse, (torch.float32,), nq * H, False)]
+    _check_tensors(specs)
+
+
 def segmla_forward(plan, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope=None, lse=None,
                    stream=None):
+    check_forward_tensors(segmla_plan_get_info(plan), q, kv, w, out, z, z_cached, kv_scale,
+                          kv_rope, lse)
     t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
                 _ptr(z), _ptr(lse))
     _check(lib().segmla_forward(plan, ctypes.byref(t), _stream(stream)), "segmla_forward")
@@ -236,8 +319,14 @@ def segmla_copy_geometry(plan, T, stream=None):
 
 def segmla_lse_merge(partial_o, partial_ml, out, lse=None, stream=None):
     """partial_o fp32 [n_split, n_vec, d], partial_ml fp32 [n_split, n_vec, 2] (device tensors)."""
-    n_split, n_vec, d = partial_o.shape
     import torch
+    if not torch.is_tensor(partial_o) or partial_o.dim() != 3:
+        raise ValueError("partial_o must be a [n_split, n_vec, d] tensor")
+    n_split, n_vec, d = partial_o.shape
+    _check_tensors([("partial_o", partial_o, (torch.float32,), n_split * n_vec * d, True),
+                    ("partial_ml", partial_ml, (torch.float32,), n_split * n_vec * 2, True),
+                    ("out", out, (torch.float32, torch.bfloat16), n_vec * d, True),
+                    ("lse", lse, (torch.float32,), n_vec, False)])
     dt = SEGMLA_F32 if out.dtype == torch.float32 else SEGMLA_BF16
     _check(lib().segmla_lse_merge(_ptr(partial_o), _ptr(partial_ml), n_split, n_vec, d, _ptr(out), dt,
                                   _ptr(lse), _stream(stream)), "segmla_lse_merge")

@@ -9,10 +9,19 @@ from oracle import segmla_oracle as O
 from segmented_attention_amd.segmla import Plan
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
+# Absolute error bound of the natural-log log-sum-exp (the statistic the split merge consumes).
+# The fp32 path carries no rounding beyond fp32; the bf16 path rounds the segment-rotated RoPE
+# query to bf16 (about 2^-9 |s_rope| per score) and the E4M3 path also rounds code x scale to
+# bf16 (about 2^-9 |s| per score): on the synthetic workloads |s| is a few units.
+LSE_TOL = {"f32": 1e-5, "bf16": 0.2, "e4m3": 0.6}
 
 
 def tol_of(cfg):
     return TOL["e4m3"] if cfg["kv_dtype"] == "e4m3" else TOL[cfg["dtype"]]
+
+
+def lse_tol_of(cfg):
+    return LSE_TOL["e4m3"] if cfg["kv_dtype"] == "e4m3" else LSE_TOL[cfg["dtype"]]
 
 
 def say(msg):
@@ -69,7 +78,8 @@ def run_gpu(inp, split_keys=0, with_lse=True, plan=None):
 
 
 def compare(cfg, ref, out, z, lse, zc_rows, rows=None):
-    """Assert parity of one forward against the oracle result `ref` (computed on `rows`)."""
+    """Assert parity of one forward against the oracle result `ref` (computed on `rows`).
+    Returns (max rel err of O, of Z, max abs err of lse or 0)."""
     tol = tol_of(cfg)
     rows = ref["rows"] if rows is None else rows
     o = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()
@@ -85,10 +95,10 @@ def compare(cfg, ref, out, z, lse, zc_rows, rows=None):
     # replaced, never added: copied rows are bit-equal to the cached state
     if (~comp).any():
         np.testing.assert_array_equal(zz[~comp], ref["Z"][~comp])
+    e_l = 0.0
     if lse is not None:
         ls = lse[torch.as_tensor(rows, device=lse.device)].double().cpu().numpy()
-        err = np.abs(ls[comp] - ref["lse"][comp])
-        lim = max(10 * tol, 1e-4) if cfg["dtype"] != "f32" else 1e-5
-        assert err.max() <= lim, "lse max abs err %.3g" % err.max()
+        e_l = float(np.abs(ls[comp] - ref["lse"][comp]).max())
+        assert e_l <= lse_tol_of(cfg), "lse max abs err %.3g > %.1g" % (e_l, lse_tol_of(cfg))
         assert np.all(np.isnan(ls[~comp]))
-    return float(e_o.max()), float(e_z.max())
+    return float(e_o.max()), float(e_z.max()), e_l

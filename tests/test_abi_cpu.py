@@ -154,6 +154,29 @@ def test_paged_pool_errors(L):
     assert _status(cfg, pages=pages, n_pool=last) == S.SEGMLA_E_GEOMETRY
 
 
+def test_paged_pool_smaller_than_one_page(L):
+    """A pool smaller than the rows a segment uses on its first page is rejected (the check
+    must not round a negative room up to page 0): one 50-row document on 64-row pages needs
+    pool rows 0..49, so n_pool = 32 or 49 is an error and 50 is enough."""
+    cfg = dict(SMALL_CONFIGS[1], segments=[("doc", 50)])
+    one = dict(page_rows=64, page_start=np.array([0], np.int64),
+               page_table=np.array([0], np.int64))
+    for n_pool, want in ((32, S.SEGMLA_E_GEOMETRY), (49, S.SEGMLA_E_GEOMETRY),
+                         (50, S.SEGMLA_OK), (64, S.SEGMLA_OK)):
+        got = _status(cfg, kinds=[1], lens=[50], offsets=[0], pool_rows=[0], n_pool=n_pool,
+                      pages=one, edge_rows=0, tail_rows=0, budget_permille=0)
+        assert got == want, (n_pool, got)
+    # the unpaged geometry gives the same verdicts
+    for n_pool, want in ((49, S.SEGMLA_E_GEOMETRY), (50, S.SEGMLA_OK)):
+        got = _status(cfg, kinds=[1], lens=[50], offsets=[0], pool_rows=[0], n_pool=n_pool,
+                      edge_rows=0, tail_rows=0, budget_permille=0)
+        assert got == want, (n_pool, got)
+    # a page index so large that page * rows overflows int64 is rejected, not wrapped
+    huge = dict(one, page_table=np.array([2**62], np.int64))
+    assert _status(cfg, kinds=[1], lens=[50], offsets=[0], pool_rows=[0], n_pool=64,
+                   pages=huge, edge_rows=0, tail_rows=0, budget_permille=0) == S.SEGMLA_E_GEOMETRY
+
+
 def test_group_heads_errors(L):
     """Grouped state: group_heads 0 or 1 is per head; G >= 2 must divide n_heads; negative is
     an error. A valid grouping changes neither T nor |A|."""
@@ -339,3 +362,52 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), os.path.join(dirpath, f)
+
+
+def test_binding_rejects_bad_tensors(L):
+    """The binding checks every tensor before the C call (the ABI sees raw addresses only):
+    host tensors, wrong dtypes, non-contiguous views and undersized buffers raise ValueError
+    with the tensor's name, and segmla_plan_get_info reports the shapes the checks use."""
+    import torch
+    cfg = SMALL_CONFIGS[1]                      # bf16 io, bf16 latent, 64 heads
+    p = _create(cfg)
+    try:
+        info = S.segmla_plan_get_info(p)
+        T = int(segment_table(cfg)[1].sum())
+        assert info["T"] == T and (info["q_begin"], info["q_end"]) == (0, T)
+        assert info["n_heads"] == 64 and info["n_global"] == 8 and info["n_local"] == 56
+        assert info["d_v"] == 576 and info["d_state"] == 512 and info["z_slots"] == 64
+        assert info["zc_slots"] == 56 and info["n_pool"] == T
+        assert info["workspace_bytes"] == S.segmla_plan_workspace_bytes(p)
+        bf = torch.bfloat16
+        good = dict(q=torch.zeros(T, 64, 576, dtype=bf), kv=torch.zeros(T, 576, dtype=bf),
+                    w=torch.zeros(64, 512, 576, dtype=bf), out=torch.zeros(T, 64, 576, dtype=bf),
+                    z=torch.zeros(T, 64, 512, dtype=bf), z_cached=torch.zeros(T, 56, 512, dtype=bf))
+
+        def err(**over):
+            args = dict(good)
+            args.update(over)
+            with pytest.raises(ValueError) as e:
+                S.segmla_forward(p, **args)
+            return str(e.value)
+        assert "q must be on the GPU" in err()        # every check passes but the device
+        assert "q has dtype" in err(q=good["q"].float())
+        assert "kv must be contiguous" in err(kv=torch.zeros(576, T, dtype=bf).t())
+        assert "out holds" in err(out=torch.zeros(T - 1, 64, 576, dtype=bf))
+        assert "z_cached is required" in err(z_cached=None)
+        assert "lse has dtype" in err(lse=torch.zeros(T, 64, dtype=bf))
+        assert "w must be a torch tensor" in err(w=np.zeros((64, 512, 576)))
+        with pytest.raises(ValueError, match="workspace must be on the GPU"):
+            S.segmla_plan_build(p, torch.zeros(info["workspace_bytes"], dtype=torch.uint8))
+        with pytest.raises(ValueError, match="workspace holds"):
+            S.segmla_plan_build(p, torch.zeros(16, dtype=torch.uint8))
+    finally:
+        S.segmla_plan_destroy(p)
+    # the standalone merge: fp16 output is not an accepted dtype (no silent bf16 reading)
+    po, pm = torch.zeros(2, 4, 8), torch.zeros(2, 4, 2)
+    with pytest.raises(ValueError, match="out has dtype"):
+        S.segmla_lse_merge(po, pm, torch.zeros(4, 8, dtype=torch.float16))
+    with pytest.raises(ValueError, match="partial_ml holds"):
+        S.segmla_lse_merge(po, torch.zeros(2, 4, 1), torch.zeros(4, 8))
+    with pytest.raises(ValueError, match="partial_o must be on the GPU"):
+        S.segmla_lse_merge(po, pm, torch.zeros(4, 8))

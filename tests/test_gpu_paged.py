@@ -88,7 +88,7 @@ def test_paged_parity_with_oracle(cfg, pool, split):
     np.testing.assert_array_equal(plan.protected(), ref["A"])
     plan.close()
     e = compare(cfg, ref, out, z, lse, None)
-    say("  max rel err O %.2e Z %.2e" % e)
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
 def test_paged_full_size_32k_sampled():
@@ -114,4 +114,5 @@ def test_paged_full_size_32k_sampled():
     ref = O.layer_forward(oi, rows=rows)
     plan.close()
     e = compare(cfg, ref, out, z, lse, None, rows=rows)
-    say("  %d sampled rows, max rel err O %.2e Z %.2e (tol %.0e)" % ((len(rows),) + e + (tol_of(cfg),)))
+    say("  %d sampled rows, max rel err O %.2e Z %.2e (tol %.0e), lse max abs err %.2e"
+        % (len(rows), e[0], e[1], tol_of(cfg), e[2]))

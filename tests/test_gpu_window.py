@@ -98,7 +98,7 @@ def test_window_parity_with_oracle(cfg, q0, q1):
     _check_pairs(plan, inp, ref["A"], q0, q1)
     plan.close()
     e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
-    say("  max rel err O %.2e Z %.2e" % e)
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
 @pytest.mark.parametrize("ci,where", [(1, "last_row"), (1, "last_4_rows"), (1, "doc_interior_row"),
@@ -123,7 +123,7 @@ def test_decode_windows(ci, where):
     _check_pairs(plan, inp, ref["A"], q0, q1)
     plan.close()
     e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
-    say("  max rel err O %.2e Z %.2e" % e)
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
 def test_misaligned_tensor_is_rejected():

@@ -515,3 +515,36 @@ def test_grouped_exact_cache_identity():
     ref = full["Z"].reshape(T, H // G, G, -1).sum(axis=2)
     assert len(grouped["A"]) < T
     np.testing.assert_allclose(grouped["Z"], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------ error metric
+def test_rel_err_rows_hand_values():
+    """The pass/fail metric of every parity check: per (row, head), the L2 norm of the error
+    over the channel axis divided by the L2 norm of the reference over the same axis (the
+    per-head output L2 norm of the stated tolerances, taken row by row). Hand-computed
+    values: a wrong axis, a denominator taken from x instead of ref, a missing square root
+    or a mean instead of a sum each change at least one of them."""
+    ref = np.array([[3.0, 4.0], [0.0, 5.0], [1.0, 0.0]])
+    # identical rows: zero error
+    np.testing.assert_array_equal(O.rel_err_rows(ref, ref), [0.0, 0.0, 0.0])
+    # row 0 off by (0, 0); row 1 x = 0 (error = the whole row, ratio 1); row 2 x = 3 ref
+    x = np.array([[3.0, 4.0], [0.0, 0.0], [3.0, 0.0]])
+    np.testing.assert_array_equal(O.rel_err_rows(x, ref), [0.0, 1.0, 2.0])
+    # denominator is ||ref||, not ||x||: x = 2 ref gives 1 (||x||-based would give 0.5)
+    np.testing.assert_array_equal(O.rel_err_rows(2 * ref, ref), [1.0, 1.0, 1.0])
+    # a known error vector per row: ||(0.3, 0.4)|| / ||(3, 4)|| = 0.5 / 5 = 0.1
+    got = O.rel_err_rows(ref + np.array([[0.3, 0.4], [1.2, 0.0], [0.0, 0.25]]), ref)
+    np.testing.assert_allclose(got, [0.1, 0.24, 0.25], rtol=0, atol=1e-15)
+    # three axes [rows, heads, channels]: one value per (row, head), reduced over the last
+    # axis only; the same numbers along the other two axes would give other values
+    ref3 = np.zeros((2, 3, 4))
+    ref3[..., 0] = 2.0                       # ||ref|| = 2 for every (row, head)
+    x3 = ref3.copy()
+    x3[1, 2, 3] = 1.0                        # one error of 1 in (row 1, head 2)
+    e3 = O.rel_err_rows(x3, ref3)
+    assert e3.shape == (2, 3)
+    expect = np.zeros((2, 3))
+    expect[1, 2] = 0.5
+    np.testing.assert_array_equal(e3, expect)
+    # a zero reference row with a nonzero x is an infinite relative error, never a pass
+    assert O.rel_err_rows(np.array([[1e-3, 0.0]]), np.array([[0.0, 0.0]]))[0] > 1e100
