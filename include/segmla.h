@@ -253,9 +253,9 @@ segmla_status segmla_plan_get_info(const segmla_plan *plan, segmla_plan_info *in
  * the protected set A and the ordered work list. indexer_score: device uint32 [T],
  * required iff the budget needs Indexer rows, else may be NULL. The workspace must
  * stay allocated and unmodified while the plan is used. It also holds forward scratch
- * (key-range split partials; with bf16 io, a copy of W in the projection's operand
- * order, H * d_state * d_v * 2 bytes), so forwards of one plan must not overlap: run them
- * in order on one stream. */
+ * (key-range split partials; with bf16 io and a window of more than 8 rows, a copy of W in
+ * the projection's operand order, H * d_state * d_v * 2 bytes), so forwards of one plan must
+ * not overlap: run them in order on one stream. */
 segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t workspace_bytes,
                                 const uint32_t *indexer_score, void *stream);
 

@@ -111,9 +111,9 @@ struct AttnArgs {
 };
 
 // Launchers (defined in the kernel sources), all on `stream`.
-hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, double base,
-                           int32_t* seg_of_row, float2* segcs, float2* stepcs, float2* rowcs,
-                           hipStream_t stream);
+hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int q0, int q1, int d_rope,
+                           double base, int32_t* seg_of_row, float2* segcs, float2* stepcs,
+                           float2* rowcs, hipStream_t stream);
 hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_t* seg_of_row, int T,
                           int edge_rows, int tail_rows, const int32_t* dirty, int n_dirty,
                           const uint32_t* score, int64_t need, uint8_t* flags,
@@ -126,13 +126,22 @@ hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t strea
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
                             int d, void* out, int out_dtype, float* lse, hipStream_t stream);
 
+// Matrix-vector projection of small bf16 windows (decode): windows of at most kThinRows rows
+// with d_v a multiple of 64, at most kThinMaxDv, and d_state a multiple of kThinCols.
+constexpr int kThinRows = 8;
+constexpr int kThinCols = 64;
+constexpr int kThinMaxDv = 576;
+__host__ __device__ inline bool thin_projection(int nq, int d_v, int d_state) {
+  return nq <= kThinRows && d_v % 64 == 0 && d_v <= kThinMaxDv && d_state % kThinCols == 0;
+}
+
 struct EpiArgs {
   const void* out;        // [nq][H][d_v] merged head outputs (row t at t - q0)
   const void* w;          // [H][d_state][d_v]
   void* wt;               // W in the projection's MFMA operand order (bf16; see k_w_tile)
   const void* z_cached;   // [n_pool][HL][d_state]
   void* z;                // [nq][H][d_state] (row t at t - q0)
-  const float2* rowcs;    // [T][d_rope/2]
+  const float2* rowcs;    // [nq][d_rope/2] cos/sin(t theta_k) of window row t at t - q0
   const int32_t* alist;
   const int32_t* nalist;
   const int32_t* rng;     // device {a_lo, a_hi, na_lo, na_hi} (see TileMap)
@@ -149,6 +158,7 @@ struct EpiArgs {
   // window [q0, q0 + nq); nA, nNA: the largest number of its rows inside / outside A (grid
   // sizes; the actual numbers are in rng)
   int32_t q0, nq, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;
+  int32_t thin;  // bf16: the matrix-vector projection (else operand-ordered W copy + MFMA tiles)
 };
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
 

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void k_project_f32(EpiArgs e) {
     if (e.v_has_rope) {
       const int half_r = e.d_rope / 2;
       for (int k = lane; k < half_r; k += 64) {  // u^r <- R(-t) O^r
-        float2 cs = e.rowcs[(int64_t)t * half_r + k];
+        float2 cs = e.rowcs[(int64_t)(t - e.q0) * half_r + k];
         float x = o[e.d_nope + 2 * k], y = o[e.d_nope + 2 * k + 1];
         u[e.d_nope + 2 * k] = x * cs.x + y * cs.y;
         u[e.d_nope + 2 * k + 1] = -x * cs.y + y * cs.x;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
         __bf16 y[8];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float2 cs = e.rowcs[(int64_t)t * half_r + 4 * c + k];
+          const float2 cs = e.rowcs[(int64_t)(t - e.q0) * half_r + 4 * c + k];
           const float a0 = (float)(x[2 * k]), a1 = (float)(x[2 * k + 1]);
           y[2 * k] = (__bf16)(a0 * cs.x + a1 * cs.y);
           y[2 * k + 1] = (__bf16)(-a0 * cs.y + a1 * cs.x);
@@ -372,9 +372,6 @@ __global__ __launch_bounds__(256, 1) void k_project_bf16(EpiArgs e) {
 // column's W row (each team step reads 128 contiguous bytes) and the team's partial sums meet
 // by lane shuffles. The u rows sit in LDS as fp32 holding the values the tile path
 // multiplies (nope features as given, RoPE pairs de-rotated by R(-t) and rounded to bf16).
-constexpr int kThinRows = 8;
-constexpr int kThinCols = 64;
-constexpr int kThinMaxDv = 576;
 constexpr int kThinMaxK = kThinMaxDv / 64;  // 16-byte chunks per lane and column
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -410,7 +407,7 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
         const __bf16* o = outp + ((int64_t)(t - e.q0) * e.H + h) * d_v + 2 * k2;
         float a0 = (float)o[0], a1 = (float)o[1];
         if (k2 >= nope_pairs) {  // v carries the RoPE part (d_v > d_nope)
-          const float2 cs = e.rowcs[(int64_t)t * half_r + (k2 - nope_pairs)];
+          const float2 cs = e.rowcs[(int64_t)(t - e.q0) * half_r + (k2 - nope_pairs)];
           const float y0 = (float)(__bf16)(a0 * cs.x + a1 * cs.y);
           const float y1 = (float)(__bf16)(-a0 * cs.y + a1 * cs.x);
           a0 = y0;
@@ -553,8 +550,7 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
       return hipSuccess;
     }();
     if (attr != hipSuccess) return attr;
-    const bool thin = e.nq <= kThinRows && e.d_v % 64 == 0 && e.d_v <= kThinMaxDv &&
-                      e.d_state % kThinCols == 0;
+    const bool thin = e.thin != 0;  // decided by the plan (it sizes the W copy only without)
     if (blocks > 0 && thin && e.zpart) {  // grouped: per-head projections, then group sums
       const int64_t tiles = (int64_t)e.HG * ((e.nq + kThinRows - 1) / kThinRows) +
                             (int64_t)e.HL * ((e.nA + kThinRows - 1) / kThinRows);

@@ -11,18 +11,21 @@ __device__ __forceinline__ double rope_theta(double base, int k, int d_rope) {
   return pow(base, -2.0 * (double)k / (double)d_rope);
 }
 
-// Per-row segment map and the inverse-output-RoPE table cos/sin(t * theta_k).
-__global__ void k_geom_rows(const SegDesc* __restrict__ seg, int n_seg, int T, int d_rope,
-                            double base, int32_t* __restrict__ seg_of_row,
+// Per-row segment map (every request row) and the inverse-output-RoPE table
+// cos/sin(t * theta_k) of the computed window's rows t in [q0, q1) (at t - q0).
+__global__ void k_geom_rows(const SegDesc* __restrict__ seg, int n_seg, int T, int q0, int q1,
+                            int d_rope, double base, int32_t* __restrict__ seg_of_row,
                             float2* __restrict__ rowcs) {
   const int half = d_rope / 2;
   int64_t n = (int64_t)T * half;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     int t = (int)(i / half), k = (int)(i - (int64_t)t * half);
-    double s, c;
-    sincos((double)t * rope_theta(base, k, d_rope), &s, &c);
-    rowcs[i] = make_float2((float)c, (float)s);
+    if (t >= q0 && t < q1) {
+      double s, c;
+      sincos((double)t * rope_theta(base, k, d_rope), &s, &c);
+      rowcs[(int64_t)(t - q0) * half + k] = make_float2((float)c, (float)s);
+    }
     if (k == 0) seg_of_row[t] = seg_of(seg, n_seg, t);
   }
 }
@@ -46,14 +49,14 @@ __global__ void k_geom_segs(const SegDesc* __restrict__ seg, int n_seg, int d_ro
   }
 }
 
-hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int d_rope, double base,
-                           int32_t* seg_of_row, float2* segcs, float2* stepcs, float2* rowcs,
-                           hipStream_t stream) {
+hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int q0, int q1, int d_rope,
+                           double base, int32_t* seg_of_row, float2* segcs, float2* stepcs,
+                           float2* rowcs, hipStream_t stream) {
   int64_t n = (int64_t)T * (d_rope / 2);
   int blocks = (int)((n + 255) / 256);
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(k_geom_rows, dim3(blocks), dim3(256), 0, stream, seg, n_seg, T, d_rope, base,
-                     seg_of_row, rowcs);
+  hipLaunchKernelGGL(k_geom_rows, dim3(blocks), dim3(256), 0, stream, seg, n_seg, T, q0, q1,
+                     d_rope, base, seg_of_row, rowcs);
   int ns = n_seg * (d_rope / 2);
   hipLaunchKernelGGL(k_geom_segs, dim3((ns + 255) / 256), dim3(256), 0, stream, seg, n_seg,
                      d_rope, base, segcs, stepcs);

@@ -38,6 +38,7 @@ struct segmla_plan {
   // work decomposition
   int32_t nF = 0, nG = 0, n_split = 1, split_keys = 0, n_blk = 0;
   int32_t n_cu = 256;  // compute units of the device the plan was sized for
+  bool thin = false;   // bf16 projection as matrix-vector products (small windows)
   // workspace layout (byte offsets, 256-aligned)
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
@@ -368,7 +369,7 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_lseg = take(sizeof(SegDesc) * p->n_seg);
   p->o_segcs = take(sizeof(float2) * half * p->n_run);
   p->o_stepcs = take(sizeof(float2) * half * p->n_run);
-  p->o_rowcs = take(sizeof(float2) * half * (size_t)T);
+  p->o_rowcs = take(sizeof(float2) * half * (size_t)(p->q1 - p->q0));  // window rows only
   p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
   p->o_flags = take((size_t)T);
   p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
@@ -388,10 +389,13 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
     p->o_part_o = take(sizeof(float) * (size_t)p->n_split * nvec * p->d_v);
     p->o_part_ml = take(sizeof(float) * 2 * (size_t)p->n_split * nvec);
   }
+  // bf16 projection: matrix-vector for small windows, else MFMA tiles reading W in their
+  // operand order from a per-forward copy (forward scratch)
+  p->thin = p->io_dtype == SEGMLA_BF16 && thin_projection(p->q1 - p->q0, p->d_v, p->d_state);
   // grouped state in a small window (decode): per-head fp32 projections, summed per group
-  if (p->io_dtype == SEGMLA_BF16 && p->G >= 2 && (int64_t)p->q1 - p->q0 <= 8)
+  if (p->thin && p->G >= 2)
     p->o_zpart = take(sizeof(float) * (size_t)(p->q1 - p->q0) * p->H * p->d_state);
-  if (p->io_dtype == SEGMLA_BF16)  // forward scratch: W in the projection's operand order
+  if (p->io_dtype == SEGMLA_BF16 && !p->thin)
     p->o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
   p->ws_bytes = o;
   *out_plan = p;
@@ -472,8 +476,8 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
   up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
      sizeof(int32_t) * p->grp_ghead.size());
   if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->d_rope, p->rope_base,
-                      p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
+  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->q0, p->q1, p->d_rope,
+                      p->rope_base, p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
                       p->at<float2>(p->o_stepcs), p->at<float2>(p->o_rowcs), s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
   e = launch_protect(p->at<SegDesc>(p->o_lseg), p->at<SegDesc>(p->o_seg), p->at<int32_t>(p->o_seg_of_row), p->T,
@@ -541,7 +545,8 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   EpiArgs ep;
   ep.out = t->out;
   ep.w = t->w;
-  ep.wt = p->io_dtype == SEGMLA_BF16 ? p->at<void>(p->o_wt) : nullptr;
+  ep.wt = (p->io_dtype == SEGMLA_BF16 && !p->thin) ? p->at<void>(p->o_wt) : nullptr;
+  ep.thin = p->thin ? 1 : 0;
   ep.z_cached = t->z_cached;
   ep.z = t->z;
   ep.rowcs = p->at<float2>(p->o_rowcs);
@@ -568,7 +573,7 @@ segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void
   ep.n_groups = p->n_groups;
   ep.grp_gstart = p->at<int32_t>(p->o_grp);
   ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
-  ep.zpart = p->o_zpart ? p->at<float>(p->o_zpart) : nullptr;
+  ep.zpart = (p->thin && p->G >= 2) ? p->at<float>(p->o_zpart) : nullptr;
   e = launch_epilogue(ep, p->io_dtype, s);
   if (e == hipSuccess && p->prof) {
     e = hipEventRecord(p->ev[3], s);
