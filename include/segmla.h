@@ -263,6 +263,23 @@ segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t works
  * epilogue) on a built plan. A plan may run many forwards with new tensors. */
 segmla_status segmla_forward(const segmla_plan *plan, const segmla_tensors *t, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): segmla_plan_build followed by
+ * segmla_forward in one call, with the plan's workspace in a device array that the library
+ * itself holds, SEGMLA_NOALLOC_MAX_BYTES per GPU, instead of caller memory. The caller
+ * passes only the Indexer scores (as for segmla_plan_build) and the forward's tensors (as for
+ * segmla_forward). Nothing is allocated: the array is part of the library's device code and
+ * each GPU keeps its copy from the first call there until the process ends. A plan whose
+ * workspace (segmla_plan_workspace_bytes) exceeds SEGMLA_NOALLOC_MAX_BYTES returns
+ * SEGMLA_E_WORKSPACE before anything is enqueued. Every call on one GPU uses that GPU's one
+ * array, which keeps the last call's contents: calls that overlap on one GPU (on different
+ * streams or from several host threads) race and must be ordered by the caller, e.g. on one
+ * stream. The plan itself is left as it was: a plan built with segmla_plan_build keeps its own
+ * workspace, and an unbuilt plan stays unbuilt. No event profiling is recorded. */
+#define SEGMLA_NOALLOC_MAX_BYTES (96ull << 20)
+segmla_status segmla_forward_noalloc(segmla_plan *plan, const uint32_t *indexer_score,
+                                     const segmla_tensors *t, void *stream);
+
 /* Copy A (sorted ascending, |A| rows) to host memory; synchronizes `stream`. */
 segmla_status segmla_copy_protected(const segmla_plan *plan, int32_t *host_rows, int64_t cap,
                                     void *stream);

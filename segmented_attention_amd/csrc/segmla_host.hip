@@ -3,6 +3,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -158,6 +159,180 @@ segmla_status check_geometry(const segmla_geometry* G, const segmla_pages* P, in
   }
   *T_out = pos;
   return SEGMLA_OK;
+}
+
+TileMap tile_map(const segmla_plan* p) {
+  TileMap m;
+  m.alist = p->at<int32_t>(p->o_alist);
+  m.nalist = p->at<int32_t>(p->o_nalist);
+  m.ghead = p->at<int32_t>(p->o_ghead);
+  m.rng = p->at<int32_t>(p->o_rng);
+  m.H = p->H;
+  m.HG = p->HG;
+  m.nF = p->nF;
+  m.nG = p->nG;
+  return m;
+}
+
+// Enqueue the plan build into workspace `ws` (validated by the caller) on stream s.
+segmla_status build_impl(segmla_plan* p, char* ws, const uint32_t* indexer_score, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (p->prof) {
+    if (flush_profile(p) != hipSuccess || hipEventRecord(p->ev[4], s) != hipSuccess) return SEGMLA_E_HIP;
+  }
+  p->ws = ws;
+  p->built = false;
+  auto up = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
+  };
+  up(p->o_seg, p->runs.data(), sizeof(SegDesc) * p->runs.size());
+  up(p->o_lseg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
+  up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
+  up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
+  up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
+  up(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
+  up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
+     sizeof(int32_t) * p->grp_ghead.size());
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->q0, p->q1, p->d_rope,
+                      p->rope_base, p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
+                      p->at<float2>(p->o_stepcs), p->at<float2>(p->o_rowcs), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_protect(p->at<SegDesc>(p->o_lseg), p->at<SegDesc>(p->o_seg), p->at<int32_t>(p->o_seg_of_row), p->T,
+                     p->edge_rows, p->tail_rows, p->at<int32_t>(p->o_dirty), (int)p->dirty.size(),
+                     indexer_score, p->need, p->at<uint8_t>(p->o_flags), p->at<uint32_t>(p->o_sel),
+                     p->at<int32_t>(p->o_blk_count), p->at<uint64_t>(p->o_blk_sum), p->n_blk,
+                     p->at<int32_t>(p->o_alist), p->at<int32_t>(p->o_nalist), (int)p->nA,
+                     p->at<uint64_t>(p->o_sum_a), p->q0, p->q1, p->at<int32_t>(p->o_rng), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  if (p->prof) {
+    if (hipEventRecord(p->ev[5], s) != hipSuccess) return SEGMLA_E_HIP;
+    p->build_pending = true;
+  }
+  p->built = true;
+  return SEGMLA_OK;
+}
+
+// Tensor checks of one forward (host only).
+segmla_status check_tensors(const segmla_plan* p, const segmla_tensors* t) {
+  if (!t->q || !t->kv || !t->w || !t->out || !t->z) return SEGMLA_E_NULL;
+  if (p->HL > 0 && !t->z_cached) return SEGMLA_E_NULL;
+  if (p->kv_dtype == SEGMLA_E4M3_B128 && (!t->kv_scale || !t->kv_rope)) return SEGMLA_E_NULL;
+  for (const void* ptr : {t->q, t->kv, (const void*)t->kv_scale, t->kv_rope, t->w, t->z_cached,
+                          (const void*)t->out, (const void*)t->z, (const void*)t->lse})
+    if ((uintptr_t)ptr % 16 != 0) return SEGMLA_E_SHAPE;
+  return SEGMLA_OK;
+}
+
+// Enqueue one forward of a built plan (tensors checked by the caller) on stream s.
+segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStream_t s) {
+  AttnArgs a;
+  a.q = t->q;
+  a.kv = t->kv;
+  a.kv_scale = t->kv_scale;
+  a.kv_rope = t->kv_rope;
+  a.out = t->out;
+  a.lse = t->lse;
+  a.part_o = p->n_split > 1 ? p->at<float>(p->o_part_o) : nullptr;
+  a.part_ml = p->n_split > 1 ? p->at<float>(p->o_part_ml) : nullptr;
+  a.seg = p->at<SegDesc>(p->o_seg);
+  a.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
+  a.segcs = p->at<float2>(p->o_segcs);
+  a.stepcs = p->at<float2>(p->o_stepcs);
+  a.work = p->at<int32_t>(p->o_work);
+  a.map = tile_map(p);
+  a.n_seg = p->n_run;
+  a.T = p->T;
+  a.d_nope = p->d_nope;
+  a.d_rope = p->d_rope;
+  a.d_v = p->d_v;
+  a.q0 = p->q0;
+  a.n_split = p->n_split;
+  a.split_keys = p->split_keys;
+  a.sigma = p->sigma;
+  hipError_t e = hipSuccess;
+  segmla_plan* pm = const_cast<segmla_plan*>(p);  // profiling state only
+  if (p->prof) {
+    if (flush_profile(pm) != hipSuccess || hipEventRecord(p->ev[0], s) != hipSuccess)
+      return SEGMLA_E_HIP;
+  }
+  if (p->nF + p->nG > 0) e = launch_attn(a, p->kv_dtype, p->v_has_rope, s);
+  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
+  if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1) e = launch_merge_tiles(a, p->io_dtype, s);
+  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[2], s);
+  if (e != hipSuccess) return SEGMLA_E_HIP;
+  EpiArgs ep;
+  ep.out = t->out;
+  ep.w = t->w;
+  ep.wt = (p->io_dtype == SEGMLA_BF16 && !p->thin) ? p->at<void>(p->o_wt) : nullptr;
+  ep.thin = p->thin ? 1 : 0;
+  ep.z_cached = t->z_cached;
+  ep.z = t->z;
+  ep.rowcs = p->at<float2>(p->o_rowcs);
+  ep.alist = p->at<int32_t>(p->o_alist);
+  ep.nalist = p->at<int32_t>(p->o_nalist);
+  ep.rng = p->at<int32_t>(p->o_rng);
+  ep.ghead = p->at<int32_t>(p->o_ghead);
+  ep.lhead = p->at<int32_t>(p->o_lhead);
+  ep.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
+  ep.seg = p->at<SegDesc>(p->o_seg);
+  ep.q0 = p->q0;
+  ep.nq = p->q1 - p->q0;
+  ep.H = p->H;
+  ep.HG = p->HG;
+  ep.HL = p->HL;
+  ep.nA = (int32_t)p->nA_w;
+  ep.nNA = (int32_t)p->nNA_w;
+  ep.d_nope = p->d_nope;
+  ep.d_rope = p->d_rope;
+  ep.d_v = p->d_v;
+  ep.d_state = p->d_state;
+  ep.v_has_rope = p->v_has_rope;
+  ep.G = p->G;
+  ep.n_groups = p->n_groups;
+  ep.grp_gstart = p->at<int32_t>(p->o_grp);
+  ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
+  ep.zpart = (p->thin && p->G >= 2) ? p->at<float>(p->o_zpart) : nullptr;
+  e = launch_epilogue(ep, p->io_dtype, s);
+  if (e == hipSuccess && p->prof) {
+    e = hipEventRecord(p->ev[3], s);
+    pm->fwd_pending = e == hipSuccess;
+  }
+  return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ forward without allocation
+// The plan's workspace in a device array of the library's own. Each GPU the library runs on
+// holds its copy from the first call there until the process ends; the address of a device's
+// copy is taken once, with that device current, and kept per device. Host code uses only these
+// addresses: the array's name stands for a host-side shadow, not for device memory.
+static __device__ __align__(256) char scratch[SEGMLA_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -438,18 +613,6 @@ segmla_status segmla_plan_get_info(const segmla_plan* p, segmla_plan_info* info)
   return SEGMLA_OK;
 }
 
-static TileMap tile_map(const segmla_plan* p) {
-  TileMap m;
-  m.alist = p->at<int32_t>(p->o_alist);
-  m.nalist = p->at<int32_t>(p->o_nalist);
-  m.ghead = p->at<int32_t>(p->o_ghead);
-  m.rng = p->at<int32_t>(p->o_rng);
-  m.H = p->H;
-  m.HG = p->HG;
-  m.nF = p->nF;
-  m.nG = p->nG;
-  return m;
-}
 
 segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspace_bytes,
                                 const uint32_t* indexer_score, void* stream) {
@@ -457,129 +620,38 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
   if (workspace_bytes < p->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return SEGMLA_E_WORKSPACE;
   if (p->need > 0 && !indexer_score) return SEGMLA_E_PROTECT;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  if (p->prof) {
-    if (flush_profile(p) != hipSuccess || hipEventRecord(p->ev[4], s) != hipSuccess) return SEGMLA_E_HIP;
-  }
-  p->ws = (char*)workspace;
-  p->built = false;
-  auto up = [&](size_t off, const void* src, size_t bytes) {
-    if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
-  };
-  up(p->o_seg, p->runs.data(), sizeof(SegDesc) * p->runs.size());
-  up(p->o_lseg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
-  up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
-  up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
-  up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
-  up(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
-  up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
-     sizeof(int32_t) * p->grp_ghead.size());
-  if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->q0, p->q1, p->d_rope,
-                      p->rope_base, p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
-                      p->at<float2>(p->o_stepcs), p->at<float2>(p->o_rowcs), s);
-  if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_protect(p->at<SegDesc>(p->o_lseg), p->at<SegDesc>(p->o_seg), p->at<int32_t>(p->o_seg_of_row), p->T,
-                     p->edge_rows, p->tail_rows, p->at<int32_t>(p->o_dirty), (int)p->dirty.size(),
-                     indexer_score, p->need, p->at<uint8_t>(p->o_flags), p->at<uint32_t>(p->o_sel),
-                     p->at<int32_t>(p->o_blk_count), p->at<uint64_t>(p->o_blk_sum), p->n_blk,
-                     p->at<int32_t>(p->o_alist), p->at<int32_t>(p->o_nalist), (int)p->nA,
-                     p->at<uint64_t>(p->o_sum_a), p->q0, p->q1, p->at<int32_t>(p->o_rng), s);
-  if (e != hipSuccess) return SEGMLA_E_HIP;
-  e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
-  if (e != hipSuccess) return SEGMLA_E_HIP;
-  if (p->prof) {
-    if (hipEventRecord(p->ev[5], s) != hipSuccess) return SEGMLA_E_HIP;
-    p->build_pending = true;
-  }
-  p->built = true;
-  return SEGMLA_OK;
+  return build_impl(p, (char*)workspace, indexer_score, (hipStream_t)stream);
 }
 
 segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void* stream) {
   if (!p || !t) return SEGMLA_E_NULL;
   if (!p->built) return SEGMLA_E_STATE;
-  if (!t->q || !t->kv || !t->w || !t->out || !t->z) return SEGMLA_E_NULL;
-  if (p->HL > 0 && !t->z_cached) return SEGMLA_E_NULL;
-  if (p->kv_dtype == SEGMLA_E4M3_B128 && (!t->kv_scale || !t->kv_rope)) return SEGMLA_E_NULL;
-  for (const void* ptr : {t->q, t->kv, (const void*)t->kv_scale, t->kv_rope, t->w, t->z_cached,
-                          (const void*)t->out, (const void*)t->z, (const void*)t->lse})
-    if ((uintptr_t)ptr % 16 != 0) return SEGMLA_E_SHAPE;
-  hipStream_t s = (hipStream_t)stream;
-  AttnArgs a;
-  a.q = t->q;
-  a.kv = t->kv;
-  a.kv_scale = t->kv_scale;
-  a.kv_rope = t->kv_rope;
-  a.out = t->out;
-  a.lse = t->lse;
-  a.part_o = p->n_split > 1 ? p->at<float>(p->o_part_o) : nullptr;
-  a.part_ml = p->n_split > 1 ? p->at<float>(p->o_part_ml) : nullptr;
-  a.seg = p->at<SegDesc>(p->o_seg);
-  a.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
-  a.segcs = p->at<float2>(p->o_segcs);
-  a.stepcs = p->at<float2>(p->o_stepcs);
-  a.work = p->at<int32_t>(p->o_work);
-  a.map = tile_map(p);
-  a.n_seg = p->n_run;
-  a.T = p->T;
-  a.d_nope = p->d_nope;
-  a.d_rope = p->d_rope;
-  a.d_v = p->d_v;
-  a.q0 = p->q0;
-  a.n_split = p->n_split;
-  a.split_keys = p->split_keys;
-  a.sigma = p->sigma;
-  hipError_t e = hipSuccess;
-  segmla_plan* pm = const_cast<segmla_plan*>(p);  // profiling state only
-  if (p->prof) {
-    if (flush_profile(pm) != hipSuccess || hipEventRecord(p->ev[0], s) != hipSuccess)
-      return SEGMLA_E_HIP;
-  }
-  if (p->nF + p->nG > 0) e = launch_attn(a, p->kv_dtype, p->v_has_rope, s);
-  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
-  if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1) e = launch_merge_tiles(a, p->io_dtype, s);
-  if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[2], s);
-  if (e != hipSuccess) return SEGMLA_E_HIP;
-  EpiArgs ep;
-  ep.out = t->out;
-  ep.w = t->w;
-  ep.wt = (p->io_dtype == SEGMLA_BF16 && !p->thin) ? p->at<void>(p->o_wt) : nullptr;
-  ep.thin = p->thin ? 1 : 0;
-  ep.z_cached = t->z_cached;
-  ep.z = t->z;
-  ep.rowcs = p->at<float2>(p->o_rowcs);
-  ep.alist = p->at<int32_t>(p->o_alist);
-  ep.nalist = p->at<int32_t>(p->o_nalist);
-  ep.rng = p->at<int32_t>(p->o_rng);
-  ep.ghead = p->at<int32_t>(p->o_ghead);
-  ep.lhead = p->at<int32_t>(p->o_lhead);
-  ep.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
-  ep.seg = p->at<SegDesc>(p->o_seg);
-  ep.q0 = p->q0;
-  ep.nq = p->q1 - p->q0;
-  ep.H = p->H;
-  ep.HG = p->HG;
-  ep.HL = p->HL;
-  ep.nA = (int32_t)p->nA_w;
-  ep.nNA = (int32_t)p->nNA_w;
-  ep.d_nope = p->d_nope;
-  ep.d_rope = p->d_rope;
-  ep.d_v = p->d_v;
-  ep.d_state = p->d_state;
-  ep.v_has_rope = p->v_has_rope;
-  ep.G = p->G;
-  ep.n_groups = p->n_groups;
-  ep.grp_gstart = p->at<int32_t>(p->o_grp);
-  ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
-  ep.zpart = (p->thin && p->G >= 2) ? p->at<float>(p->o_zpart) : nullptr;
-  e = launch_epilogue(ep, p->io_dtype, s);
-  if (e == hipSuccess && p->prof) {
-    e = hipEventRecord(p->ev[3], s);
-    pm->fwd_pending = e == hipSuccess;
-  }
-  return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+  const segmla_status st = check_tensors(p, t);
+  if (st != SEGMLA_OK) return st;
+  return forward_impl(p, t, (hipStream_t)stream);
+}
+
+segmla_status segmla_forward_noalloc(segmla_plan* p, const uint32_t* indexer_score,
+                                     const segmla_tensors* t, void* stream) {
+  if (!p || !t) return SEGMLA_E_NULL;
+  if (p->ws_bytes > (size_t)SEGMLA_NOALLOC_MAX_BYTES) return SEGMLA_E_WORKSPACE;
+  if (p->need > 0 && !indexer_score) return SEGMLA_E_PROTECT;
+  segmla_status st = check_tensors(p, t);
+  if (st != SEGMLA_OK) return st;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return SEGMLA_E_HIP;
+  // build and run into the shared array; the plan's own workspace state (if it was built with
+  // segmla_plan_build) and its profiling are left as they were
+  char* const own_ws = p->ws;
+  const bool own_built = p->built, own_prof = p->prof;
+  p->prof = false;
+  const hipStream_t s = (hipStream_t)stream;
+  st = build_impl(p, (char*)ws, indexer_score, s);
+  if (st == SEGMLA_OK) st = forward_impl(p, t, s);
+  p->ws = own_ws;
+  p->built = own_built;
+  p->prof = own_prof;
+  return st;
 }
 
 segmla_status segmla_profile_enable(segmla_plan* p, int32_t enable) {

@@ -26,7 +26,10 @@ EXPORTED = [
     "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
     "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
     "segmla_plan_create_range", "segmla_plan_create_paged", "segmla_plan_get_info",
+    "segmla_forward_noalloc",
 ]
+
+NOALLOC_MAX_BYTES = 96 << 20  # SEGMLA_NOALLOC_MAX_BYTES
 
 
 class SegmlaError(RuntimeError):
@@ -105,6 +108,7 @@ def lib():
             "segmla_plan_get_info": (i32, [P, ctypes.POINTER(PlanInfo)]),
             "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
             "segmla_forward": (i32, [P, ctypes.POINTER(Tensors), P]),
+            "segmla_forward_noalloc": (i32, [P, P, ctypes.POINTER(Tensors), P]),
             "segmla_copy_protected": (i32, [P, ctypes.POINTER(i32), i64, P]),
             "segmla_copy_geometry": (i32, [P, ctypes.POINTER(i32), ctypes.POINTER(i64), i64, P]),
             "segmla_lse_merge": (i32, [P, P, i32, i64, i32, P, i32, P, P]),
@@ -299,6 +303,20 @@ def segmla_forward(plan, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope
     t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
                 _ptr(z), _ptr(lse))
     _check(lib().segmla_forward(plan, ctypes.byref(t), _stream(stream)), "segmla_forward")
+
+
+def segmla_forward_noalloc(plan, indexer_score, q, kv, w, out, z, z_cached=None, kv_scale=None,
+                           kv_rope=None, lse=None, stream=None):
+    """Plan build + forward with the workspace in the library's own device array (no device
+    memory allocated anywhere in the call)."""
+    import torch
+    info = segmla_plan_get_info(plan)
+    _check_tensors([("indexer_score", indexer_score, (torch.int32, torch.uint32), info["T"], False)])
+    check_forward_tensors(info, q, kv, w, out, z, z_cached, kv_scale, kv_rope, lse)
+    t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
+                _ptr(z), _ptr(lse))
+    _check(lib().segmla_forward_noalloc(plan, _ptr(indexer_score), ctypes.byref(t), _stream(stream)),
+           "segmla_forward_noalloc")
 
 
 def segmla_copy_protected(plan, n_protected, stream=None):

@@ -411,3 +411,30 @@ def test_binding_rejects_bad_tensors(L):
         S.segmla_lse_merge(po, torch.zeros(2, 4, 1), torch.zeros(4, 8))
     with pytest.raises(ValueError, match="partial_o must be on the GPU"):
         S.segmla_lse_merge(po, pm, torch.zeros(4, 8))
+
+
+def test_noalloc_rejects_oversized_workspace(L):
+    """segmla_forward_noalloc refuses a plan whose workspace exceeds the library's array before
+    anything is enqueued or any tensor is touched (the addresses here are never dereferenced);
+    a plan that fits passes the size check and reaches the tensor checks."""
+    cfg = SMALL_CONFIGS[1]
+    big = _create(cfg, split_keys=64)  # 15 key splits: the partials alone take ~600 MB
+    small = _create(CONFIGS[1])        # the 32K layer: its budget needs 999 Indexer rows
+    try:
+        assert S.segmla_plan_workspace_bytes(big) > S.NOALLOC_MAX_BYTES
+        assert S.segmla_plan_workspace_bytes(small) <= S.NOALLOC_MAX_BYTES
+        t = S.Tensors(*([16] * 9))
+        score = ctypes.c_void_p(16)
+        assert L.segmla_forward_noalloc(big, score, ctypes.byref(t), None) == S.SEGMLA_E_WORKSPACE
+        assert L.segmla_forward_noalloc(big, None, ctypes.byref(t), None) == S.SEGMLA_E_WORKSPACE
+        assert L.segmla_forward_noalloc(small, None, ctypes.byref(t), None) == S.SEGMLA_E_PROTECT
+        t_bad = S.Tensors(*([16] * 6 + [24, 16, 16]))  # out off a 16-byte boundary
+        assert L.segmla_forward_noalloc(small, score, ctypes.byref(t_bad), None) == S.SEGMLA_E_SHAPE
+        assert L.segmla_forward_noalloc(None, score, ctypes.byref(t), None) == S.SEGMLA_E_NULL
+        # every check passed: without a visible GPU the device step fails, and says so
+        import torch
+        if not torch.cuda.is_available():
+            assert L.segmla_forward_noalloc(small, score, ctypes.byref(t), None) == S.SEGMLA_E_HIP
+    finally:
+        S.segmla_plan_destroy(big)
+        S.segmla_plan_destroy(small)
