@@ -8,8 +8,10 @@ row-replacement epilogue). The default workload is the Flash-like 32K layer
 prefix, 128 question rows, 10 % Local budget); the 128K layer is measured as a
 secondary figure, its 8 Global heads alone (every row, the part the throughput target is
 stated on) as the "target" figure, the Pro-like 64K layer with the E4M3 latent as the
-"fp8" figure, and the layer of 256 short documents (a 256-way merge per question row) as the
-"many_short" figure. A row-window plan of the 128K layer's last row (decode: one new row against
+"fp8" figure, the layer of 256 short documents (a 256-way merge per question row) as the
+"many_short" figure, and the 32K request with sink + window heads (56 heads with 4 sink tokens
+and a 256-token window beside 8 Global heads; and every head a 128-token window, the SWA
+layer) as the "window_heads" figures. A row-window plan of the 128K layer's last row (decode: one new row against
 131,584 keys) is the "decode" figure, its whole forward against the HBM roofline (latent
 rows, W, and the row's q, out and z moved once). The main workload over a paged latent pool
 (64-row pages in shuffled order) is the "paged" figure, and the main workload with its
@@ -19,7 +21,7 @@ attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, di
 step time.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
-                [--no-target] [--no-fp8] [--many-short NAME] [--no-cpu-baseline]
+                [--no-target] [--no-fp8] [--many-short NAME] [--window NAMES] [--no-cpu-baseline]
                 [--decode-rows N] [--decode-only] [--paged-rows P] [--grouped NAME]
 """
 import argparse
@@ -155,20 +157,20 @@ def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
         prev = list(ms)
     S.segmla_profile_enable(plan.handle, False)
     torch.cuda.synchronize()
-    g_pairs, l_pairs = plan.pairs()
+    g_pairs, l_pairs, w_pairs = plan.pairs()
     fpp = flops_per_pair(cfg)
-    flops = fpp * (g_pairs + l_pairs)
+    flops = fpp * (g_pairs + l_pairs + w_pairs)
     attn_ms = ms[0] / max(1, n_fwd)
     res = dict(
         cfg=cfg, T=T, n_protected=plan.n_protected, wall_s=wall, flops=flops,
-        g_pairs=g_pairs, l_pairs=l_pairs,
+        g_pairs=g_pairs, l_pairs=l_pairs, w_pairs=w_pairs,
         attn_ms=attn_ms, merge_ms=ms[1] / max(1, n_fwd), epi_ms=ms[2] / max(1, n_fwd),
         attn_ms_median=statistics.median(attn_steps), attn_ms_min=min(attn_steps),
         fwd_ms_median=statistics.median(fwd_steps), fwd_ms_min=min(fwd_steps),
         build_ms=ms[3] / max(1, n_build),
         attn_tflops=flops / (attn_ms * 1e-3) / 1e12,
         tflops=flops / wall / 1e12,
-        tflops_576_512=(2.0 * (576 + 512)) * (g_pairs + l_pairs) / wall / 1e12,
+        tflops_576_512=(2.0 * (576 + 512)) * (g_pairs + l_pairs + w_pairs) / wall / 1e12,
     )
     plan.close()
     if decode_rows > 0:
@@ -263,6 +265,9 @@ def main():
     ap.add_argument("--no-target", action="store_true")
     ap.add_argument("--fp8", default="pro_64k_fp8", help="E4M3-latent workload reported alongside")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--window", default="flash_32k_window_bf16,swa_32k_bf16",
+                    help="comma-separated workloads with sink + window heads reported alongside; "
+                         "'' for none")
     ap.add_argument("--many-short", default="many_short_bf16",
                     help="many-short-segments workload (256 documents, 256-way merge per row) "
                          "reported alongside; '' for none")
@@ -320,6 +325,7 @@ def main():
     msh = None
     if args.many_short:
         msh = measure(args.many_short, max(3, args.steps // 4), 1)
+    wins = [measure(name, max(3, args.steps // 2), 2) for name in args.window.split(",") if name]
     gr = None
     if args.grouped:
         gr = measure(args.grouped, max(2, args.steps // 2), 1)
@@ -395,6 +401,18 @@ def main():
             "stage_ms": {"attention": round(msh["attn_ms"], 3), "split_merge": round(msh["merge_ms"], 3),
                          "epilogue": round(msh["epi_ms"], 3), "plan_build": round(msh["build_ms"], 3)},
         }
+    if wins:
+        line["window_heads"] = [{
+            "workload": w["cfg"]["name"], "rows": w["T"], "heads": w["cfg"]["n_heads"],
+            "global_heads": len(w["cfg"]["global_heads"]), "window_heads": len(w["cfg"]["window_heads"]),
+            "n_sink": w["cfg"]["n_sink"], "window": w["cfg"]["window"],
+            "pairs": {"global": w["g_pairs"], "local": w["l_pairs"], "window": w["w_pairs"]},
+            "tflops": round(w["tflops"], 3), "us_per_layer": round(w["wall_s"] * 1e6, 1),
+            "attention_tflops": round(w["attn_tflops"], 3),
+            "attention_frac_bf16_peak": round(w["attn_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "stage_ms": {"attention": round(w["attn_ms"], 3), "epilogue": round(w["epi_ms"], 3),
+                         "plan_build": round(w["build_ms"], 3)},
+        } for w in wins]
     if gr is not None:
         line["grouped"] = {
             "workload": gr["cfg"]["name"], "group_heads": gr["cfg"]["group_heads"],

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SEGMLA_ABI_VERSION 2
+#define SEGMLA_ABI_VERSION 3
 
 typedef enum segmla_status {
   SEGMLA_OK = 0,
@@ -104,7 +104,11 @@ typedef struct segmla_layer {
   int32_t d_rope;                /* even, >= 2 */
   int32_t d_state;               /* rows of each head's projection slice, >= 1 */
   int32_t v_has_rope;            /* 1 or 0, see above */
-  const uint8_t *head_is_global; /* host [n_heads]: 1 Global, 0 Local; read at plan_create */
+  const uint8_t *head_is_global; /* host [n_heads], each head's role, read at plan_create:
+                                    1 Global (every row, full causal context), 0 Local (rows
+                                    of A with full context, the cached contribution elsewhere),
+                                    2 sink + window (every row, keys of W(t) below; projected
+                                    like a Global head, never cached) */
   double rope_base;              /* > 1 */
   float softmax_scale;           /* sigma multiplying q.k, > 0 */
   int32_t kv_dtype;              /* segmla_dtype of the latent pool */
@@ -120,6 +124,11 @@ typedef struct segmla_layer {
                                     form group g, z holds one vector per group, the sum of
                                     its heads' projections, and z_cached the group's cached
                                     Local contribution (else SEGMLA_E_SHAPE) */
+  int32_t n_sink;                /* sink + window heads (RedKnot explainer, "Insight 1: heads
+                                    have different jobs", W(i) = S_sink U [i - w, i]): key p
+                                    is visible from row t iff p <= t and (p < n_sink or
+                                    p >= t - window); n_sink >= 0 request positions */
+  int32_t window;                /* w >= 0; both unused when no head has role 2 */
 } segmla_layer;
 
 /* Protected-row rule (RedKnot-MLA paper, protected-row paragraph, Eq. 6):
@@ -152,14 +161,15 @@ typedef struct segmla_protect {
  *  z_cached [n_pool][H_L][d_state] io_dtype, cached projected contribution of the Local
  *           heads (in head order), indexed by latent-pool row; may be NULL when H_L = 0
  *  out      [q_end - q_begin][H][d_v] io_dtype: merged head outputs in request phase;
- *           written for Global heads on every row and for Local heads on rows in A only
+ *           written for Global and sink + window heads on every row and for Local heads
+ *           on rows in A only
  *  z        [q_end - q_begin][H][d_state] io_dtype: projected state, every (row, head)
  *           written
  *  lse      optional fp32 [q_end - q_begin][H]: natural-log log-sum-exp of sigma*q.k for
  *           every computed (row, head); NULL to skip
  * With grouped state (group_heads = G >= 2, n_groups = H / G): z is
- * [q_end - q_begin][n_groups][d_state] with z[t][g] = the sum over the group's Global heads of
- * W_h u_h plus, on rows in A, the sum over its Local heads of W_h u_h, or else
+ * [q_end - q_begin][n_groups][d_state] with z[t][g] = the sum over the group's Global and
+ * sink + window heads of W_h u_h plus, on rows in A, the sum over its Local heads of W_h u_h, or else
  * z_cached[pool_row(t)][g]; z_cached is [n_pool][n_groups][d_state] (may be NULL when H_L = 0). */
 typedef struct segmla_tensors {
   const void *q;
@@ -240,7 +250,7 @@ typedef struct segmla_plan_info {
   int64_t n_pool;          /* latent-pool rows the plan was validated against */
   int64_t n_protected;     /* |A| */
   int64_t workspace_bytes; /* as segmla_plan_workspace_bytes */
-  int32_t n_heads, n_global, n_local;
+  int32_t n_heads, n_global, n_local, n_window;
   int32_t d_nope, d_rope, d_v, d_state;
   int32_t z_slots, zc_slots;
   int32_t kv_dtype, io_dtype;
@@ -304,9 +314,10 @@ segmla_status segmla_lse_merge(const float *partial_o, const float *partial_ml, 
                                float *lse, void *stream);
 
 /* Number of (row, head, key) triples the forward computes, by role: out[0] Global
- * heads (every window row), out[1] Local heads (window rows in A). Needs a built plan;
- * copies the device-side sum over A and synchronizes `stream`. */
-segmla_status segmla_plan_pairs(const segmla_plan *plan, double out[2], void *stream);
+ * heads (every window row), out[1] Local heads (window rows in A), out[2] sink + window
+ * heads (every window row, |W(t)| keys each). Needs a built plan; copies the device-side
+ * sum over A and synchronizes `stream`. */
+segmla_status segmla_plan_pairs(const segmla_plan *plan, double out[3], void *stream);
 
 /* The analytic ledger, namespaces kept apart (RedKnot-MLA paper, namespaces
  * paragraph; head-row ceiling Eq. 8). Host only:
@@ -314,6 +325,7 @@ segmla_status segmla_plan_pairs(const segmla_plan *plan, double out[2], void *st
  * out[1] physical token-row saving of one reusable layer, h_local * (T - n_protected) / (h * T);
  * out[2] analytic attention operator saving of one reusable layer,
  *        1 - (global_pairs + local_pairs) / (h * T * (T + 1) / 2), with the pair counts
+ *        (global_pairs: every head computed on every row, Global and sink + window)
  *        of segmla_plan_pairs; NaN when local_pairs < 0.
  * Wall-clock time, the fourth namespace, is measured by the caller. */
 segmla_status segmla_ledger(int32_t f_front, int32_t r, int32_t f_back, int32_t h,

@@ -27,6 +27,10 @@ It computes, slowly and in the most direct way, what the GPU path computes:
   head's slice of the bias-free first output projection; Local heads outside
   A take their cached contribution unchanged (replacement, never addition,
   protected-row paragraph).
+* sink + window heads (RedKnot explainer, "Insight 1: heads have different
+  jobs": a local head sees the sink tokens and the recent window,
+  W(i) = S_sink U [i - w, i]): the same dense attention with the keys outside
+  that set masked out, on every row, over the same physically re-rotated keys.
 
 Readings of points the pages leave open (each listed in the design notes):
 values are the full latent row (keys = values, RoPE dims last); RoPE pairs
@@ -222,6 +226,32 @@ def attend_rows(q_rows, t_rows, keys, sigma, d_v):
     return O, lse
 
 
+def window_visible(t, n_sink, window):
+    """Keys a sink + window head sees from request row t (RedKnot explainer, "Insight 1: heads
+    have different jobs": W(i) = S_sink U [i - w, i]): boolean mask over positions 0..t, key p
+    visible iff p < n_sink (the sink, the first n_sink request positions) or p >= t - window
+    (the recent window, t itself included)."""
+    p = np.arange(int(t) + 1)
+    return (p < int(n_sink)) | (p >= int(t) - int(window))
+
+
+def attend_rows_window(q_rows, t_rows, keys, sigma, d_v, n_sink, window):
+    """attend_rows restricted to the sink + window key set of each row (window_visible)."""
+    n, Hs, _ = q_rows.shape
+    O = np.empty((n, Hs, d_v), dtype=np.float64)
+    lse = np.empty((n, Hs), dtype=np.float64)
+    for i in range(n):
+        t = int(t_rows[i])
+        K = keys[:t + 1][window_visible(t, n_sink, window)]
+        s = sigma * (q_rows[i] @ K.T)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        l = e.sum(axis=1, keepdims=True)
+        O[i] = (e @ K[:, :d_v]) / l
+        lse[i] = (m + np.log(l))[:, 0]
+    return O, lse
+
+
 # --------------------------------------------------------------------- projected state
 def project_rows(O_rows, t_rows, heads, W, d_nope, d_rope, base, v_has_rope):
     """Per-head projected contribution Z[t,h] = W_h u (fp64 [n, Hs, d_state]).
@@ -247,7 +277,12 @@ def layer_forward(inp, rows=None, A_override=None, zc_override=None):
     n_pool, head_is_global, q [T,H,d_qk], latent [n_pool, d_qk] (already
     decoded to values), w [H, d_state, d_v], z_cached [n_pool, H_L, d_state],
     scores [T], and cfg (d_nope, d_rope, rope_base, softmax_scale, v_has_rope,
-    edge_rows, tail_rows, budget_permille).
+    edge_rows, tail_rows, budget_permille, and n_sink / window when some head
+    has role 2).
+
+    head_is_global holds each head's role: 1 Global (every row, full causal context),
+    0 Local (rows of A with full causal context; elsewhere the cached contribution is
+    copied), 2 sink + window (every row, keys window_visible(t, n_sink, window)).
 
     Returns dict(geom, prot, A, rows, O [n,H,d_v] (NaN where a Local head is not
     computed), lse [n,H], Z [n,H,d_state], computed [n,H] bool).
@@ -266,9 +301,13 @@ def layer_forward(inp, rows=None, A_override=None, zc_override=None):
     in_A[A] = True
     T = geom["T"]
     rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
-    gmask = np.asarray(inp["head_is_global"]).astype(bool)
-    H = len(gmask)
-    local_heads = np.nonzero(~gmask)[0]
+    role = np.asarray(inp["head_is_global"]).astype(np.int64)
+    if np.any((role < 0) | (role > 2)):
+        raise ValueError("head roles are 0 (Local), 1 (Global) or 2 (sink + window)")
+    H = len(role)
+    local_heads = np.nonzero(role == 0)[0]
+    win_heads = np.nonzero(role == 2)[0]
+    n_sink, window = int(cfg.get("n_sink", 0)), int(cfg.get("window", 0))
     local_index = np.full(H, -1, dtype=np.int64)
     local_index[local_heads] = np.arange(len(local_heads))
 
@@ -282,13 +321,21 @@ def layer_forward(inp, rows=None, A_override=None, zc_override=None):
     Z = np.empty((n, H, W.shape[1]), dtype=np.float64)
     computed = np.zeros((n, H), dtype=bool)
     for i, t in enumerate(rows):
-        heads = np.arange(H) if in_A[t] else np.nonzero(gmask)[0]
-        qt = np.asarray(q[t], dtype=np.float64)[heads][None]
-        o, ls = attend_rows(qt, [t], keys, sigma, d_v)
-        O[i, heads] = o[0]
-        lse[i, heads] = ls[0]
-        computed[i, heads] = True
-        Z[i, heads] = project_rows(o, [t], heads, W, d_nope, d_rope, base, v_rope)[0]
+        # full causal context: Global heads, and Local heads on rows of A
+        heads = np.nonzero((role == 1) | ((role == 0) & in_A[t]))[0]
+        qrow = np.asarray(q[t], dtype=np.float64)
+        if len(heads):
+            o, ls = attend_rows(qrow[heads][None], [t], keys, sigma, d_v)
+            O[i, heads] = o[0]
+            lse[i, heads] = ls[0]
+            computed[i, heads] = True
+            Z[i, heads] = project_rows(o, [t], heads, W, d_nope, d_rope, base, v_rope)[0]
+        if len(win_heads):  # sink + window heads, every row
+            o, ls = attend_rows_window(qrow[win_heads][None], [t], keys, sigma, d_v, n_sink, window)
+            O[i, win_heads] = o[0]
+            lse[i, win_heads] = ls[0]
+            computed[i, win_heads] = True
+            Z[i, win_heads] = project_rows(o, [t], win_heads, W, d_nope, d_rope, base, v_rope)[0]
         if not in_A[t]:
             zc_row = np.asarray(Zc[geom["pool_of_row"][t]], dtype=np.float64)
             Z[i, local_heads] = zc_row[local_index[local_heads]]
@@ -310,16 +357,16 @@ def layer_forward_grouped(inp, rows=None):
     Eq. 3: z = z_L + z_G, with the producer retaining the projected Local contribution).
 
     Heads gG .. gG+G-1 form group g (G = cfg["group_heads"]). For request row t:
-    z[t][g] = sum over the group's Global heads of W_h u_h(t)
+    z[t][g] = sum over the group's Global and sink + window heads of W_h u_h(t)
               + (t in A ? sum over its Local heads of W_h u_h(t) : z_cached[pool_row(t)][g]),
     with z_cached [n_pool, n_groups, d_state] the cached Local contribution per group. O, lse
     and A are those of layer_forward. Returns its dict with Z [n, n_groups, d_state].
     """
     cfg = inp["cfg"]
     G = int(cfg["group_heads"])
-    gmask = np.asarray(inp["head_is_global"]).astype(bool)
-    H = len(gmask)
-    none = _NoCache(int((~gmask).sum()), cfg["d_state"])
+    role = np.asarray(inp["head_is_global"]).astype(np.int64)
+    H = len(role)
+    none = _NoCache(int((role == 0).sum()), cfg["d_state"])
     res = layer_forward(inp, rows=rows, zc_override=none)  # Local heads outside A add 0
     geom, A = res["geom"], res["A"]
     in_A = np.zeros(geom["T"], dtype=bool)
@@ -385,6 +432,11 @@ def flops_pairs(T, A, n_global, n_local):
     g = n_global * T * (T + 1) // 2
     l_ = n_local * int(np.sum(A + 1))
     return g, l_
+
+
+def window_pairs(q0, q1, n_sink, window):
+    """Keys one sink + window head attends over the request rows [q0, q1): sum of |W(t)|."""
+    return int(sum(int(window_visible(t, n_sink, window).sum()) for t in range(q0, q1)))
 
 
 def flops_pairs_window(q0, q1, A, n_global, n_local):

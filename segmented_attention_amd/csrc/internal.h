@@ -23,10 +23,12 @@ struct SegDesc {
 // Row flag bits written by the protected-row builder.
 enum : uint8_t { kFlagForced = 1, kFlagCand = 2, kFlagIndexer = 4 };
 
-// Work decomposition of the attention: (row, head) query vectors ("qvecs") come from two
-// streams. Stream F: rows of A with every head, flattened (a * H + h). Stream G: rows
-// outside A with the Global heads only (a * HG + g). Each stream is cut into tiles of
-// kTileQ consecutive qvecs; tiles [0, nF) are F tiles, [nF, nF + nG) are G tiles.
+// Work decomposition of the attention: (row, head) query vectors ("qvecs") come from three
+// streams. Stream F: rows of A with every full-context head (Global and Local), flattened
+// (a * HF + f). Stream G: rows outside A with the Global heads only (a * HG + g). Stream W:
+// every window row with the sink + window heads (a * HW + w). Each stream is cut into tiles
+// of kTileQ consecutive qvecs; tiles [0, nF) are F tiles, [nF, nF + nG) G tiles and
+// [nF + nG, nF + nG + nW) W tiles.
 constexpr int kTileQ = 128;
 
 // The computed rows are a window [q0, q1) of the request (all of it for a whole prefill).
@@ -38,26 +40,36 @@ constexpr int kTileQ = 128;
 struct TileMap {
   const int32_t* alist;   // [nA] rows of A, ascending
   const int32_t* nalist;  // [T - nA] rows outside A, ascending
+  const int32_t* fhead;   // [HF] full-context head ids (Global and Local); null: heads 0..H-1
   const int32_t* ghead;   // [HG] Global head ids
+  const int32_t* whead;   // [HW] sink + window head ids
   const int32_t* rng;     // device {a_lo, a_hi, na_lo, na_hi}
-  int32_t H, HG, nF, nG;
+  int32_t H, HF, HG, HW, nF, nG, nW;
+  int32_t q0, nq;         // window rows [q0, q0 + nq) (stream W walks them in order)
 };
 
 __device__ __forceinline__ bool tile_qvec(const TileMap& m, int tile, int qi, int& t, int& h) {
   if (tile < m.nF) {
     const int a0 = m.rng[0], na = m.rng[1] - a0;
     int64_t f = (int64_t)tile * kTileQ + qi;
-    if (f >= (int64_t)na * m.H) return false;
-    int a = (int)(f / m.H);
-    h = (int)(f - (int64_t)a * m.H);
+    if (f >= (int64_t)na * m.HF) return false;
+    int a = (int)(f / m.HF);
+    h = (int)(f - (int64_t)a * m.HF);
+    if (m.fhead) h = m.fhead[h];
     t = m.alist[a0 + a];
-  } else {
+  } else if (tile < m.nF + m.nG) {
     const int b0 = m.rng[2], nb = m.rng[3] - b0;
     int64_t f = (int64_t)(tile - m.nF) * kTileQ + qi;
     if (f >= (int64_t)nb * m.HG) return false;
     int a = (int)(f / m.HG);
     h = m.ghead[(int)(f - (int64_t)a * m.HG)];
     t = m.nalist[b0 + a];
+  } else {
+    int64_t f = (int64_t)(tile - m.nF - m.nG) * kTileQ + qi;
+    if (f >= (int64_t)m.nq * m.HW) return false;
+    int a = (int)(f / m.HW);
+    h = m.whead[(int)(f - (int64_t)a * m.HW)];
+    t = m.q0 + a;
   }
   return true;
 }
@@ -66,16 +78,27 @@ __device__ __forceinline__ bool tile_qvec(const TileMap& m, int tile, int qi, in
 __device__ __forceinline__ int tile_max_row(const TileMap& m, int tile) {
   if (tile < m.nF) {
     const int a0 = m.rng[0], na = m.rng[1] - a0;
-    const int64_t first = (int64_t)tile * kTileQ, cap = (int64_t)na * m.H - 1;
+    const int64_t first = (int64_t)tile * kTileQ, cap = (int64_t)na * m.HF - 1;
     if (first > cap) return -1;
     const int64_t last = first + kTileQ - 1 < cap ? first + kTileQ - 1 : cap;
-    return m.alist[a0 + (int)(last / m.H)];
+    return m.alist[a0 + (int)(last / m.HF)];
   }
-  const int b0 = m.rng[2], nb = m.rng[3] - b0;
-  const int64_t first = (int64_t)(tile - m.nF) * kTileQ, cap = (int64_t)nb * m.HG - 1;
+  if (tile < m.nF + m.nG) {
+    const int b0 = m.rng[2], nb = m.rng[3] - b0;
+    const int64_t first = (int64_t)(tile - m.nF) * kTileQ, cap = (int64_t)nb * m.HG - 1;
+    if (first > cap) return -1;
+    const int64_t last = first + kTileQ - 1 < cap ? first + kTileQ - 1 : cap;
+    return m.nalist[b0 + (int)(last / m.HG)];
+  }
+  const int64_t first = (int64_t)(tile - m.nF - m.nG) * kTileQ, cap = (int64_t)m.nq * m.HW - 1;
   if (first > cap) return -1;
   const int64_t last = first + kTileQ - 1 < cap ? first + kTileQ - 1 : cap;
-  return m.nalist[b0 + (int)(last / m.HG)];
+  return m.q0 + (int)(last / m.HW);
+}
+
+// Smallest request row of a W tile's qvecs (stream W walks the window rows in order).
+__device__ __forceinline__ int wtile_min_row(const TileMap& m, int tile) {
+  return m.q0 + (int)((int64_t)(tile - m.nF - m.nG) * kTileQ / m.HW);
 }
 
 // Index of the segment containing request row `row` (segments contiguous from 0).
@@ -108,6 +131,8 @@ struct AttnArgs {
   int32_t q0;             // first computed row: q, out and lse rows are t - q0
   int32_t n_split, split_keys;
   float sigma;            // softmax scale
+  int32_t n_sink, win;    // W tiles: key p visible from row t iff p <= t and (p < n_sink or
+                          // p >= t - win)
 };
 
 // Launchers (defined in the kernel sources), all on `stream`.
@@ -122,6 +147,8 @@ hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_
                           int q0, int q1, int32_t* rng, hipStream_t stream);
 hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
+// the W tiles (sink + window heads): one workgroup per tile, outputs written directly
+hipError_t launch_attn_window(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
 hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
                             int d, void* out, int out_dtype, float* lse, hipStream_t stream);
@@ -145,12 +172,12 @@ struct EpiArgs {
   const int32_t* alist;
   const int32_t* nalist;
   const int32_t* rng;     // device {a_lo, a_hi, na_lo, na_hi} (see TileMap)
-  const int32_t* ghead;   // [HG]
-  const int32_t* lhead;   // [HL]
+  const int32_t* ghead;   // [HG] heads computed on every row (Global, sink + window)
+  const int32_t* lhead;   // [HL] Local heads
   const int32_t* seg_of_row;
   const SegDesc* seg;
-  // grouped state (G >= 2): group g's Global heads are grp_ghead[grp_gstart[g] ..
-  // grp_gstart[g + 1]); z and z_cached hold n_groups slots per row
+  // grouped state (G >= 2): group g's heads computed on every row are grp_ghead[grp_gstart[g]
+  // .. grp_gstart[g + 1]); z and z_cached hold n_groups slots per row
   const int32_t* grp_gstart;
   const int32_t* grp_ghead;
   int32_t G, n_groups;

@@ -25,21 +25,25 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 }  // namespace
 
+// WIN: the W tiles (sink + window heads), in order, never split: key p is visible from row t
+// iff p <= t and (p < n_sink or p >= t - win) (RedKnot explainer, "Insight 1"); 64-key chunks
+// with no visible key are skipped (they would leave the running state unchanged).
+template <bool WIN>
 __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   __shared__ float qs[1024];   // query, RoPE part rotated for the current segment
   __shared__ float q0[1024];   // query as stored
   const int lane = threadIdx.x;
   const int qi = blockIdx.x % kTileQ;
   const int item = blockIdx.x / kTileQ;
-  const int rank = item / a.n_split, split = item % a.n_split;
-  const int tile = a.work[rank];
-  if (tile < 0 || tile >= a.map.nF + a.map.nG) return;
+  const int rank = WIN ? item : item / a.n_split, split = WIN ? 0 : item % a.n_split;
+  const int tile = WIN ? a.map.nF + a.map.nG + rank : a.work[rank];
+  if (tile < 0 || tile >= a.map.nF + a.map.nG + (WIN ? a.map.nW : 0)) return;
   int t, h;
   if (!tile_qvec(a.map, tile, qi, t, h)) return;
   const int d_qk = a.d_nope + a.d_rope, d_v = a.d_v, half_r = a.d_rope / 2;
   const int S = a.split_keys;
   int k_lo = 0, k_hi = t + 1;
-  if (a.n_split > 1) {
+  if (!WIN && a.n_split > 1) {
     k_lo = split * S;
     if (k_lo > tile_max_row(a.map, tile)) return;  // this split is not read by the merge
     k_hi = min(k_hi, k_lo + S);
@@ -81,7 +85,12 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
       const int j_lo = max(0, k_lo - sd.offset), j_hi = min(sd.len, k_hi - sd.offset);
       for (int j0 = j_lo; j0 < j_hi; j0 += 64) {
         const int j = j0 + lane;
-        const bool valid = j < j_hi;
+        if (WIN) {  // uniform: no key of the chunk in the sink or the window
+          const int p_lo = sd.offset + j0, p_hi = sd.offset + min(j0 + 64, j_hi) - 1;
+          if (p_lo >= a.n_sink && p_hi < t - a.win) continue;
+        }
+        const int pos = sd.offset + j;
+        const bool valid = j < j_hi && (!WIN || pos < a.n_sink || pos >= t - a.win);
         const float* krow = kv + (sd.pool_row + (valid ? j : j0)) * (int64_t)d_qk;
         float s = -INFINITY;
         if (valid) {
@@ -98,6 +107,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
         const int nk = min(64, j_hi - j0);
         for (int k = 0; k < nk; ++k) {
           const float pk = __shfl(p, k);
+          if (WIN && pk == 0.f) continue;  // a masked key (uniform: the value is shuffled)
           const float* vrow = kv + (sd.pool_row + j0 + k) * (int64_t)d_qk;
           for (int r = 0; r < kMaxPairsPerLane; ++r) {
             int d0 = 2 * (lane + 64 * r);
@@ -149,7 +159,16 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)(a.map.nF + a.map.nG) * a.n_split;
   const int64_t blocks = items * kTileQ;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_attn_f32, dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_attn_f32<false>, dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32_window(const AttnArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.map.nW * kTileQ;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_attn_f32<true>, dim3((unsigned)blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

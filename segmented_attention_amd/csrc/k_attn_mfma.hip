@@ -57,6 +57,7 @@
 namespace segmla {
 
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32_window(const AttnArgs& a, hipStream_t stream);
 
 namespace {
 
@@ -316,7 +317,11 @@ static_assert(kKT * (kDN / 16) == 4 * kThreads, "4 code chunks per thread");
 
 }  // namespace
 
-template <bool VROPE, bool FP8>
+// WIN: the W tiles (sink + window heads), one workgroup per tile in order: the key walk
+// covers the sink [0, min(n_sink, lo)) and the window [lo, t_max] with lo = max(0, t_min - win)
+// over the tile's rows, skips the keys between them, and masks per query vector the keys
+// below its own window (RedKnot explainer, "Insight 1": W(i) = S_sink U [i - w, i]).
+template <bool VROPE, bool FP8, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   // The kernel has no static LDS, so the dynamic area, and with it every tile buffer, starts
   // on a 256-byte boundary: the operand addresses below rely on it.
@@ -325,9 +330,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
-  const int rank = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
-  const int tile = a.work[rank];
-  if (tile < 0 || tile >= a.map.nF + a.map.nG) return;  // uniform; the work list is a permutation
+  const int rank = WIN ? (int)blockIdx.x : (int)blockIdx.x / a.n_split;
+  const int split = WIN ? 0 : (int)blockIdx.x % a.n_split;
+  const int tile = WIN ? a.map.nF + a.map.nG + rank : a.work[rank];
+  // uniform; the work list is a permutation of the F and G tiles
+  if (tile < 0 || tile >= a.map.nF + a.map.nG + (WIN ? a.map.nW : 0)) return;
   int t = -1, h = 0;
   const bool valid = tile_qvec(a.map, tile, wave * 32 + col, t, h);
   if (!valid) t = -1;
@@ -338,7 +345,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   t_max = __builtin_amdgcn_readfirstlane(t_max);
   cseg_t* const sg = (cseg_t*)a.seg;
   int k_lo = 0, k_hi = t_max + 1;
-  if (a.n_split > 1) {
+  // WIN: keys [g_lo, g_hi) lie between the sink and the window of every row of the tile
+  int g_lo = 0, g_hi = 0;
+  if (WIN) {
+    const int lo = max(0, wtile_min_row(a.map, tile) - a.win);
+    const int sink_end = min(a.n_sink, lo);
+    if (sink_end > 0) {
+      g_lo = sink_end;
+      g_hi = lo;
+    } else {
+      k_lo = lo;
+    }
+  } else if (a.n_split > 1) {
     k_lo = split * a.split_keys;
     k_hi = min(k_hi, k_lo + a.split_keys);
   }
@@ -389,12 +407,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 
   // ---- tile sequence over the key range [k_lo, k_hi), segment-aligned
   constexpr int64_t kSrcStride = FP8 ? 1 : kRowBytes;  // TileIt::src units per latent row
+  // end of the key range that position `pos` belongs to (WIN: the sink ends at the gap)
+  auto range_end = [&](int pos) __attribute__((always_inline)) -> int {
+    return (WIN && pos < g_lo && g_lo < g_hi) ? g_lo : k_hi;
+  };
   auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
     const int lo = a.seg_of_row[k_lo];  // k_lo < k_hi <= T
     c.seg = lo;
     const int off = sg[lo].offset, len = sg[lo].len;
     c.pos0 = k_lo;
-    c.pend = min(off + len, k_hi);
+    c.pend = min(off + len, range_end(k_lo));
     c.nval = min(kKT, c.pend - k_lo);
     c.src = (sg[lo].pool_row + (k_lo - off)) * kSrcStride;
   };
@@ -407,12 +429,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       nx.src = c.src + kKT * kSrcStride;
       return true;
     }
+    if (WIN && c.pend == g_lo && g_lo < g_hi) {  // the sink is done: jump to the window
+      if (g_hi >= k_hi) return false;
+      typedef const __attribute__((address_space(4))) int32_t cint_t;
+      const int ns = ((cint_t*)a.seg_of_row)[g_hi];  // uniform: a scalar load
+      const int off = sg[ns].offset;
+      nx.seg = ns;
+      nx.pos0 = g_hi;
+      nx.pend = min(off + sg[ns].len, k_hi);
+      nx.nval = min(kKT, nx.pend - g_hi);
+      nx.src = (sg[ns].pool_row + (g_hi - off)) * kSrcStride;
+      return true;
+    }
     if (c.seg + 1 >= a.n_seg) return false;
     const int off = sg[c.seg + 1].offset;  // the segments are contiguous: off == c.pend
     if (off >= k_hi) return false;
     nx.seg = c.seg + 1;
     nx.pos0 = off;
-    nx.pend = min(off + sg[c.seg + 1].len, k_hi);
+    nx.pend = min(off + sg[c.seg + 1].len, range_end(off));
     nx.nval = min(kKT, nx.pend - off);
     nx.src = sg[c.seg + 1].pool_row * kSrcStride;
     return true;
@@ -447,13 +481,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   };
   // acc^r <- R(angle of table[seg]) acc^r; O^T tile f, register i: feature
   // 32 f + 8 (i >> 2) + 4 hf + (i & 3), so registers i, i + 1 (i even) hold one RoPE pair
-  auto frame_step = [&](int seg, const float2* table) __attribute__((always_inline)) {
+  auto frame_step = [&](int seg, const float2* table, float sgn = 1.f) __attribute__((always_inline)) {
 #pragma unroll
     for (int f = 0; f < NR; ++f) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const int k = 16 * f + 4 * (i >> 2) + 2 * hf + ((i & 3) >> 1);
-        const float2 cs = table[seg * half_r + k];
+        float2 cs = table[seg * half_r + k];
+        cs.y *= sgn;  // -1: the inverse rotation
         const float x = accr[f][i], y = accr[f][i + 1];
         accr[f][i] = fmaf(x, cs.x, -(y * cs.y));  // explicit contraction: fixed rounding
         accr[f][i + 1] = fmaf(x, cs.y, y * cs.x);
@@ -560,12 +595,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     if (__builtin_expect(v2, 1)) issue(w2, fb);
     if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
       rotate_q(w1.seg);
-    // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
-    if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT)) != 0ull, 0)) {
+    // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3);
+    // WIN: also the keys below the query vector's window that are not sink keys
+    if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT) ||
+                                  (WIN && w0.pos0 < t - a.win)) != 0ull, 0)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int k = 8 * (i >> 2) + 4 * hf + (i & 3);
-        if (w0.pos0 + k > t || k >= w0.nval) Sc[i] = -INFINITY;
+        const int p = w0.pos0 + k;
+        if (p > t || k >= w0.nval || (WIN && p >= a.n_sink && p < t - a.win)) Sc[i] = -INFINITY;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -684,8 +722,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
       return false;
     }
     // next tile starts a new segment (a new run of the same segment keeps the frame)
-    if (__builtin_expect(VROPE && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
-      frame_step(w0.seg, a.stepcs);
+    if (__builtin_expect(VROPE && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame) {
+      if (!WIN || w1.seg == w0.seg + 1) {
+        frame_step(w0.seg, a.stepcs);
+      } else {  // past the gap: R(-rot_j) R(rot_i), through the request phase
+        frame_step(w0.seg, a.segcs);
+        frame_step(w1.seg, a.segcs, -1.f);
+      }
+    }
     return true;
   };
   for (;;) {
@@ -744,26 +788,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 }
 
 namespace {
-template <bool VROPE, bool FP8>
+template <bool VROPE, bool FP8, bool WIN>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
   const int lds = kLdsAlloc;
   // once per process and instantiation; a function-local static is initialized exactly once
   // even when several host threads launch at the same time
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_attn_mfma<VROPE, FP8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      (const void*)k_attn_mfma<VROPE, FP8, WIN>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  const int64_t blocks = (int64_t)(a.map.nF + a.map.nG) * a.n_split;
+  const int64_t blocks = WIN ? (int64_t)a.map.nW : (int64_t)(a.map.nF + a.map.nG) * a.n_split;
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((k_attn_mfma<VROPE, FP8>), dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_attn_mfma<VROPE, FP8, WIN>), dim3((unsigned)blocks), dim3(kThreads), lds,
+                     stream, a);
   return hipGetLastError();
+}
+
+template <bool WIN>
+hipError_t launch_any(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream) {
+  const bool fp8 = kv_dtype == 2;
+  if (v_has_rope)
+    return fp8 ? launch_mfma<true, true, WIN>(a, stream) : launch_mfma<true, false, WIN>(a, stream);
+  return fp8 ? launch_mfma<false, true, WIN>(a, stream) : launch_mfma<false, false, WIN>(a, stream);
 }
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream) {
   if (kv_dtype == 0) return launch_attn_f32(a, stream);
-  const bool fp8 = kv_dtype == 2;
-  if (v_has_rope) return fp8 ? launch_mfma<true, true>(a, stream) : launch_mfma<true, false>(a, stream);
-  return fp8 ? launch_mfma<false, true>(a, stream) : launch_mfma<false, false>(a, stream);
+  return launch_any<false>(a, kv_dtype, v_has_rope, stream);
+}
+
+hipError_t launch_attn_window(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream) {
+  if (kv_dtype == 0) return launch_attn_f32_window(a, stream);
+  return launch_any<true>(a, kv_dtype, v_has_rope, stream);
 }
 
 }  // namespace segmla

@@ -340,7 +340,7 @@ hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_
 // sizing); the empty ones take the last ranks, so `work` stays a permutation of all tiles.
 __global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
   const int n = m.nF + m.nG;
-  const int nF_act = (int)(((int64_t)(m.rng[1] - m.rng[0]) * m.H + kTileQ - 1) / kTileQ);
+  const int nF_act = (int)(((int64_t)(m.rng[1] - m.rng[0]) * m.HF + kTileQ - 1) / kTileQ);
   const int nG_act = (int)(((int64_t)(m.rng[3] - m.rng[2]) * m.HG + kTileQ - 1) / kTileQ);
   const int n_act = nF_act + nG_act;
   for (int tile = blockIdx.x * blockDim.x + threadIdx.x; tile < n; tile += gridDim.x * blockDim.x) {

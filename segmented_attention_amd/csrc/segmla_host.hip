@@ -25,24 +25,29 @@ struct segmla_plan {
   std::vector<SegDesc> runs;
   int32_t n_run = 0;
   // layer
-  int32_t H = 0, HG = 0, HL = 0, d_nope = 0, d_rope = 0, d_qk = 0, d_v = 0, d_state = 0;
+  int32_t H = 0, HG = 0, HL = 0, HW = 0, d_nope = 0, d_rope = 0, d_qk = 0, d_v = 0, d_state = 0;
   int32_t v_has_rope = 1, kv_dtype = 0, io_dtype = 0;
   double rope_base = 10000.0;
   float sigma = 1.f;
-  std::vector<int32_t> ghead, lhead;
+  // head lists by role: Global (1), Local (0), sink + window (2); the full-context heads
+  // (Global and Local, stream F) and the heads computed on every row (Global and sink + window,
+  // the epilogue's all-row heads)
+  std::vector<int32_t> ghead, lhead, whead, fhead, rowhead;
+  int32_t n_sink = 0, window = 0;
   int32_t G = 1, n_groups = 0;             // grouped projected state when G >= 2
-  std::vector<int32_t> grp_gstart, grp_ghead;  // each group's Global heads (CSR)
+  std::vector<int32_t> grp_gstart, grp_ghead;  // each group's all-row heads (CSR)
   // protection
   int32_t edge_rows = 0, tail_rows = 0, budget_permille = 0;
   std::vector<int32_t> dirty;  // sorted, unique
   int64_t n_forced = 0, n_cand = 0, K = 0, need = 0, nA = 0;
   // work decomposition
-  int32_t nF = 0, nG = 0, n_split = 1, split_keys = 0, n_blk = 0;
+  int32_t nF = 0, nG = 0, nW = 0, n_split = 1, split_keys = 0, n_blk = 0;
   int32_t n_cu = 256;  // compute units of the device the plan was sized for
   bool thin = false;   // bf16 projection as matrix-vector products (small windows)
   // workspace layout (byte offsets, 256-aligned)
   size_t o_seg = 0, o_segcs = 0, o_stepcs = 0, o_rowcs = 0, o_seg_of_row = 0, o_flags = 0,
-         o_dirty = 0, o_ghead = 0, o_lhead = 0, o_alist = 0, o_nalist = 0, o_blk_count = 0,
+         o_dirty = 0, o_ghead = 0, o_lhead = 0, o_whead = 0, o_fhead = 0, o_rowhead = 0,
+         o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
          o_rng = 0, o_lseg = 0, o_grp = 0, o_zpart = 0, ws_bytes = 0;
   // largest number of window rows inside / outside A (the Indexer picks decide the actual)
@@ -112,7 +117,8 @@ segmla_status check_layer(const segmla_layer* L) {
   if (!(L->rope_base > 1.0) || !std::isfinite(L->rope_base)) return SEGMLA_E_SHAPE;
   if (!(L->softmax_scale > 0.f) || !std::isfinite(L->softmax_scale)) return SEGMLA_E_SHAPE;
   for (int h = 0; h < L->n_heads; ++h)
-    if (L->head_is_global[h] > 1) return SEGMLA_E_SHAPE;
+    if (L->head_is_global[h] > 2) return SEGMLA_E_SHAPE;
+  if (L->n_sink < 0 || L->window < 0) return SEGMLA_E_SHAPE;
   if (!is_dtype(L->kv_dtype) || !is_dtype(L->io_dtype)) return SEGMLA_E_DTYPE;
   if (L->io_dtype == SEGMLA_E4M3_B128) return SEGMLA_E_DTYPE;
   if (L->split_keys < -1 || (L->split_keys > 0 && (L->split_keys % 64) != 0)) return SEGMLA_E_SHAPE;
@@ -166,9 +172,16 @@ TileMap tile_map(const segmla_plan* p) {
   m.alist = p->at<int32_t>(p->o_alist);
   m.nalist = p->at<int32_t>(p->o_nalist);
   m.ghead = p->at<int32_t>(p->o_ghead);
+  m.whead = p->at<int32_t>(p->o_whead);
+  m.fhead = p->HW > 0 ? p->at<int32_t>(p->o_fhead) : nullptr;  // else heads 0 .. H - 1
   m.rng = p->at<int32_t>(p->o_rng);
   m.H = p->H;
+  m.HF = p->H - p->HW;
   m.HG = p->HG;
+  m.HW = p->HW;
+  m.nW = p->nW;
+  m.q0 = p->q0;
+  m.nq = p->q1 - p->q0;
   m.nF = p->nF;
   m.nG = p->nG;
   return m;
@@ -190,6 +203,9 @@ segmla_status build_impl(segmla_plan* p, char* ws, const uint32_t* indexer_score
   up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
   up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
   up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
+  up(p->o_whead, p->whead.data(), sizeof(int32_t) * p->whead.size());
+  up(p->o_fhead, p->fhead.data(), sizeof(int32_t) * p->fhead.size());
+  up(p->o_rowhead, p->rowhead.data(), sizeof(int32_t) * p->rowhead.size());
   up(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
   up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
      sizeof(int32_t) * p->grp_ghead.size());
@@ -252,6 +268,8 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   a.n_split = p->n_split;
   a.split_keys = p->split_keys;
   a.sigma = p->sigma;
+  a.n_sink = p->n_sink;
+  a.win = p->window;
   hipError_t e = hipSuccess;
   segmla_plan* pm = const_cast<segmla_plan*>(p);  // profiling state only
   if (p->prof) {
@@ -259,6 +277,13 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
       return SEGMLA_E_HIP;
   }
   if (p->nF + p->nG > 0) e = launch_attn(a, p->kv_dtype, p->v_has_rope, s);
+  if (e == hipSuccess && p->nW > 0) {  // sink + window heads: their own grid, never split
+    AttnArgs aw = a;
+    aw.n_split = 1;
+    aw.split_keys = 0;
+    aw.part_o = aw.part_ml = nullptr;
+    e = launch_attn_window(aw, p->kv_dtype, p->v_has_rope, s);
+  }
   if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
   if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1) e = launch_merge_tiles(a, p->io_dtype, s);
   if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[2], s);
@@ -274,14 +299,14 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   ep.alist = p->at<int32_t>(p->o_alist);
   ep.nalist = p->at<int32_t>(p->o_nalist);
   ep.rng = p->at<int32_t>(p->o_rng);
-  ep.ghead = p->at<int32_t>(p->o_ghead);
+  ep.ghead = p->at<int32_t>(p->o_rowhead);  // every-row heads: Global and sink + window
   ep.lhead = p->at<int32_t>(p->o_lhead);
   ep.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
   ep.seg = p->at<SegDesc>(p->o_seg);
   ep.q0 = p->q0;
   ep.nq = p->q1 - p->q0;
   ep.H = p->H;
-  ep.HG = p->HG;
+  ep.HG = p->HG + p->HW;
   ep.HL = p->HL;
   ep.nA = (int32_t)p->nA_w;
   ep.nNA = (int32_t)p->nNA_w;
@@ -433,16 +458,24 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   }
   p->n_run = (int32_t)p->runs.size();
   p->H = layer->n_heads;
-  for (int h = 0; h < p->H; ++h) (layer->head_is_global[h] ? p->ghead : p->lhead).push_back(h);
+  for (int h = 0; h < p->H; ++h) {
+    const int role = layer->head_is_global[h];
+    (role == 1 ? p->ghead : role == 2 ? p->whead : p->lhead).push_back(h);
+    if (role != 2) p->fhead.push_back(h);
+    if (role != 0) p->rowhead.push_back(h);
+  }
   p->HG = (int32_t)p->ghead.size();
   p->HL = (int32_t)p->lhead.size();
+  p->HW = (int32_t)p->whead.size();
+  p->n_sink = layer->n_sink;
+  p->window = layer->window;
   if (layer->group_heads >= 2) {
     p->G = layer->group_heads;
     p->n_groups = p->H / p->G;
     p->grp_gstart.push_back(0);
     for (int g = 0; g < p->n_groups; ++g) {
       for (int h = g * p->G; h < (g + 1) * p->G; ++h)
-        if (layer->head_is_global[h]) p->grp_ghead.push_back(h);
+        if (layer->head_is_global[h] != 0) p->grp_ghead.push_back(h);
       p->grp_gstart.push_back((int32_t)p->grp_ghead.size());
     }
   }
@@ -502,15 +535,19 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
     p->nNA_w = L - nf_w;
   }
 
-  // Work decomposition: qvec tiles of stream F (window rows of A x all heads) and stream G
-  // (other window rows x Global heads), optionally split along the key axis. For a window
-  // smaller than the request, the split between the streams depends on the Indexer picks:
-  // both are sized for their largest share (above).
-  const int64_t qF = p->nA_w * p->H, qG = p->nNA_w * p->HG;
+  // Work decomposition: qvec tiles of stream F (window rows of A x the full-context heads),
+  // stream G (other window rows x Global heads), optionally split along the key axis, and
+  // stream W (every window row x the sink + window heads, never split). For a window smaller
+  // than the request, the split between F and G depends on the Indexer picks: both are sized
+  // for their largest share (above).
+  const int64_t qF = p->nA_w * (p->H - p->HW), qG = p->nNA_w * p->HG;
+  const int64_t qW = ((int64_t)p->q1 - p->q0) * p->HW;
   const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
-  if (nF + nG > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
+  const int64_t nW = (qW + kTileQ - 1) / kTileQ;
+  if (nF + nG + nW > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
   p->nF = (int32_t)nF;
   p->nG = (int32_t)nG;
+  p->nW = (int32_t)nW;
   const int64_t n_tiles = nF + nG;
   int32_t sk = layer->split_keys;
   const int32_t keys = p->q1;  // the window's rows see keys [0, q1) at most
@@ -550,6 +587,9 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
   p->o_ghead = take(sizeof(int32_t) * p->ghead.size());
   p->o_lhead = take(sizeof(int32_t) * p->lhead.size());
+  p->o_whead = take(sizeof(int32_t) * p->whead.size());
+  p->o_fhead = take(sizeof(int32_t) * p->fhead.size());
+  p->o_rowhead = take(sizeof(int32_t) * p->rowhead.size());
   p->o_grp = take(sizeof(int32_t) * (p->grp_gstart.size() + p->grp_ghead.size()));
   p->o_alist = take(sizeof(int32_t) * (size_t)p->nA);
   p->o_nalist = take(sizeof(int32_t) * (size_t)(T - p->nA));
@@ -601,6 +641,7 @@ segmla_status segmla_plan_get_info(const segmla_plan* p, segmla_plan_info* info)
   info->n_heads = p->H;
   info->n_global = p->HG;
   info->n_local = p->HL;
+  info->n_window = p->HW;
   info->d_nope = p->d_nope;
   info->d_rope = p->d_rope;
   info->d_v = p->d_v;
@@ -715,7 +756,7 @@ segmla_status segmla_copy_geometry(const segmla_plan* p, int32_t* seg_of_row, in
   return SEGMLA_OK;
 }
 
-segmla_status segmla_plan_pairs(const segmla_plan* p, double out[2], void* stream) {
+segmla_status segmla_plan_pairs(const segmla_plan* p, double out[3], void* stream) {
   if (!p || !out) return SEGMLA_E_NULL;
   if (!p->built) return SEGMLA_E_STATE;
   uint64_t sum_a = 0;
@@ -727,6 +768,10 @@ segmla_status segmla_plan_pairs(const segmla_plan* p, double out[2], void* strea
   const double q0 = (double)p->q0, q1 = (double)p->q1;  // window rows t see t + 1 keys
   out[0] = (double)p->HG * (q1 * (q1 + 1.0) - q0 * (q0 + 1.0)) / 2.0;
   out[1] = (double)p->HL * (double)sum_a;
+  // a sink + window head sees t + 1 keys while t <= c = window + n_sink, then c + 1
+  const double c = (double)p->window + (double)p->n_sink;
+  const double t_full = std::min(q1, std::max(q0, c + 1.0));  // rows [q0, t_full) see t + 1
+  out[2] = (double)p->HW * ((t_full * (t_full + 1.0) - q0 * (q0 + 1.0)) / 2.0 + (q1 - t_full) * (c + 1.0));
   return SEGMLA_OK;
 }
 

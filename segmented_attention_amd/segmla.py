@@ -56,7 +56,8 @@ class Layer(ctypes.Structure):
                 ("head_is_global", ctypes.POINTER(ctypes.c_uint8)), ("rope_base", ctypes.c_double),
                 ("softmax_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("split_keys", ctypes.c_int32),
-                ("group_heads", ctypes.c_int32)]
+                ("group_heads", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("window", ctypes.c_int32)]
 
 
 class Protect(ctypes.Structure):
@@ -76,6 +77,7 @@ class PlanInfo(ctypes.Structure):
                 ("n_pool", ctypes.c_int64), ("n_protected", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("n_heads", ctypes.c_int32),
                 ("n_global", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("n_window", ctypes.c_int32),
                 ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("d_state", ctypes.c_int32), ("z_slots", ctypes.c_int32),
                 ("zc_slots", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
@@ -205,7 +207,7 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                        d_rope, d_state, v_has_rope=1, rope_base=10000.0, softmax_scale=1.0,
                        kv_dtype=SEGMLA_BF16, io_dtype=SEGMLA_BF16, split_keys=0, edge_rows=0,
                        tail_rows=0, budget_permille=0, dirty_rows=(), q_range=None, pages=None,
-                       group_heads=0):
+                       group_heads=0, n_sink=0, window=0):
     """Validate and size a plan; returns the plan handle. q_range = (q_begin, q_end): a plan
     for that window of request rows (segmla_plan_create_range); None: the whole request.
     pages = dict(page_rows, page_start, page_table): a paged latent pool
@@ -219,7 +221,7 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                  keep["kind"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
     L = Layer(n_heads, d_nope, d_rope, d_state, v_has_rope,
               keep["glob"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), rope_base, softmax_scale,
-              kv_dtype, io_dtype, split_keys, group_heads)
+              kv_dtype, io_dtype, split_keys, group_heads, n_sink, window)
     pr = Protect(edge_rows, tail_rows, budget_permille, len(keep["dirty"]),
                  keep["dirty"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(keep["dirty"])
                  else None)
@@ -351,9 +353,10 @@ def segmla_lse_merge(partial_o, partial_ml, out, lse=None, stream=None):
 
 
 def segmla_plan_pairs(plan, stream=None):
-    out = (ctypes.c_double * 2)()
+    """(Global, Local, sink + window) counts of computed (row, head, key) triples."""
+    out = (ctypes.c_double * 3)()
     _check(lib().segmla_plan_pairs(plan, out, _stream(stream)), "segmla_plan_pairs")
-    return float(out[0]), float(out[1])
+    return float(out[0]), float(out[1]), float(out[2])
 
 
 def segmla_ledger(f_front, r, f_back, h, h_local, T, n_protected, global_pairs=-1.0,
@@ -397,7 +400,8 @@ class Plan:
             kinds, lens, offsets, pool_rows, n_pool, cfg["n_heads"], head_is_global, cfg["d_nope"],
             cfg["d_rope"], cfg["d_state"], cfg["v_has_rope"], cfg["rope_base"], cfg["softmax_scale"],
             _DT[cfg["kv_dtype"]], _DT[cfg["dtype"]], split_keys, cfg["edge_rows"], cfg["tail_rows"],
-            cfg["budget_permille"], dirty_rows, q_range, pages, cfg.get("group_heads", 0))
+            cfg["budget_permille"], dirty_rows, q_range, pages, cfg.get("group_heads", 0),
+            cfg.get("n_sink", 0), cfg.get("window", 0))
         self.T, self.n_protected = segmla_plan_rows(self.handle)
         # computed window: q, out, z and lse hold rows q0 .. q1 - 1
         self.q0, self.q1 = (0, self.T) if q_range is None else (int(q_range[0]), int(q_range[1]))

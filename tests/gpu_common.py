@@ -12,8 +12,10 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
 # Absolute error bound of the natural-log log-sum-exp (the statistic the split merge consumes).
 # The fp32 path carries no rounding beyond fp32; the bf16 path rounds the segment-rotated RoPE
 # query to bf16 (about 2^-9 |s_rope| per score) and the E4M3 path also rounds code x scale to
-# bf16 (about 2^-9 |s| per score): on the synthetic workloads |s| is a few units.
-LSE_TOL = {"f32": 1e-5, "bf16": 0.2, "e4m3": 0.6}
+# bf16 (about 2^-9 |s| per score): on the synthetic workloads |s| is a few units. Measured over
+# every parity case: at most 8.7e-7 (fp32), 8.8e-4 (bf16) and 5.0e-3 (E4M3); the bounds keep a
+# margin of 2x or more. Tests that drive the scores far larger pass their own bound.
+LSE_TOL = {"f32": 1e-5, "bf16": 2e-3, "e4m3": 1e-2}
 
 
 def tol_of(cfg):
@@ -77,9 +79,10 @@ def run_gpu(inp, split_keys=0, with_lse=True, plan=None):
     return plan, out, z, lse
 
 
-def compare(cfg, ref, out, z, lse, zc_rows, rows=None):
+def compare(cfg, ref, out, z, lse, zc_rows, rows=None, lse_tol=None):
     """Assert parity of one forward against the oracle result `ref` (computed on `rows`).
     Returns (max rel err of O, of Z, max abs err of lse or 0)."""
+    lse_tol = lse_tol_of(cfg) if lse_tol is None else lse_tol
     tol = tol_of(cfg)
     rows = ref["rows"] if rows is None else rows
     o = out[torch.as_tensor(rows, device=out.device)].double().cpu().numpy()
@@ -99,6 +102,6 @@ def compare(cfg, ref, out, z, lse, zc_rows, rows=None):
     if lse is not None:
         ls = lse[torch.as_tensor(rows, device=lse.device)].double().cpu().numpy()
         e_l = float(np.abs(ls[comp] - ref["lse"][comp]).max())
-        assert e_l <= lse_tol_of(cfg), "lse max abs err %.3g > %.1g" % (e_l, lse_tol_of(cfg))
+        assert e_l <= lse_tol, "lse max abs err %.3g > %.1g" % (e_l, lse_tol)
         assert np.all(np.isnan(ls[~comp]))
     return float(e_o.max()), float(e_z.max()), e_l

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert S.segmla_abi_version() == 2
+    assert S.segmla_abi_version() == 3
     for st in range(-9, 1):
         assert S.segmla_status_string(st) not in ("", "unknown status")
     assert S.segmla_status_string(-100) == "unknown status"
@@ -235,8 +235,12 @@ def test_shape_dtype_protect_errors(L):
     assert _status(cfg, softmax_scale=0.0) == S.SEGMLA_E_SHAPE
     assert _status(cfg, softmax_scale=float("nan")) == S.SEGMLA_E_SHAPE
     glob = np.zeros(cfg["n_heads"], np.uint8)
-    glob[3] = 2
+    glob[3] = 3                                   # roles are 0, 1 or 2
     assert _status(cfg, head_is_global=glob) == S.SEGMLA_E_SHAPE
+    glob[3] = 2                                   # a sink + window head
+    assert _status(cfg, head_is_global=glob, n_sink=4, window=16) == S.SEGMLA_OK
+    assert _status(cfg, head_is_global=glob, n_sink=-1, window=16) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, head_is_global=glob, n_sink=0, window=-1) == S.SEGMLA_E_SHAPE
     assert _status(cfg, split_keys=100) == S.SEGMLA_E_SHAPE
     assert _status(cfg, split_keys=-2) == S.SEGMLA_E_SHAPE
     assert _status(cfg, kv_dtype=9) == S.SEGMLA_E_DTYPE
@@ -307,7 +311,7 @@ def test_null_and_state_errors(L):
             S.SEGMLA_E_PROTECT
         buf = (ctypes.c_int32 * 4)()
         assert lib.segmla_copy_protected(p, buf, 4, None) == S.SEGMLA_E_STATE
-        out = (ctypes.c_double * 2)()
+        out = (ctypes.c_double * 3)()
         assert lib.segmla_plan_pairs(p, out, None) == S.SEGMLA_E_STATE
     finally:
         S.segmla_plan_destroy(p)

@@ -31,10 +31,12 @@ def _full_case(cfg, pool="identity", split_keys=0):
     np.testing.assert_array_equal(plan.protected(), ref["A"])
     e = compare(cfg, ref, out, z, lse, None)
     say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
-    g_pairs, l_pairs = plan.pairs()
+    g_pairs, l_pairs, w_pairs = plan.pairs()
+    hw = len(cfg.get("window_heads", ()))
     rg, rl = O.flops_pairs(inp["T"], ref["A"], len(cfg["global_heads"]),
-                           cfg["n_heads"] - len(cfg["global_heads"]))
-    assert (g_pairs, l_pairs) == (rg, rl)
+                           cfg["n_heads"] - len(cfg["global_heads"]) - hw)
+    rw = hw * O.window_pairs(0, inp["T"], cfg.get("n_sink", 0), cfg.get("window", 0))
+    assert (g_pairs, l_pairs, w_pairs) == (rg, rl, rw)
     plan.close()
     return inp, out, z
 
@@ -315,7 +317,10 @@ def test_parity_growing_scores(cfg, split, top, nope_only):
     assert s[-64:].max() - s[:32].max() > 8.0
     plan, out, z, lse = run_gpu(inp, split)
     ref = O.layer_forward(d)
-    e = compare(cfg, ref, out, z, lse, None)
+    # scores of 5 to 100 units: the rounded score part (the rotated RoPE query on the bf16
+    # latent; the dequantized latent with E4M3) carries proportionally larger lse errors
+    # (measured at most 7.0e-3 bf16, 2.4e-2 E4M3)
+    e = compare(cfg, ref, out, z, lse, None, lse_tol=5e-2 if cfg["kv_dtype"] == "e4m3" else 1.5e-2)
     say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
     plan.close()
 

@@ -83,7 +83,7 @@ def test_attention_kernel_asm_invariants(tmp_path):
                 name = None
                 continue
             funcs[name].append(line)
-    assert len(funcs) == 4, sorted(funcs)
+    assert len(funcs) == 8, sorted(funcs)  # (v_has_rope, E4M3, sink + window) instantiations
 
     for fname, lines in funcs.items():
         # no calls (s_setpc alone is also the far-jump form of a branch in a large kernel)
@@ -187,7 +187,7 @@ def _valu_mfma_hazards(lines, window=2):
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not found")
 def test_assembly_mfmas_without_nop_read_no_fresh_valu_result(tmp_path):
     funcs = {k: v for k, v in _functions(_asm(tmp_path)).items() if "k_attn_mfma" in k}
-    assert len(funcs) == 4, sorted(funcs)
+    assert len(funcs) == 8, sorted(funcs)  # (v_has_rope, E4M3, sink + window) instantiations
     checked = 0
     for fname, lines in funcs.items():
         bad = _valu_mfma_hazards(lines)

@@ -263,11 +263,12 @@ def test_sdpa_float64_pin():
 
 
 # ------------------------------------------------------- segmented fp64 computation
-def _segmented_fp64(inp, rows, rng):
+def _segmented_fp64(inp, rows, rng, visible=None):
     """The method itself in fp64, written independently: for each visible segment
     rotate q's RoPE part by -rot_i, attend the stored latent in place, restore the
     partial output's phase by +rot_i, then merge (max, sum, partial) statistics with
-    a log-sum-exp merge taken in a random segment order."""
+    a log-sum-exp merge taken in a random segment order. visible(t, positions) -> bool
+    mask restricts the keys (request positions) a row sees; segments with none are skipped."""
     cfg = inp["cfg"]
     dn, dr, base, sig = cfg["d_nope"], cfg["d_rope"], cfg["rope_base"], cfg["softmax_scale"]
     k = np.arange(dr // 2)
@@ -300,6 +301,11 @@ def _segmented_fp64(inp, rows, rng):
             nvis = min(int(lens[i]), t - int(offs[i]) + 1)
             rot_i = float(offs[i]) if kinds[i] == 1 else 0.0
             C = lat[seg_rows(i, nvis)]
+            if visible is not None:
+                keep = visible(t, int(offs[i]) + np.arange(nvis))
+                if not keep.any():
+                    continue
+                C = C[keep]
             q = rot(inp["q"][t], -rot_i * theta)            # [H, d]
             s = sig * q @ C.T
             m = s.max(axis=1)
@@ -548,3 +554,140 @@ def test_rel_err_rows_hand_values():
     np.testing.assert_array_equal(e3, expect)
     # a zero reference row with a nonzero x is an infinite relative error, never a pass
     assert O.rel_err_rows(np.array([[1e-3, 0.0]]), np.array([[0.0, 0.0]]))[0] > 1e100
+
+
+# ------------------------------------------------------------------ sink + window heads
+def test_window_printed_example():
+    """RedKnot explainer, "Insight 1: heads have different jobs": with a window of w = 256,
+    token 1000 of a local head needs tokens 744-1000 and the sink."""
+    vis = O.window_visible(1000, n_sink=4, window=256)
+    assert len(vis) == 1001
+    np.testing.assert_array_equal(np.nonzero(vis)[0], np.r_[0:4, 744:1001])
+    # a row inside the sink's reach sees a contiguous prefix; row 0 sees itself
+    np.testing.assert_array_equal(np.nonzero(O.window_visible(200, 4, 256))[0], np.arange(201))
+    np.testing.assert_array_equal(np.nonzero(O.window_visible(0, 0, 0))[0], [0])
+    np.testing.assert_array_equal(np.nonzero(O.window_visible(10, 0, 0))[0], [10])
+    assert O.window_pairs(1000, 1001, 4, 256) == 261
+
+
+def _role_inputs(cfg, roles, n_sink, window, pool="identity"):
+    inp = _oracle_inputs(make_inputs(cfg, "cpu", pool=pool))
+    inp["head_is_global"] = np.asarray(roles, dtype=np.uint8)
+    inp["cfg"] = dict(cfg, n_sink=n_sink, window=window)
+    n_local = int(np.sum(np.asarray(roles) == 0))
+    inp["z_cached"] = inp["z_cached"][:, :n_local]
+    return inp
+
+
+def test_window_brute_force_tiny():
+    """Sink + window heads on an 11-row request (d_nope = d_rope = 2): raw unrotated vectors,
+    explicit 2x2 matrices, the key set enumerated position by position, unshifted softmax."""
+    rng = np.random.default_rng(5)
+    kinds = np.array([0, 1, 1, 2], dtype=np.uint8)
+    lens = np.array([2, 3, 4, 2])
+    offsets = np.array([0, 2, 5, 9])
+    T, H, n_sink, w = 11, 3, 2, 3
+    kh = rng.normal(size=(T, 4))
+    qh = rng.normal(size=(T, H, 4))
+    seg = np.repeat(np.arange(4), lens)
+    j = np.arange(T) - offsets[seg]
+    stored_pos = np.where(kinds[seg] == 1, j, np.arange(T))
+    lat, q = kh.copy(), qh.copy()
+    for p in range(T):
+        lat[p, 2:] = _rot2(stored_pos[p]) @ kh[p, 2:]
+        for h in range(H):
+            q[p, h, 2:] = _rot2(p) @ qh[p, h, 2:]
+    Wp = rng.normal(size=(H, 3, 4))
+    cfg = dict(d_nope=2, d_rope=2, rope_base=10000.0, softmax_scale=0.9, v_has_rope=1,
+               edge_rows=1, tail_rows=2, budget_permille=0, n_sink=n_sink, window=w)
+    inp = dict(cfg=cfg, kinds=kinds, lens=lens, offsets=offsets, pool_rows=offsets, n_pool=T,
+               head_is_global=np.array([2, 1, 2], dtype=np.uint8), q=q, latent=lat, w=Wp,
+               z_cached=np.zeros((T, 0, 3)), scores=np.zeros(T))
+    res = O.layer_forward(inp)
+    assert res["computed"].all()
+    for t in range(T):
+        for h in (0, 2):
+            keys = [p for p in range(t + 1) if p < n_sink or t - w <= p]
+            sc = np.array([0.9 * float(q[t, h] @ np.concatenate([kh[p, :2], _rot2(p) @ kh[p, 2:]]))
+                           for p in keys])
+            P = np.exp(sc) / np.exp(sc).sum()
+            o, u = np.zeros(4), np.zeros(4)
+            for pk, p in zip(P, keys):
+                o[:2] += pk * kh[p, :2]
+                o[2:] += pk * (_rot2(p) @ kh[p, 2:])
+                u[:2] += pk * kh[p, :2]
+                u[2:] += pk * (_rot2(p - t) @ kh[p, 2:])
+            np.testing.assert_allclose(res["O"][t, h], o, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(res["Z"][t, h], Wp[h] @ u, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(res["lse"][t, h], np.log(np.exp(sc).sum()), rtol=0, atol=1e-12)
+
+
+def test_window_special_cases():
+    """A window reaching row 0 (or a sink covering the request) is full causal attention; a
+    zero window without sink is each row attending to itself alone (O = the row's own value,
+    whatever the query)."""
+    cfg = CONFIGS[0]
+    T = 274
+    roles = [1, 2, 2, 0, 0, 2, 0, 0]
+    full = O.layer_forward(_role_inputs(cfg, [1 if r == 2 else r for r in roles], 0, 0))
+    for n_sink, w in ((0, T), (T, 0), (5, T - 1)):
+        res = O.layer_forward(_role_inputs(cfg, roles, n_sink, w))
+        for h in (1, 2, 5):
+            np.testing.assert_allclose(res["O"][:, h], full["O"][:, h], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(res["Z"][:, h], full["Z"][:, h], rtol=0, atol=1e-12)
+    inp = _role_inputs(cfg, roles, 0, 0)
+    res = O.layer_forward(inp)
+    keys = O.relocated_keys(inp["latent"], res["geom"], cfg["d_nope"], cfg["d_rope"], cfg["rope_base"])
+    for h in (1, 2, 5):
+        np.testing.assert_allclose(res["O"][:, h], keys, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(res["lse"][:, h], np.einsum("td,td->t", inp["q"][:, h], keys),
+                                   rtol=0, atol=1e-12)
+    # Local heads outside A still copy the cache and Global heads keep full context
+    np.testing.assert_allclose(res["O"][:, 0], full["O"][:, 0], rtol=0, atol=1e-13)
+
+
+def test_window_sdpa_float64_pin():
+    """Library routine: torch scaled_dot_product_attention in float64 with an explicit boolean
+    mask (key p visible from row t iff p <= t and (p < n_sink or p >= t - w)), built here
+    from the index grids, on the physically re-rotated keys."""
+    cfg = SMALL_CONFIGS[0]
+    roles = [1, 2, 0, 2, 0, 0, 2, 0]
+    n_sink, w = 3, 40
+    inp = _role_inputs(cfg, roles, n_sink, w)
+    res = O.layer_forward(inp)
+    keys = O.relocated_keys(inp["latent"], res["geom"], cfg["d_nope"], cfg["d_rope"], cfg["rope_base"])
+    T = len(keys)
+    tt, pp = np.meshgrid(np.arange(T), np.arange(T), indexing="ij")
+    mask = torch.from_numpy((pp <= tt) & ((pp < n_sink) | (pp >= tt - w)))
+    kt = torch.from_numpy(keys)[None, None]
+    for h in (1, 3, 6):
+        qt = torch.from_numpy(np.ascontiguousarray(inp["q"][:, h]))[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, kt, attn_mask=mask, scale=cfg["softmax_scale"])[0, 0].numpy()
+        np.testing.assert_allclose(res["O"][:, h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["identity", "shuffled", "paged:16"])
+def test_window_relocation_identity(mode):
+    """Sink + window heads under relocation: the independent segmented fp64 computation (rotate
+    q per segment, attend the stored latent, restore the phase, log-sum-exp merge) restricted
+    to each row's window equals the oracle on physically re-rotated keys, across windows that
+    span segment boundaries."""
+    cfg = SMALL_CONFIGS[0]
+    roles = [2] * 8
+    n_sink, w = 2, 60
+    inp = _role_inputs(cfg, roles, n_sink, w, pool=mode)
+    T = inp["T"]
+    rows = sorted(set([0, 1, 5, 70, 71, T - 1] + list(np.random.default_rng(2).choice(T, 20, replace=False))))
+    res = O.layer_forward(inp, rows=rows)
+    seg = _segmented_fp64(inp, rows, np.random.default_rng(3),
+                          visible=lambda t, pos: (pos < n_sink) | (pos >= t - w))
+    for i, t in enumerate(rows):
+        np.testing.assert_allclose(res["O"][i], seg[t], rtol=0, atol=1e-10)
+
+
+def test_window_pairs_brute_force():
+    for n_sink, w in ((0, 0), (4, 256), (3, 10), (1000, 5)):
+        for q0, q1 in ((0, 1), (0, 300), (250, 700), (999, 1300)):
+            brute = sum(1 for t in range(q0, q1) for p in range(t + 1) if p < n_sink or p >= t - w)
+            assert O.window_pairs(q0, q1, n_sink, w) == brute

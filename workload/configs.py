@@ -122,8 +122,49 @@ GROUPED_CONFIGS = [
 ]
 
 
+def _windowed(cfg, name, window_heads, n_sink, window, global_heads=None, seed=None, **over):
+    """cfg with sink + window heads (role 2): key p visible from row t iff p <= t and
+    (p < n_sink or p >= t - window) (RedKnot explainer, "Insight 1: heads have different jobs").
+    The remaining heads keep their roles (Global where listed, else Local)."""
+    g = cfg["global_heads"] if global_heads is None else list(global_heads)
+    w = sorted(window_heads)
+    assert not set(w) & set(g)
+    return dict(cfg, name=name, index=None, global_heads=g, window_heads=w, n_sink=n_sink,
+                window=window, seed=cfg["seed"] if seed is None else seed, **over)
+
+
+# Sink + window heads under relocation. The small layers mix all three roles (Global, Local,
+# sink + window) with windows that cross segment boundaries; the SWA layers give every head a
+# 128-token window without sink (DeepSeek-V4's sliding-window layers, TensorRT-LLM reading
+# notes: dense attention over the most recent 128 raw tokens).
+WINDOW_CONFIGS = [
+    _windowed(_cfg("tiny_window_fp32", None, "f32", 8, 64, 16, 64,
+                   [("prefix", 16), ("doc", 50), ("doc", 80), ("doc", 120), ("new", 8)],
+                   edge_rows=8, tail_rows=32, budget_permille=100, seed=30),
+              "tiny_window_fp32", [1, 4, 6], n_sink=4, window=20),
+    _windowed(SMALL_CONFIGS[1], "flash_window_small_bf16", [h for h in range(64) if h % 8 in (1, 2, 3)],
+              n_sink=4, window=96, seed=31),
+    _windowed(SMALL_CONFIGS[1], "swa_small_bf16", list(range(64)), n_sink=0, window=127,
+              global_heads=[], seed=32),
+    _windowed(SMALL_CONFIGS[4], "pro_window_small_fp8", [h for h in range(128) if h % 8 in (1, 2)],
+              n_sink=4, window=64, seed=33),
+    _windowed(SMALL_CONFIGS[5], "flash_window_small_vnope_bf16", [h for h in range(64) if h % 4 == 1],
+              n_sink=0, window=50, seed=34),
+    # tiny windows (a row and its predecessor) and a sink that covers a whole segment
+    _windowed(SMALL_CONFIGS[0], "tiny_window_edge_fp32", [2, 3, 5], n_sink=9, window=1, seed=35),
+]
+
+# Full-size: the Flash-like 32K layer with its 56 non-Global heads as sink + window heads (the
+# explainer's w = 256 example, 4 sink tokens), and the same request as an SWA-128 layer.
+FLASH_32K_WINDOW = _windowed(CONFIGS[1], "flash_32k_window_bf16",
+                             [h for h in range(64) if h % 8 != 0], n_sink=4, window=256)
+SWA_32K = _windowed(CONFIGS[1], "swa_32k_bf16", list(range(64)), n_sink=0, window=127,
+                    global_heads=[])
+
+
 def config_by_name(name):
-    for c in CONFIGS + SMALL_CONFIGS + GROUPED_CONFIGS + [FLASH_TAIL32K, LONG_128K_GLOBAL]:
+    for c in (CONFIGS + SMALL_CONFIGS + GROUPED_CONFIGS + WINDOW_CONFIGS +
+              [FLASH_TAIL32K, LONG_128K_GLOBAL, FLASH_32K_WINDOW, SWA_32K]):
         if c["name"] == name:
             return c
     raise KeyError(name)

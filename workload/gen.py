@@ -169,9 +169,10 @@ def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
     d_nope, d_rope = cfg["d_nope"], cfg["d_rope"]
     d_qk = d_nope + d_rope
     d_v = d_qk if cfg["v_has_rope"] else d_nope
-    head_is_global = np.zeros(H, dtype=np.uint8)
-    head_is_global[cfg["global_heads"]] = 1
-    n_local = H - int(head_is_global.sum())
+    head_is_global = np.zeros(H, dtype=np.uint8)   # each head's role: 0 Local, 1 Global,
+    head_is_global[cfg["global_heads"]] = 1         # 2 sink + window
+    head_is_global[list(cfg.get("window_heads", ()))] = 2
+    n_local = int(np.sum(head_is_global == 0))
     io = _TORCH_DT[cfg["dtype"]]
 
     used = np.zeros(n_pool, dtype=bool)
