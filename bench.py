@@ -105,11 +105,98 @@ def measure_window(inp, cfg, n_rows, steps, warmup):
                 forward_us=fwd_us, bytes=nbytes, gbps=gbps)
 
 
+def measure_decode_walk(inp, cfg, n_steps, warmup=3):
+    """Decode walk: one plan for the request's final length, moved row by row over the last
+    n_steps + warmup rows with segmla_plan_set_window (no geometry, table or protected-set
+    rebuild); each step is the window update plus the forward, timed with HIP events on the
+    launch stream."""
+    import torch
+    from segmented_attention_amd import segmla as S
+
+    T, H = inp["T"], cfg["n_heads"]
+    first = T - n_steps - warmup
+    dt = inp["q"].dtype
+    out = torch.empty((1, H, inp["d_v"]), dtype=dt, device="cuda")
+    z = torch.empty((1, H, cfg["d_state"]), dtype=dt, device="cuda")
+    plan = S.Plan.for_inputs(inp, q_range=(first, first + 1))
+    plan.build(inp["scores"], min_bytes=2 * S.segmla_plan_workspace_bytes(plan.handle))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    for k in range(n_steps + warmup):
+        t = first + k
+        if k >= warmup:
+            ev[k - warmup].record()
+        if k > 0:
+            plan.set_window(t, t + 1)
+        plan.forward(inp, out, z)
+    ev[n_steps].record()
+    torch.cuda.synchronize()
+    plan.close()
+    steps = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n_steps)]
+    return dict(steps=n_steps, step_us_median=statistics.median(steps), step_us_min=min(steps))
+
+
+def measure_prefetch(cfg_name, steps):
+    """The layer's forward alone, then with the next layer's artifacts (its latent rows and the
+    cached state of its first document) staged from pinned host memory on the prefetch stream
+    at the same time; HIP-event times on the launch stream, the transfer time on the prefetch
+    stream."""
+    import torch
+    from segmented_attention_amd import segmla as S
+    from workload import config_by_name, make_inputs
+
+    cfg = config_by_name(cfg_name)
+    inp = make_inputs(cfg, "cuda")
+    T, H = inp["T"], cfg["n_heads"]
+    dt = inp["q"].dtype
+    out = torch.empty((T, H, inp["d_v"]), dtype=dt, device="cuda")
+    z = torch.empty((T, H, cfg["d_state"]), dtype=dt, device="cuda")
+    plan = S.Plan.for_inputs(inp)
+    plan.build(inp["scores"])
+    n_doc = int(inp["lens"][1])  # the first document after the prefix
+    p0 = int(inp["pool_rows"][1])
+    src = [inp["kv"].cpu().pin_memory(), inp["z_cached"][p0:p0 + n_doc].cpu().pin_memory()]
+    dst = [torch.empty_like(src[0], device="cuda"), torch.empty_like(src[1], device="cuda")]
+    nbytes = sum(x.numel() * x.element_size() for x in src)
+    pf = S.Prefetcher()
+
+    def timed(with_prefetch):
+        ms, pms = [], []
+        for _ in range(steps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if with_prefetch:
+                pf.prefetch(list(zip(src, dst)))
+            a.record()
+            plan.forward(inp, out, z)
+            b.record()
+            if with_prefetch:
+                pf.wait()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+            if with_prefetch:
+                pms.append(pf.elapsed_ms())
+        return statistics.median(ms[1:]), (statistics.median(pms[1:]) if pms else None)
+
+    alone, _ = timed(False)
+    shared, copy_ms = timed(True)
+    pf.close()
+    plan.close()
+    del inp, out, z, src, dst
+    torch.cuda.empty_cache()
+    return dict(workload=cfg_name, forward_ms=round(alone, 3),
+                forward_ms_with_prefetch=round(shared, 3), prefetch_bytes=nbytes,
+                prefetch_ms=round(copy_ms, 3), prefetch_gbps=round(nbytes / copy_ms / 1e6, 1),
+                source="pinned host memory")
+
+
 def decode_json(name, d):
     return {
         "workload": name, "window_rows": d["rows"], "keys": d["keys"],
         "attention_us": round(d["attention_us"], 2), "split_merge_us": round(d["merge_us"], 2),
         "epilogue_us": round(d["epilogue_us"], 2), "forward_us": round(d["forward_us"], 2),
+        **({"walk_step_us_median": round(d["walk"]["step_us_median"], 2),
+            "walk_step_us_min": round(d["walk"]["step_us_min"], 2),
+            "walk": "%d consecutive decode rows on one plan: window update + forward per row"
+                    % d["walk"]["steps"]} if "walk" in d else {}),
         "roofline": {"bound": "hbm", "achieved": round(d["gbps"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(d["gbps"] / PEAK_HBM_GBS, 4),
                      "bytes": int(d["bytes"]), "over": "whole forward"},
@@ -176,6 +263,8 @@ def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
     if decode_rows > 0:
         log("workload %s: decode window of the last %d row(s)" % (cfg_name, decode_rows))
         res["decode"] = measure_window(inp, cfg, decode_rows, 20, 3)
+        log("workload %s: decode walk over the last rows (set_window + forward)" % cfg_name)
+        res["decode"]["walk"] = measure_decode_walk(inp, cfg, 16)
     del inp, out, z
     torch.cuda.empty_cache()
     return res
@@ -268,6 +357,8 @@ def main():
     ap.add_argument("--window", default="flash_32k_window_bf16,swa_32k_bf16",
                     help="comma-separated workloads with sink + window heads reported alongside; "
                          "'' for none")
+    ap.add_argument("--prefetch", type=int, default=1,
+                    help="1: time the main workload's forward with a concurrent artifact prefetch")
     ap.add_argument("--many-short", default="many_short_bf16",
                     help="many-short-segments workload (256 documents, 256-way merge per row) "
                          "reported alongside; '' for none")
@@ -326,6 +417,10 @@ def main():
     if args.many_short:
         msh = measure(args.many_short, max(3, args.steps // 4), 1)
     wins = [measure(name, max(3, args.steps // 2), 2) for name in args.window.split(",") if name]
+    pfx = None
+    if args.prefetch:
+        log("workload %s: forward with a concurrent artifact prefetch" % args.workload)
+        pfx = measure_prefetch(args.workload, 5)
     gr = None
     if args.grouped:
         gr = measure(args.grouped, max(2, args.steps // 2), 1)
@@ -413,6 +508,8 @@ def main():
             "stage_ms": {"attention": round(w["attn_ms"], 3), "epilogue": round(w["epi_ms"], 3),
                          "plan_build": round(w["build_ms"], 3)},
         } for w in wins]
+    if pfx is not None:
+        line["prefetch"] = pfx
     if gr is not None:
         line["grouped"] = {
             "workload": gr["cfg"]["name"], "group_heads": gr["cfg"]["group_heads"],

@@ -269,6 +269,21 @@ segmla_status segmla_plan_get_info(const segmla_plan *plan, segmla_plan_info *in
 segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t workspace_bytes,
                                 const uint32_t *indexer_score, void *stream);
 
+/* Re-target a built plan to another window [q_begin, q_end) of the same request (q_end = -1:
+ * T): the next chunk of a chunked prefill, or the next decode row on a plan created for the
+ * request's final length (a window's rows attend keys [0, t] only, so rows after the window
+ * need no latent yet). The segment descriptors, RoPE tables, row maps and the protected set A
+ * are the request's and are kept (RedKnot-MLA paper, TP8 fast-path paragraph: repeated
+ * document bundles reuse compact segment-pointer geometry); only the window's RoPE rows, its
+ * ranges in A and in the complement, the work list and the key-range split are redone, on
+ * `stream`, ahead of the forwards that follow there. The window's workspace part must fit the
+ * workspace the plan was built into (the key split is coarsened until it does), else
+ * SEGMLA_E_WORKSPACE and the plan is unchanged; 0 <= q_begin < q_end <= T, else SEGMLA_E_SHAPE;
+ * an unbuilt plan gives SEGMLA_E_STATE. Afterwards segmla_plan_workspace_bytes, _pairs and
+ * _get_info describe the new window. */
+segmla_status segmla_plan_set_window(segmla_plan *plan, int64_t q_begin, int64_t q_end,
+                                     void *stream);
+
 /* One layer forward (per-segment rotate / attend / restore, LSE merge, replacement
  * epilogue) on a built plan. A plan may run many forwards with new tensors. */
 segmla_status segmla_forward(const segmla_plan *plan, const segmla_tensors *t, void *stream);
@@ -345,6 +360,39 @@ segmla_status segmla_profile_enable(segmla_plan *plan, int32_t enable);
  * ms[3] plan build (geometry, protected rows, work list); *n_forward = profiled forwards. */
 segmla_status segmla_profile_read(segmla_plan *plan, double ms[4], int64_t *n_forward,
                                   int64_t *n_build);
+
+/* Artifact prefetch (RedKnot-MLA paper, TP8 fast-path paragraph: while a layer runs, a
+ * dedicated stream prefetches the tiles of a future layer group, and device events, not host
+ * polling, guard their consumption). A prefetcher owns one stream of default priority and its
+ * events. segmla_prefetch stages row ranges, e.g. the latent rows and cached projected state
+ * of the segments a later layer reads, from host memory (pinned) or device memory into device
+ * buffers: the transfers start once all work enqueued on `after_stream` before the call has
+ * finished (the destination may be buffers that work read) and run beside work enqueued there
+ * afterwards. segmla_prefetch_wait makes `stream` wait for the transfers on the device; work
+ * enqueued on it afterwards sees the staged rows. Each prefetch call replaces the previous
+ * one's events. The library allocates no device memory: all buffers are the caller's. */
+typedef struct segmla_copy_range {
+  const void *src;      /* first source row: host (pinned) or device memory */
+  void *dst;            /* first destination row: device memory */
+  int64_t rows;         /* rows to copy, >= 0 */
+  int64_t row_bytes;    /* bytes per row, >= 1 */
+  int64_t src_stride;   /* bytes from one source row to the next, >= row_bytes */
+  int64_t dst_stride;   /* bytes from one destination row to the next, >= row_bytes */
+} segmla_copy_range;
+typedef struct segmla_prefetcher segmla_prefetcher;
+
+/* Create a prefetcher (its stream and events); SEGMLA_E_HIP if the runtime refuses. */
+segmla_status segmla_prefetcher_create(segmla_prefetcher **out);
+/* Enqueue the transfers of n_ranges ranges (SEGMLA_E_SHAPE for negative sizes or strides
+ * below row_bytes, SEGMLA_E_NULL for missing pointers; nothing is enqueued then). */
+segmla_status segmla_prefetch(segmla_prefetcher *pf, const segmla_copy_range *ranges,
+                              int32_t n_ranges, void *after_stream);
+/* Make `stream` wait for the last prefetch's transfers (SEGMLA_E_STATE before any prefetch). */
+segmla_status segmla_prefetch_wait(segmla_prefetcher *pf, void *stream);
+/* Milliseconds the last prefetch's transfers took on the prefetch stream (waits for them). */
+segmla_status segmla_prefetch_elapsed(segmla_prefetcher *pf, float *ms);
+/* Wait for outstanding transfers, then release the stream and events. */
+void segmla_prefetcher_destroy(segmla_prefetcher *pf);
 
 void segmla_plan_destroy(segmla_plan *plan);
 const char *segmla_status_string(int32_t status);

@@ -17,7 +17,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["segmla_host.hip", "k_plan.hip", "k_attn_f32.hip", "k_attn_mfma.hip", "k_merge.hip",
-           "k_epilogue.hip"]
+           "k_epilogue.hip", "prefetch.hip"]
 
 # The attention kernel keeps the score MFMAs in VGPR form (its nope output accumulators live
 # in AGPRs, written by inline assembly), so it selects the VGPR MFMA form explicitly.

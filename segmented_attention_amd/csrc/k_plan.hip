@@ -332,6 +332,64 @@ hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------- another window of a plan
+// The inverse-output-RoPE table of the window's rows [q0, q1) (at t - q0), and the window's
+// ranges in the ascending list of A and in its complement, with the Local heads' key count
+// sum over the window's rows of A of (t + 1). The request's geometry and A are kept.
+__global__ void k_geom_window_rows(int q0, int q1, int d_rope, double base, float2* __restrict__ rowcs) {
+  const int half = d_rope / 2;
+  const int64_t n = (int64_t)(q1 - q0) * half;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / half), k = (int)(i - (int64_t)r * half);
+    double s, c;
+    sincos((double)(q0 + r) * rope_theta(base, k, d_rope), &s, &c);
+    rowcs[i] = make_float2((float)c, (float)s);
+  }
+}
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_window_ranges(const int32_t* __restrict__ alist, int nA,
+                                                       int q0, int q1, int32_t* __restrict__ rng,
+                                                       uint64_t* __restrict__ sum_a) {
+  __shared__ int s_lo, s_hi;
+  __shared__ uint64_t part[4];
+  if (threadIdx.x == 0) {
+    s_lo = lower_bound_i32(alist, nA, q0);
+    s_hi = lower_bound_i32(alist, nA, q1);
+    rng[0] = s_lo;
+    rng[1] = s_hi;
+    rng[2] = q0 - s_lo;  // rows outside A before q0
+    rng[3] = q1 - s_hi;
+  }
+  __syncthreads();
+  uint64_t v = 0;
+  for (int i = s_lo + threadIdx.x; i < s_hi; i += 256) v += (uint64_t)alist[i] + 1;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) *sum_a = part[0] + part[1] + part[2] + part[3];
+}
+
+hipError_t launch_window(const int32_t* alist, int nA, int q0, int q1, int d_rope, double base,
+                         float2* rowcs, int32_t* rng, uint64_t* sum_a, hipStream_t stream) {
+  const int64_t n = (int64_t)(q1 - q0) * (d_rope / 2);
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_geom_window_rows, dim3(blocks), dim3(256), 0, stream, q0, q1, d_rope, base,
+                     rowcs);
+  hipLaunchKernelGGL(k_window_ranges, dim3(1), dim3(256), 0, stream, alist, nA, q0, q1, rng, sum_a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------ work list
 // Tiles sorted by decreasing largest row (their key count), F and G tiles interleaved by a
 // merge-by-rank: each tile's rank = its position in its own descending list plus the number

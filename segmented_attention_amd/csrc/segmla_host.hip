@@ -40,6 +40,10 @@ struct segmla_plan {
   int32_t edge_rows = 0, tail_rows = 0, budget_permille = 0;
   std::vector<int32_t> dirty;  // sorted, unique
   int64_t n_forced = 0, n_cand = 0, K = 0, need = 0, nA = 0;
+  // prefix counts over request rows: forced rows, and candidate rows not forced (a window's
+  // share of A is bounded by them without the Indexer's picks)
+  std::vector<int32_t> cum_forced, cum_free_cand;
+  int32_t split_req = 0;  // the layer's split_keys request (0: the library decides)
   // work decomposition
   int32_t nF = 0, nG = 0, nW = 0, n_split = 1, split_keys = 0, n_blk = 0;
   int32_t n_cu = 256;  // compute units of the device the plan was sized for
@@ -60,6 +64,8 @@ struct segmla_plan {
   // build state
   bool built = false;
   char* ws = nullptr;
+  size_t ws_capacity = 0;  // bytes of the workspace the plan was built into
+  size_t o_tail = 0;       // first byte of the window-dependent part of the workspace
   template <typename X>
   X* at(size_t off) const { return reinterpret_cast<X*>(ws + off); }
 };
@@ -187,6 +193,89 @@ TileMap tile_map(const segmla_plan* p) {
   return m;
 }
 
+// The window-dependent sizing of a plan: its computed rows [q0, q1), the tile streams, the key
+// split, and the workspace tail from o_tail on (the window's RoPE rows, the work list, the split
+// partials and the projection's scratch). Fails with SEGMLA_E_WORKSPACE, leaving the plan as it
+// was, when the tail would end past `capacity` (fewer key splits are tried first: the split only
+// spreads work, it changes no result beyond the summation order).
+segmla_status size_window(segmla_plan* p, int32_t q0, int32_t q1, size_t capacity) {
+  // window rows of A: its forced rows, plus at most min(need, free candidates) Indexer picks
+  const int64_t nf_w = p->cum_forced[q1] - p->cum_forced[q0];
+  const int64_t nc_w = p->cum_free_cand[q1] - p->cum_free_cand[q0];
+  const int64_t L = (int64_t)q1 - q0;
+  const int64_t nA_w = std::min<int64_t>(nf_w + std::min(p->need, nc_w), L);
+  const int64_t nNA_w = L - nf_w;
+  // Work decomposition: qvec tiles of stream F (window rows of A x the full-context heads),
+  // stream G (other window rows x Global heads), optionally split along the key axis, and
+  // stream W (every window row x the sink + window heads, never split). For a window smaller
+  // than the request, the split between F and G depends on the Indexer picks: both are sized
+  // for their largest share.
+  const int64_t qF = nA_w * (p->H - p->HW), qG = nNA_w * p->HG, qW = L * p->HW;
+  const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
+  const int64_t nW = (qW + kTileQ - 1) / kTileQ;
+  if (nF + nG + nW > INT32_MAX / 4) return SEGMLA_E_UNSUPPORTED;
+  const int64_t n_tiles = nF + nG;
+  const int32_t keys = q1;  // the window's rows see keys [0, q1) at most
+  const int64_t ncu = p->n_cu;
+  int32_t sk = p->split_req;
+  if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
+    sk = -1;
+    if (n_tiles > 0 && n_tiles < 2 * ncu && keys > 2048) {
+      // about four workgroups per CU, each with at least 1024 keys; where that leaves CUs idle
+      // (decode: one or two tiles), one workgroup per CU, each with at least 256 keys
+      int64_t want = std::min<int64_t>((4 * ncu + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
+      if (want * n_tiles < ncu)
+        want = std::min<int64_t>((ncu + n_tiles - 1) / n_tiles, (keys + 255) / 256);
+      if (want > 1) sk = (int32_t)((((keys + want - 1) / want) + 63) / 64 * 64);
+    }
+  }
+  const bool thin = p->io_dtype == SEGMLA_BF16 && thin_projection((int)L, p->d_v, p->d_state);
+  const size_t half = (size_t)p->d_rope / 2;
+  for (;;) {
+    const int32_t n_split = (sk > 0 && sk < keys) ? (int32_t)((keys + sk - 1) / sk) : 1;
+    size_t o = p->o_tail;
+    auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
+    const size_t o_rowcs = take(sizeof(float2) * half * (size_t)L);
+    const size_t o_work = take(sizeof(int32_t) * (size_t)n_tiles);
+    size_t o_part_o = 0, o_part_ml = 0, o_zpart = 0, o_wt = 0;
+    if (n_split > 1) {
+      const size_t nvec = (size_t)n_tiles * kTileQ;
+      o_part_o = take(sizeof(float) * (size_t)n_split * nvec * p->d_v);
+      o_part_ml = take(sizeof(float) * 2 * (size_t)n_split * nvec);
+    }
+    // bf16 projection: matrix-vector for small windows, else MFMA tiles reading W in their
+    // operand order from a per-forward copy (forward scratch); grouped state in a small window
+    // (decode): per-head fp32 projections, summed per group
+    if (thin && p->G >= 2) o_zpart = take(sizeof(float) * (size_t)L * p->H * p->d_state);
+    if (p->io_dtype == SEGMLA_BF16 && !thin) o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
+    if (o > capacity) {
+      if (n_split > 1 && sk < keys) {  // fewer, longer splits
+        sk = (int32_t)std::min<int64_t>((int64_t)sk * 2, keys);
+        continue;
+      }
+      return SEGMLA_E_WORKSPACE;
+    }
+    p->q0 = q0;
+    p->q1 = q1;
+    p->nA_w = nA_w;
+    p->nNA_w = nNA_w;
+    p->nF = (int32_t)nF;
+    p->nG = (int32_t)nG;
+    p->nW = (int32_t)nW;
+    p->split_keys = n_split > 1 ? sk : 0;
+    p->n_split = n_split;
+    p->thin = thin;
+    p->o_rowcs = o_rowcs;
+    p->o_work = o_work;
+    p->o_part_o = o_part_o;
+    p->o_part_ml = o_part_ml;
+    p->o_zpart = o_zpart;
+    p->o_wt = o_wt;
+    p->ws_bytes = o;
+    return SEGMLA_OK;
+  }
+}
+
 // Enqueue the plan build into workspace `ws` (validated by the caller) on stream s.
 segmla_status build_impl(segmla_plan* p, char* ws, const uint32_t* indexer_score, hipStream_t s) {
   hipError_t e = hipSuccess;
@@ -195,6 +284,7 @@ segmla_status build_impl(segmla_plan* p, char* ws, const uint32_t* indexer_score
   }
   p->ws = ws;
   p->built = false;
+  p->ws_capacity = p->ws_bytes;
   auto up = [&](size_t off, const void* src, size_t bytes) {
     if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
   };
@@ -511,17 +601,19 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
     }
     for (int32_t r : p->dirty) forced[r] = 1;
     for (int64_t t = std::max<int64_t>(0, (int64_t)T - p->tail_rows); t < T; ++t) forced[t] = 1;
-    int64_t nf = 0, nc = 0, nfc = 0, nf_w = 0, nc_w = 0;  // _w: window rows; nc_w: not forced
+    int64_t nf = 0, nc = 0, nfc = 0;
+    p->cum_forced.assign((size_t)T + 1, 0);
+    p->cum_free_cand.assign((size_t)T + 1, 0);
     for (const SegDesc& d : p->segs) {
       bool cand = d.kind != SEGMLA_SEG_NEW;
       for (int j = 0; j < d.len; ++j) {
         const int64_t t = d.offset + j;
-        bool f = forced[t] != 0, in_w = t >= p->q0 && t < p->q1;
+        bool f = forced[t] != 0;
         nf += f;
         nc += cand;
         nfc += (f && cand);
-        nf_w += (f && in_w);
-        nc_w += (!f && cand && in_w);
+        p->cum_forced[t + 1] = p->cum_forced[t] + (f ? 1 : 0);
+        p->cum_free_cand[t + 1] = p->cum_free_cand[t] + ((!f && cand) ? 1 : 0);
       }
     }
     p->n_forced = nf;
@@ -529,51 +621,13 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
     p->K = ((int64_t)p->budget_permille * nc + 999) / 1000;
     p->need = std::max<int64_t>(0, p->K - nfc);
     p->nA = nf + p->need;
-    // Window rows of A: all its forced rows, plus at most min(need, nc_w) Indexer picks.
-    const int64_t L = (int64_t)p->q1 - p->q0;
-    p->nA_w = std::min<int64_t>(nf_w + std::min(p->need, nc_w), L);
-    p->nNA_w = L - nf_w;
-  }
-
-  // Work decomposition: qvec tiles of stream F (window rows of A x the full-context heads),
-  // stream G (other window rows x Global heads), optionally split along the key axis, and
-  // stream W (every window row x the sink + window heads, never split). For a window smaller
-  // than the request, the split between F and G depends on the Indexer picks: both are sized
-  // for their largest share (above).
-  const int64_t qF = p->nA_w * (p->H - p->HW), qG = p->nNA_w * p->HG;
-  const int64_t qW = ((int64_t)p->q1 - p->q0) * p->HW;
-  const int64_t nF = (qF + kTileQ - 1) / kTileQ, nG = (qG + kTileQ - 1) / kTileQ;
-  const int64_t nW = (qW + kTileQ - 1) / kTileQ;
-  if (nF + nG + nW > INT32_MAX / 4) { delete p; return SEGMLA_E_UNSUPPORTED; }
-  p->nF = (int32_t)nF;
-  p->nG = (int32_t)nG;
-  p->nW = (int32_t)nW;
-  const int64_t n_tiles = nF + nG;
-  int32_t sk = layer->split_keys;
-  const int32_t keys = p->q1;  // the window's rows see keys [0, q1) at most
-  p->n_cu = device_cus();
-  const int64_t ncu = p->n_cu;
-  if (sk == 0) {  // few tiles and a long context: spread the key axis over more workgroups
-    sk = -1;
-    if (n_tiles > 0 && n_tiles < 2 * ncu && keys > 2048) {
-      // about four workgroups per CU, each with at least 1024 keys; where that leaves CUs idle
-      // (decode: one or two tiles), one workgroup per CU, each with at least 256 keys
-      int64_t want = std::min<int64_t>((4 * ncu + n_tiles - 1) / n_tiles, (keys + 1023) / 1024);
-      if (want * n_tiles < ncu)
-        want = std::min<int64_t>((ncu + n_tiles - 1) / n_tiles, (keys + 255) / 256);
-      if (want > 1) sk = (int32_t)((((keys + want - 1) / want) + 63) / 64 * 64);
-    }
-  }
-  if (sk > 0 && sk < keys) {
-    p->split_keys = sk;
-    p->n_split = (int32_t)((keys + sk - 1) / sk);
-  } else {
-    p->split_keys = 0;
-    p->n_split = 1;
   }
   p->n_blk = (T + 1023) / 1024;
+  p->n_cu = device_cus();
+  p->split_req = layer->split_keys;
 
-  // Workspace layout.
+  // Workspace layout: the request's part (geometry, tables, row maps, A) first, then the
+  // window's part (size_window), so that another window of the same request reuses the first.
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
   const size_t half = (size_t)p->d_rope / 2;
@@ -581,7 +635,6 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_lseg = take(sizeof(SegDesc) * p->n_seg);
   p->o_segcs = take(sizeof(float2) * half * p->n_run);
   p->o_stepcs = take(sizeof(float2) * half * p->n_run);
-  p->o_rowcs = take(sizeof(float2) * half * (size_t)(p->q1 - p->q0));  // window rows only
   p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
   p->o_flags = take((size_t)T);
   p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
@@ -598,21 +651,9 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_sum_a = take(sizeof(uint64_t));
   p->o_sel = take(sizeof(uint32_t) * 4);
   p->o_rng = take(sizeof(int32_t) * 4);
-  p->o_work = take(sizeof(int32_t) * (size_t)n_tiles);
-  if (p->n_split > 1) {
-    const size_t nvec = (size_t)n_tiles * kTileQ;
-    p->o_part_o = take(sizeof(float) * (size_t)p->n_split * nvec * p->d_v);
-    p->o_part_ml = take(sizeof(float) * 2 * (size_t)p->n_split * nvec);
-  }
-  // bf16 projection: matrix-vector for small windows, else MFMA tiles reading W in their
-  // operand order from a per-forward copy (forward scratch)
-  p->thin = p->io_dtype == SEGMLA_BF16 && thin_projection(p->q1 - p->q0, p->d_v, p->d_state);
-  // grouped state in a small window (decode): per-head fp32 projections, summed per group
-  if (p->thin && p->G >= 2)
-    p->o_zpart = take(sizeof(float) * (size_t)(p->q1 - p->q0) * p->H * p->d_state);
-  if (p->io_dtype == SEGMLA_BF16 && !p->thin)
-    p->o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
-  p->ws_bytes = o;
+  p->o_tail = o;
+  const segmla_status st2 = size_window(p, p->q0, p->q1, ~size_t(0));
+  if (st2 != SEGMLA_OK) { delete p; return st2; }
   *out_plan = p;
   return SEGMLA_OK;
 }
@@ -661,7 +702,9 @@ segmla_status segmla_plan_build(segmla_plan* p, void* workspace, size_t workspac
   if (workspace_bytes < p->ws_bytes || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return SEGMLA_E_WORKSPACE;
   if (p->need > 0 && !indexer_score) return SEGMLA_E_PROTECT;
-  return build_impl(p, (char*)workspace, indexer_score, (hipStream_t)stream);
+  const segmla_status st = build_impl(p, (char*)workspace, indexer_score, (hipStream_t)stream);
+  if (st == SEGMLA_OK) p->ws_capacity = workspace_bytes;
+  return st;
 }
 
 segmla_status segmla_forward(const segmla_plan* p, const segmla_tensors* t, void* stream) {
@@ -684,15 +727,36 @@ segmla_status segmla_forward_noalloc(segmla_plan* p, const uint32_t* indexer_sco
   // build and run into the shared array; the plan's own workspace state (if it was built with
   // segmla_plan_build) and its profiling are left as they were
   char* const own_ws = p->ws;
+  const size_t own_capacity = p->ws_capacity;
   const bool own_built = p->built, own_prof = p->prof;
   p->prof = false;
   const hipStream_t s = (hipStream_t)stream;
   st = build_impl(p, (char*)ws, indexer_score, s);
   if (st == SEGMLA_OK) st = forward_impl(p, t, s);
   p->ws = own_ws;
+  p->ws_capacity = own_capacity;
   p->built = own_built;
   p->prof = own_prof;
   return st;
+}
+
+segmla_status segmla_plan_set_window(segmla_plan* p, int64_t q_begin, int64_t q_end, void* stream) {
+  if (!p) return SEGMLA_E_NULL;
+  if (!p->built) return SEGMLA_E_STATE;
+  if (q_end == -1) q_end = p->T;
+  if (q_begin < 0 || q_end <= q_begin || q_end > p->T) return SEGMLA_E_SHAPE;
+  const segmla_status st = size_window(p, (int32_t)q_begin, (int32_t)q_end, p->ws_capacity);
+  if (st != SEGMLA_OK) return st;  // the plan is unchanged
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_window(p->at<int32_t>(p->o_alist), (int)p->nA, p->q0, p->q1, p->d_rope,
+                               p->rope_base, p->at<float2>(p->o_rowcs), p->at<int32_t>(p->o_rng),
+                               p->at<uint64_t>(p->o_sum_a), s);
+  if (e == hipSuccess && p->nF + p->nG > 0) e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
+  if (e != hipSuccess) {
+    p->built = false;
+    return SEGMLA_E_HIP;
+  }
+  return SEGMLA_OK;
 }
 
 segmla_status segmla_profile_enable(segmla_plan* p, int32_t enable) {

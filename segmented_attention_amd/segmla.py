@@ -26,7 +26,9 @@ EXPORTED = [
     "segmla_plan_pairs", "segmla_ledger", "segmla_plan_destroy", "segmla_status_string",
     "segmla_abi_version", "segmla_profile_enable", "segmla_profile_read",
     "segmla_plan_create_range", "segmla_plan_create_paged", "segmla_plan_get_info",
-    "segmla_forward_noalloc",
+    "segmla_forward_noalloc", "segmla_plan_set_window", "segmla_prefetcher_create",
+    "segmla_prefetch", "segmla_prefetch_wait", "segmla_prefetch_elapsed",
+    "segmla_prefetcher_destroy",
 ]
 
 NOALLOC_MAX_BYTES = 96 << 20  # SEGMLA_NOALLOC_MAX_BYTES
@@ -72,6 +74,12 @@ class Tensors(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
+class CopyRange(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("row_bytes", ctypes.c_int64), ("src_stride", ctypes.c_int64),
+                ("dst_stride", ctypes.c_int64)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("q_begin", ctypes.c_int64), ("q_end", ctypes.c_int64),
                 ("n_pool", ctypes.c_int64), ("n_protected", ctypes.c_int64),
@@ -108,6 +116,12 @@ def lib():
             "segmla_plan_workspace_bytes": (i32, [P, ctypes.POINTER(ctypes.c_size_t)]),
             "segmla_plan_rows": (i32, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
             "segmla_plan_get_info": (i32, [P, ctypes.POINTER(PlanInfo)]),
+            "segmla_plan_set_window": (i32, [P, i64, i64, P]),
+            "segmla_prefetcher_create": (i32, [ctypes.POINTER(P)]),
+            "segmla_prefetch": (i32, [P, ctypes.POINTER(CopyRange), i32, P]),
+            "segmla_prefetch_wait": (i32, [P, P]),
+            "segmla_prefetch_elapsed": (i32, [P, ctypes.POINTER(ctypes.c_float)]),
+            "segmla_prefetcher_destroy": (None, [P]),
             "segmla_plan_build": (i32, [P, P, ctypes.c_size_t, P, P]),
             "segmla_forward": (i32, [P, ctypes.POINTER(Tensors), P]),
             "segmla_forward_noalloc": (i32, [P, P, ctypes.POINTER(Tensors), P]),
@@ -265,6 +279,11 @@ def segmla_plan_get_info(plan):
     return {name: int(getattr(info, name)) for name, _ in PlanInfo._fields_}
 
 
+def segmla_plan_set_window(plan, q_begin, q_end, stream=None):
+    _check(lib().segmla_plan_set_window(plan, int(q_begin), int(q_end), _stream(stream)),
+           "segmla_plan_set_window")
+
+
 def segmla_plan_build(plan, workspace, indexer_score=None, stream=None):
     import torch
     info = segmla_plan_get_info(plan)
@@ -385,6 +404,68 @@ def segmla_plan_destroy(plan):
         lib().segmla_plan_destroy(plan)
 
 
+class Prefetcher:
+    """Staging of a later layer's artifact rows on the library's own stream (segmla_prefetch*).
+
+    prefetch(pairs): each pair (src, dst) of tensors of one dtype and shape, rows along dim 0,
+    each row contiguous; src on the GPU or in pinned host memory, dst on the GPU. The transfers
+    start after the work already enqueued on `after_stream` (default: torch's current stream)
+    and run beside what is enqueued there next; wait(stream) orders `stream` after them."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib().segmla_prefetcher_create(ctypes.byref(h)), "segmla_prefetcher_create")
+        self.handle = h
+        self._keep = None
+
+    @staticmethod
+    def _range(src, dst):
+        import torch
+        if not (torch.is_tensor(src) and torch.is_tensor(dst)):
+            raise ValueError("prefetch pairs are (src, dst) tensors")
+        if src.dtype != dst.dtype or src.shape != dst.shape or src.dim() < 1:
+            raise ValueError("src and dst must share dtype and shape, got %s %s and %s %s"
+                             % (src.dtype, tuple(src.shape), dst.dtype, tuple(dst.shape)))
+        if dst.device.type != "cuda":
+            raise ValueError("dst must be on the GPU")
+        if src.device.type != "cuda" and not src.is_pinned():
+            raise ValueError("src must be on the GPU or in pinned host memory")
+        rows = src.shape[0]
+        if rows and not (src[0].is_contiguous() and dst[0].is_contiguous()):
+            raise ValueError("each row must be contiguous")
+        es = src.element_size()
+        row_bytes = max(1, src[0].numel() * es) if rows else 1
+        return CopyRange(src.data_ptr(), dst.data_ptr(), rows, row_bytes,
+                         src.stride(0) * es if rows > 1 else row_bytes,
+                         dst.stride(0) * es if rows > 1 else row_bytes)
+
+    def prefetch(self, pairs, after_stream=None):
+        ranges = [self._range(s, d) for s, d in pairs]
+        arr = (CopyRange * max(1, len(ranges)))(*ranges)
+        self._keep = (pairs, arr)  # the tensors stay alive until the next prefetch
+        _check(lib().segmla_prefetch(self.handle, arr, len(ranges), _stream(after_stream)),
+               "segmla_prefetch")
+
+    def wait(self, stream=None):
+        _check(lib().segmla_prefetch_wait(self.handle, _stream(stream)), "segmla_prefetch_wait")
+
+    def elapsed_ms(self):
+        ms = ctypes.c_float()
+        _check(lib().segmla_prefetch_elapsed(self.handle, ctypes.byref(ms)), "segmla_prefetch_elapsed")
+        return float(ms.value)
+
+    def close(self):
+        if self.handle:
+            lib().segmla_prefetcher_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ------------------------------------------------------------------ convenience
 _DT = {"f32": SEGMLA_F32, "bf16": SEGMLA_BF16, "e4m3": SEGMLA_E4M3_B128}
 
@@ -407,9 +488,11 @@ class Plan:
         self.q0, self.q1 = (0, self.T) if q_range is None else (int(q_range[0]), int(q_range[1]))
         self.workspace = None
 
-    def build(self, scores=None, stream=None):
+    def build(self, scores=None, stream=None, min_bytes=0):
+        """Build into a workspace of at least the plan's need, or of min_bytes when larger (room
+        for the larger windows that set_window may move the plan to)."""
         import torch
-        nbytes = segmla_plan_workspace_bytes(self.handle)
+        nbytes = max(segmla_plan_workspace_bytes(self.handle), int(min_bytes))
         if self.workspace is None or self.workspace.numel() < nbytes:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         segmla_plan_build(self.handle, self.workspace, scores, stream)
@@ -422,6 +505,11 @@ class Plan:
             q = q[self.q0:self.q1]
         segmla_forward(self.handle, q, inp["kv"], inp["w"], out, z, inp.get("z_cached"),
                        inp.get("kv_scale"), inp.get("kv_rope"), lse, stream)
+
+    def set_window(self, q_begin, q_end, stream=None):
+        """Another window of the same request on the built plan (segmla_plan_set_window)."""
+        segmla_plan_set_window(self.handle, q_begin, q_end, stream)
+        self.q0, self.q1 = int(q_begin), int(self.T if q_end == -1 else q_end)
 
     def protected(self):
         return segmla_copy_protected(self.handle, self.n_protected)

@@ -442,3 +442,31 @@ def test_noalloc_rejects_oversized_workspace(L):
     finally:
         S.segmla_plan_destroy(big)
         S.segmla_plan_destroy(small)
+
+
+def test_set_window_needs_a_built_plan(L):
+    """segmla_plan_set_window on an unbuilt plan is SEGMLA_E_STATE (before any argument is
+    used), on no plan SEGMLA_E_NULL; nothing is enqueued either way."""
+    p = _create(SMALL_CONFIGS[1])
+    try:
+        assert L.segmla_plan_set_window(p, 0, 5, None) == S.SEGMLA_E_STATE
+        assert L.segmla_plan_set_window(p, 7, 3, None) == S.SEGMLA_E_STATE
+        assert L.segmla_plan_set_window(None, 0, 5, None) == S.SEGMLA_E_NULL
+    finally:
+        S.segmla_plan_destroy(p)
+
+
+def test_prefetch_argument_errors(L):
+    """Prefetch calls fail explicitly: no prefetcher or no output slot is SEGMLA_E_NULL; without
+    a visible GPU the prefetcher cannot get its stream and says so (SEGMLA_E_HIP)."""
+    r = S.CopyRange(16, 32, 1, 8, 8, 8)
+    assert L.segmla_prefetch(None, ctypes.byref(r), 1, None) == S.SEGMLA_E_NULL
+    assert L.segmla_prefetch_wait(None, None) == S.SEGMLA_E_NULL
+    assert L.segmla_prefetcher_create(None) == S.SEGMLA_E_NULL
+    ms = ctypes.c_float()
+    assert L.segmla_prefetch_elapsed(None, ctypes.byref(ms)) == S.SEGMLA_E_NULL
+    L.segmla_prefetcher_destroy(None)
+    import torch
+    if not torch.cuda.is_available():
+        h = ctypes.c_void_p()
+        assert L.segmla_prefetcher_create(ctypes.byref(h)) == S.SEGMLA_E_HIP and not h.value
