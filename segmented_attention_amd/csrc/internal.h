@@ -133,6 +133,13 @@ struct AttnArgs {
   float sigma;            // softmax scale
   int32_t n_sink, win;    // W tiles: key p visible from row t iff p <= t and (p < n_sink or
                           // p >= t - win)
+  // The replacement copy of the rows outside A, done by the full-context attention grid (each
+  // workgroup copies rc_rows consecutive rows of the window's complement list before its tile):
+  // z[t][lhead[l]] = z_cached[pool_row(t)][l] for the HL Local heads; rc_rows = 0: not here.
+  const void* z_cached;   // [n_pool][HL][d_state] bf16
+  void* z;                // [q1 - q0][H][d_state] bf16
+  const int32_t* lhead;   // [HL]
+  int32_t HL, z_chunks, rc_rows;  // z_chunks: 16-byte chunks per head's state vector
 };
 
 // Launchers (defined in the kernel sources), all on `stream`.
@@ -188,6 +195,7 @@ struct EpiArgs {
   // sizes; the actual numbers are in rng)
   int32_t q0, nq, H, HG, HL, nA, nNA, d_nope, d_rope, d_v, d_state, v_has_rope;
   int32_t thin;  // bf16: the matrix-vector projection (else operand-ordered W copy + MFMA tiles)
+  int32_t restore_done;  // the attention grid already copied the rows outside A (bf16)
 };
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
 

@@ -315,6 +315,48 @@ __device__ __forceinline__ void convert_tile_e4m3(char* buf, int wave) {
 }
 static_assert(kKT * (kDN / 16) == 4 * kThreads, "4 code chunks per thread");
 
+// Replacement of the Local heads' state on the window's rows outside A (RedKnot-MLA paper,
+// protected-row paragraph: cached values are replaced, never added to): workgroup `wg` copies
+// rows [wg * rc_rows, (wg + 1) * rc_rows) of the window's complement list, z[t][lhead[l]] =
+// z_cached[pool_row(t)][l] bit for bit. The attention's registers are still free here; each
+// thread keeps kRcBatch 16-byte loads in flight before their stores.
+constexpr int kRcBatch = 8;  // loads in flight per thread (v0 .. v7 below)
+__device__ __forceinline__ void restore_slice(const AttnArgs& a, int wg) {
+  const int na0 = a.map.rng[2], n = a.map.rng[3] - na0;
+  const int r0 = wg * a.rc_rows;
+  const int r1 = min(n, r0 + a.rc_rows);
+  const int per_row = a.HL * a.z_chunks;  // 16-byte chunks of one row's Local state
+  const uint4* zc = (const uint4*)a.z_cached;
+  uint4* z = (uint4*)a.z;
+  for (int r = r0; r < r1; ++r) {
+    const int t = a.map.nalist[na0 + r];
+    const SegDesc sd = a.seg[a.seg_of_row[t]];
+    const uint4* src = zc + (sd.pool_row + (t - sd.offset)) * a.HL * a.z_chunks;
+    uint4* dst = z + (int64_t)(t - a.q0) * a.map.H * a.z_chunks;
+    // kRcBatch loads in flight per thread (named values: they stay in registers), then stores
+    auto ld = [&](int e) __attribute__((always_inline)) { return src[min(e, per_row - 1)]; };
+    auto st = [&](int e, const uint4& v) __attribute__((always_inline)) {
+      if (e < per_row) {
+        const int l = e / a.z_chunks;
+        dst[a.lhead[l] * a.z_chunks + (e - l * a.z_chunks)] = v;
+      }
+    };
+    for (int e0 = threadIdx.x; e0 < per_row; e0 += kThreads * kRcBatch) {
+      const uint4 v0 = ld(e0), v1 = ld(e0 + kThreads), v2 = ld(e0 + 2 * kThreads),
+                  v3 = ld(e0 + 3 * kThreads), v4 = ld(e0 + 4 * kThreads), v5 = ld(e0 + 5 * kThreads),
+                  v6 = ld(e0 + 6 * kThreads), v7 = ld(e0 + 7 * kThreads);
+      st(e0, v0);
+      st(e0 + kThreads, v1);
+      st(e0 + 2 * kThreads, v2);
+      st(e0 + 3 * kThreads, v3);
+      st(e0 + 4 * kThreads, v4);
+      st(e0 + 5 * kThreads, v5);
+      st(e0 + 6 * kThreads, v6);
+      st(e0 + 7 * kThreads, v7);
+    }
+  }
+}
+
 }  // namespace
 
 // WIN: the W tiles (sink + window heads), one workgroup per tile in order: the key walk
@@ -330,6 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hf = lane >> 5;
+  if (!WIN && a.rc_rows > 0) restore_slice(a, blockIdx.x);  // every workgroup, before any exit
   const int rank = WIN ? (int)blockIdx.x : (int)blockIdx.x / a.n_split;
   const int split = WIN ? 0 : (int)blockIdx.x % a.n_split;
   const int tile = WIN ? a.map.nF + a.map.nG + rank : a.work[rank];

@@ -568,7 +568,7 @@ hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
       else
         hipLaunchKernelGGL(k_project_bf16<false>, dim3((unsigned)blocks), dim3(256), lds, stream, e);
     }
-    if (!grouped && e.HL > 0 && e.nNA > 0)
+    if (!grouped && e.HL > 0 && e.nNA > 0 && !e.restore_done)
       hipLaunchKernelGGL(k_restore_copy<uint4>, dim3(e.nNA), dim3(256), 0, stream, e,
                          e.d_state * 2 / 16);
   }

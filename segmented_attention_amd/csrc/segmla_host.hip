@@ -360,6 +360,17 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   a.sigma = p->sigma;
   a.n_sink = p->n_sink;
   a.win = p->window;
+  // the replacement copy rides on the full-context attention grid (bf16 per-head state)
+  const int64_t n_wg = (int64_t)(p->nF + p->nG) * p->n_split;
+  const bool fuse_rc = p->io_dtype == SEGMLA_BF16 && p->G < 2 && p->HL > 0 && p->nNA_w > 0 && n_wg > 0;
+  a.z_cached = t->z_cached;
+  a.z = t->z;
+  a.lhead = p->at<int32_t>(p->o_lhead);
+  a.HL = p->HL;
+  a.z_chunks = p->d_state * 2 / 16;
+  // (a grid too small for the rows keeps the separate copy kernel: at most 64 rows per workgroup)
+  const int64_t rc_rows = fuse_rc ? (p->nNA_w + n_wg - 1) / n_wg : 0;
+  a.rc_rows = rc_rows <= 64 ? (int32_t)rc_rows : 0;
   hipError_t e = hipSuccess;
   segmla_plan* pm = const_cast<segmla_plan*>(p);  // profiling state only
   if (p->prof) {
@@ -372,6 +383,7 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
     aw.n_split = 1;
     aw.split_keys = 0;
     aw.part_o = aw.part_ml = nullptr;
+    aw.rc_rows = 0;
     e = launch_attn_window(aw, p->kv_dtype, p->v_has_rope, s);
   }
   if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
@@ -383,6 +395,7 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   ep.w = t->w;
   ep.wt = (p->io_dtype == SEGMLA_BF16 && !p->thin) ? p->at<void>(p->o_wt) : nullptr;
   ep.thin = p->thin ? 1 : 0;
+  ep.restore_done = a.rc_rows > 0 ? 1 : 0;
   ep.z_cached = t->z_cached;
   ep.z = t->z;
   ep.rowcs = p->at<float2>(p->o_rowcs);
