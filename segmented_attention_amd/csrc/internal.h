@@ -158,6 +158,9 @@ hipError_t launch_window(const int32_t* alist, int nA, int q0, int q1, int d_rop
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
 // the W tiles (sink + window heads): one workgroup per tile, outputs written directly
 hipError_t launch_attn_window(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);
+// bf16 latent, tiles of at most 64 query vectors (one-row windows), split key ranges: two wave
+// sets take alternate key tiles and merge at the end
+hipError_t launch_attn_decode(const AttnArgs& a, int v_has_rope, hipStream_t stream);
 hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
                             int d, void* out, int out_dtype, float* lse, hipStream_t stream);

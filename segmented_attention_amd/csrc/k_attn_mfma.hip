@@ -635,9 +635,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     if constexpr (FP8) {  // tile i+1 arrived raw: convert it in place
       if (v1) convert_tile_e4m3(lds + nb * kTileBytes, wave);
     }
-    if (__builtin_expect(v2, 1)) issue(w2, fb);
+    // a new segment's query rotation reads the stored query and the RoPE table before the next
+    // copy is issued: vector loads retire in order, so behind the copy they would wait for the
+    // whole tile to land
     if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
       rotate_q(w1.seg);
+    if (__builtin_expect(v2, 1)) issue(w2, fb);
     // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3);
     // WIN: also the keys below the query vector's window that are not sink keys
     if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT) ||
@@ -830,6 +833,462 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
   if (a.lse && hf == 0) a.lse[(int64_t)(t - a.q0) * a.map.H + h] = (m_run + log2f(l_tot)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------- decode tiles
+// Split key ranges of tiles that hold at most 64 query vectors (a one-row window: one row x at
+// most 64 heads), the same per-key arithmetic as above. In k_attn_mfma such a tile would leave
+// two of its four waves without a real query vector. Here the workgroup's four waves form two
+// sets over the same 64 vectors (wave & 1 picks the 32-vector group): the key range is walked
+// in 32-key tiles as above, set 0 taking the even tiles and set 1 the odd ones, so a step
+// consumes two tiles, each in its own LDS buffer, while the next step's two are copied into the
+// other two (four buffers, two tiles in flight per workgroup). Each set keeps its own running
+// softmax and output, in its own RoPE frame; at the end set 1's (max, sum, output) go through
+// LDS and set 0 merges them by the stable log-sum-exp rule (RedKnot-MLA paper, relocation
+// paragraph) before the partial or final stores of k_attn_mfma.
+constexpr int kDecBuf = 4;
+#ifndef SEGMLA_DEC_QREG
+#define SEGMLA_DEC_QREG 24
+#endif
+#ifndef SEGMLA_DEC_QK
+#define SEGMLA_DEC_QK 3
+#endif
+#ifndef SEGMLA_DEC_PV
+#define SEGMLA_DEC_PV 4
+#endif
+constexpr int kDecQReg = SEGMLA_DEC_QREG;              // query steps 0..kDecQReg-1 in registers
+constexpr int kDecQkDepth = SEGMLA_DEC_QK;
+constexpr int kDecPvDepth = SEGMLA_DEC_PV;
+constexpr int kDecQSlot = 2 * 64 * 16;                 // steps kDecQReg..31: one slot per vector group
+constexpr int kDecQBase = kDecBuf * kTileBytes;        // 147456
+constexpr int kDecLds = kDecQBase + (32 - kDecQReg) * kDecQSlot;
+constexpr int kDecLdsAlloc = kDecLds;
+static_assert(kDecLdsAlloc <= 160 * 1024, "LDS budget");
+static_assert(2 * 64 * 18 * 16 * 4 <= kDecQBase, "set 1's outputs fit in the tile buffers");
+static_assert(2 * 64 * 8 <= (32 - kDecQReg) * kDecQSlot, "set 1's (max, sum) fit in the slots");
+
+template <bool VROPE>
+__global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(256))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int set = wave >> 1, grp = wave & 1;
+  const int col = lane & 31, hf = lane >> 5;
+  const int rank = (int)blockIdx.x / a.n_split, split = (int)blockIdx.x % a.n_split;
+  // keys up to the window's last row (the row itself for one-row windows): the key range needs
+  // no load, so the first copies can go out after two scalar loads (the work-list entry and the
+  // split's first segment; scalar loads do not queue behind vector-memory copies)
+  const int t_max = a.map.q0 + a.map.nq - 1;
+  int k_lo = 0, k_hi = t_max + 1;
+  if (a.n_split > 1) {
+    k_lo = split * a.split_keys;
+    k_hi = min(k_hi, k_lo + a.split_keys);
+  }
+  if (k_lo >= k_hi) return;  // uniform over the workgroup
+  typedef const __attribute__((address_space(4))) int32_t cint_t;
+  const int tile = ((cint_t*)a.work)[rank];
+  const int seg_lo = ((cint_t*)a.seg_of_row)[k_lo];
+  if (tile < 0 || tile >= a.map.nF + a.map.nG) return;  // uniform, before any copy is issued
+  cseg_t* const sg = (cseg_t*)a.seg;
+  // the tile's query vectors: set after the first copies are issued
+  int t = -1, h = 0;
+  bool valid = false;
+  const __bf16* qrow = nullptr;
+
+  const float qk_scale = a.sigma * kLog2e;
+  // B operand of S^T = K Q^T, step s: lane holds Q[qvec col][16 s + 8 hf + 0..7]; steps below
+  // kDecQReg and the RoPE steps 32..35 (rotated per segment) in registers, steps kDecQReg..31 in
+  // LDS slots shared by the two sets
+  bf16x8 qf[kDecQReg], qr[4] = {};
+  const char* const qslot = lds + kDecQBase + grp * 1024 + lane * 16;  // + (s - kDecQReg) * kDecQSlot
+  constexpr int NF = VROPE ? 18 : 16;
+  constexpr int NR = NF - 16;
+  floatx16 acc[16], accr[NR > 0 ? NR : 1];
+#pragma unroll
+  for (int f = 0; f < 16; ++f)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[f][i] = 0.f;
+#pragma unroll
+  for (int f = 0; f < NR; ++f)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) accr[f][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, m_thr = -INFINITY;
+  const int half_r = a.d_rope / 2;
+
+  // per-lane LDS offsets inside a tile buffer (as in k_attn_mfma)
+  const int fcol = fn(col), rcol = fr(col);
+  const int kx0 = (col * kNRow + 16 * (hf ^ (fcol & 1))) | (16 * (fcol & 14));
+  const int krx0 = (kRBase + col * kRRow + 16 * (hf ^ (rcol & 1))) | (16 * (rcol & 6));
+  const int G = lane >> 4, jj = lane & 15;
+  const int cl = 2 * (G & 1) + ((jj & 3) >> 1);
+  const int vrow = 4 * (G >> 1) + (jj >> 2);
+  const int vx0 = (vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1))) | (64 * (jj >> 2));
+  const int vx1 = (vrow * kNRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2))) | (64 * (jj >> 2));
+  const int vrx0 = (kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ (G >> 1))) | (64 * ((jj >> 3) & 1));
+  const int vrx1 = (kRBase + vrow * kRRow + 8 * (jj & 1) + 16 * (cl ^ ((G >> 1) | 2))) | (64 * ((jj >> 3) & 1));
+
+  // ---- tile sequence over [k_lo, k_hi), segment-aligned (every wave walks all of it)
+  auto first_tile = [&](TileIt& c) __attribute__((always_inline)) {
+    const int lo = seg_lo;
+    c.seg = lo;
+    const int off = sg[lo].offset, len = sg[lo].len;
+    c.pos0 = k_lo;
+    c.pend = min(off + len, k_hi);
+    c.nval = min(kKT, c.pend - k_lo);
+    c.src = (sg[lo].pool_row + (k_lo - off)) * kRowBytes;
+    c.v = 1;
+  };
+  auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) {
+    nx.v = 0;  // no next tile: a fully masked dummy (see the step loop)
+    nx.seg = c.seg;
+    nx.nval = 0;
+    nx.pos0 = c.pos0;
+    nx.pend = c.pend;
+    nx.src = c.src;
+    if (!c.v) return;
+    if (c.pos0 + kKT < c.pend) {
+      nx.v = 1;
+      nx.seg = c.seg;
+      nx.pos0 = c.pos0 + kKT;
+      nx.pend = c.pend;
+      nx.nval = min(kKT, c.pend - nx.pos0);
+      nx.src = c.src + kKT * kRowBytes;
+      return;
+    }
+    if (c.seg + 1 >= a.n_seg) return;
+    const int off = sg[c.seg + 1].offset;  // segments are contiguous: off == c.pend
+    if (off >= k_hi) return;
+    nx.v = 1;
+    nx.seg = c.seg + 1;
+    nx.pos0 = off;
+    nx.pend = min(off + sg[c.seg + 1].len, k_hi);
+    nx.nval = min(kKT, nx.pend - off);
+    nx.src = sg[c.seg + 1].pool_row * kRowBytes;
+  };
+  auto issue = [&](const TileIt& c, int b) __attribute__((always_inline)) {
+    char* buf = lds + b * kTileBytes;
+    if (__builtin_expect(c.nval == kKT, 1))
+      load_tile_bf16_full(buf, (const char*)a.kv + c.src, wave);
+    else
+      load_tile_bf16(buf, (const char*)a.kv + c.src, c.nval, wave);
+  };
+  // q^r <- R(-rot_i) q^r from the stored query (registers)
+  auto rotate_q = [&](int seg) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 32; s < 36; ++s) {
+      uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
+      if (!valid) v = make_uint4(0, 0, 0, 0);
+      const bf16x8 x = *(bf16x8*)&v;
+      bf16x8 y;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int k = 8 * (s - 32) + 4 * hf + p;
+        const float2 cs = a.segcs[seg * half_r + k];
+        const float x0 = bf2f(x[2 * p]), x1 = bf2f(x[2 * p + 1]);
+        y[2 * p] = (__bf16)(x0 * cs.x + x1 * cs.y);
+        y[2 * p + 1] = (__bf16)(-x0 * cs.y + x1 * cs.x);
+      }
+      qr[s - 32] = y;
+    }
+  };
+  auto frame_step = [&](int seg, float sgn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < NR; ++f) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const int k = 16 * f + 4 * (i >> 2) + 2 * hf + ((i & 3) >> 1);
+        float2 cs = a.segcs[seg * half_r + k];
+        cs.y *= sgn;
+        const float x = accr[f][i], y = accr[f][i + 1];
+        accr[f][i] = fmaf(x, cs.x, -(y * cs.y));
+        accr[f][i + 1] = fmaf(x, cs.y, y * cs.x);
+      }
+      asm volatile("" ::: "memory");
+    }
+  };
+  auto qk_reads = [&](uint32_t kt, uint32_t krt, int k, bf16x8& kf) __attribute__((always_inline)) {
+    if (k < 32) {
+      const int s8 = k >> 3, sl = k & 7;
+      kf = *(const lds_bf16x8*)(size_t)((kt ^ (32 * sl)) + 256 * s8);
+    } else {
+      kf = *(const lds_bf16x8*)(size_t)(krt ^ (32 * (k - 32)));
+    }
+  };
+
+  // ---- a new segment for this set: the output moves to its RoPE frame, R(-rot_new) R(rot_old)
+  // through the request phase (the set may skip the segment the other set took), and the query
+  // is rotated. Called before the step's copies are issued: vector loads retire in order, so
+  // behind the copies these table and query reads would wait for both tiles to land.
+  int cur_seg = -1;  // segment whose RoPE frame the query and the output are in
+  auto prepare = [&](const TileIt& w) __attribute__((always_inline)) {
+    if (__builtin_expect(w.v && w.seg != cur_seg, 0)) {
+      if (cur_seg < 0 || sg[w.seg].frame != sg[cur_seg].frame) {
+        if (VROPE && cur_seg >= 0) {
+          frame_step(cur_seg, 1.f);
+          frame_step(w.seg, -1.f);
+        }
+        rotate_q(w.seg);
+      }
+      cur_seg = w.seg;
+    }
+  };
+  // ---- one key tile of this set: scores, mask, online softmax, O^T += V^T P^T
+  auto process = [&](const TileIt& w, const char* buf) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    floatx16 S;
+    {
+      uint32_t kt = lds_addr(buf) + kx0, krt = lds_addr(buf) + krx0;
+      asm volatile("" : "+v"(kt), "+v"(krt));
+      bf16x8 ring[kDecQkDepth], qring[kDecQkDepth];
+#pragma unroll
+      for (int k = 0; k < kDecQkDepth; ++k) {
+        qk_reads(kt, krt, k, ring[k]);
+        if (k >= kDecQReg && k < 32) qring[k] = *(const bf16x8*)(qslot + (k - kDecQReg) * kDecQSlot);
+      }
+#pragma unroll
+      for (int k = 0; k < kQSteps; ++k) {
+        const bf16x8 kf = ring[k % kDecQkDepth];
+        const bf16x8 qv = k < kDecQReg ? qf[k < kDecQReg ? k : 0]
+                                       : (k < 32 ? qring[k % kDecQkDepth] : qr[k < 32 ? 0 : k - 32]);
+        if (k + kDecQkDepth < kQSteps) {
+          const int kn = k + kDecQkDepth;
+          qk_reads(kt, krt, kn, ring[k % kDecQkDepth]);
+          if (kn >= kDecQReg && kn < 32)
+            qring[k % kDecQkDepth] = *(const bf16x8*)(qslot + (kn - kDecQReg) * kDecQSlot);
+        }
+        if (k == 0) {
+          const floatx16 zero = {};
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, zero, 0, 0, 0);
+        } else {
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, S, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // causal / range mask: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3)
+    const int nval = w.v ? w.nval : 0;  // no tile: every key masked
+    if (__builtin_expect(__ballot((w.pos0 + kKT - 1 > t) || (nval < kKT)) != 0ull, 0)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int k = 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (w.pos0 + k > t || k >= nval) S[i] = -INFINITY;
+      }
+    }
+    // online softmax (log2 domain, lazy wave-uniform rescale)
+    float mx = max3r(max3r(S[0], S[1], S[2]), S[3], S[4]);
+    mx = max3r(max3r(mx, S[5], S[6]), S[7], S[8]);
+    mx = max3r(max3r(mx, S[9], S[10]), S[11], S[12]);
+    mx = max3r(max3r(mx, S[13], S[14]), S[15], S[15]) * qk_scale;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = max3r(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+    }
+    float alpha = 1.f;
+    const bool resc = __ballot(mx > m_thr) != 0ull;
+    if (__builtin_expect(resc, 0)) {
+      const float m_new = fmaxf(m_run, mx);
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      m_thr = m_run + kRescaleThreshold;
+      l_run *= alpha;
+    }
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(S[i], qk_scale, -m_use));
+    uint32_t pw[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pw[j] = pack_bf16(p[2 * j], p[2 * j + 1]);
+      lsum += p[2 * j] + p[2 * j + 1];
+    }
+    l_run += lsum;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 pw0 = {pw[0], pw[1], pw[2], pw[3]}, pw1 = {pw[4], pw[5], pw[6], pw[7]};
+    const bf16x8 pf[2] = {__builtin_bit_cast(bf16x8, pw0), __builtin_bit_cast(bf16x8, pw1)};
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_expect(resc, 0)) {
+#pragma unroll
+      for (int f = 0; f < 16; ++f) rescale_agpr(acc[f], alpha);
+#pragma unroll
+      for (int f = 0; f < NR; ++f) accr[f] *= alpha;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const uint32_t bb = lds_addr(buf);
+      uint32_t vt0 = bb + vx0, vt1 = bb + vx1, vrt0 = bb + vrx0, vrt1 = bb + vrx1;
+      asm volatile("" : "+v"(vt0), "+v"(vt1), "+v"(vrt0), "+v"(vrt1));
+      auto tr = [](uint32_t addr) __attribute__((always_inline)) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)addr);
+      };
+      auto vread = [&](int n, bf16x4& lo, bf16x4& hi) __attribute__((always_inline)) {
+        const int u = n / NF, f = n % NF;
+        if (f < 16) {
+          const int f4 = f >> 2, fl = f & 3;
+          lo = tr((vt0 ^ (64 * fl)) + 256 * f4 + 16384 * u);
+          hi = tr((vt1 ^ (64 * fl)) + 8192 + 256 * f4 + 16384 * u);
+        } else {
+          lo = tr((vrt0 ^ (64 * (f - 16))) + 2048 * u);
+          hi = tr((vrt1 ^ (64 * (f - 16))) + 1024 + 2048 * u);
+        }
+      };
+      bf16x4 lo[kDecPvDepth], hi[kDecPvDepth];
+#pragma unroll
+      for (int n = 0; n < kDecPvDepth; ++n) vread(n, lo[n], hi[n]);
+#pragma unroll
+      for (int n = 0; n < 2 * NF; ++n) {
+        const int r = n % kDecPvDepth;
+        const bf16x8 vt = {lo[r][0], lo[r][1], lo[r][2], lo[r][3], hi[r][0], hi[r][1], hi[r][2], hi[r][3]};
+        if (n + kDecPvDepth < 2 * NF) vread(n + kDecPvDepth, lo[r], hi[r]);
+        const int f = n % NF;
+        if (f < 16) {
+          if (n == 0) mfma_agpr<true>(acc[f], vt, pf[n / NF]);
+          else mfma_agpr<false>(acc[f], vt, pf[n / NF]);
+        } else {
+          accr[f - 16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pf[n / NF], accr[f - 16], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: the first step's two tiles in flight, then the query and this set's first
+  // segment (their loads retire after the copies), all behind one wait
+  TileIt a0, b0, a1, b1;
+  first_tile(a0);
+  advance(a0, b0);
+  issue(a0, 0);
+  if (b0.v) issue(b0, 1);
+  valid = tile_qvec(a.map, tile, grp * 32 + col, t, h);
+  if (!valid) t = -1;
+  qrow = (const __bf16*)a.q + ((int64_t)(valid ? t - a.q0 : 0) * a.map.H + h) * kD;
+#pragma unroll
+  for (int s = 0; s < kDecQReg; ++s) {
+    uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
+    if (!valid) v = make_uint4(0, 0, 0, 0);
+    qf[s] = *(bf16x8*)&v;
+  }
+  if (set == 0) {
+#pragma unroll
+    for (int s = kDecQReg; s < 32; ++s) {
+      uint4 v = *(const uint4*)(qrow + 16 * s + 8 * hf);
+      if (!valid) v = make_uint4(0, 0, 0, 0);
+      *(uint4*)(lds + kDecQBase + (s - kDecQReg) * kDecQSlot + grp * 1024 + lane * 16) = v;
+    }
+  }
+  {
+    TileIt w;
+    w.v = set ? b0.v : a0.v;
+    w.seg = set ? b0.seg : a0.seg;
+    w.nval = w.pos0 = w.pend = 0;
+    w.src = 0;
+    prepare(w);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // One step per pair of tiles: (a0, b0) resident in buffers cb, cb + 1 (set 0 takes a0, set 1
+  // b0), (a1, b1) copied into the other two; then the roles swap.
+  int cb = 0;
+  for (;;) {
+    const int ob = 2 - cb;
+    TileIt w;  // this set's tile (field by field: no whole-descriptor copies)
+    w.v = set ? b0.v : a0.v;
+    w.seg = set ? b0.seg : a0.seg;
+    w.nval = set ? b0.nval : a0.nval;
+    w.pos0 = set ? b0.pos0 : a0.pos0;
+    w.pend = 0;
+    w.src = 0;
+    prepare(w);
+    advance(b0, a1);
+    advance(a1, b1);
+    if (a1.v) issue(a1, ob);
+    if (b1.v) issue(b1, ob + 1);
+    // a set without a tile in this step (the range's last, odd tile) runs the same code on the
+    // other set's buffer with every key masked: no state changes, and the accumulator MFMAs
+    // stay unconditional (a conditional call made the register allocator shuffle them)
+    process(w, lds + (cb + (w.v ? set : 0)) * kTileBytes);
+    // next step's tiles have landed, and every wave is done with this step's buffers
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!a1.v) break;
+    a0.v = a1.v; a0.seg = a1.seg; a0.nval = a1.nval; a0.pos0 = a1.pos0; a0.pend = a1.pend; a0.src = a1.src;
+    b0.v = b1.v; b0.seg = b1.seg; b0.nval = b1.nval; b0.pos0 = b1.pos0; b0.pend = b1.pend; b0.src = b1.src;
+    cb = ob;
+  }
+  settle_agpr(acc);
+  auto tile_vgpr = [&](int f) __attribute__((always_inline)) -> floatx16 {
+    floatx16 x = f < 16 ? acc[f < 16 ? f : 0] : accr[f < 16 ? 0 : f - 16];
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  if (VROPE && cur_seg >= 0) frame_step(cur_seg, 1.f);  // restore the request phase
+  // ---- set 1 hands (max, sum, output) to set 0 through LDS (the tile buffers are free)
+  float* const xo = (float*)lds + grp * (64 * 18 * 16) + lane * 4;  // + f * 1024 + q * 256 floats
+  float* const xml = (float*)(lds + kDecQBase) + (grp * 64 + lane) * 2;
+  if (set == 1) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const floatx16 x = tile_vgpr(f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(xo + f * 1024 + q * 256) = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+    }
+    xml[0] = m_run;
+    xml[1] = l_run;
+  }
+  __syncthreads();
+  if (set == 1) return;
+  const float m1 = xml[0], l1 = xml[1];
+  const float mm = fmaxf(m_run, m1);
+  const float w0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mm);
+  const float w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float l_tot = pair_sum(l_run * w0 + l1 * w1);
+  auto merged = [&](int f) __attribute__((always_inline)) -> floatx16 {
+    floatx16 x = tile_vgpr(f);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 y = *(const float4*)(xo + f * 1024 + q * 256);
+      x[4 * q] = fmaf(x[4 * q], w0, y.x * w1);
+      x[4 * q + 1] = fmaf(x[4 * q + 1], w0, y.y * w1);
+      x[4 * q + 2] = fmaf(x[4 * q + 2], w0, y.z * w1);
+      x[4 * q + 3] = fmaf(x[4 * q + 3], w0, y.w * w1);
+    }
+    return x;
+  };
+  const int d_v = a.d_v;
+  if (!valid) return;
+  if (a.n_split > 1) {
+    const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
+    const int64_t v = (int64_t)tile * kTileQ + grp * 32 + col;
+    float* po = a.part_o + ((int64_t)split * nvec + v) * d_v;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const floatx16 x = merged(f);
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *(float4*)(po + 32 * f + 8 * (i >> 2) + 4 * hf) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+    if (hf == 0) {
+      float* pm = a.part_ml + ((int64_t)split * nvec + v) * 2;
+      pm[0] = mm == -INFINITY ? -INFINITY : mm * kLn2;
+      pm[1] = l_tot;
+    }
+    return;
+  }
+  const float inv = 1.f / l_tot;
+  __bf16* o = (__bf16*)a.out + ((int64_t)(t - a.q0) * a.map.H + h) * d_v;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const floatx16 x = merged(f);
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      bf16x4 y = {(__bf16)(x[i] * inv), (__bf16)(x[i + 1] * inv), (__bf16)(x[i + 2] * inv),
+                  (__bf16)(x[i + 3] * inv)};
+      *(bf16x4*)(o + 32 * f + 8 * (i >> 2) + 4 * hf) = y;
+    }
+  }
+  if (a.lse && hf == 0) a.lse[(int64_t)(t - a.q0) * a.map.H + h] = (mm + log2f(l_tot)) * kLn2;
+}
+
 namespace {
 template <bool VROPE, bool FP8, bool WIN>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t stream) {
@@ -855,6 +1314,25 @@ hipError_t launch_any(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream
   return fp8 ? launch_mfma<false, true, WIN>(a, stream) : launch_mfma<false, false, WIN>(a, stream);
 }
 }  // namespace
+
+namespace {
+template <bool VROPE>
+hipError_t launch_dec(const AttnArgs& a, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)k_attn_dec<VROPE>, hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsAlloc);
+  if (attr != hipSuccess) return attr;
+  const int64_t blocks = (int64_t)(a.map.nF + a.map.nG) * a.n_split;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_attn_dec<VROPE>), dim3((unsigned)blocks), dim3(kThreads), kDecLdsAlloc,
+                     stream, a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attn_decode(const AttnArgs& a, int v_has_rope, hipStream_t stream) {
+  return v_has_rope ? launch_dec<true>(a, stream) : launch_dec<false>(a, stream);
+}
 
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream) {
   if (kv_dtype == 0) return launch_attn_f32(a, stream);

@@ -360,9 +360,14 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   a.sigma = p->sigma;
   a.n_sink = p->n_sink;
   a.win = p->window;
+  // one-row windows (decode) with a key split: at most 64 query vectors per tile, which the
+  // decode kernel runs on all four waves (two sets over alternate key tiles)
+  const bool dec = p->kv_dtype == SEGMLA_BF16 && p->n_split > 1 && p->q1 - p->q0 == 1 &&
+                   p->H - p->HW <= 64 && p->HG <= 64;
   // the replacement copy rides on the full-context attention grid (bf16 per-head state)
   const int64_t n_wg = (int64_t)(p->nF + p->nG) * p->n_split;
-  const bool fuse_rc = p->io_dtype == SEGMLA_BF16 && p->G < 2 && p->HL > 0 && p->nNA_w > 0 && n_wg > 0;
+  const bool fuse_rc = !dec && p->io_dtype == SEGMLA_BF16 && p->G < 2 && p->HL > 0 && p->nNA_w > 0 &&
+                       n_wg > 0;
   a.z_cached = t->z_cached;
   a.z = t->z;
   a.lhead = p->at<int32_t>(p->o_lhead);
@@ -377,7 +382,8 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
     if (flush_profile(pm) != hipSuccess || hipEventRecord(p->ev[0], s) != hipSuccess)
       return SEGMLA_E_HIP;
   }
-  if (p->nF + p->nG > 0) e = launch_attn(a, p->kv_dtype, p->v_has_rope, s);
+  if (p->nF + p->nG > 0)
+    e = dec ? launch_attn_decode(a, p->v_has_rope, s) : launch_attn(a, p->kv_dtype, p->v_has_rope, s);
   if (e == hipSuccess && p->nW > 0) {  // sink + window heads: their own grid, never split
     AttnArgs aw = a;
     aw.n_split = 1;

@@ -73,7 +73,7 @@ def test_attention_kernel_asm_invariants(tmp_path):
     funcs = {}
     name = None
     for line in text.splitlines():
-        m = re.match(r"^(_ZN6segmla11k_attn_mfma\S*):", line)
+        m = re.match(r"^(_ZN6segmla(?:11k_attn_mfma|10k_attn_dec)\S*):", line)
         if m:
             name = m.group(1)
             funcs[name] = []
@@ -83,7 +83,8 @@ def test_attention_kernel_asm_invariants(tmp_path):
                 name = None
                 continue
             funcs[name].append(line)
-    assert len(funcs) == 8, sorted(funcs)  # (v_has_rope, E4M3, sink + window) instantiations
+    # (v_has_rope, E4M3, sink + window) instantiations, and the decode kernel's two
+    assert len(funcs) == 10, sorted(funcs)
 
     for fname, lines in funcs.items():
         # no calls (s_setpc alone is also the far-jump form of a branch in a large kernel)
@@ -103,7 +104,7 @@ def test_attention_kernel_asm_invariants(tmp_path):
     # kernel descriptors: AGPRs reserved for the accumulators
     for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
         kname, body = m.group(1), m.group(2)
-        if "k_attn_mfma" not in kname:
+        if "k_attn_mfma" not in kname and "k_attn_dec" not in kname:
             continue
         nfv = int(re.search(r"\.amdhsa_next_free_vgpr (\d+)", body).group(1))
         acc = int(re.search(r"\.amdhsa_accum_offset (\d+)", body).group(1))
@@ -186,8 +187,8 @@ def _valu_mfma_hazards(lines, window=2):
 
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not found")
 def test_assembly_mfmas_without_nop_read_no_fresh_valu_result(tmp_path):
-    funcs = {k: v for k, v in _functions(_asm(tmp_path)).items() if "k_attn_mfma" in k}
-    assert len(funcs) == 8, sorted(funcs)  # (v_has_rope, E4M3, sink + window) instantiations
+    funcs = {k: v for k, v in _functions(_asm(tmp_path)).items() if "k_attn_mfma" in k or "k_attn_dec" in k}
+    assert len(funcs) == 10, sorted(funcs)  # 8 prefill instantiations + 2 decode
     checked = 0
     for fname, lines in funcs.items():
         bad = _valu_mfma_hazards(lines)
@@ -211,3 +212,18 @@ def test_hazard_checker_flags_a_fresh_valu_write():
     assert not _valu_mfma_hazards(other)
     assert _valu_mfma_hazards(label)
     assert not _valu_mfma_hazards(nop)
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not found")
+def test_decode_kernel_keeps_everything_in_registers(tmp_path):
+    """The decode kernel holds 256 accumulator values, 29 query steps and its operand rings per
+    lane: any private (scratch) memory would mean spilled accumulators or query fragments."""
+    text = _asm(tmp_path)
+    found = 0
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+        if "k_attn_dec" not in m.group(1):
+            continue
+        found += 1
+        priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2)).group(1))
+        assert priv == 0, (m.group(1), priv)
+    assert found == 2, found
