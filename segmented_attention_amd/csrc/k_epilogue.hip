@@ -386,10 +386,11 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
   const int n_here = min(kThinRows, et.n_rows - et.r0);
   if (n_here <= 0) return;  // uniform: a tile past the window's rows of its list
   const int tid = threadIdx.x, d_v = e.d_v;
-  if (tid < kThinRows) row_id[tid] = epi_row(et, et.r0 + min(tid, n_here - 1));
-  __syncthreads();
   const int lane = tid & 63, wave = tid >> 6, team = lane >> 3, j = lane & 7;
   const int nk = d_v / 64;
+  // the tile's request rows: loaded first, written to LDS after the first head's W loads are
+  // issued (its wait then counts only this load)
+  const int rid = tid < kThinRows ? epi_row(et, et.r0 + min(tid, n_here - 1)) : 0;
   float acc[2][kThinRows];
 #pragma unroll
   for (int ps = 0; ps < 2; ++ps)
@@ -397,7 +398,20 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
     for (int r = 0; r < kThinRows; ++r) acc[ps][r] = 0.f;
   for (int hj = 0; hj < et.nh; ++hj) {  // the slot's heads (grouped state: the group's)
     const int h = epi_head(et, hj);
-    if (hj > 0) __syncthreads();  // every wave is done with the previous head's u
+    // this head's W rows first: they depend on nothing staged, and the u loads below then
+    // overlap them instead of following them
+    const __bf16* wh = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
+    uint4 wv[2][kThinMaxK];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const __bf16* wc = wh + (int64_t)(cb * kThinCols + wave * 16 + ps * 8 + team) * d_v + 8 * j;
+#pragma unroll
+      for (int k = 0; k < kThinMaxK; ++k)
+        if (k < nk) wv[ps][k] = *(const uint4*)(wc + 64 * k);
+    }
+    if (hj == 0 && tid < kThinRows) row_id[tid] = rid;
+    __syncthreads();  // first head: the row ids are visible; later heads: every wave is done
+                      // with the previous head's u
     {
       const __bf16* outp = (const __bf16*)e.out;
       const int n_pairs = d_v / 2, nope_pairs = e.d_nope / 2, half_r = e.d_rope / 2;
@@ -418,15 +432,6 @@ __global__ __launch_bounds__(256) void k_project_thin(EpiArgs e) {
       }
     }
     __syncthreads();
-    const __bf16* wh = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
-    uint4 wv[2][kThinMaxK];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const __bf16* wc = wh + (int64_t)(cb * kThinCols + wave * 16 + ps * 8 + team) * d_v + 8 * j;
-#pragma unroll
-      for (int k = 0; k < kThinMaxK; ++k)
-        if (k < nk) wv[ps][k] = *(const uint4*)(wc + 64 * k);
-    }
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
 #pragma unroll

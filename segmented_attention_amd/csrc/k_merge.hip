@@ -89,7 +89,7 @@ __device__ __forceinline__ void fma4(float4& acc, float w, const float4& x) {
 
 template <typename OutT>
 __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
-  __shared__ float sw[kWideMaxSplits];
+  __shared__ float sw[kWideMaxSplits], sl[kWideMaxSplits];
   __shared__ float red[4], dens[4];
   __shared__ float4 accs[3][64];
   const int nchunk = (a.d_v + kWideChunk - 1) / kWideChunk;
@@ -101,12 +101,29 @@ __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
   if (!tile_qvec(a.map, tile, qi, t, h)) return;  // uniform over the workgroup
   const int n = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // every split's (m, l) first, then this wave's first batch of partials: the batch is in
+  // flight while the weights are computed (loads retire in order, so the (m, l) wait does not
+  // include the batch)
   float m = -INFINITY;
   for (int s = tid; s < n; s += 256) {
-    const float ms = a.part_ml[((int64_t)s * nvec + v) * 2];
-    sw[s] = ms;
-    m = fmaxf(m, ms);
+    const float2 ml = *(const float2*)(a.part_ml + ((int64_t)s * nvec + v) * 2);
+    sw[s] = ml.x;
+    sl[s] = ml.y;
+    m = fmaxf(m, ml.x);
   }
+  const int c = chunk * kWideChunk + 4 * lane;
+  const bool on = c < a.d_v;
+  const int64_t sstride = nvec * a.d_v;
+  const float* po = a.part_o + v * a.d_v + (on ? c : 0);
+  float4 x[kWideBatch];
+  auto load_batch = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kWideBatch; ++k) {  // past the last split: reread split s, weight 0
+      const int sk = s + 4 * k < n ? s + 4 * k : s;
+      x[k] = *(const float4*)(po + (int64_t)sk * sstride);
+    }
+  };
+  if (wave < n) load_batch(wave);
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (lane == 0) red[wave] = m;
   __syncthreads();
@@ -116,26 +133,16 @@ __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
     const float ms = sw[s];
     const float w = ms == -INFINITY ? 0.f : expf(ms - M);
     sw[s] = w;
-    den += w * a.part_ml[((int64_t)s * nvec + v) * 2 + 1];
+    den += w * sl[s];
   }
   for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
   if (lane == 0) dens[wave] = den;
   __syncthreads();
-  const int c = chunk * kWideChunk + 4 * lane;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (c < a.d_v) {
-    const int64_t sstride = nvec * a.d_v;
-    const float* po = a.part_o + v * a.d_v + c;
-    for (int s = wave; s < n; s += 4 * kWideBatch) {
-      float4 x[kWideBatch];
+  for (int s = wave; s < n; s += 4 * kWideBatch) {
+    if (s != wave) load_batch(s);
 #pragma unroll
-      for (int k = 0; k < kWideBatch; ++k) {  // past the last split: reread split s, weight 0
-        const int sk = s + 4 * k < n ? s + 4 * k : s;
-        x[k] = *(const float4*)(po + (int64_t)sk * sstride);
-      }
-#pragma unroll
-      for (int k = 0; k < kWideBatch; ++k) fma4(acc, s + 4 * k < n ? sw[s + 4 * k] : 0.f, x[k]);
-    }
+    for (int k = 0; k < kWideBatch; ++k) fma4(acc, s + 4 * k < n ? sw[s + 4 * k] : 0.f, x[k]);
   }
   if (wave > 0) accs[wave - 1][lane] = acc;
   __syncthreads();
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
   const float dt = dens[0] + dens[1] + dens[2] + dens[3];
   const float inv = dt > 0.f ? 1.f / dt : 0.f;
   const int64_t o = (int64_t)(t - a.q0) * a.map.H + h;
-  if (c < a.d_v) {
+  if (on) {
 #pragma unroll
     for (int w = 0; w < 3; ++w) {
       acc.x += accs[w][lane].x;
