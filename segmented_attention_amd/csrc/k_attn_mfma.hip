@@ -637,10 +637,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
     }
     // a new segment's query rotation reads the stored query and the RoPE table before the next
     // copy is issued: vector loads retire in order, so behind the copy they would wait for the
-    // whole tile to land
-    if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
-      rotate_q(w1.seg);
+    // whole tile to land. (E4M3: after the copy. Next to the in-place conversion the earlier
+    // rotation made the register allocator spill.)
+    if constexpr (!FP8) {
+      if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
+        rotate_q(w1.seg);
+    }
     if (__builtin_expect(v2, 1)) issue(w2, fb);
+    if constexpr (FP8) {
+      if (__builtin_expect(v1 && w1.seg != w0.seg, 0) && sg[w1.seg].frame != sg[w0.seg].frame)
+        rotate_q(w1.seg);
+    }
     // causal / range mask of tile i: register i of lane (hf, col) is key 8 (i >> 2) + 4 hf + (i & 3);
     // WIN: also the keys below the query vector's window that are not sink keys
     if (__builtin_expect(__ballot((w0.pos0 + kKT - 1 > t) || (w0.nval < kKT) ||

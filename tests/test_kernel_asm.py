@@ -227,3 +227,17 @@ def test_decode_kernel_keeps_everything_in_registers(tmp_path):
         priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2)).group(1))
         assert priv == 0, (m.group(1), priv)
     assert found == 2, found
+
+
+@pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not found")
+def test_attention_kernels_spill_at_most_a_few_values(tmp_path):
+    """The prefill attention instantiations hold 256 accumulator values and the query in
+    registers; a reordering that tips one into spilling its operands (the E4M3 variant once
+    spilled 152 bytes and ran 7.5 % slower) shows up as private memory."""
+    text = _asm(tmp_path)
+    sizes = {}
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+        if "k_attn_mfma" in m.group(1):
+            sizes[m.group(1)] = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2)).group(1))
+    assert len(sizes) == 8, sorted(sizes)
+    assert max(sizes.values()) <= 16, sizes
