@@ -39,6 +39,7 @@ struct segmla_plan {
   // protection
   int32_t edge_rows = 0, tail_rows = 0, budget_permille = 0;
   std::vector<int32_t> dirty;  // sorted, unique
+  std::vector<char> upload;    // workspace bytes [0, o_segcs): the host-built tables, in place
   int64_t n_forced = 0, n_cand = 0, K = 0, need = 0, nA = 0;
   // prefix counts over request rows: forced rows, and candidate rows not forced (a window's
   // share of A is bounded by them without the Indexer's picks)
@@ -285,20 +286,8 @@ segmla_status build_impl(segmla_plan* p, char* ws, const uint32_t* indexer_score
   p->ws = ws;
   p->built = false;
   p->ws_capacity = p->ws_bytes;
-  auto up = [&](size_t off, const void* src, size_t bytes) {
-    if (bytes && e == hipSuccess) e = hipMemcpyAsync(p->ws + off, src, bytes, hipMemcpyHostToDevice, s);
-  };
-  up(p->o_seg, p->runs.data(), sizeof(SegDesc) * p->runs.size());
-  up(p->o_lseg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
-  up(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
-  up(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
-  up(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
-  up(p->o_whead, p->whead.data(), sizeof(int32_t) * p->whead.size());
-  up(p->o_fhead, p->fhead.data(), sizeof(int32_t) * p->fhead.size());
-  up(p->o_rowhead, p->rowhead.data(), sizeof(int32_t) * p->rowhead.size());
-  up(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
-  up(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
-     sizeof(int32_t) * p->grp_ghead.size());
+  // the segment, run and head tables: one upload of the image laid out at plan creation
+  e = hipMemcpyAsync(p->ws, p->upload.data(), p->upload.size(), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
   e = launch_geometry(p->at<SegDesc>(p->o_seg), p->n_run, p->T, p->q0, p->q1, p->d_rope,
                       p->rope_base, p->at<int32_t>(p->o_seg_of_row), p->at<float2>(p->o_segcs),
@@ -650,12 +639,9 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
   const size_t half = (size_t)p->d_rope / 2;
+  // the host-built tables first, contiguous: one upload of a host image per build
   p->o_seg = take(sizeof(SegDesc) * p->n_run);
   p->o_lseg = take(sizeof(SegDesc) * p->n_seg);
-  p->o_segcs = take(sizeof(float2) * half * p->n_run);
-  p->o_stepcs = take(sizeof(float2) * half * p->n_run);
-  p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
-  p->o_flags = take((size_t)T);
   p->o_dirty = take(sizeof(int32_t) * p->dirty.size());
   p->o_ghead = take(sizeof(int32_t) * p->ghead.size());
   p->o_lhead = take(sizeof(int32_t) * p->lhead.size());
@@ -663,6 +649,26 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->o_fhead = take(sizeof(int32_t) * p->fhead.size());
   p->o_rowhead = take(sizeof(int32_t) * p->rowhead.size());
   p->o_grp = take(sizeof(int32_t) * (p->grp_gstart.size() + p->grp_ghead.size()));
+  p->upload.assign(o, 0);
+  auto put = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(p->upload.data() + off, src, bytes);
+  };
+  put(p->o_seg, p->runs.data(), sizeof(SegDesc) * p->runs.size());
+  put(p->o_lseg, p->segs.data(), sizeof(SegDesc) * p->segs.size());
+  put(p->o_dirty, p->dirty.data(), sizeof(int32_t) * p->dirty.size());
+  put(p->o_ghead, p->ghead.data(), sizeof(int32_t) * p->ghead.size());
+  put(p->o_lhead, p->lhead.data(), sizeof(int32_t) * p->lhead.size());
+  put(p->o_whead, p->whead.data(), sizeof(int32_t) * p->whead.size());
+  put(p->o_fhead, p->fhead.data(), sizeof(int32_t) * p->fhead.size());
+  put(p->o_rowhead, p->rowhead.data(), sizeof(int32_t) * p->rowhead.size());
+  put(p->o_grp, p->grp_gstart.data(), sizeof(int32_t) * p->grp_gstart.size());
+  put(p->o_grp + sizeof(int32_t) * p->grp_gstart.size(), p->grp_ghead.data(),
+      sizeof(int32_t) * p->grp_ghead.size());
+  // then what the build computes on the device
+  p->o_segcs = take(sizeof(float2) * half * p->n_run);
+  p->o_stepcs = take(sizeof(float2) * half * p->n_run);
+  p->o_seg_of_row = take(sizeof(int32_t) * (size_t)T);
+  p->o_flags = take((size_t)T);
   p->o_alist = take(sizeof(int32_t) * (size_t)p->nA);
   p->o_nalist = take(sizeof(int32_t) * (size_t)(T - p->nA));
   p->o_blk_count = take(sizeof(int32_t) * p->n_blk);
