@@ -235,7 +235,7 @@ def decode_json(name, d):
     }
 
 
-def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
+def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity", also_e4m3=False):
     import torch
     from segmented_attention_amd import segmla as S
     from workload import config_by_name, make_inputs
@@ -292,6 +292,24 @@ def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity"):
         tflops_576_512=(2.0 * (576 + 512)) * (g_pairs + l_pairs + w_pairs) / wall / 1e12,
     )
     plan.close()
+    if also_e4m3:  # the same layer with the grouped state emitted as 1x128 E4M3 blocks
+        log("workload %s: forward with the state emitted as E4M3 blocks" % cfg_name)
+        pe = S.Plan.for_inputs(dict(inp, cfg=dict(cfg, z_e4m3=1)))
+        pe.build(inp["scores"])
+        zc = torch.empty(z.shape, dtype=torch.uint8, device="cuda")
+        zsc = torch.empty(z.shape[:-1] + (cfg["d_state"] // 128,), dtype=torch.float32, device="cuda")
+        for _ in range(warmup + 1):
+            pe.forward(inp, out, zc, z_scale=zsc)
+        torch.cuda.synchronize()
+        S.segmla_profile_enable(pe.handle, True)
+        for _ in range(steps):
+            pe.forward(inp, out, zc, z_scale=zsc)
+        ms_e, n_e, _ = S.segmla_profile_read(pe.handle)
+        S.segmla_profile_enable(pe.handle, False)
+        torch.cuda.synchronize()
+        pe.close()
+        res["epi_ms_e4m3"] = ms_e[2] / max(1, n_e)
+        del zc, zsc
     if decode_rows > 0:
         log("workload %s: decode window of the last %d row(s)" % (cfg_name, decode_rows))
         res["decode"] = measure_window(inp, cfg, decode_rows, 20, 3)
@@ -455,7 +473,7 @@ def main():
         pfx = measure_prefetch(args.workload, 5)
     gr = None
     if args.grouped:
-        gr = measure(args.grouped, max(2, args.steps // 2), 1)
+        gr = measure(args.grouped, max(2, args.steps // 2), 1, also_e4m3=True)
     pg = None
     if args.paged_rows > 0:
         pg = measure(args.workload, max(2, args.steps // 2), 1, pool="paged:%d" % args.paged_rows)
@@ -546,6 +564,7 @@ def main():
         line["grouped"] = {
             "workload": gr["cfg"]["name"], "group_heads": gr["cfg"]["group_heads"],
             "epilogue_ms": round(gr["epi_ms"], 3), "epilogue_ms_per_head_state": round(r["epi_ms"], 3),
+            "epilogue_ms_e4m3_state": round(gr["epi_ms_e4m3"], 3),
             "attention_ms": round(gr["attn_ms"], 3), "us_per_layer": round(gr["wall_s"] * 1e6, 1),
         }
     if pg is not None:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SEGMLA_ABI_VERSION 3
+#define SEGMLA_ABI_VERSION 4
 
 typedef enum segmla_status {
   SEGMLA_OK = 0,
@@ -129,6 +129,15 @@ typedef struct segmla_layer {
                                     is visible from row t iff p <= t and (p < n_sink or
                                     p >= t - window); n_sink >= 0 request positions */
   int32_t window;                /* w >= 0; both unused when no head has role 2 */
+  int32_t z_e4m3;                /* 0: z in io_dtype. 1: the grouped state is emitted for the
+                                    next projection as 1x128 E4M3 blocks ("Reading notes on
+                                    DeepSeek-V4 serving in TensorRT-LLM", Part I, FP8
+                                    dataflow bullet): per (row, group) and block of 128
+                                    channels, scale = amax / 448 (fp32) and code = the OCP E4M3
+                                    value of channel / scale, rounded to nearest even; the
+                                    block is quantized from the bf16 state z would otherwise
+                                    hold. Requires io_dtype BF16, group_heads >= 2 and
+                                    d_state a multiple of 128 (else SEGMLA_E_SHAPE) */
 } segmla_layer;
 
 /* Protected-row rule (RedKnot-MLA paper, protected-row paragraph, Eq. 6):
@@ -170,7 +179,10 @@ typedef struct segmla_protect {
  * With grouped state (group_heads = G >= 2, n_groups = H / G): z is
  * [q_end - q_begin][n_groups][d_state] with z[t][g] = the sum over the group's Global and
  * sink + window heads of W_h u_h plus, on rows in A, the sum over its Local heads of W_h u_h, or else
- * z_cached[pool_row(t)][g]; z_cached is [n_pool][n_groups][d_state] (may be NULL when H_L = 0). */
+ * z_cached[pool_row(t)][g]; z_cached is [n_pool][n_groups][d_state] (may be NULL when H_L = 0).
+ * With z_e4m3 = 1: z holds the codes, uint8 [q_end - q_begin][n_groups][d_state], and
+ *  z_scale  fp32 [q_end - q_begin][n_groups][d_state / 128] their block scales (z[t][g][c]
+ *           stands for decode(code) * z_scale[t][g][c / 128]); NULL otherwise. */
 typedef struct segmla_tensors {
   const void *q;
   const void *kv;
@@ -181,6 +193,7 @@ typedef struct segmla_tensors {
   void *out;
   void *z;
   float *lse;
+  float *z_scale;
 } segmla_tensors;
 
 typedef struct segmla_plan segmla_plan;
@@ -255,6 +268,7 @@ typedef struct segmla_plan_info {
   int32_t z_slots, zc_slots;
   int32_t kv_dtype, io_dtype;
   int32_t n_split;         /* key-range splits of the attention (1: none) */
+  int32_t z_e4m3;          /* the layer's z_e4m3 */
 } segmla_plan_info;
 segmla_status segmla_plan_get_info(const segmla_plan *plan, segmla_plan_info *info);
 
@@ -264,7 +278,8 @@ segmla_status segmla_plan_get_info(const segmla_plan *plan, segmla_plan_info *in
  * required iff the budget needs Indexer rows, else may be NULL. The workspace must
  * stay allocated and unmodified while the plan is used. It also holds forward scratch
  * (key-range split partials; with bf16 io and a window of more than 8 rows, a copy of W in
- * the projection's operand order, H * d_state * d_v * 2 bytes), so forwards of one plan must
+ * the projection's operand order, H * d_state * d_v * 2 bytes; with z_e4m3, the bf16 state
+ * before quantization), so forwards of one plan must
  * not overlap: run them in order on one stream. */
 segmla_status segmla_plan_build(segmla_plan *plan, void *workspace, size_t workspace_bytes,
                                 const uint32_t *indexer_score, void *stream);

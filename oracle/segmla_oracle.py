@@ -425,6 +425,39 @@ def e4m3_b128_values(codes, scales, rope):
     return np.concatenate([v.reshape(rows, d), np.asarray(rope, dtype=np.float64)], axis=1)
 
 
+def e4m3_encode(x):
+    """fp64 values of magnitude below 464 -> the nearest OCP E4M3 code, ties to the code with
+    an even mantissa, from the format definition (see e4m3_decode): below 2^-6 the codes step by
+    2^-9 (subnormals, m * 2^-9), in the binade [2^E, 2^(E+1)) by 2^(E-3). A value that rounds up
+    to the next power of two gets that binade's first code. The sign is kept for zeros."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    E = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.where(a < 2.0 ** -6, 2.0 ** -9, np.power(2.0, E - 3.0))
+    v = np.rint(a / step) * step  # rint: round half to even, on the step count
+    sub = v < 2.0 ** -6
+    Ev = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    m = np.where(sub, 0, np.rint(v / np.power(2.0, Ev) * 8.0 - 8.0))
+    code = np.where(sub, np.rint(v / 2.0 ** -9), (Ev + 7.0) * 8.0 + m).astype(np.int64)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3_b128_fp32(z):
+    """Projected state -> 1x128 E4M3 blocks for the next projection ("Reading notes on
+    DeepSeek-V4 serving in TensorRT-LLM", Part I, FP8 dataflow bullet), in fp32 as the producer
+    computes it: per block of 128 channels the amax (exact), scale = amax / 448 rounded to fp32
+    (1 for an all-zero block), each quotient value / scale rounded to fp32, then the nearest E4M3
+    code. z: [..., d] with d a multiple of 128 (taken as fp32). Returns (codes uint8 [..., d],
+    scales fp32 [..., d / 128])."""
+    z = np.asarray(z, dtype=np.float32)
+    lead, d = z.shape[:-1], z.shape[-1]
+    zb = z.reshape(*lead, d // 128, 128)
+    amax = np.abs(zb).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = (zb / scale[..., None]).astype(np.float32)
+    return e4m3_encode(y.astype(np.float64)).reshape(*lead, d), scale
+
+
 # --------------------------------------------------------------------------- helpers
 def flops_pairs(T, A, n_global, n_local):
     """(Global, Local) counts of computed (row, head, key) triples."""

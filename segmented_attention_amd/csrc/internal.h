@@ -201,5 +201,8 @@ struct EpiArgs {
   int32_t restore_done;  // the attention grid already copied the rows outside A (bf16)
 };
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
+// n_blocks blocks of 128 bf16 values -> OCP E4M3 codes + one fp32 scale (amax / 448) each
+hipError_t launch_quant_e4m3(const __bf16* src, uint8_t* codes, float* scales, int64_t n_blocks,
+                             hipStream_t stream);
 
 }  // namespace segmla

@@ -527,6 +527,45 @@ __global__ __launch_bounds__(256) void k_restore_copy(EpiArgs e, int vec_per_hea
   }
 }
 
+// ------------------------------------------------------------------- E4M3 output
+// The grouped state for the next projection as 1x128 E4M3 blocks ("Reading notes on
+// DeepSeek-V4 serving in TensorRT-LLM", Part I, FP8 dataflow bullet): 16 lanes per block of
+// 128 channels, 8 per lane (one 16-byte load, one 8-byte store). scale = amax / 448 in fp32 (1
+// for an all-zero block), and the hardware conversion rounds value / scale to the nearest OCP
+// E4M3 code (ties to even); every quotient is at most 448 in magnitude up to the rounding of
+// the scale, far below the first value that would round past the largest finite code (464).
+__global__ __launch_bounds__(256) void k_quant_e4m3(const __bf16* __restrict__ src,
+                                                    uint8_t* __restrict__ codes,
+                                                    float* __restrict__ scales, int64_t n_blocks) {
+  const int64_t b = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  if (b >= n_blocks) return;  // uniform per 16-lane group (the shuffles stay inside it)
+  const int j = threadIdx.x & 15;
+  const uint4 v = ((const uint4*)(src + b * 128))[j];
+  const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(x[k]));
+  for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const float scale = m > 0.f ? m / 448.f : 1.f;
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / scale, x[1] / scale, 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / scale, x[3] / scale, lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / scale, x[5] / scale, 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / scale, x[7] / scale, hi, true);
+  ((uint2*)(codes + b * 128))[j] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  if (j == 0) scales[b] = scale;
+}
+
+hipError_t launch_quant_e4m3(const __bf16* src, uint8_t* codes, float* scales, int64_t n_blocks,
+                             hipStream_t stream) {
+  const int64_t blocks = (n_blocks + 15) / 16;
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_e4m3, dim3((unsigned)blocks), dim3(256), 0, stream, src, codes, scales,
+                     n_blocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream) {
   const bool grouped = e.G >= 2;
   // tiles of `rows` rows: per-head state: Global heads x window rows + Local heads x rows of A

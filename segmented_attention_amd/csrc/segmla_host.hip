@@ -34,6 +34,7 @@ struct segmla_plan {
   // the epilogue's all-row heads)
   std::vector<int32_t> ghead, lhead, whead, fhead, rowhead;
   int32_t n_sink = 0, window = 0;
+  int32_t z_e4m3 = 0;  // grouped state emitted as 1x128 E4M3 codes + fp32 block scales
   int32_t G = 1, n_groups = 0;             // grouped projected state when G >= 2
   std::vector<int32_t> grp_gstart, grp_ghead;  // each group's all-row heads (CSR)
   // protection
@@ -54,7 +55,7 @@ struct segmla_plan {
          o_dirty = 0, o_ghead = 0, o_lhead = 0, o_whead = 0, o_fhead = 0, o_rowhead = 0,
          o_alist = 0, o_nalist = 0, o_blk_count = 0,
          o_blk_sum = 0, o_sum_a = 0, o_sel = 0, o_work = 0, o_part_o = 0, o_part_ml = 0, o_wt = 0,
-         o_rng = 0, o_lseg = 0, o_grp = 0, o_zpart = 0, ws_bytes = 0;
+         o_rng = 0, o_lseg = 0, o_grp = 0, o_zpart = 0, o_zbf = 0, ws_bytes = 0;
   // largest number of window rows inside / outside A (the Indexer picks decide the actual)
   int64_t nA_w = 0, nNA_w = 0;
   // profiling (events on the caller's stream)
@@ -130,6 +131,9 @@ segmla_status check_layer(const segmla_layer* L) {
   if (L->io_dtype == SEGMLA_E4M3_B128) return SEGMLA_E_DTYPE;
   if (L->split_keys < -1 || (L->split_keys > 0 && (L->split_keys % 64) != 0)) return SEGMLA_E_SHAPE;
   if (L->group_heads < 0 || (L->group_heads >= 2 && L->n_heads % L->group_heads != 0))
+    return SEGMLA_E_SHAPE;
+  if (L->z_e4m3 != 0 && (L->z_e4m3 != 1 || L->io_dtype != SEGMLA_BF16 || L->group_heads < 2 ||
+                         L->d_state % 128 != 0))
     return SEGMLA_E_SHAPE;
   const int d_qk = L->d_nope + L->d_rope;
   if (L->kv_dtype == SEGMLA_F32) {
@@ -238,7 +242,7 @@ segmla_status size_window(segmla_plan* p, int32_t q0, int32_t q1, size_t capacit
     auto take = [&](size_t bytes) { size_t at = o; o = align256(o + std::max<size_t>(bytes, 1)); return at; };
     const size_t o_rowcs = take(sizeof(float2) * half * (size_t)L);
     const size_t o_work = take(sizeof(int32_t) * (size_t)n_tiles);
-    size_t o_part_o = 0, o_part_ml = 0, o_zpart = 0, o_wt = 0;
+    size_t o_part_o = 0, o_part_ml = 0, o_zpart = 0, o_wt = 0, o_zbf = 0;
     if (n_split > 1) {
       const size_t nvec = (size_t)n_tiles * kTileQ;
       o_part_o = take(sizeof(float) * (size_t)n_split * nvec * p->d_v);
@@ -249,6 +253,8 @@ segmla_status size_window(segmla_plan* p, int32_t q0, int32_t q1, size_t capacit
     // (decode): per-head fp32 projections, summed per group
     if (thin && p->G >= 2) o_zpart = take(sizeof(float) * (size_t)L * p->H * p->d_state);
     if (p->io_dtype == SEGMLA_BF16 && !thin) o_wt = take((size_t)p->H * p->d_state * p->d_v * 2);
+    // E4M3 output of the grouped state: the bf16 state, quantized block by block afterwards
+    if (p->z_e4m3) o_zbf = take((size_t)L * p->n_groups * p->d_state * 2);
     if (o > capacity) {
       if (n_split > 1 && sk < keys) {  // fewer, longer splits
         sk = (int32_t)std::min<int64_t>((int64_t)sk * 2, keys);
@@ -272,6 +278,7 @@ segmla_status size_window(segmla_plan* p, int32_t q0, int32_t q1, size_t capacit
     p->o_part_ml = o_part_ml;
     p->o_zpart = o_zpart;
     p->o_wt = o_wt;
+    p->o_zbf = o_zbf;
     p->ws_bytes = o;
     return SEGMLA_OK;
   }
@@ -315,8 +322,10 @@ segmla_status check_tensors(const segmla_plan* p, const segmla_tensors* t) {
   if (!t->q || !t->kv || !t->w || !t->out || !t->z) return SEGMLA_E_NULL;
   if (p->HL > 0 && !t->z_cached) return SEGMLA_E_NULL;
   if (p->kv_dtype == SEGMLA_E4M3_B128 && (!t->kv_scale || !t->kv_rope)) return SEGMLA_E_NULL;
+  if (p->z_e4m3 && !t->z_scale) return SEGMLA_E_NULL;
   for (const void* ptr : {t->q, t->kv, (const void*)t->kv_scale, t->kv_rope, t->w, t->z_cached,
-                          (const void*)t->out, (const void*)t->z, (const void*)t->lse})
+                          (const void*)t->out, (const void*)t->z, (const void*)t->lse,
+                          (const void*)t->z_scale})
     if ((uintptr_t)ptr % 16 != 0) return SEGMLA_E_SHAPE;
   return SEGMLA_OK;
 }
@@ -418,7 +427,11 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   ep.grp_gstart = p->at<int32_t>(p->o_grp);
   ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
   ep.zpart = (p->thin && p->G >= 2) ? p->at<float>(p->o_zpart) : nullptr;
+  if (p->z_e4m3) ep.z = p->at<void>(p->o_zbf);  // the bf16 state, then its E4M3 blocks
   e = launch_epilogue(ep, p->io_dtype, s);
+  if (e == hipSuccess && p->z_e4m3)
+    e = launch_quant_e4m3((const __bf16*)ep.z, (uint8_t*)t->z, t->z_scale,
+                          (int64_t)(p->q1 - p->q0) * p->n_groups * (p->d_state / 128), s);
   if (e == hipSuccess && p->prof) {
     e = hipEventRecord(p->ev[3], s);
     pm->fwd_pending = e == hipSuccess;
@@ -567,6 +580,7 @@ segmla_status segmla_plan_create_paged(const segmla_geometry* geom, const segmla
   p->HW = (int32_t)p->whead.size();
   p->n_sink = layer->n_sink;
   p->window = layer->window;
+  p->z_e4m3 = layer->z_e4m3;
   if (layer->group_heads >= 2) {
     p->G = layer->group_heads;
     p->n_groups = p->H / p->G;
@@ -717,6 +731,7 @@ segmla_status segmla_plan_get_info(const segmla_plan* p, segmla_plan_info* info)
   info->kv_dtype = p->kv_dtype;
   info->io_dtype = p->io_dtype;
   info->n_split = p->n_split;
+  info->z_e4m3 = p->z_e4m3;
   return SEGMLA_OK;
 }
 

@@ -59,7 +59,7 @@ class Layer(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("split_keys", ctypes.c_int32),
                 ("group_heads", ctypes.c_int32), ("n_sink", ctypes.c_int32),
-                ("window", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("z_e4m3", ctypes.c_int32)]
 
 
 class Protect(ctypes.Structure):
@@ -71,7 +71,8 @@ class Protect(ctypes.Structure):
 class Tensors(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
                 ("kv_rope", ctypes.c_void_p), ("w", ctypes.c_void_p), ("z_cached", ctypes.c_void_p),
-                ("out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+                ("out", ctypes.c_void_p), ("z", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("z_scale", ctypes.c_void_p)]
 
 
 class CopyRange(ctypes.Structure):
@@ -89,7 +90,8 @@ class PlanInfo(ctypes.Structure):
                 ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("d_state", ctypes.c_int32), ("z_slots", ctypes.c_int32),
                 ("zc_slots", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("n_split", ctypes.c_int32),
+                ("z_e4m3", ctypes.c_int32)]
 
 
 _lib = None
@@ -221,7 +223,7 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                        d_rope, d_state, v_has_rope=1, rope_base=10000.0, softmax_scale=1.0,
                        kv_dtype=SEGMLA_BF16, io_dtype=SEGMLA_BF16, split_keys=0, edge_rows=0,
                        tail_rows=0, budget_permille=0, dirty_rows=(), q_range=None, pages=None,
-                       group_heads=0, n_sink=0, window=0):
+                       group_heads=0, n_sink=0, window=0, z_e4m3=0):
     """Validate and size a plan; returns the plan handle. q_range = (q_begin, q_end): a plan
     for that window of request rows (segmla_plan_create_range); None: the whole request.
     pages = dict(page_rows, page_start, page_table): a paged latent pool
@@ -235,7 +237,7 @@ def segmla_plan_create(kinds, lens, offsets, pool_rows, n_pool, n_heads, head_is
                  keep["kind"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
     L = Layer(n_heads, d_nope, d_rope, d_state, v_has_rope,
               keep["glob"].ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), rope_base, softmax_scale,
-              kv_dtype, io_dtype, split_keys, group_heads, n_sink, window)
+              kv_dtype, io_dtype, split_keys, group_heads, n_sink, window, z_e4m3)
     pr = Protect(edge_rows, tail_rows, budget_permille, len(keep["dirty"]),
                  keep["dirty"].ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(keep["dirty"])
                  else None)
@@ -295,7 +297,7 @@ def segmla_plan_build(plan, workspace, indexer_score=None, stream=None):
 
 
 def check_forward_tensors(info, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope=None,
-                          lse=None):
+                          lse=None, z_scale=None):
     """Validate the tensors of one forward against a plan's shapes (segmla_plan_get_info)."""
     import torch
     io = _torch_dtypes(info["io_dtype"])
@@ -312,30 +314,34 @@ def check_forward_tensors(info, q, kv, w, out, z, z_cached=None, kv_scale=None, 
     specs += [("w", w, io, H * ds * dv, True),
               ("z_cached", z_cached, io, n_pool * info["zc_slots"] * ds, info["n_local"] > 0),
               ("out", out, io, nq * H * dv, True),
-              ("z", z, io, nq * info["z_slots"] * ds, True),
+              ("z", z, (torch.uint8,) if info["z_e4m3"] else io, nq * info["z_slots"] * ds, True),
               ("lse", lse, (torch.float32,), nq * H, False)]
+    if info["z_e4m3"]:
+        specs.append(("z_scale", z_scale, (torch.float32,), nq * info["z_slots"] * (ds // 128), True))
+    elif z_scale is not None:
+        raise ValueError("z_scale is given but the plan's z is not E4M3")
     _check_tensors(specs)
 
 
 def segmla_forward(plan, q, kv, w, out, z, z_cached=None, kv_scale=None, kv_rope=None, lse=None,
-                   stream=None):
+                   stream=None, z_scale=None):
     check_forward_tensors(segmla_plan_get_info(plan), q, kv, w, out, z, z_cached, kv_scale,
-                          kv_rope, lse)
+                          kv_rope, lse, z_scale)
     t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
-                _ptr(z), _ptr(lse))
+                _ptr(z), _ptr(lse), _ptr(z_scale))
     _check(lib().segmla_forward(plan, ctypes.byref(t), _stream(stream)), "segmla_forward")
 
 
 def segmla_forward_noalloc(plan, indexer_score, q, kv, w, out, z, z_cached=None, kv_scale=None,
-                           kv_rope=None, lse=None, stream=None):
+                           kv_rope=None, lse=None, stream=None, z_scale=None):
     """Plan build + forward with the workspace in the library's own device array (no device
     memory allocated anywhere in the call)."""
     import torch
     info = segmla_plan_get_info(plan)
     _check_tensors([("indexer_score", indexer_score, (torch.int32, torch.uint32), info["T"], False)])
-    check_forward_tensors(info, q, kv, w, out, z, z_cached, kv_scale, kv_rope, lse)
+    check_forward_tensors(info, q, kv, w, out, z, z_cached, kv_scale, kv_rope, lse, z_scale)
     t = Tensors(_ptr(q), _ptr(kv), _ptr(kv_scale), _ptr(kv_rope), _ptr(w), _ptr(z_cached), _ptr(out),
-                _ptr(z), _ptr(lse))
+                _ptr(z), _ptr(lse), _ptr(z_scale))
     _check(lib().segmla_forward_noalloc(plan, _ptr(indexer_score), ctypes.byref(t), _stream(stream)),
            "segmla_forward_noalloc")
 
@@ -482,7 +488,7 @@ class Plan:
             cfg["d_rope"], cfg["d_state"], cfg["v_has_rope"], cfg["rope_base"], cfg["softmax_scale"],
             _DT[cfg["kv_dtype"]], _DT[cfg["dtype"]], split_keys, cfg["edge_rows"], cfg["tail_rows"],
             cfg["budget_permille"], dirty_rows, q_range, pages, cfg.get("group_heads", 0),
-            cfg.get("n_sink", 0), cfg.get("window", 0))
+            cfg.get("n_sink", 0), cfg.get("window", 0), cfg.get("z_e4m3", 0))
         self.T, self.n_protected = segmla_plan_rows(self.handle)
         # computed window: q, out, z and lse hold rows q0 .. q1 - 1
         self.q0, self.q1 = (0, self.T) if q_range is None else (int(q_range[0]), int(q_range[1]))
@@ -497,14 +503,14 @@ class Plan:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         segmla_plan_build(self.handle, self.workspace, scores, stream)
 
-    def forward(self, inp, out, z, lse=None, stream=None):
-        """out, z, lse: the window's rows. inp["q"] may hold the whole request (its window
-        rows are passed, a view) or the window only."""
+    def forward(self, inp, out, z, lse=None, stream=None, z_scale=None):
+        """out, z, lse (and z_scale for an E4M3 state): the window's rows. inp["q"] may hold
+        the whole request (its window rows are passed, a view) or the window only."""
         q = inp["q"]
         if q.shape[0] != self.q1 - self.q0:
             q = q[self.q0:self.q1]
         segmla_forward(self.handle, q, inp["kv"], inp["w"], out, z, inp.get("z_cached"),
-                       inp.get("kv_scale"), inp.get("kv_rope"), lse, stream)
+                       inp.get("kv_scale"), inp.get("kv_rope"), lse, stream, z_scale)
 
     def set_window(self, q_begin, q_end, stream=None):
         """Another window of the same request on the built plan (segmla_plan_set_window)."""

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert S.segmla_abi_version() == 3
+    assert S.segmla_abi_version() == 4
     for st in range(-9, 1):
         assert S.segmla_status_string(st) not in ("", "unknown status")
     assert S.segmla_status_string(-100) == "unknown status"
@@ -194,6 +194,61 @@ def test_group_heads_errors(L):
             S.segmla_plan_destroy(p)
     for G in (-1, 3, 7, 65):
         assert _status(cfg, group_heads=G) == S.SEGMLA_E_SHAPE, G
+
+
+def test_e4m3_state_errors(L):
+    """The E4M3 output of the projected state needs bf16 io, grouped state and d_state a
+    multiple of 128 (else SEGMLA_E_SHAPE); the plan reports it, and a forward without the scale
+    buffer is SEGMLA_E_NULL before any device work; the binding asks for uint8 codes and the
+    scales."""
+    import torch
+    cfg = SMALL_CONFIGS[1]  # bf16, 64 heads, d_state 512
+    assert _status(cfg, group_heads=8, z_e4m3=1) == S.SEGMLA_OK
+    assert _status(cfg, group_heads=0, z_e4m3=1) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, group_heads=8, z_e4m3=2) == S.SEGMLA_E_SHAPE
+    assert _status(cfg, group_heads=8, z_e4m3=1, d_state=192) == S.SEGMLA_E_SHAPE
+    assert _status(SMALL_CONFIGS[0], group_heads=4, z_e4m3=1) == S.SEGMLA_E_SHAPE  # fp32 io
+    p = _create(cfg, group_heads=8, z_e4m3=1)
+    try:
+        info = S.segmla_plan_get_info(p)
+        assert info["z_e4m3"] == 1 and info["z_slots"] == 8
+        T = info["T"]
+        lib = S.lib()
+        need = S.segmla_plan_workspace_bytes(p)
+        p0 = _create(cfg, group_heads=8)
+        try:  # the bf16 state before quantization: T x 8 groups x 512 x 2 bytes more workspace
+            assert need - S.segmla_plan_workspace_bytes(p0) >= T * 8 * 512 * 2
+        finally:
+            S.segmla_plan_destroy(p0)
+        bf = torch.bfloat16
+        good = dict(q=torch.zeros(T, 64, 576, dtype=bf), kv=torch.zeros(T, 576, dtype=bf),
+                    w=torch.zeros(64, 512, 576, dtype=bf), out=torch.zeros(T, 64, 576, dtype=bf),
+                    z=torch.zeros(T, 8, 512, dtype=torch.uint8),
+                    z_cached=torch.zeros(T, 8, 512, dtype=bf),
+                    z_scale=torch.zeros(T, 8, 4, dtype=torch.float32))
+
+        def err(**over):
+            args = dict(good)
+            args.update(over)
+            with pytest.raises(ValueError) as e:
+                S.segmla_forward(p, **args)
+            return str(e.value)
+        assert "q must be on the GPU" in err()
+        assert "z has dtype" in err(z=torch.zeros(T, 8, 512, dtype=bf))
+        assert "z_scale is required" in err(z_scale=None)
+        assert "z_scale holds" in err(z_scale=torch.zeros(T, 8, 3))
+        if _no_gpu():  # a built plan needs a device; the NULL check comes first on the host
+            t = S.Tensors()
+            assert lib.segmla_forward(p, ctypes.byref(t), None) == S.SEGMLA_E_STATE
+    finally:
+        S.segmla_plan_destroy(p)
+    p = _create(cfg, group_heads=8)
+    try:
+        with pytest.raises(ValueError, match="z_scale is given"):
+            S.segmla_forward(p, q=None, kv=None, w=None, out=None, z=None,
+                             z_scale=torch.zeros(4))
+    finally:
+        S.segmla_plan_destroy(p)
 
 
 def test_geometry_errors(L):

@@ -444,6 +444,74 @@ def test_e4m3_generator_roundtrip_error():
     np.testing.assert_allclose(amax, 448 * sc, rtol=2 ** -4)
 
 
+def _e4m3_finite_codes():
+    return np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def test_e4m3_encode_inverts_decode():
+    """Every finite code (both zeros included) encodes back from its own value."""
+    codes = _e4m3_finite_codes()
+    np.testing.assert_array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+
+
+def test_e4m3_encode_nearest_even_by_brute_force():
+    """Against a brute-force search over all finite codes: the nearest value, and on an exact
+    tie (every midpoint between neighbouring positive codes, both signs) the code with an even
+    mantissa field."""
+    codes = _e4m3_finite_codes()
+    pos = codes[codes < 0x80]
+    pv = O.e4m3_decode(pos)
+    order = np.argsort(pv)
+    pv, pos = pv[order], pos[order]
+    mids = (pv[1:] + pv[:-1]) / 2.0
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([mids, -mids, rng.uniform(-463.0, 463.0, 4000), rng.uniform(-0.03, 0.03, 4000)])
+    allv = O.e4m3_decode(codes)
+    got = O.e4m3_encode(xs)
+    for x, g in zip(xs, got):
+        d = np.abs(allv - x)
+        best = codes[d == d.min()]
+        best = best[(best & 0x80) == (0x80 if x < 0 else 0)] if best.size > 1 else best
+        if best.size > 1:  # a tie: the even mantissa
+            best = best[(best & 1) == 0]
+        assert best.size == 1 and g == best[0], (x, g, best)
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """The same rounding as torch's float8_e4m3fn cast (round to nearest even) on fp32 values
+    within the format's range."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-460, 460, 50000), rng.standard_normal(50000) * 2.0,
+                        rng.uniform(-2.0 ** -5, 2.0 ** -5, 50000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_quantize_e4m3_b128_blocks():
+    """Each block's largest magnitude becomes +-448 exactly (code 0x7E / 0xFE), the scale is
+    the fp32 quotient amax / 448, an all-zero block has scale 1 and zero codes, and every value
+    comes back within half a code step (relative 2^-4 for normals, 2^-10 * scale below 2^-6 *
+    scale)."""
+    rng = np.random.default_rng(3)
+    z = (rng.standard_normal((5, 3, 512)) * np.exp(rng.uniform(-6, 6, (5, 3, 1)))).astype(np.float32)
+    z[2, 1, 128:256] = 0.0
+    codes, scale = O.quantize_e4m3_b128_fp32(z)
+    assert codes.shape == z.shape and scale.shape == (5, 3, 4) and scale.dtype == np.float32
+    zb = z.reshape(5, 3, 4, 128)
+    amax = np.abs(zb).max(-1)
+    np.testing.assert_array_equal(scale, np.where(amax > 0, amax / np.float32(448), np.float32(1)))
+    assert scale[2, 1, 1] == 1.0 and np.all(codes.reshape(5, 3, 4, 128)[2, 1, 1] == 0)
+    cb = codes.reshape(5, 3, 4, 128)
+    k = np.abs(zb).argmax(-1)
+    top = np.take_along_axis(cb, k[..., None], -1)[..., 0]
+    nz = amax > 0
+    assert np.all(np.isin(top[nz], [0x7E, 0xFE]))
+    back = O.e4m3_decode(cb) * scale[..., None].astype(np.float64)
+    err = np.abs(back - zb)
+    bound = np.maximum(2.0 ** -4 * np.abs(zb), 2.0 ** -10 * scale[..., None])
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
 @pytest.mark.parametrize("page_rows", [1, 5, 32])
 def test_paged_pool_equals_contiguous(page_rows):
     """The same latent rows and cached state placed on shuffled pages instead of contiguous
