@@ -73,3 +73,32 @@ def test_decode_rows_match_oracle(cfg, split_keys):
         ref = O.layer_forward(oi, rows=np.arange(t, t + 1))
         e = compare(cfg, ref, out, z, lse, None, rows=np.arange(1))
         say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+
+
+@pytest.mark.parametrize("cfg,page_rows", [(SMALL_CONFIGS[1], 32), (SMALL_CONFIGS[3], 48),
+                                           (SMALL_CONFIGS[5], 40)],
+                         ids=lambda x: x["name"] if isinstance(x, dict) else str(x))
+@pytest.mark.parametrize("split_keys", [64, 192])
+def test_decode_rows_on_paged_pool(cfg, page_rows, split_keys):
+    """The decode kernel over a paged latent pool: shuffled pages, some of a size that does not
+    divide the 32-key tile, so a segment's keys arrive in runs that cut tiles (each run keeps
+    its segment's RoPE frame, and the two sets may meet a run boundary at different steps)."""
+    from tests.test_gpu_paged import _paged_copy
+    base = make_inputs(cfg, "cuda")
+    inp = _paged_copy(base, page_rows, cfg["seed"] + 1)
+    H = cfg["n_heads"]
+    oi = oracle_inputs(inp)
+    for t in _rows(base):
+        say("case decode paged %s pages %d row %d split %d" % (cfg["name"], page_rows, t, split_keys))
+        plan = Plan.for_inputs(inp, split_keys, q_range=(t, t + 1))
+        plan.build(inp["scores"])
+        dt = inp["q"].dtype
+        out = torch.full((1, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+        z = torch.full((1, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+        plan.forward(inp, out, z, lse)
+        torch.cuda.synchronize()
+        plan.close()
+        ref = O.layer_forward(oi, rows=np.arange(t, t + 1))
+        e = compare(cfg, ref, out, z, lse, None, rows=np.arange(1))
+        say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
