@@ -31,6 +31,11 @@ It computes, slowly and in the most direct way, what the GPU path computes:
   jobs": a local head sees the sink tokens and the recent window,
   W(i) = S_sink U [i - w, i]): the same dense attention with the keys outside
   that set masked out, on every row, over the same physically re-rotated keys.
+* compressed-history layers of DeepSeek-V4 (TensorRT-LLM reading notes,
+  section 1: CSA / HCA): per segment, entries of m rows stored in a second
+  pool; each row attends its recent raw window and its compressed entries
+  (all available ones for HCA, its Indexer list for CSA) in one dense
+  softmax, entries re-rotated physically by their segment's shift.
 
 Readings of points the pages leave open (each listed in the design notes):
 values are the full latent row (keys = values, RoPE dims last); RoPE pairs
@@ -400,6 +405,115 @@ def ledger(f_front, r, f_back, n_heads, n_local, T, A):
     dense = n_heads * T * (T + 1) / 2.0
     computed = n_global * T * (T + 1) / 2.0 + n_local * float(np.sum(A + 1))
     return logical, physical, 1.0 - computed / dense
+
+
+# -------------------------------------------------- compressed history (dual-pool layers)
+def compressed_entries(geom, ratio, cpool_rows, n_cpool):
+    """Compressed entries of a request for the DeepSeek-V4 CSA and HCA layers ("Reading notes on
+    DeepSeek-V4 serving in TensorRT-LLM", section 1: besides the recent raw tokens, such a layer
+    attends a history compressed m to 1; HCA pools disjoint windows of m' tokens).
+
+    Reading (the pages say nothing of relocation here): compression runs per segment when the
+    segment is stored, so a cached document is compressed alone at its canonical positions and
+    segment i holds floor(len_i / m) entries. Entry j of segment i stands for the segment's rows
+    [m j, m j + m), lies at compressed-pool row cpool_rows[i] + j, is encoded in the segment's
+    stored RoPE frame (like its raw rows) and becomes available to request row t once its last
+    row, offset_i + m j + m - 1, is <= t. Entries are numbered in request order, segment by
+    segment.
+
+    Returns dict(n, seg [n], j [n], pool [n], first_row [n] (the first request row that sees
+    the entry), base [n_seg] (id of each segment's entry 0), count [n_seg])."""
+    m = int(ratio)
+    if m < 1:
+        raise ValueError("ratio must be >= 1")
+    lens, offsets = geom["lens"], geom["offsets"]
+    cpool_rows = np.asarray(cpool_rows, dtype=np.int64)
+    count = lens // m
+    if np.any(cpool_rows < 0) or np.any(cpool_rows + count > int(n_cpool)):
+        raise ValueError("compressed pool range out of bounds")
+    base = np.zeros(len(lens), dtype=np.int64)
+    base[1:] = np.cumsum(count[:-1])
+    seg = np.repeat(np.arange(len(lens), dtype=np.int64), count)
+    j = np.arange(int(count.sum()), dtype=np.int64) - base[seg]
+    return dict(n=int(count.sum()), m=m, seg=seg, j=j, pool=cpool_rows[seg] + j,
+                first_row=offsets[seg] + m * j + m - 1, base=base, count=count)
+
+
+def relocated_entries(centries, geom, ce, d_nope, d_rope, base):
+    """Entry keys in the request frame by physical re-rotation (fp64 [n, d_nope + d_rope]): an
+    entry of segment i moves by its segment's phase shift, R(offset_i - stored_pos_base_i), the
+    same move relocated_keys gives every raw row of that segment (R(p) R(p_stored)^-1 =
+    R(p - p_stored), and p - p_stored is constant over a segment)."""
+    theta = rope_theta(d_rope, base)
+    lat = np.asarray(centries, dtype=np.float64)[ce["pool"]]
+    shift = (geom["offsets"] - geom["stored_pos_base"])[ce["seg"]].astype(np.float64)
+    keys = lat.copy()
+    keys[:, d_nope:] = apply_blocks(rot_blocks(shift, theta), lat[:, d_nope:])
+    return keys
+
+
+def entries_of_row(ce, t, ids=None, n_list=None):
+    """Entry ids one row attends. HCA (ids None): every entry available at row t, in id order.
+    CSA: the row's Indexer list ids[:n_list] (the pages' per-query list length over a fixed-width
+    buffer), read up to, not including, the first id that is not an entry available at row t
+    (negative, past the last entry, or not yet available); an id listed twice counts twice."""
+    avail = ce["first_row"] <= int(t)
+    if ids is None:
+        return np.flatnonzero(avail)
+    out = []
+    for c in np.asarray(ids, dtype=np.int64)[:max(0, int(n_list))]:
+        if c < 0 or c >= ce["n"] or not avail[c]:
+            break
+        out.append(int(c))
+    return np.asarray(out, dtype=np.int64)
+
+
+def dual_pool_rows(q_rows, t_rows, keys, ekeys, ce, sigma, d_v, window, lists=None, list_lens=None):
+    """One softmax over two key pools ("Reading notes on DeepSeek-V4 serving in TensorRT-LLM",
+    section 1, the dual-pool kernel paragraph): for row t, the raw keys p with
+    max(0, t - window) <= p <= t (keys: relocated_keys) and the compressed entries of
+    entries_of_row (ekeys: relocated_entries), all heads sharing the key set. Values are the
+    first d_v dims of each key. Returns (O [n, Hs, d_v], lse [n, Hs])."""
+    n, Hs, _ = q_rows.shape
+    O = np.empty((n, Hs, d_v), dtype=np.float64)
+    lse = np.empty((n, Hs), dtype=np.float64)
+    for i in range(n):
+        t = int(t_rows[i])
+        lo = max(0, t - int(window))
+        ids = entries_of_row(ce, t, None if lists is None else lists[i],
+                             None if list_lens is None else list_lens[i])
+        K = np.concatenate([keys[lo:t + 1], ekeys[ids]], axis=0)
+        s = sigma * (q_rows[i] @ K.T)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - mx)
+        l = e.sum(axis=1, keepdims=True)
+        O[i] = (e @ K[:, :d_v]) / l
+        lse[i] = (mx + np.log(l))[:, 0]
+    return O, lse
+
+
+def dual_pool_forward(inp, dual, rows, lists=None, list_lens=None):
+    """Oracle of the dual-pool attention on request rows `rows` (every head of q). `inp` as for
+    layer_forward (q, latent, geometry, cfg), `dual` = dict(ratio, window, cpool_rows, n_cpool,
+    centries fp64 [n_cpool, d_qk]); lists / list_lens: per row of `rows`, the CSA list and its
+    length (None: HCA). Returns dict(O, lse, ce, n_keys [n] (keys attended per head))."""
+    cfg = inp["cfg"]
+    d_nope, d_rope = cfg["d_nope"], cfg["d_rope"]
+    base, sigma = cfg["rope_base"], cfg["softmax_scale"]
+    d_v = d_nope + d_rope if cfg["v_has_rope"] else d_nope
+    geom = geometry(inp["kinds"], inp["lens"], inp["offsets"], inp["pool_rows"], inp["n_pool"],
+                    inp.get("pages"))
+    ce = compressed_entries(geom, dual["ratio"], dual["cpool_rows"], dual["n_cpool"])
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = relocated_keys(inp["latent"], geom, d_nope, d_rope, base)
+    ekeys = relocated_entries(dual["centries"], geom, ce, d_nope, d_rope, base)
+    q = np.stack([np.asarray(inp["q"][int(t)], dtype=np.float64) for t in rows])
+    O, lse = dual_pool_rows(q, rows, keys, ekeys, ce, sigma, d_v, dual["window"], lists, list_lens)
+    n_keys = np.array([min(int(t), int(dual["window"])) + 1 +
+                       len(entries_of_row(ce, t, None if lists is None else lists[i],
+                                          None if list_lens is None else list_lens[i]))
+                       for i, t in enumerate(rows)], dtype=np.int64)
+    return dict(O=O, lse=lse, ce=ce, n_keys=n_keys)
 
 
 # ------------------------------------------------------------------------------ E4M3

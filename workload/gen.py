@@ -23,6 +23,7 @@ from .configs import segment_table
 SEG_PREFIX, SEG_DOC, SEG_NEW = 0, 1, 2
 
 TAG_Q, TAG_LAT, TAG_W, TAG_ZC, TAG_SCORE, TAG_POOL, TAG_PAGES = 1, 2, 3, 4, 5, 7, 8
+TAG_CKV, TAG_CIDX, TAG_CPOOL = 9, 10, 11
 CHUNK_ROWS = 2048
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -210,4 +211,63 @@ def make_inputs(cfg, device="cpu", pool="identity", with_scores=True):
     out["z_cached"] = randn_rows((n_pool, slots, cfg["d_state"]), seed, TAG_ZC, device, io)
     if with_scores:
         out["scores"] = uint32_scores(T, seed, device)
+    return out
+
+
+def make_dual_inputs(inp, ratio, window, top_k, device="cpu", pool="identity"):
+    """A compressed pool and Indexer lists for the compressed-history (dual-pool) layers, next
+    to the inputs `inp` of make_inputs.
+
+    Pool layout: segment i gets a block of ceil(len_i / ratio) + 1 rows (room for every entry
+    it can hold), the blocks in segment order back to back (identity) or in a random order
+    with random gaps (shuffled); rows ~ N(0, 1) in the latent's dtype (bf16 or fp32), rows
+    outside every block NaN.
+
+    Lists (top_k > 0): a stand-in for an Indexer's top-K picks. Row t draws from the ids
+    [0, n_t) with n_t = (t + 1) // ratio (the entries of a request whose segments are multiples
+    of `ratio` long): all of them when n_t <= top_k, else one uniformly drawn id from each of
+    top_k equal strata of [0, n_t) (ascending, no repeats). cidx int32 [T][top_k] (unused
+    slots -1), clen int32 [T]."""
+    cfg = inp["cfg"]
+    lens = np.asarray(inp["lens"], dtype=np.int64)
+    T = int(inp["T"])
+    seed = cfg["seed"]
+    blk = -(-lens // int(ratio)) + 1
+    n = len(lens)
+    cpool_rows = np.zeros(n, dtype=np.int64)
+    if pool == "identity":
+        cpool_rows[1:] = np.cumsum(blk[:-1])
+        n_cpool = int(blk.sum())
+    elif pool == "shuffled":
+        rng = np.random.default_rng([seed, TAG_CPOOL])
+        cur = int(rng.integers(0, 5))
+        for i in rng.permutation(n):
+            cpool_rows[i] = cur
+            cur += int(blk[i]) + int(rng.integers(0, 5))
+        n_cpool = cur
+    else:
+        raise ValueError(pool)
+    d_qk = cfg["d_nope"] + cfg["d_rope"]
+    dt = _TORCH_DT[cfg["kv_dtype"]] if cfg["kv_dtype"] in _TORCH_DT else torch.bfloat16
+    ckv = randn_rows((n_cpool, d_qk), seed, TAG_CKV, device, torch.float32)
+    used = np.zeros(n_cpool, dtype=bool)
+    for r, b in zip(cpool_rows, blk):
+        used[r:r + b] = True
+    if not used.all():
+        ckv[torch.from_numpy(~used).to(device)] = float("nan")
+    out = dict(ratio=int(ratio), window=int(window), top_k=int(top_k), cpool_rows=cpool_rows,
+               n_cpool=int(n_cpool), ckv=ckv.to(dt))
+    if top_k > 0:
+        g = _gen(device, seed, TAG_CIDX, 0)
+        nt = torch.div(torch.arange(1, T + 1, device=device, dtype=torch.int64), int(ratio),
+                       rounding_mode="floor")
+        k = torch.arange(top_k, device=device, dtype=torch.int64)
+        u = torch.rand((T, top_k), generator=g, device=device, dtype=torch.float64)
+        strat = torch.floor((k[None, :] + u) * nt[:, None].double() / top_k).to(torch.int64)
+        every = k[None, :].expand(T, top_k)
+        ids = torch.where((nt >= top_k)[:, None], strat, every)
+        clen = torch.clamp(nt, max=top_k)
+        ids = torch.where(k[None, :] < clen[:, None], ids, torch.full_like(ids, -1))
+        out["cidx"] = ids.to(torch.int32).contiguous()
+        out["clen"] = clen.to(torch.int32).contiguous()
     return out
