@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SEGMLA_ABI_VERSION 4
+#define SEGMLA_ABI_VERSION 5
 
 typedef enum segmla_status {
   SEGMLA_OK = 0,
@@ -408,6 +408,81 @@ segmla_status segmla_prefetch_wait(segmla_prefetcher *pf, void *stream);
 segmla_status segmla_prefetch_elapsed(segmla_prefetcher *pf, float *ms);
 /* Wait for outstanding transfers, then release the stream and events. */
 void segmla_prefetcher_destroy(segmla_prefetcher *pf);
+
+/* Compressed-history attention of the DeepSeek-V4 CSA and HCA layers ("Reading notes on
+ * DeepSeek-V4 serving in TensorRT-LLM", section 1: the hybrid attention bullets and the
+ * dual-pool kernel paragraph) over the relocated segments of a plan. Each request row t attends,
+ * with every one of the plan's n_heads heads sharing the keys, in one softmax:
+ *  - the raw keys p with max(0, t - window) <= p <= t of the plan's latent pool (128 most recent
+ *    tokens: window = 127), and
+ *  - compressed entries of a second pool: every entry available at t (HCA, top_k = 0), or the
+ *    row's Indexer list (CSA, top_k = K > 0).
+ * Entries under relocation (the pages say nothing of it; the plainest reading): compression runs
+ * per segment when the segment is stored, so segment i holds floor(len[i] / ratio) entries.
+ * Entry j of segment i stands for the segment's rows [ratio j, ratio j + ratio), lies at
+ * compressed-pool row cpool_row[i] + j, is encoded in the segment's stored RoPE frame (like its
+ * raw rows: documents canonical, prefix and new rows at request positions) and becomes available
+ * to row t once offset[i] + ratio (j + 1) - 1 <= t. Entry ids number the request's entries in
+ * request order, segment by segment. Both pools are attended in place: the query is rotated by
+ * -Delta_i per segment and the output phase restored, as for the layer forward (RedKnot-MLA
+ * paper, relocation paragraph, Eq. 5).
+ * Supported: plans with kv_dtype and io_dtype BF16 (d_nope = 512, d_rope = 64), any head roles
+ * (ignored here: every head attends), contiguous or paged latent pools; else
+ * SEGMLA_E_UNSUPPORTED. Requirements (else SEGMLA_E_SHAPE): ratio >= 1, window >= 0,
+ * top_k >= 0, 0 <= n_cpool < 2^31; (else SEGMLA_E_GEOMETRY) for every segment
+ * 0 <= cpool_row[i] and cpool_row[i] + floor(len[i] / ratio) <= n_cpool. */
+typedef struct segmla_dual_pool {
+  int32_t ratio;             /* request rows per compressed entry (4 for CSA, 128 for HCA) */
+  int32_t window;            /* raw keys t - window .. t */
+  int32_t top_k;             /* width K of the per-row lists; 0: every available entry */
+  int64_t n_cpool;           /* rows of the compressed pool */
+  const int64_t *cpool_row;  /* host [n_seg], read during segmla_dual_create only */
+} segmla_dual_pool;
+
+/* Device tensors of one dual-pool forward, row-major, caller-owned, 16-byte aligned (cidx and
+ * clen 4-byte aligned), else SEGMLA_E_SHAPE. Rows are the plan's window [q_begin, q_end).
+ *  q     [q_end - q_begin][H][576] bf16, stored post-RoPE at request position t
+ *  kv    [n_pool][576] bf16, the plan's latent pool
+ *  ckv   [n_cpool][576] bf16, the compressed pool
+ *  cidx  CSA: int32 [q_end - q_begin][top_k], the row's entry ids; NULL for HCA
+ *  clen  CSA: int32 [q_end - q_begin], how many of the row's ids to read (clamped to
+ *        [0, top_k]); NULL for HCA
+ *  out   [q_end - q_begin][H][d_v] bf16, merged outputs in request phase
+ *  lse   optional fp32 [q_end - q_begin][H]: natural-log log-sum-exp of sigma*q.k
+ * A list is read in order up to, not including, the first id that is not an entry available at
+ * the row (negative, at least the request's entry count, or not yet available), so an Indexer
+ * may pad its fixed-width buffer with -1. Ids need not be sorted (sorted lists touch each
+ * segment's RoPE frame once); an id listed twice is attended twice. */
+typedef struct segmla_dual_tensors {
+  const void *q;
+  const void *kv;
+  const void *ckv;
+  const int32_t *cidx;
+  const int32_t *clen;
+  void *out;
+  float *lse;
+} segmla_dual_tensors;
+
+typedef struct segmla_dual segmla_dual;
+
+/* Validate the compressed geometry against a plan and size its tables (host only). The plan
+ * must outlive the dual-pool object; it need not be built yet. */
+segmla_status segmla_dual_create(const segmla_plan *plan, const segmla_dual_pool *dp,
+                                 segmla_dual **out_dual);
+/* Device workspace bytes segmla_dual_build needs, and the request's entry count (host only;
+ * either pointer may be NULL). */
+segmla_status segmla_dual_sizes(const segmla_dual *dual, size_t *workspace_bytes,
+                                int64_t *n_entries);
+/* Copy the entry tables into `workspace` (256-byte aligned, >= segmla_dual_sizes bytes) on
+ * `stream`. The workspace must stay allocated and unmodified while the object is used. */
+segmla_status segmla_dual_build(segmla_dual *dual, void *workspace, size_t workspace_bytes,
+                                void *stream);
+/* One dual-pool forward on the rows of the plan's current window (the plan and the object
+ * built: else SEGMLA_E_STATE). Enqueues one kernel, no synchronization; capturable in a HIP
+ * graph. */
+segmla_status segmla_dual_forward(const segmla_dual *dual, const segmla_dual_tensors *t,
+                                  void *stream);
+void segmla_dual_destroy(segmla_dual *dual);
 
 void segmla_plan_destroy(segmla_plan *plan);
 const char *segmla_status_string(int32_t status);

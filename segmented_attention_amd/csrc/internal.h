@@ -111,6 +111,16 @@ __device__ __forceinline__ int seg_of(const SegDesc* seg, int n_seg, int row) {
   return lo;
 }
 
+// Compressed entry (16 bytes, read with one scalar load): a run of the entry's segment (its
+// RoPE frame), the segment's entry ids [lo, hi), and pool row - id for the segment's entries.
+struct CEnt {
+  int32_t run, lo, hi, delta;
+};
+// Per logical segment: id of its entry 0, its entry count, and its request offset.
+struct CSeg {
+  int32_t base, count, offset, pad;
+};
+
 // Arguments of the attention kernels (one struct so every variant shares the launch code).
 struct AttnArgs {
   const void* q;          // [q1 - q0][H][d_qk] io dtype (row t at t - q0)
@@ -140,7 +150,16 @@ struct AttnArgs {
   void* z;                // [q1 - q0][H][d_state] bf16
   const int32_t* lhead;   // [HL]
   int32_t HL, z_chunks, rc_rows;  // z_chunks: 16-byte chunks per head's state vector
+  // Compressed-history (dual-pool) launches: one workgroup per (window row, block of 64 heads),
+  // raw keys [t - cwin, t] of kv, then entries of ckv (all available ones, or the row's list).
+  const void* ckv = nullptr;             // [n_cpool][576] bf16
+  const int32_t* cidx = nullptr;         // [nq][topk] entry ids (lists)
+  const int32_t* clen = nullptr;         // [nq] list lengths (lists)
+  const CEnt* cent = nullptr;     // [n_entries]
+  const CSeg* cseg = nullptr;     // [logical segments]
+  int32_t ratio = 1, topk = 0, n_hb = 1, cwin = 0;
 };
+
 
 // Launchers (defined in the kernel sources), all on `stream`.
 hipError_t launch_geometry(const SegDesc* seg, int n_seg, int T, int q0, int q1, int d_rope,
@@ -161,6 +180,9 @@ hipError_t launch_attn_window(const AttnArgs& a, int kv_dtype, int v_has_rope, h
 // bf16 latent, tiles of at most 64 query vectors (one-row windows), split key ranges: two wave
 // sets take alternate key tiles and merge at the end
 hipError_t launch_attn_decode(const AttnArgs& a, int v_has_rope, hipStream_t stream);
+// the same kernel over two pools (bf16): window rows x blocks of 64 heads, outputs written
+// directly; lists = 1 reads per-row entry lists, 0 takes every available entry
+hipError_t launch_attn_dual(const AttnArgs& a, int v_has_rope, int lists, hipStream_t stream);
 hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const float* part_o, const float* part_ml, int n_split, int64_t n_vec,
                             int d, void* out, int out_dtype, float* lse, hipStream_t stream);

@@ -192,7 +192,11 @@ struct TileIt {  // assigned field by field: a whole-struct copy between the rot
   int nval;     // rows of the tile that are in range (1..kKT)
   int pos0;     // request position of the tile's first row
   int pend;     // end (exclusive) of the segment's positions inside the key range
-  int64_t src;  // the tile's first row: bf16 latent, byte offset in the pool; E4M3, its row
+  int64_t src;  // the tile's first row: bf16 latent, byte offset in the pool; E4M3, its row;
+                // listed entries: pool row - id of the segment's entries
+  int ph;       // decode kernel over two pools: 0 raw keys, 1 compressed entries
+  int cur;      // compressed entries: id of the first (all available) or list position (lists)
+  int lo;       // listed entries: lane of the first id in the step's id vector
 };
 
 // Stage one bf16 tile of up to 32 latent rows with direct global->LDS 16-byte copies: one
@@ -851,6 +855,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_mfma(AttnArgs a) {
 // softmax and output, in its own RoPE frame; at the end set 1's (max, sum, output) go through
 // LDS and set 0 merges them by the stable log-sum-exp rule (RedKnot-MLA paper, relocation
 // paragraph) before the partial or final stores of k_attn_mfma.
+//
+// The same kernel runs the compressed-history layers of DeepSeek-V4 (CSA / HCA: TensorRT-LLM
+// reading notes, section 1, the dual-pool kernel paragraph) under relocation: a workgroup takes
+// one request row and 64 heads; its key walk covers the raw window [t - w, t] of the latent
+// pool (runs of segments, as above) and then compressed entries of a second pool, one softmax
+// over both. Entries come either as every entry available at the row (HCA: consecutive ids,
+// contiguous per segment in the pool) or as the row's list (CSA): a tile then holds up to 32
+// consecutive list entries of one segment, each gathered row by row (one 64-lane copy per nope
+// row from a scalar address, per-lane addresses for the RoPE copy). The list ids of a step are
+// read a step ahead, one id per lane, before that step's copies are issued (vector loads retire
+// in order), and the run of a segment is cut with a ballot. An entry's RoPE frame is its
+// segment's, so the query rotation and output frame steps are the raw keys' ones.
+constexpr int kDecSplit = 0, kDecAll = 1, kDecList = 2;  // decode-kernel modes
 constexpr int kDecBuf = 4;
 #ifndef SEGMLA_DEC_QREG
 #define SEGMLA_DEC_QREG 24
@@ -872,7 +889,10 @@ static_assert(kDecLdsAlloc <= 160 * 1024, "LDS budget");
 static_assert(2 * 64 * 18 * 16 * 4 <= kDecQBase, "set 1's outputs fit in the tile buffers");
 static_assert(2 * 64 * 8 <= (32 - kDecQReg) * kDecQSlot, "set 1's (max, sum) fit in the slots");
 
-template <bool VROPE>
+typedef const __attribute__((address_space(4))) CEnt ccent_t;
+typedef const __attribute__((address_space(4))) CSeg ccseg_t;
+
+template <bool VROPE, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   extern __shared__ __attribute__((aligned(256))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -885,16 +905,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   // split's first segment; scalar loads do not queue behind vector-memory copies)
   const int t_max = a.map.q0 + a.map.nq - 1;
   int k_lo = 0, k_hi = t_max + 1;
-  if (a.n_split > 1) {
+  if (MODE == kDecSplit && a.n_split > 1) {
     k_lo = split * a.split_keys;
     k_hi = min(k_hi, k_lo + a.split_keys);
   }
+  int t_row = 0, row_i = 0, hb = 0;
+  if constexpr (MODE != kDecSplit) {
+    // consecutive rows (which share most keys) on one XCD: blocks are dealt to the 8 XCDs in
+    // turn, so block b runs on XCD b % 8 and takes the (b / 8)-th item of that XCD's share
+    const int nwg = a.map.nq * a.n_hb;
+    const int per = (nwg + 7) >> 3;
+    const int item = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+    if (item >= nwg) return;
+    row_i = item / a.n_hb;
+    hb = item - row_i * a.n_hb;
+    t_row = a.map.q0 + row_i;
+    k_lo = max(0, t_row - a.cwin);
+    k_hi = t_row + 1;
+  }
   if (k_lo >= k_hi) return;  // uniform over the workgroup
   typedef const __attribute__((address_space(4))) int32_t cint_t;
-  const int tile = ((cint_t*)a.work)[rank];
+  const int tile = MODE == kDecSplit ? ((cint_t*)a.work)[rank] : 0;
   const int seg_lo = ((cint_t*)a.seg_of_row)[k_lo];
-  if (tile < 0 || tile >= a.map.nF + a.map.nG) return;  // uniform, before any copy is issued
+  if (MODE == kDecSplit && (tile < 0 || tile >= a.map.nF + a.map.nG)) return;  // uniform, before any copy
   cseg_t* const sg = (cseg_t*)a.seg;
+  // compressed entries: those with ids below n_avail are available at the row; lists are read
+  // up to position n_list
+  int n_avail = 0, n_list = 0;
+  if constexpr (MODE != kDecSplit) {
+    ccseg_t* const cs = (ccseg_t*)a.cseg + sg[((cint_t*)a.seg_of_row)[t_row]].frame;
+    n_avail = cs->base + min(cs->count, (t_row - cs->offset + 1) / a.ratio);
+    if constexpr (MODE == kDecList) n_list = min(max(((cint_t*)a.clen)[row_i], 0), a.topk);
+  }
+  // list ids of the step being set up (lane j: position ibase + j), and of the next step
+  int idv = 0, idv_n = 0, ibase = 0, ibase_n = 0;
+  const int32_t* const clist = MODE == kDecList ? a.cidx + (int64_t)row_i * a.topk : nullptr;
+  auto load_ids = [&](int base) __attribute__((always_inline)) -> int {
+    return clist[min(base + lane, a.topk - 1)];
+  };
   // the tile's query vectors: set after the first copies are issued
   int t = -1, h = 0;
   bool valid = false;
@@ -942,6 +990,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
     c.nval = min(kKT, c.pend - k_lo);
     c.src = (sg[lo].pool_row + (k_lo - off)) * kRowBytes;
     c.v = 1;
+    if constexpr (MODE != kDecSplit) {
+      c.ph = 0;
+      c.cur = 0;
+      c.lo = 0;
+    }
+  };
+  // the compressed tile that starts at id (all entries) or list position `cursor`
+  auto comp_at = [&](TileIt& nx, int cursor) __attribute__((always_inline)) {
+    if constexpr (MODE == kDecAll) {
+      if (cursor >= n_avail) return;
+      ccent_t* const e = (ccent_t*)a.cent + cursor;
+      const int lim = min(e->hi, n_avail);
+      nx.v = 1;
+      nx.ph = 1;
+      nx.seg = e->run;
+      nx.cur = cursor;
+      nx.lo = 0;
+      nx.pos0 = -kKT;  // no causal mask: every entry of the walk is available
+      nx.pend = 0;
+      nx.nval = min(kKT, lim - cursor);
+      nx.src = (int64_t)(cursor + e->delta) * kRowBytes;
+    } else if constexpr (MODE == kDecList) {
+      if (cursor >= n_list) return;
+      const int o = cursor - ibase;  // 0..32: at most one tile before it in the step
+      const int c0 = __builtin_amdgcn_readlane(idv, o);
+      if (c0 < 0 || c0 >= n_avail) return;  // the list ends at an id that is not available
+      ccent_t* const e = (ccent_t*)a.cent + c0;
+      const int lim = min(e->hi, n_avail);
+      // the leading run of list entries inside this segment's available ids
+      const bool in = lane >= o && lane < o + kKT && ibase + lane < n_list && idv >= e->lo && idv < lim;
+      const uint64_t run = __ballot(in) >> o;
+      nx.v = 1;
+      nx.ph = 1;
+      nx.seg = e->run;
+      nx.cur = cursor;
+      nx.lo = o;
+      nx.pos0 = -kKT;
+      nx.pend = 0;
+      nx.nval = min(kKT, (int)__builtin_ctzll(~run));
+      nx.src = e->delta;
+    }
   };
   auto advance = [&](const TileIt& c, TileIt& nx) __attribute__((always_inline)) {
     nx.v = 0;  // no next tile: a fully masked dummy (see the step loop)
@@ -950,32 +1039,83 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
     nx.pos0 = c.pos0;
     nx.pend = c.pend;
     nx.src = c.src;
-    if (!c.v) return;
-    if (c.pos0 + kKT < c.pend) {
+    if constexpr (MODE == kDecSplit) {
+      if (!c.v) return;
+      if (c.pos0 + kKT < c.pend) {
+        nx.v = 1;
+        nx.seg = c.seg;
+        nx.pos0 = c.pos0 + kKT;
+        nx.pend = c.pend;
+        nx.nval = min(kKT, c.pend - nx.pos0);
+        nx.src = c.src + kKT * kRowBytes;
+        return;
+      }
+      if (c.seg + 1 >= a.n_seg) return;
+      const int off = sg[c.seg + 1].offset;  // segments are contiguous: off == c.pend
+      if (off >= k_hi) return;
       nx.v = 1;
-      nx.seg = c.seg;
-      nx.pos0 = c.pos0 + kKT;
-      nx.pend = c.pend;
-      nx.nval = min(kKT, c.pend - nx.pos0);
-      nx.src = c.src + kKT * kRowBytes;
-      return;
+      nx.seg = c.seg + 1;
+      nx.pos0 = off;
+      nx.pend = min(off + sg[c.seg + 1].len, k_hi);
+      nx.nval = min(kKT, nx.pend - off);
+      nx.src = sg[c.seg + 1].pool_row * kRowBytes;
+    } else {
+      nx.ph = c.ph;
+      nx.cur = c.cur;
+      nx.lo = c.lo;
+      if (!c.v) return;
+      if (c.ph) {
+        comp_at(nx, c.cur + c.nval);
+        return;
+      }
+      if (c.pos0 + kKT < c.pend) {
+        nx.v = 1;
+        nx.pos0 = c.pos0 + kKT;
+        nx.nval = min(kKT, c.pend - nx.pos0);
+        nx.src = c.src + kKT * kRowBytes;
+        return;
+      }
+      if (c.seg + 1 < a.n_seg) {
+        const int off = sg[c.seg + 1].offset;
+        if (off < k_hi) {
+          nx.v = 1;
+          nx.seg = c.seg + 1;
+          nx.pos0 = off;
+          nx.pend = min(off + sg[c.seg + 1].len, k_hi);
+          nx.nval = min(kKT, nx.pend - off);
+          nx.src = sg[c.seg + 1].pool_row * kRowBytes;
+          return;
+        }
+      }
+      comp_at(nx, 0);  // the raw window is done: the first compressed tile
     }
-    if (c.seg + 1 >= a.n_seg) return;
-    const int off = sg[c.seg + 1].offset;  // segments are contiguous: off == c.pend
-    if (off >= k_hi) return;
-    nx.v = 1;
-    nx.seg = c.seg + 1;
-    nx.pos0 = off;
-    nx.pend = min(off + sg[c.seg + 1].len, k_hi);
-    nx.nval = min(kKT, nx.pend - off);
-    nx.src = sg[c.seg + 1].pool_row * kRowBytes;
   };
-  auto issue = [&](const TileIt& c, int b) __attribute__((always_inline)) {
+  auto issue = [&](const TileIt& c, int b, int ids) __attribute__((always_inline)) {
     char* buf = lds + b * kTileBytes;
+    if constexpr (MODE == kDecList) {
+      if (c.ph) {  // listed entries, row by row; rows past nval repeat the last one
+        const uint32_t lb = lds_addr(buf);
+        const int ln = lane_id();
+        const char* const cp = (const char*)a.ckv;
+#pragma unroll
+        for (int n = 0; n < kKT / kWaves; ++n) {
+          const int r = wave + kWaves * n;
+          const int id = __builtin_amdgcn_readlane(ids, c.lo + min(r, c.nval - 1));
+          dma16(cp + (int64_t)(id + (int)c.src) * kRowBytes, (ln * 16) ^ (fn(r) << 4), lb + r * kNRow);
+        }
+        const int r = 8 * wave + (ln >> 3);
+        const int id = __builtin_amdgcn_ds_bpermute(4 * (c.lo + min(r, c.nval - 1)), ids);
+        dma16_v(cp + (int64_t)(id + (int)c.src) * kRowBytes + kNRow + (((ln & 7) ^ fr(r)) << 4),
+                lb + kRBase + wave * 1024);
+        return;
+      }
+    }
+    const char* pool = (const char*)a.kv;
+    if constexpr (MODE == kDecAll) pool = c.ph ? (const char*)a.ckv : pool;
     if (__builtin_expect(c.nval == kKT, 1))
-      load_tile_bf16_full(buf, (const char*)a.kv + c.src, wave);
+      load_tile_bf16_full(buf, pool + c.src, wave);
     else
-      load_tile_bf16(buf, (const char*)a.kv + c.src, c.nval, wave);
+      load_tile_bf16(buf, pool + c.src, c.nval, wave);
   };
   // q^r <- R(-rot_i) q^r from the stored query (registers)
   auto rotate_q = [&](int seg) __attribute__((always_inline)) {
@@ -1162,10 +1302,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   // segment (their loads retire after the copies), all behind one wait
   TileIt a0, b0, a1, b1;
   first_tile(a0);
+  if constexpr (MODE == kDecList) {
+    // a one-tile window: the second tile is listed and its ids are needed now (read before any
+    // copy is issued; otherwise the first ids are read with the step's copies, below)
+    if (__builtin_expect(k_lo + a0.nval >= k_hi, 0)) {
+      idv = load_ids(0);
+      // a use the compiler sees: its own wait goes here, before any copy, and the load is
+      // known complete on every path after it (a wait it cannot see would leave the load
+      // pending in its books, and later waits for it would also wait for the copies)
+      asm volatile("" ::"v"(idv));
+    }
+  }
   advance(a0, b0);
-  issue(a0, 0);
-  if (b0.v) issue(b0, 1);
-  valid = tile_qvec(a.map, tile, grp * 32 + col, t, h);
+  if constexpr (MODE == kDecList) {
+    ibase_n = b0.ph ? b0.cur + b0.nval : 0;
+    idv_n = load_ids(ibase_n);
+  }
+  issue(a0, 0, idv);
+  if (b0.v) issue(b0, 1, idv);
+  if constexpr (MODE == kDecSplit) {
+    valid = tile_qvec(a.map, tile, grp * 32 + col, t, h);
+  } else {
+    t = t_row;
+    h = hb * 64 + grp * 32 + col;
+    valid = h < a.map.H;
+    if (!valid) h = 0;  // a past-the-end head of the last block reads head 0's query (masked)
+  }
   if (!valid) t = -1;
   qrow = (const __bf16*)a.q + ((int64_t)(valid ? t - a.q0 : 0) * a.map.H + h) * kD;
 #pragma unroll
@@ -1192,6 +1354,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (MODE == kDecList) {
+    idv = idv_n;
+    ibase = ibase_n;
+  }
   // One step per pair of tiles: (a0, b0) resident in buffers cb, cb + 1 (set 0 takes a0, set 1
   // b0), (a1, b1) copied into the other two; then the roles swap.
   int cb = 0;
@@ -1207,8 +1373,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
     prepare(w);
     advance(b0, a1);
     advance(a1, b1);
-    if (a1.v) issue(a1, ob);
-    if (b1.v) issue(b1, ob + 1);
+    if constexpr (MODE == kDecList) {  // the next step's ids, ahead of this step's copies
+      ibase_n = b1.ph ? b1.cur + b1.nval : 0;
+      idv_n = load_ids(ibase_n);
+    }
+    if (a1.v) issue(a1, ob, idv);
+    if (b1.v) issue(b1, ob + 1, idv);
     // a set without a tile in this step (the range's last, odd tile) runs the same code on the
     // other set's buffer with every key masked: no state changes, and the accumulator MFMAs
     // stay unconditional (a conditional call made the register allocator shuffle them)
@@ -1219,6 +1389,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
     if (!a1.v) break;
     a0.v = a1.v; a0.seg = a1.seg; a0.nval = a1.nval; a0.pos0 = a1.pos0; a0.pend = a1.pend; a0.src = a1.src;
     b0.v = b1.v; b0.seg = b1.seg; b0.nval = b1.nval; b0.pos0 = b1.pos0; b0.pend = b1.pend; b0.src = b1.src;
+    if constexpr (MODE != kDecSplit) {
+      a0.ph = a1.ph; a0.cur = a1.cur; a0.lo = a1.lo;
+      b0.ph = b1.ph; b0.cur = b1.cur; b0.lo = b1.lo;
+    }
+    if constexpr (MODE == kDecList) {
+      idv = idv_n;
+      ibase = ibase_n;
+    }
     cb = ob;
   }
   settle_agpr(acc);
@@ -1263,7 +1441,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   };
   const int d_v = a.d_v;
   if (!valid) return;
-  if (a.n_split > 1) {
+  if (MODE == kDecSplit && a.n_split > 1) {
     const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
     const int64_t v = (int64_t)tile * kTileQ + grp * 32 + col;
     float* po = a.part_o + ((int64_t)split * nvec + v) * d_v;
@@ -1323,22 +1501,29 @@ hipError_t launch_any(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream
 }  // namespace
 
 namespace {
-template <bool VROPE>
+template <bool VROPE, int MODE>
 hipError_t launch_dec(const AttnArgs& a, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)k_attn_dec<VROPE>, hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsAlloc);
+      (const void*)k_attn_dec<VROPE, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsAlloc);
   if (attr != hipSuccess) return attr;
-  const int64_t blocks = (int64_t)(a.map.nF + a.map.nG) * a.n_split;
+  const int64_t blocks = MODE == kDecSplit ? (int64_t)(a.map.nF + a.map.nG) * a.n_split
+                                           : 8 * (((int64_t)a.map.nq * a.n_hb + 7) / 8);
   if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_attn_dec<VROPE>), dim3((unsigned)blocks), dim3(kThreads), kDecLdsAlloc,
+  hipLaunchKernelGGL((k_attn_dec<VROPE, MODE>), dim3((unsigned)blocks), dim3(kThreads), kDecLdsAlloc,
                      stream, a);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs& a, int v_has_rope, hipStream_t stream) {
-  return v_has_rope ? launch_dec<true>(a, stream) : launch_dec<false>(a, stream);
+  return v_has_rope ? launch_dec<true, kDecSplit>(a, stream) : launch_dec<false, kDecSplit>(a, stream);
+}
+
+hipError_t launch_attn_dual(const AttnArgs& a, int v_has_rope, int lists, hipStream_t stream) {
+  if (lists)
+    return v_has_rope ? launch_dec<true, kDecList>(a, stream) : launch_dec<false, kDecList>(a, stream);
+  return v_has_rope ? launch_dec<true, kDecAll>(a, stream) : launch_dec<false, kDecAll>(a, stream);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream) {

@@ -905,6 +905,138 @@ segmla_status segmla_lse_merge(const float* partial_o, const float* partial_ml, 
   return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
 }
 
+// ----------------------------------------------------------- compressed-history layers
+struct segmla_dual {
+  const segmla_plan* plan = nullptr;
+  int32_t ratio = 1, window = 0, top_k = 0;
+  int64_t n_cpool = 0, n_entries = 0;
+  std::vector<char> upload;  // CSeg per segment, then CEnt per entry (the device tables)
+  size_t o_cseg = 0, o_cent = 0, ws_bytes = 0;
+  bool built = false;
+  char* ws = nullptr;
+};
+
+segmla_status segmla_dual_create(const segmla_plan* p, const segmla_dual_pool* dp,
+                                 segmla_dual** out) {
+  if (!p || !dp || !out || !dp->cpool_row) return SEGMLA_E_NULL;
+  if (p->kv_dtype != SEGMLA_BF16 || p->io_dtype != SEGMLA_BF16 || p->d_nope != 512 || p->d_rope != 64)
+    return SEGMLA_E_UNSUPPORTED;
+  if (dp->ratio < 1 || dp->window < 0 || dp->top_k < 0 || dp->n_cpool < 0 || dp->n_cpool > INT32_MAX)
+    return SEGMLA_E_SHAPE;
+  const int32_t n = p->n_seg;
+  std::vector<CSeg> cs(n);
+  int64_t base = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t cnt = p->segs[i].len / dp->ratio;
+    const int64_t r0 = dp->cpool_row[i];
+    if (r0 < 0 || r0 + cnt > dp->n_cpool) return SEGMLA_E_GEOMETRY;
+    cs[i].base = (int32_t)base;
+    cs[i].count = (int32_t)cnt;
+    cs[i].offset = p->segs[i].offset;
+    cs[i].pad = 0;
+    base += cnt;
+  }
+  // a run of each segment: its RoPE frame (every run of a segment has the same phase shift)
+  std::vector<int32_t> first_run(n, -1);
+  for (int32_t r = p->n_run - 1; r >= 0; --r) first_run[p->runs[r].frame] = r;
+  std::vector<CEnt> ce((size_t)base);
+  for (int32_t i = 0; i < n; ++i) {
+    const CEnt e = {first_run[i], cs[i].base, cs[i].base + cs[i].count,
+                    (int32_t)(dp->cpool_row[i] - cs[i].base)};
+    for (int32_t j = 0; j < cs[i].count; ++j) ce[(size_t)cs[i].base + j] = e;
+  }
+  segmla_dual* d = new segmla_dual;
+  d->plan = p;
+  d->ratio = dp->ratio;
+  d->window = dp->window;
+  d->top_k = dp->top_k;
+  d->n_cpool = dp->n_cpool;
+  d->n_entries = base;
+  d->o_cseg = 0;
+  d->o_cent = align256(sizeof(CSeg) * n);
+  d->ws_bytes = align256(d->o_cent + sizeof(CEnt) * ce.size());
+  d->upload.assign(d->ws_bytes, 0);
+  std::memcpy(d->upload.data() + d->o_cseg, cs.data(), sizeof(CSeg) * n);
+  if (!ce.empty()) std::memcpy(d->upload.data() + d->o_cent, ce.data(), sizeof(CEnt) * ce.size());
+  *out = d;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_dual_sizes(const segmla_dual* d, size_t* workspace_bytes, int64_t* n_entries) {
+  if (!d) return SEGMLA_E_NULL;
+  if (workspace_bytes) *workspace_bytes = d->ws_bytes;
+  if (n_entries) *n_entries = d->n_entries;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_dual_build(segmla_dual* d, void* workspace, size_t bytes, void* stream) {
+  if (!d || !workspace) return SEGMLA_E_NULL;
+  if (bytes < d->ws_bytes || (uintptr_t)workspace % 256 != 0) return SEGMLA_E_WORKSPACE;
+  d->built = false;
+  if (hipMemcpyAsync(workspace, d->upload.data(), d->ws_bytes, hipMemcpyHostToDevice,
+                     (hipStream_t)stream) != hipSuccess)
+    return SEGMLA_E_HIP;
+  d->ws = (char*)workspace;
+  d->built = true;
+  return SEGMLA_OK;
+}
+
+segmla_status segmla_dual_forward(const segmla_dual* d, const segmla_dual_tensors* t, void* stream) {
+  if (!d || !t) return SEGMLA_E_NULL;
+  if (!t->q || !t->kv || !t->ckv || !t->out) return SEGMLA_E_NULL;
+  if (d->top_k > 0 && (!t->cidx || !t->clen)) return SEGMLA_E_NULL;
+  const segmla_plan* p = d->plan;
+  if (!p->built || !d->built) return SEGMLA_E_STATE;
+  for (const void* ptr : {t->q, t->kv, t->ckv, (const void*)t->out, (const void*)t->lse})
+    if ((uintptr_t)ptr % 16 != 0) return SEGMLA_E_SHAPE;
+  if ((uintptr_t)t->cidx % 4 != 0 || (uintptr_t)t->clen % 4 != 0) return SEGMLA_E_SHAPE;
+  AttnArgs a;
+  a.q = t->q;
+  a.kv = t->kv;
+  a.kv_scale = nullptr;
+  a.kv_rope = nullptr;
+  a.out = t->out;
+  a.lse = t->lse;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.seg = p->at<SegDesc>(p->o_seg);
+  a.seg_of_row = p->at<int32_t>(p->o_seg_of_row);
+  a.segcs = p->at<float2>(p->o_segcs);
+  a.stepcs = p->at<float2>(p->o_stepcs);
+  a.work = nullptr;
+  a.map = tile_map(p);
+  a.n_seg = p->n_run;
+  a.T = p->T;
+  a.d_nope = p->d_nope;
+  a.d_rope = p->d_rope;
+  a.d_v = p->d_v;
+  a.q0 = p->q0;
+  a.n_split = 1;
+  a.split_keys = 0;
+  a.sigma = p->sigma;
+  a.n_sink = 0;
+  a.win = 0;
+  a.z_cached = nullptr;
+  a.z = nullptr;
+  a.lhead = nullptr;
+  a.HL = 0;
+  a.z_chunks = 0;
+  a.rc_rows = 0;
+  a.ckv = t->ckv;
+  a.cidx = d->top_k > 0 ? t->cidx : nullptr;
+  a.clen = d->top_k > 0 ? t->clen : nullptr;
+  a.cent = reinterpret_cast<const CEnt*>(d->ws + d->o_cent);
+  a.cseg = reinterpret_cast<const CSeg*>(d->ws + d->o_cseg);
+  a.ratio = d->ratio;
+  a.topk = d->top_k;
+  a.n_hb = (p->H + 63) / 64;
+  a.cwin = d->window;
+  const hipError_t e = launch_attn_dual(a, p->v_has_rope, d->top_k > 0, (hipStream_t)stream);
+  return e == hipSuccess ? SEGMLA_OK : SEGMLA_E_HIP;
+}
+
+void segmla_dual_destroy(segmla_dual* d) { delete d; }
+
 void segmla_plan_destroy(segmla_plan* p) {
   if (!p) return;
   for (hipEvent_t ev : p->ev)

@@ -28,7 +28,8 @@ EXPORTED = [
     "segmla_plan_create_range", "segmla_plan_create_paged", "segmla_plan_get_info",
     "segmla_forward_noalloc", "segmla_plan_set_window", "segmla_prefetcher_create",
     "segmla_prefetch", "segmla_prefetch_wait", "segmla_prefetch_elapsed",
-    "segmla_prefetcher_destroy",
+    "segmla_prefetcher_destroy", "segmla_dual_create", "segmla_dual_sizes", "segmla_dual_build",
+    "segmla_dual_forward", "segmla_dual_destroy",
 ]
 
 NOALLOC_MAX_BYTES = 96 << 20  # SEGMLA_NOALLOC_MAX_BYTES
@@ -79,6 +80,15 @@ class CopyRange(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("row_bytes", ctypes.c_int64), ("src_stride", ctypes.c_int64),
                 ("dst_stride", ctypes.c_int64)]
+
+
+class DualPool(ctypes.Structure):
+    _fields_ = [("ratio", ctypes.c_int32), ("window", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_cpool", ctypes.c_int64), ("cpool_row", ctypes.c_void_p)]
+
+
+class DualTensors(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "kv", "ckv", "cidx", "clen", "out", "lse")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -138,6 +148,11 @@ def lib():
             "segmla_profile_enable": (i32, [P, i32]),
             "segmla_profile_read": (i32, [P, ctypes.POINTER(dbl), ctypes.POINTER(i64),
                                           ctypes.POINTER(i64)]),
+            "segmla_dual_create": (i32, [P, ctypes.POINTER(DualPool), ctypes.POINTER(P)]),
+            "segmla_dual_sizes": (i32, [P, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i64)]),
+            "segmla_dual_build": (i32, [P, P, ctypes.c_size_t, P]),
+            "segmla_dual_forward": (i32, [P, ctypes.POINTER(DualTensors), P]),
+            "segmla_dual_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -470,6 +485,95 @@ class Prefetcher:
             self.close()
         except Exception:
             pass
+
+
+def segmla_dual_create(plan, ratio, window, top_k, cpool_rows, n_cpool):
+    rows = _arr(cpool_rows, np.int64)
+    dp = DualPool(int(ratio), int(window), int(top_k), int(n_cpool),
+                  rows.ctypes.data_as(ctypes.c_void_p))
+    h = ctypes.c_void_p()
+    _check(lib().segmla_dual_create(plan, ctypes.byref(dp), ctypes.byref(h)), "segmla_dual_create")
+    return h
+
+
+def segmla_dual_sizes(dual):
+    nb, ne = ctypes.c_size_t(), ctypes.c_int64()
+    _check(lib().segmla_dual_sizes(dual, ctypes.byref(nb), ctypes.byref(ne)), "segmla_dual_sizes")
+    return int(nb.value), int(ne.value)
+
+
+def segmla_dual_build(dual, workspace, stream=None):
+    import torch
+    need, _ = segmla_dual_sizes(dual)
+    _check_tensors([("workspace", workspace, (torch.uint8,), need, True)])
+    _check(lib().segmla_dual_build(dual, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "segmla_dual_build")
+
+
+def check_dual_tensors(info, top_k, n_cpool, q, kv, ckv, out, cidx=None, clen=None, lse=None):
+    """Validate the tensors of one dual-pool forward against the plan's shapes."""
+    import torch
+    nq = info["q_end"] - info["q_begin"]
+    H, dqk, dv = info["n_heads"], info["d_nope"] + info["d_rope"], info["d_v"]
+    bf = (torch.bfloat16,)
+    specs = [("q", q, bf, nq * H * dqk, True), ("kv", kv, bf, info["n_pool"] * dqk, True),
+             ("ckv", ckv, bf, n_cpool * dqk, True), ("out", out, bf, nq * H * dv, True),
+             ("lse", lse, (torch.float32,), nq * H, False)]
+    if top_k > 0:
+        specs += [("cidx", cidx, (torch.int32,), nq * top_k, True),
+                  ("clen", clen, (torch.int32,), nq, True)]
+    elif cidx is not None or clen is not None:
+        raise ValueError("cidx / clen are given but the layer takes every available entry (top_k = 0)")
+    _check_tensors(specs)
+
+
+def segmla_dual_forward(dual, info, top_k, n_cpool, q, kv, ckv, out, cidx=None, clen=None,
+                        lse=None, stream=None):
+    check_dual_tensors(info, top_k, n_cpool, q, kv, ckv, out, cidx, clen, lse)
+    t = DualTensors(_ptr(q), _ptr(kv), _ptr(ckv), _ptr(cidx), _ptr(clen), _ptr(out), _ptr(lse))
+    _check(lib().segmla_dual_forward(dual, ctypes.byref(t), _stream(stream)), "segmla_dual_forward")
+
+
+def segmla_dual_destroy(dual):
+    if dual:
+        lib().segmla_dual_destroy(dual)
+
+
+class Dual:
+    """Compressed-history (dual-pool) attention on a plan (segmla_dual_*), with the workspace
+    of its entry tables (torch uint8 tensor on the current GPU). The plan must outlive it."""
+
+    def __init__(self, plan, ratio, window, top_k, cpool_rows, n_cpool):
+        self.plan, self.top_k, self.n_cpool = plan, int(top_k), int(n_cpool)
+        self.handle = segmla_dual_create(plan.handle, ratio, window, top_k, cpool_rows, n_cpool)
+        self.ws_bytes, self.n_entries = segmla_dual_sizes(self.handle)
+        self.workspace = None
+
+    def build(self, stream=None):
+        import torch
+        self.workspace = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device="cuda")
+        segmla_dual_build(self.handle, self.workspace, stream)
+
+    def forward(self, q, kv, ckv, out, cidx=None, clen=None, lse=None, stream=None):
+        """q, out, lse, cidx and clen: the rows of the plan's window."""
+        segmla_dual_forward(self.handle, segmla_plan_get_info(self.plan.handle), self.top_k,
+                            self.n_cpool, q, kv, ckv, out, cidx, clen, lse, stream)
+
+    def close(self):
+        if self.handle:
+            segmla_dual_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @classmethod
+    def for_inputs(cls, plan, dual_inp):
+        return cls(plan, dual_inp["ratio"], dual_inp["window"], dual_inp["top_k"],
+                   dual_inp["cpool_rows"], dual_inp["n_cpool"])
 
 
 # ------------------------------------------------------------------ convenience

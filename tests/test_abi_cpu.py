@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert S.segmla_abi_version() == 4
+    assert S.segmla_abi_version() == 5
     for st in range(-9, 1):
         assert S.segmla_status_string(st) not in ("", "unknown status")
     assert S.segmla_status_string(-100) == "unknown status"
@@ -525,3 +525,85 @@ def test_prefetch_argument_errors(L):
     if not torch.cuda.is_available():
         h = ctypes.c_void_p()
         assert L.segmla_prefetcher_create(ctypes.byref(h)) == S.SEGMLA_E_HIP and not h.value
+
+
+def test_dual_pool_errors(L):
+    """Compressed-history attention (segmla_dual_*): the compressed geometry is validated at
+    create time (ratio, window, list width, pool size: SEGMLA_E_SHAPE; a segment's entries
+    outside the pool: SEGMLA_E_GEOMETRY; an fp32 or E4M3 layer: SEGMLA_E_UNSUPPORTED), the entry
+    count is the sum of floor(len / ratio) over segments, a forward of an unbuilt object is
+    SEGMLA_E_STATE, and the binding checks every tensor (lists required exactly when top_k > 0)."""
+    import torch
+    cfg = SMALL_CONFIGS[1]
+    kinds, lens, offsets = segment_table(cfg)
+    T = int(lens.sum())
+    p = _create(cfg)
+    lib = S.lib()
+    try:
+        cpr = np.concatenate([[0], np.cumsum(lens // 4)[:-1]])
+        n_c = int((lens // 4).sum())
+
+        def st(ratio=4, window=127, top_k=8, rows=cpr, n_cpool=n_c):
+            try:
+                d = S.segmla_dual_create(p, ratio, window, top_k, rows, n_cpool)
+            except S.SegmlaError as e:
+                return e.status
+            S.segmla_dual_destroy(d)
+            return S.SEGMLA_OK
+        assert st() == S.SEGMLA_OK
+        assert st(ratio=0) == S.SEGMLA_E_SHAPE
+        assert st(window=-1) == S.SEGMLA_E_SHAPE
+        assert st(top_k=-1) == S.SEGMLA_E_SHAPE
+        assert st(n_cpool=-1) == S.SEGMLA_E_SHAPE
+        assert st(n_cpool=2 ** 31) == S.SEGMLA_E_SHAPE
+        assert st(n_cpool=n_c - 1) == S.SEGMLA_E_GEOMETRY
+        assert st(rows=cpr - 1) == S.SEGMLA_E_GEOMETRY
+        assert st(ratio=10 ** 6, n_cpool=0, rows=np.zeros_like(cpr)) == S.SEGMLA_OK  # no entries
+        dp = S.DualPool(4, 127, 8, n_c, None)
+        h = ctypes.c_void_p()
+        assert lib.segmla_dual_create(p, ctypes.byref(dp), ctypes.byref(h)) == S.SEGMLA_E_NULL
+        d = S.segmla_dual_create(p, 4, 127, 8, cpr, n_c)
+        try:
+            ws, ne = S.segmla_dual_sizes(d)
+            assert ne == n_c and ws % 256 == 0 and ws >= 16 * (n_c + len(lens))
+            info = S.segmla_plan_get_info(p)
+            bf = torch.bfloat16
+            good = dict(q=torch.zeros(T, 64, 576, dtype=bf), kv=torch.zeros(T, 576, dtype=bf),
+                        ckv=torch.zeros(n_c, 576, dtype=bf), out=torch.zeros(T, 64, 576, dtype=bf),
+                        cidx=torch.zeros(T, 8, dtype=torch.int32),
+                        clen=torch.zeros(T, dtype=torch.int32))
+
+            def err(top_k=8, **over):
+                args = dict(good)
+                args.update(over)
+                with pytest.raises(ValueError) as e:
+                    S.segmla_dual_forward(d, info, top_k, n_c, **args)
+                return str(e.value)
+            assert "q must be on the GPU" in err()
+            assert "ckv holds" in err(ckv=torch.zeros(n_c - 1, 576, dtype=bf))
+            assert "cidx is required" in err(cidx=None)
+            assert "cidx has dtype" in err(cidx=torch.zeros(T, 8, dtype=torch.int64))
+            assert "clen holds" in err(clen=torch.zeros(T - 1, dtype=torch.int32))
+            assert "every available entry" in err(top_k=0)
+            assert "out has dtype" in err(out=torch.zeros(T, 64, 576))
+            if _no_gpu():  # unbuilt plan and object: nothing is enqueued
+                t = S.DualTensors(*([8192] * 6 + [None]))
+                assert lib.segmla_dual_forward(d, ctypes.byref(t), None) == S.SEGMLA_E_STATE
+                t = S.DualTensors(8192, 8192, 8192, None, None, 8192, None)
+                assert lib.segmla_dual_forward(d, ctypes.byref(t), None) == S.SEGMLA_E_NULL
+                # a workspace off the 256-byte grid or too small, before any copy
+                assert lib.segmla_dual_build(d, ctypes.c_void_p(4096 + 8), ws, None) == S.SEGMLA_E_WORKSPACE
+                assert lib.segmla_dual_build(d, ctypes.c_void_p(4096), ws - 256, None) == S.SEGMLA_E_WORKSPACE
+        finally:
+            S.segmla_dual_destroy(d)
+    finally:
+        S.segmla_plan_destroy(p)
+    for c in (SMALL_CONFIGS[0], SMALL_CONFIGS[4]):  # fp32 layer, E4M3 latent
+        q = _create(c)
+        try:
+            k2, l2, _ = segment_table(c)
+            with pytest.raises(S.SegmlaError) as e:
+                S.segmla_dual_create(q, 4, 127, 0, np.zeros(len(l2), np.int64), 10 ** 6)
+            assert e.value.status == S.SEGMLA_E_UNSUPPORTED
+        finally:
+            S.segmla_plan_destroy(q)
