@@ -15,7 +15,10 @@ layer) as the "window_heads" figures. A row-window plan of the 128K layer's last
 131,584 keys) is the "decode" figure, its whole forward against the HBM roofline (latent
 rows, W, and the row's q, out and z moved once). The main workload over a paged latent pool
 (64-row pages in shuffled order) is the "paged" figure, and the main workload with its
-projected state in groups of 8 heads (z and the cache per group) the "grouped" figure.
+projected state in groups of 8 heads (z and the cache per group) the "grouped" figure. The
+main request as DeepSeek-V4 compressed-history layers (a CSA layer: 128-token window and
+512-entry lists of 4-to-1 entries; an HCA layer: 128-token window and every 128-to-1 entry),
+every row and the last row alone, are the "dual_pool" figures.
 Throughput is algorithmic
 attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the
 step time.
@@ -23,6 +26,7 @@ step time.
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                 [--no-target] [--no-fp8] [--many-short NAME] [--window NAMES] [--no-cpu-baseline]
                 [--decode-rows N] [--decode-only] [--paged-rows P] [--grouped NAME]
+                [--dual SPECS] [--dual-only]
 """
 import argparse
 import json
@@ -320,6 +324,105 @@ def measure(cfg_name, steps, warmup, decode_rows=0, pool="identity", also_e4m3=F
     return res
 
 
+def dual_keys(inp, dual, rows):
+    """Keys one head attends per row of `rows` in the dual-pool forward (host count for the
+    FLOP figure): the raw window min(t, w) + 1, plus the entries of the row's walk (every
+    available entry, or the list up to its first id that is not available)."""
+    import numpy as np
+    m, w = dual["ratio"], dual["window"]
+    lens = np.asarray(inp["lens"], dtype=np.int64)
+    offs = np.asarray(inp["offsets"], dtype=np.int64)
+    cnt = lens // m
+    base = np.concatenate([[0], np.cumsum(cnt)[:-1]])
+    rows = np.asarray(rows, dtype=np.int64)
+    s = np.searchsorted(offs, rows, side="right") - 1
+    n_avail = base[s] + np.minimum(cnt[s], (rows - offs[s] + 1) // m)
+    raw = np.minimum(rows, w) + 1
+    if not dual["top_k"]:
+        return raw + n_avail
+    ids = dual["cidx"][torch_index(rows, dual["cidx"])].cpu().numpy().astype(np.int64)
+    clen = dual["clen"][torch_index(rows, dual["clen"])].cpu().numpy().astype(np.int64)
+    k = np.arange(ids.shape[1])[None, :]
+    ok = (k < clen[:, None]) & (ids >= 0) & (ids < n_avail[:, None])
+    lead = np.where(ok.all(axis=1), ids.shape[1], np.argmin(ok, axis=1))
+    return raw + lead
+
+
+def torch_index(rows, t):
+    import torch
+    return torch.as_tensor(rows, device=t.device)
+
+
+def measure_dual(cfg_name, ratio, window, top_k, steps, warmup):
+    """The compressed-history (dual-pool) attention of the workload's request: every row with
+    all its heads (a CSA layer: ratio 4, 512-entry lists; an HCA layer: ratio 128, every
+    available entry), and its last row alone (decode). Event-timed on the launch stream."""
+    import numpy as np
+    import torch
+    from segmented_attention_amd import segmla as S
+    from workload import config_by_name, make_dual_inputs, make_inputs
+
+    cfg = config_by_name(cfg_name)
+    kind = "csa" if top_k else "hca"
+    log("workload %s: %s dual-pool layer (ratio %d, window %d, lists %d)"
+        % (cfg_name, kind, ratio, window, top_k))
+    inp = make_inputs(cfg, "cuda")
+    dual = make_dual_inputs(inp, ratio, window, top_k, "cuda")
+    T, H = inp["T"], cfg["n_heads"]
+    res = {"workload": cfg_name, "layer": kind, "ratio": ratio, "window": window,
+           "top_k": top_k, "rows": T, "heads": H}
+    for q_range in (None, (T - 1, T)):
+        q0, q1 = q_range if q_range else (0, T)
+        plan = S.Plan.for_inputs(inp, q_range=q_range)
+        plan.build(inp["scores"])
+        d = S.Dual.for_inputs(plan, dual)
+        d.build()
+        out = torch.empty((q1 - q0, H, inp["d_v"]), dtype=torch.bfloat16, device="cuda")
+        args = (inp["q"][q0:q1], inp["kv"], dual["ckv"], out,
+                dual["cidx"][q0:q1] if top_k else None, dual["clen"][q0:q1] if top_k else None)
+        n = steps if q_range is None else 50
+        for _ in range(warmup):
+            d.forward(*args)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record(st)
+            d.forward(*args)
+            e1.record(st)
+        torch.cuda.synchronize()
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        keys = dual_keys(inp, dual, np.arange(q0, q1))
+        pairs = float(keys.sum()) * H
+        if q_range is None:
+            med = statistics.median(ms)
+            res.update({
+                "keys_per_row_mean": round(float(keys.mean()), 1), "pairs": pairs,
+                "attention_ms_median": round(med, 4), "attention_ms_min": round(min(ms), 4),
+                "attention_tflops": round(flops_per_pair(cfg) * pairs / (med * 1e-3) / 1e12, 3),
+                "attention_frac_bf16_peak": round(flops_per_pair(cfg) * pairs / (med * 1e-3) / 1e12
+                                                  / PEAK_BF16_TFLOPS, 4),
+            })
+        else:
+            us = statistics.median(ms) * 1e3
+            # HBM bytes of one decode row: its keys (raw rows and entries, 1152 bytes each, read
+            # once), the row's q and out (bf16) and its list
+            nbytes = float(keys.sum()) * 1152 + 2 * H * 576 * 2 + 4 * top_k
+            res["decode"] = {"keys": int(keys.sum()), "forward_us_median": round(us, 2),
+                             "forward_us_min": round(min(ms) * 1e3, 2),
+                             "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
+                                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                          "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                                          "bytes": int(nbytes)}}
+        d.close()
+        plan.close()
+        del out
+    del inp, dual
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg_name, budget_s=20.0):
     """The fp64 oracle, as it stands, on a bounded row sample of the same workload."""
     import numpy as np
@@ -426,6 +529,11 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode window of the secondary workload (for kernel "
                          "traces of the decode path) and print its figures")
+    ap.add_argument("--dual", default="csa:4:127:512,hca:128:127:0",
+                    help="compressed-history (dual-pool) layers over the main workload's request, "
+                         "kind:ratio:window:list width, comma-separated; '' for none")
+    ap.add_argument("--dual-only", action="store_true",
+                    help="time only the dual-pool layers (for their kernel traces)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -450,6 +558,14 @@ def main():
         log("workload %s: decode window of the last %d row(s)" % (cfg["name"], args.decode_rows))
         d = measure_window(inp, cfg, args.decode_rows, args.steps, args.warmup)
         print(json.dumps({"decode": decode_json(cfg["name"], d)}), flush=True)
+        return
+    duals = []
+    for spec in [x for x in args.dual.split(",") if x]:
+        _, ratio, window, top_k = spec.split(":")
+        duals.append((int(ratio), int(window), int(top_k)))
+    if args.dual_only:
+        print(json.dumps({"dual_pool": [measure_dual(args.workload, *d, max(5, args.steps), 2)
+                                        for d in duals]}), flush=True)
         return
     main_res = measure(args.workload, args.steps, args.warmup, pool=args.pool)
     # the target figure comes before the long layers (a chip that has run them for seconds
@@ -477,6 +593,7 @@ def main():
     pg = None
     if args.paged_rows > 0:
         pg = measure(args.workload, max(2, args.steps // 2), 1, pool="paged:%d" % args.paged_rows)
+    dres = [measure_dual(args.workload, *d, max(5, args.steps // 2), 2) for d in duals]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload)
 
     r = main_res
@@ -586,6 +703,8 @@ def main():
             "stage_ms": {"attention": round(f8["attn_ms"], 3), "epilogue": round(f8["epi_ms"], 3),
                          "plan_build": round(f8["build_ms"], 3)},
         }
+    if dres:
+        line["dual_pool"] = dres
     print(json.dumps(line), flush=True)
 
 
