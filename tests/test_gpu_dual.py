@@ -9,7 +9,8 @@ prologue); entry ratios 3, 4 and 16 (segments whose length is not a multiple of 
 contiguous, shuffled and paged latent pools and contiguous or shuffled compressed pools; lists
 in Indexer order (ascending), shuffled, with repeated ids, with an id that is not available
 (the walk stops there) and with -1 padding; 64, 96 (a partial head block) and 128 heads; values
-with and without RoPE dims; row windows (a prefill chunk and the last row).
+with and without RoPE dims; row windows (a prefill chunk and the last row), also reached by
+moving a built plan's window; and capture of the forward in a HIP graph.
 """
 import numpy as np
 import pytest
@@ -110,6 +111,7 @@ CASES = [
     ("vnope_csa4", SMALL_CONFIGS[5], "identity", "identity", 4, 127, 100, None),
     ("heads96_csa4", _heads(SMALL_CONFIGS[1], 96), "identity", "identity", 4, 127, 40, "dups+cut"),
     ("heads128_hca4_w40", _heads(SMALL_CONFIGS[1], 128), "shuffled", "identity", 4, 40, 0, None),
+    ("heads16_csa2_w127", _heads(SMALL_CONFIGS[2], 16), "identity", "identity", 2, 127, 64, "shuffle"),
 ]
 
 
@@ -161,3 +163,51 @@ def test_dual_pool_full_size_32k():
         dual = make_dual_inputs(inp, ratio, 127, top_k, "cuda")
         out, lse, _ = _run(inp, dual)
         _check(cfg, _oracle(inp, dual, rows), out, lse, rows)
+
+
+def test_dual_pool_moved_window_and_graph_replays():
+    """A plan built for the whole request, moved to a chunk and then to the last row with
+    segmla_plan_set_window: the dual-pool forward follows the plan's window. The last-row
+    forward captured in a HIP graph and replayed three times, with eager work in between
+    (NaN fills, an eager forward into other buffers), equals the eager forward bit for bit."""
+    cfg = SMALL_CONFIGS[1]
+    inp = make_inputs(cfg, "cuda")
+    dual = make_dual_inputs(inp, 4, 127, 40, "cuda")
+    T, H = inp["T"], cfg["n_heads"]
+    plan = Plan.for_inputs(inp)
+    plan.build(inp["scores"])
+    d = Dual.for_inputs(plan, dual)
+    d.build()
+    for q0, q1 in ((300, 700), (T - 1, T)):
+        say("case dual moved window (%d, %d)" % (q0, q1))
+        plan.set_window(q0, q1)
+        out = torch.full((q1 - q0, H, inp["d_v"]), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((q1 - q0, H), float("nan"), dtype=torch.float32, device="cuda")
+        args = (inp["q"][q0:q1], inp["kv"], dual["ckv"])
+        lists = (dual["cidx"][q0:q1], dual["clen"][q0:q1])
+        d.forward(*args, out, *lists, lse)
+        torch.cuda.synchronize()
+        rows = np.arange(q0, q1)
+        _check(cfg, _oracle(inp, dual, rows), out, lse, rows - q0)
+    # graph capture of the last-row forward
+    ref_o, ref_l = out.clone(), lse.clone()
+    g_o, g_l = torch.empty_like(out), torch.empty_like(lse)
+    e_o, e_l = torch.empty_like(out), torch.empty_like(lse)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        d.forward(*args, g_o, *lists, g_l)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (g_o, g_l, e_o, e_l):
+            t.fill_(float("nan"))
+        d.forward(*args, e_o, *lists, e_l)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in ((g_o, ref_o), (g_l, ref_l), (e_o, ref_o), (e_l, ref_l)):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32))
+        say("  replay %d equal" % rep)
+    del g
+    d.close()
+    plan.close()
