@@ -129,7 +129,7 @@ struct AttnArgs {
   const void* kv_rope;    // E4M3: [n_pool][d_rope] bf16
   void* out;              // [q1 - q0][H][d_v] io dtype (unsplit)
   float* lse;             // [q1 - q0][H] or null (unsplit)
-  float* part_o;          // [n_split][nTiles*kTileQ][d_v] (split)
+  float* part_o;          // [n_split][nTiles*kTileQ][d_v] (split); bf16 values when part_bf16
   float* part_ml;         // [n_split][nTiles*kTileQ][2] (split)
   const SegDesc* seg;
   const int32_t* seg_of_row;  // [T] segment of each request row
@@ -158,6 +158,7 @@ struct AttnArgs {
   const CEnt* cent = nullptr;     // [n_entries]
   const CSeg* cseg = nullptr;     // [logical segments]
   int32_t ratio = 1, topk = 0, n_hb = 1, cwin = 0;
+  int32_t part_bf16 = 0;                 // split partial outputs stored as bf16 (decode kernel)
 };
 
 

@@ -1442,15 +1442,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_dec(AttnArgs a) {
   const int d_v = a.d_v;
   if (!valid) return;
   if (MODE == kDecSplit && a.n_split > 1) {
+    // partial outputs in bf16 (half the bytes written here and read by the merge); the
+    // statistics (max, sum) stay fp32
     const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
     const int64_t v = (int64_t)tile * kTileQ + grp * 32 + col;
-    float* po = a.part_o + ((int64_t)split * nvec + v) * d_v;
+    __bf16* po = (__bf16*)a.part_o + ((int64_t)split * nvec + v) * d_v;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const floatx16 x = merged(f);
 #pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *(float4*)(po + 32 * f + 8 * (i >> 2) + 4 * hf) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+      for (int i = 0; i < 16; i += 4) {
+        const bf16x4 y = {(__bf16)x[i], (__bf16)x[i + 1], (__bf16)x[i + 2], (__bf16)x[i + 3]};
+        *(bf16x4*)(po + 32 * f + 8 * (i >> 2) + 4 * hf) = y;
+      }
     }
     if (hf == 0) {
       float* pm = a.part_ml + ((int64_t)split * nvec + v) * 2;

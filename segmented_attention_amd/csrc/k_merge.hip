@@ -10,9 +10,12 @@ namespace {
 __device__ __forceinline__ void store(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store(__bf16* p, float v) { *p = (__bf16)v; }
 
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const __bf16* p) { return (float)*p; }
+
 // Merge one vector: partial index base_v in split-major arrays of n_vec vectors.
-template <typename OutT>
-__device__ __forceinline__ void merge_vec(const float* __restrict__ part_o,
+template <typename OutT, typename PartT = float>
+__device__ __forceinline__ void merge_vec(const PartT* __restrict__ part_o,
                                           const float* __restrict__ part_ml, int n_split,
                                           int64_t n_vec, int64_t v, int d, OutT* __restrict__ dst,
                                           float* __restrict__ lse_dst, int lane) {
@@ -28,7 +31,7 @@ __device__ __forceinline__ void merge_vec(const float* __restrict__ part_o,
     float num = 0.f;
     for (int s = 0; s < n_split; ++s) {
       float ms = part_ml[((int64_t)s * n_vec + v) * 2];
-      if (ms != -INFINITY) num += expf(ms - M) * part_o[((int64_t)s * n_vec + v) * d + c];
+      if (ms != -INFINITY) num += expf(ms - M) * ld(part_o + ((int64_t)s * n_vec + v) * d + c);
     }
     store(dst + c, num * inv);
   }
@@ -53,8 +56,9 @@ constexpr int kWideChunk = 256;        // channels per workgroup (4 per lane)
 constexpr int kWideBatch = 16;         // splits whose loads a lane has in flight at once
 
 // Forward's merge: vector v = tile * kTileQ + qi goes to out[t][h]; only the splits the
-// attention wrote (split start <= the tile's largest row) are read.
-template <typename OutT>
+// attention wrote (split start <= the tile's largest row) are read. Partials are fp32, or bf16
+// from the decode kernel.
+template <typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void k_merge_tiles(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(256) void k_merge_tiles(AttnArgs a) {
   if (!tile_qvec(a.map, tile, qi, t, h)) return;
   const int n_valid = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);
   const int64_t o = (int64_t)(t - a.q0) * a.map.H + h;
-  merge_vec(a.part_o, a.part_ml, n_valid, nvec, v, a.d_v, (OutT*)a.out + o * a.d_v,
+  merge_vec((const PartT*)a.part_o, a.part_ml, n_valid, nvec, v, a.d_v, (OutT*)a.out + o * a.d_v,
             a.lse ? a.lse + o : nullptr, lane);
 }
 
@@ -87,7 +91,15 @@ __device__ __forceinline__ void fma4(float4& acc, float w, const float4& x) {
   acc.w = fmaf(w, x.w, acc.w);
 }
 
-template <typename OutT>
+// partials of four channels: fp32, or bf16 (the decode kernel's)
+__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const __bf16* p) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 y = *(const bf16x4*)p;
+  return make_float4((float)y[0], (float)y[1], (float)y[2], (float)y[3]);
+}
+
+template <typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
   __shared__ float sw[kWideMaxSplits], sl[kWideMaxSplits];
   __shared__ float red[4], dens[4];
@@ -114,13 +126,13 @@ __global__ __launch_bounds__(256) void k_merge_tiles_wide(AttnArgs a) {
   const int c = chunk * kWideChunk + 4 * lane;
   const bool on = c < a.d_v;
   const int64_t sstride = nvec * a.d_v;
-  const float* po = a.part_o + v * a.d_v + (on ? c : 0);
+  const PartT* po = (const PartT*)a.part_o + v * a.d_v + (on ? c : 0);
   float4 x[kWideBatch];
   auto load_batch = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kWideBatch; ++k) {  // past the last split: reread split s, weight 0
       const int sk = s + 4 * k < n ? s + 4 * k : s;
-      x[k] = *(const float4*)(po + (int64_t)sk * sstride);
+      x[k] = load4(po + (int64_t)sk * sstride);
     }
   };
   if (wave < n) load_batch(wave);
@@ -181,17 +193,21 @@ hipError_t launch_merge_tiles(const AttnArgs& a, int io_dtype, hipStream_t strea
   if (a.n_split >= kWideMergeSplits && a.n_split <= kWideMaxSplits && a.d_v % 4 == 0) {
     const int64_t blocks = nvec * ((a.d_v + kWideChunk - 1) / kWideChunk);
     if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
-    if (io_dtype == 0)
-      hipLaunchKernelGGL(k_merge_tiles_wide<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (a.part_bf16 && io_dtype != 0)
+      hipLaunchKernelGGL((k_merge_tiles_wide<__bf16, __bf16>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (io_dtype == 0)
+      hipLaunchKernelGGL((k_merge_tiles_wide<float, float>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_merge_tiles_wide<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_merge_tiles_wide<__bf16, float>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const int64_t blocks = (nvec + 3) / 4;
-  if (io_dtype == 0)
-    hipLaunchKernelGGL(k_merge_tiles<float>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.part_bf16 && io_dtype != 0)
+    hipLaunchKernelGGL((k_merge_tiles<__bf16, __bf16>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else if (io_dtype == 0)
+    hipLaunchKernelGGL((k_merge_tiles<float, float>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_merge_tiles<__bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_merge_tiles<__bf16, float>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

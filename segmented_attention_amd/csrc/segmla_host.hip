@@ -362,6 +362,7 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   // decode kernel runs on all four waves (two sets over alternate key tiles)
   const bool dec = p->kv_dtype == SEGMLA_BF16 && p->n_split > 1 && p->q1 - p->q0 == 1 &&
                    p->H - p->HW <= 64 && p->HG <= 64;
+  a.part_bf16 = dec ? 1 : 0;  // the decode kernel writes its partial outputs in bf16
   // the replacement copy rides on the full-context attention grid (bf16 per-head state)
   const int64_t n_wg = (int64_t)(p->nF + p->nG) * p->n_split;
   const bool fuse_rc = !dec && p->io_dtype == SEGMLA_BF16 && p->G < 2 && p->HL > 0 && p->nNA_w > 0 &&
