@@ -405,16 +405,11 @@ def measure_dual(cfg_name, ratio, window, top_k, steps, warmup):
                                                   / PEAK_BF16_TFLOPS, 4),
             })
         else:
-            us = statistics.median(ms) * 1e3
-            # HBM bytes of one decode row: its keys (raw rows and entries, 1152 bytes each, read
-            # once), the row's q and out (bf16) and its list
-            nbytes = float(keys.sum()) * 1152 + 2 * H * 576 * 2 + 4 * top_k
-            res["decode"] = {"keys": int(keys.sum()), "forward_us_median": round(us, 2),
-                             "forward_us_min": round(min(ms) * 1e3, 2),
-                             "roofline": {"bound": "hbm", "achieved": round(nbytes / us / 1e3, 1),
-                                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                          "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
-                                          "bytes": int(nbytes)}}
+            # one row is one workgroup (64 heads): a latency figure, not a bandwidth one (its
+            # keys are under 1 MB)
+            res["decode"] = {"keys": int(keys.sum()), "workgroups": (H + 63) // 64,
+                             "forward_us_median": round(statistics.median(ms) * 1e3, 2),
+                             "forward_us_min": round(min(ms) * 1e3, 2)}
         d.close()
         plan.close()
         del out
