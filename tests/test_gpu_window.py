@@ -126,6 +126,28 @@ def test_decode_windows(ci, where):
     say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
+@pytest.mark.parametrize("ci,n_rows", [(1, 1), (1, 2), (4, 1)],
+                         ids=["32k_last_row", "32k_last_2_rows", "64k_e4m3_last_row"])
+def test_merge_of_hundreds_of_splits(ci, n_rows):
+    """Decode windows with 64-key splits: 518 (32K layer) and 1028 (64K layer) partials per
+    vector, so the many-split merge makes several passes over the splits and reads more than
+    256 (max, sum) pairs per vector. The 32K layer's last row takes the decode kernel (bf16
+    partials); two rows, and the E4M3 latent, take the prefill kernel (fp32 partials)."""
+    from segmented_attention_amd import segmla as S
+    cfg = CONFIGS[ci]
+    inp = make_inputs(cfg, "cuda")
+    T = inp["T"]
+    q0, q1 = T - n_rows, T
+    say("case many-split merge %s [%d, %d) split 64" % (cfg["name"], q0, q1))
+    plan, out, z, lse = _run_window(inp, q0, q1, 64)
+    n_split = S.segmla_plan_get_info(plan.handle)["n_split"]
+    assert n_split == (T + 63) // 64 and n_split > 256, n_split
+    ref = O.layer_forward(oracle_inputs(inp, lazy=True), rows=np.arange(q0, q1))
+    plan.close()
+    e = compare(cfg, ref, out, z, lse, None, rows=np.arange(n_rows))
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+
+
 def test_misaligned_tensor_is_rejected():
     """A tensor pointer off a 16-byte boundary is refused before any launch."""
     from segmented_attention_amd import segmla as S
