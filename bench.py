@@ -228,6 +228,9 @@ def decode_json(name, d):
         "epilogue_us": round(d["epilogue_us"], 2), "forward_us_stage_events": round(d["forward_us"], 2),
         "forward_us": round(d["forward_us_eager"], 2),
         "forward_us_hip_graph": round(d["forward_us_graph"], 2),
+        **({"stages": "one-row window: the split merge runs inside the projection kernel, so "
+                      "epilogue_us holds both and split_merge_us is the cost of its events"}
+           if d["rows"] == 1 else {}),
         **({"walk_step_us_median": round(d["walk"]["step_us_median"], 2),
             "walk_step_us_min": round(d["walk"]["step_us_min"], 2),
             "walk": "%d consecutive decode rows on one plan: window update + forward per row"

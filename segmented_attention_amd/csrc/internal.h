@@ -224,6 +224,13 @@ struct EpiArgs {
   int32_t restore_done;  // the attention grid already copied the rows outside A (bf16)
 };
 hipError_t launch_epilogue(const EpiArgs& e, int io_dtype, hipStream_t stream);
+// One-row windows of the decode kernel (bf16 partials) with per-head state: the split merge
+// and the thin projection in one kernel, then the replacement copy of a row outside A. Needs
+// d_v a multiple of 64 (at most kThinMaxDv), d_state a multiple of 128 and at most 4096 splits.
+__host__ __device__ inline bool dec_merge_project_fits(int d_v, int d_state, int n_split) {
+  return d_v % 64 == 0 && d_v <= kThinMaxDv && d_state % 128 == 0 && n_split <= 4096;
+}
+hipError_t launch_dec_merge_project(const AttnArgs& a, const EpiArgs& e, hipStream_t stream);
 // n_blocks blocks of 128 bf16 values -> OCP E4M3 codes + one fp32 scale (amax / 448) each
 hipError_t launch_quant_e4m3(const __bf16* src, uint8_t* codes, float* scales, int64_t n_blocks,
                              hipStream_t stream);

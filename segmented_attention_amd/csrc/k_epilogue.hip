@@ -527,6 +527,202 @@ __global__ __launch_bounds__(256) void k_restore_copy(EpiArgs e, int vec_per_hea
   }
 }
 
+// ------------------------------------------------------------------- fused decode path
+// One-row windows whose key range the decode kernel split (bf16 partials), per-head state: the
+// log-sum-exp merge of the partials (RedKnot-MLA paper, relocation paragraph) and the projection
+// of the merged outputs (head-partition paragraph, Eq. 2) in one kernel, so that W streams while
+// the partials are merged rather than after them. Workgroup = (query vector v, kDmpCols columns
+// of Z), eight waves. Every workgroup of a vector merges all of its channels: thread (slot, g)
+// sums channels 8 g .. 8 g + 7 of the splits slot, slot + SS, ... in batches of kDmpLoads
+// 16-byte loads, weighted by e^(m_s - M) from an LDS table, and the slots meet in LDS. The
+// merged output is rounded to bf16 as stored (the first column block stores it and its lse),
+// u = [O^n, R(-t) O^r] is formed from those values as k_project_thin forms it, and the product
+// follows k_project_thin lane for lane (the same W chunks per lane, the same summation order).
+// A vector's workgroups run on one XCD, so its repeated partial reads meet in one L2 (blocks
+// are dispatched round-robin over the 8 XCDs): block b takes vector 8 ((b / 8) / ncb) + b % 8
+// and column block (b / 8) % ncb.
+constexpr int kDmpThreads = 512;
+constexpr int kDmpCols = (kDmpThreads / 64) * 16;  // 8 teams of 8 lanes per wave, two passes
+constexpr int kDmpLoads = 18;                      // partial loads in flight per thread
+constexpr int kDmpMaxSplits = 4096;                // LDS weight table
+static_assert(kDmpCols == 128 && kDmpMaxSplits == 4096, "the limits dec_merge_project_fits states");
+
+__global__ __launch_bounds__(kDmpThreads) void k_dec_merge_project(AttnArgs a, EpiArgs e) {
+  __shared__ float sw[kDmpMaxSplits], sl[kDmpMaxSplits];
+  __shared__ float red[2][kDmpThreads / 64];
+  __shared__ __attribute__((aligned(16))) float us[kThinMaxDv];
+  __shared__ __attribute__((aligned(16))) float ps[kDmpThreads * 8];  // [slot][channel]
+  const int ncb = e.d_state / kDmpCols;
+  const int b = (int)blockIdx.x;
+  const int64_t v = (int64_t)((b >> 3) / ncb) * 8 + (b & 7);
+  const int cb = (b >> 3) % ncb;
+  const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
+  if (v >= nvec) return;
+  const int tile = (int)(v / kTileQ), qi = (int)(v % kTileQ);
+  int t, h;
+  if (!tile_qvec(a.map, tile, qi, t, h)) return;  // uniform over the workgroup
+  const int n = min(a.n_split, tile_max_row(a.map, tile) / a.split_keys + 1);  // >= 1
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d_v = a.d_v, NG = d_v / 8, SS = kDmpThreads / NG;
+  const int slot = tid / NG, g = tid - slot * NG;
+  const bool mer = slot < SS;  // the threads past SS * NG take part in the weights only
+  const int64_t sstride = nvec * d_v;
+  const __bf16* po = (const __bf16*)a.part_o + v * d_v + 8 * g;
+  const float* pml = a.part_ml + v * 2;
+  // issue order is retire order: the (max, sum) pairs, the first batch of partials, W
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (tid < n) ml0 = *(const float2*)(pml + (int64_t)tid * nvec * 2);
+  uint4 x[kDmpLoads];
+  auto load_batch = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kDmpLoads; ++k) {  // past the last split: reread it, weight 0
+      const int s = min(s0 + slot + SS * k, n - 1);
+      x[k] = mer ? *(const uint4*)(po + (int64_t)s * sstride) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_batch(0);
+  const int team = lane >> 3, j = lane & 7, nk = d_v / 64;
+  const __bf16* wh = (const __bf16*)e.w + (int64_t)h * e.d_state * d_v;
+  uint4 wv[2][kThinMaxK];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const __bf16* wc = wh + (int64_t)(cb * kDmpCols + wave * 16 + p * 8 + team) * d_v + 8 * j;
+#pragma unroll
+    for (int k = 0; k < kThinMaxK; ++k)
+      if (k < nk) wv[p][k] = *(const uint4*)(wc + 64 * k);
+  }
+  // split weights e^(m_s - M) and the normaliser
+  float m = ml0.x;
+  if (tid < n) {
+    sw[tid] = ml0.x;
+    sl[tid] = ml0.y;
+  }
+  for (int s = tid + kDmpThreads; s < n; s += kDmpThreads) {  // more than kDmpThreads splits
+    const float2 ml = *(const float2*)(pml + (int64_t)s * nvec * 2);
+    sw[s] = ml.x;
+    sl[s] = ml.y;
+    m = fmaxf(m, ml.x);
+  }
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red[0][wave] = m;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kDmpThreads / 64; ++w) M = fmaxf(M, red[0][w]);
+  float den = 0.f;
+  for (int s = tid; s < n; s += kDmpThreads) {  // the entries this thread wrote above
+    const float ms = sw[s];
+    const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+    sw[s] = w;
+    den += w * sl[s];
+  }
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+  if (lane == 0) red[1][wave] = den;
+  __syncthreads();
+  // weighted sums of the slot's splits
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < n; s0 += SS * kDmpLoads) {
+    if (s0 > 0) load_batch(s0);
+#pragma unroll
+    for (int k = 0; k < kDmpLoads; ++k) {
+      const int s = s0 + slot + SS * k;
+      const float w = (mer && s < n) ? sw[s] : 0.f;
+      const uint32_t xw[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w, bf16_lo(xw[i]), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w, bf16_hi(xw[i]), acc[2 * i + 1]);
+      }
+    }
+  }
+  // thread (slot, g) = ps[slot * d_v + 8 g .. + 7] (tid = slot * NG + g)
+  *(float4*)&ps[tid * 8] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *(float4*)&ps[tid * 8 + 4] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  __syncthreads();
+  float dt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kDmpThreads / 64; ++w) dt += red[1][w];
+  const float inv = dt > 0.f ? 1.f / dt : 0.f;
+  const int64_t o = (int64_t)(t - a.q0) * a.map.H + h;
+  const int half_r = e.d_rope / 2, nope_pairs = e.d_nope / 2;
+  for (int k2 = tid; k2 < d_v / 2; k2 += kDmpThreads) {
+    const int c = 2 * k2;
+    float s0 = 0.f, s1 = 0.f;
+    for (int q = 0; q < SS; ++q) {
+      s0 += ps[q * d_v + c];
+      s1 += ps[q * d_v + c + 1];
+    }
+    const __bf16 b0 = (__bf16)(s0 * inv), b1 = (__bf16)(s1 * inv);
+    if (cb == 0) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t y = {b0, b1};
+      *(bf16x2_t*)((__bf16*)a.out + o * d_v + c) = y;
+    }
+    float a0 = (float)b0, a1 = (float)b1;
+    if (k2 >= nope_pairs) {  // v carries the RoPE part: u^r = R(-t) O^r, rounded as stored
+      const float2 cs = e.rowcs[(int64_t)(t - e.q0) * half_r + (k2 - nope_pairs)];
+      const float y0 = (float)(__bf16)(a0 * cs.x + a1 * cs.y);
+      const float y1 = (float)(__bf16)(-a0 * cs.y + a1 * cs.x);
+      a0 = y0;
+      a1 = y1;
+    }
+    us[c] = a0;
+    us[c + 1] = a1;
+  }
+  if (a.lse && cb == 0 && tid == 0) a.lse[o] = dt > 0.f ? M + logf(dt) : -INFINITY;
+  __syncthreads();
+  // z[t][h][columns] = W_h u: the per-lane chunks and summation order of k_project_thin
+  float pacc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int k = 0; k < kThinMaxK; ++k) {
+      if (k >= nk) continue;
+      const uint4 xv = wv[p][k];
+      const float w8[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
+                           bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
+      const float4 u0 = *(const float4*)&us[8 * (j + 8 * k)];
+      const float4 u1 = *(const float4*)&us[8 * (j + 8 * k) + 4];
+      float s = pacc[p];
+      s = fmaf(w8[0], u0.x, s);
+      s = fmaf(w8[1], u0.y, s);
+      s = fmaf(w8[2], u0.z, s);
+      s = fmaf(w8[3], u0.w, s);
+      s = fmaf(w8[4], u1.x, s);
+      s = fmaf(w8[5], u1.y, s);
+      s = fmaf(w8[6], u1.z, s);
+      s = fmaf(w8[7], u1.w, s);
+      pacc[p] = s;
+    }
+  }
+  const int zs = z_slots(e);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    float s = pacc[p];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (j == 0) {
+      const int col = cb * kDmpCols + wave * 16 + p * 8 + team;
+      ((__bf16*)e.z)[((int64_t)(t - e.q0) * zs + h) * e.d_state + col] = (__bf16)s;
+    }
+  }
+}
+
+hipError_t launch_dec_merge_project(const AttnArgs& a, const EpiArgs& e, hipStream_t stream) {
+  if (!dec_merge_project_fits(a.d_v, e.d_state, a.n_split)) return hipErrorInvalidConfiguration;
+  const int64_t nvec = (int64_t)(a.map.nF + a.map.nG) * kTileQ;
+  const int64_t blocks = (nvec + 7) / 8 * 8 * (e.d_state / kDmpCols);
+  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  if (blocks > 0)
+    hipLaunchKernelGGL(k_dec_merge_project, dim3((unsigned)blocks), dim3(kDmpThreads), 0, stream, a, e);
+  if (e.HL > 0 && e.nNA > 0 && !e.restore_done)
+    hipLaunchKernelGGL(k_restore_copy<uint4>, dim3(e.nNA), dim3(256), 0, stream, e, e.d_state * 2 / 16);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- E4M3 output
 // The grouped state for the next projection as 1x128 E4M3 blocks ("Reading notes on
 // DeepSeek-V4 serving in TensorRT-LLM", Part I, FP8 dataflow bullet): 16 lanes per block of

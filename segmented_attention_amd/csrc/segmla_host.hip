@@ -392,7 +392,12 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
     e = launch_attn_window(aw, p->kv_dtype, p->v_has_rope, s);
   }
   if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[1], s);
-  if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1) e = launch_merge_tiles(a, p->io_dtype, s);
+  // decode rows with per-head state: the merge and the projection run as one kernel (the
+  // profile's merge stage is then empty and its epilogue stage holds both)
+  const bool fuse_dec = dec && p->G < 2 && p->HW == 0 && p->thin && !p->z_e4m3 &&
+                        p->io_dtype == SEGMLA_BF16 && dec_merge_project_fits(p->d_v, p->d_state, p->n_split);
+  if (e == hipSuccess && p->nF + p->nG > 0 && p->n_split > 1 && !fuse_dec)
+    e = launch_merge_tiles(a, p->io_dtype, s);
   if (e == hipSuccess && p->prof) e = hipEventRecord(p->ev[2], s);
   if (e != hipSuccess) return SEGMLA_E_HIP;
   EpiArgs ep;
@@ -429,7 +434,7 @@ segmla_status forward_impl(const segmla_plan* p, const segmla_tensors* t, hipStr
   ep.grp_ghead = p->at<int32_t>(p->o_grp) + p->grp_gstart.size();
   ep.zpart = (p->thin && p->G >= 2) ? p->at<float>(p->o_zpart) : nullptr;
   if (p->z_e4m3) ep.z = p->at<void>(p->o_zbf);  // the bf16 state, then its E4M3 blocks
-  e = launch_epilogue(ep, p->io_dtype, s);
+  e = fuse_dec ? launch_dec_merge_project(a, ep, s) : launch_epilogue(ep, p->io_dtype, s);
   if (e == hipSuccess && p->z_e4m3)
     e = launch_quant_e4m3((const __bf16*)ep.z, (uint8_t*)t->z, t->z_scale,
                           (int64_t)(p->q1 - p->q0) * p->n_groups * (p->d_state / 128), s);
