@@ -224,10 +224,10 @@ def _sample_rows(inp, A, rng, n_a=512, n_na=512, max_new=None):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def _oracle_in_chunks(oi, rows, chunk=512):
-    """O.layer_forward on `rows`, a chunk of rows at a time with a progress line per chunk
-    (the oracle takes a minute or more on the longest layers). Every call re-rotates all keys
-    of the request, so the chunks are large: about a minute each on the 128K layer."""
+def _oracle_in_chunks(oi, rows, chunk=2048):
+    """O.layer_forward on `rows`, a chunk of rows at a time with a progress line per chunk.
+    Every call re-rotates all keys of the request, so a chunk holds every sampled row of the
+    full-size workloads (at most 1,600): one call of 10-40 s."""
     parts = []
     for i in range(0, len(rows), chunk):
         parts.append(O.layer_forward(oi, rows=rows[i:i + chunk]))
