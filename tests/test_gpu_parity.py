@@ -5,6 +5,8 @@ and the projected state must match within 1e-5 (fp32), 2e-2 (bf16) or 6e-2 (E4M3
 as max over (row, head) of ||x - ref|| / ||ref||; Local-head rows outside A must equal the
 cached state bit for bit and `out` must stay untouched there.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -271,6 +273,30 @@ def test_parity_full_size_sampled(idx):
     ref = _oracle_in_chunks(oi, rows)
     e = compare(cfg, ref, out, z, lse, None, rows=rows)
     say("  max rel err O %.2e Z %.2e (tol %.0e), lse max abs err %.2e" % (e[0], e[1], tol_of(cfg), e[2]))
+    plan.close()
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(not os.environ.get("SEGMLA_FULL_ORACLE"),
+                    reason="every row of the 32K layer against the oracle takes minutes of host "
+                           "time; SEGMLA_FULL_ORACLE=1 runs it")
+def test_parity_full_oracle_32k():
+    """Every row and head of the 32K Flash-like layer, in the bench's launch configuration,
+    against the full oracle (1.8e13 fp64 flops) in chunks of 2048 rows; the sampled test above
+    checks about 1,100 of its rows."""
+    cfg = CONFIGS[1]
+    say("case full oracle %s" % cfg["name"])
+    inp = make_inputs(cfg, "cuda")
+    plan, out, z, lse = run_gpu(inp)
+    oi = oracle_inputs(inp, lazy=True)
+    T = inp["T"]
+    worst = [0.0, 0.0, 0.0]
+    for r0 in range(0, T, 2048):
+        rows = np.arange(r0, min(T, r0 + 2048))
+        ref = O.layer_forward(oi, rows=rows)
+        e = compare(cfg, ref, out, z, lse, None, rows=rows)
+        worst = [max(a, b) for a, b in zip(worst, e)]
+        say("  rows %d/%d: max rel err O %.2e Z %.2e, lse max abs err %.2e" % (rows[-1] + 1, T, *worst))
     plan.close()
 
 
