@@ -278,6 +278,10 @@ def test_geometry_errors(L):
     alias = pr.copy()
     alias[2] = alias[1]
     assert _status(cfg, pool_rows=alias) == S.SEGMLA_OK
+    # an empty request (no segment) has no rows to compute
+    none = np.zeros(0, np.int64)
+    assert _status(cfg, kinds=np.zeros(0, np.uint8), lens=np.zeros(0, np.int32), offsets=none,
+                   pool_rows=none) == S.SEGMLA_E_GEOMETRY
 
 
 def test_shape_dtype_protect_errors(L):
