@@ -173,6 +173,11 @@ hipError_t launch_protect(const SegDesc* lseg, const SegDesc* runs, const int32_
                           int n_blk, int32_t* alist, int32_t* nalist, int n_a, uint64_t* sum_a,
                           int q0, int q1, int32_t* rng, hipStream_t stream);
 hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream);
+// launch_window and launch_worklist in one workgroup, for windows of few rows and tiles
+// (kWindowSmallPairs RoPE pairs, kWindowSmallTiles tiles at most)
+constexpr int kWindowSmallPairs = 2048, kWindowSmallTiles = 2048;
+hipError_t launch_window_small(const int32_t* alist, int nA, int d_rope, double base, float2* rowcs,
+                               TileMap map, uint64_t* sum_a, int32_t* work, hipStream_t stream);
 hipError_t launch_window(const int32_t* alist, int nA, int q0, int q1, int d_rope, double base,
                          float2* rowcs, int32_t* rng, uint64_t* sum_a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int kv_dtype, int v_has_rope, hipStream_t stream);

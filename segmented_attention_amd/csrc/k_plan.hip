@@ -357,26 +357,33 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
   return lo;
 }
 
-__global__ __launch_bounds__(256) void k_window_ranges(const int32_t* __restrict__ alist, int nA,
-                                                       int q0, int q1, int32_t* __restrict__ rng,
-                                                       uint64_t* __restrict__ sum_a) {
-  __shared__ int s_lo, s_hi;
+// by one workgroup of 256 threads; s_rng receives the four ranges too (shared memory)
+__device__ __forceinline__ void window_ranges(const int32_t* __restrict__ alist, int nA, int q0,
+                                              int q1, int32_t* __restrict__ rng,
+                                              uint64_t* __restrict__ sum_a, int32_t* s_rng) {
   __shared__ uint64_t part[4];
   if (threadIdx.x == 0) {
-    s_lo = lower_bound_i32(alist, nA, q0);
-    s_hi = lower_bound_i32(alist, nA, q1);
-    rng[0] = s_lo;
-    rng[1] = s_hi;
-    rng[2] = q0 - s_lo;  // rows outside A before q0
-    rng[3] = q1 - s_hi;
+    const int lo = lower_bound_i32(alist, nA, q0), hi = lower_bound_i32(alist, nA, q1);
+    const int32_t r[4] = {lo, hi, q0 - lo, q1 - hi};  // rows outside A before q0, before q1
+    for (int k = 0; k < 4; ++k) {
+      rng[k] = r[k];
+      s_rng[k] = r[k];
+    }
   }
   __syncthreads();
   uint64_t v = 0;
-  for (int i = s_lo + threadIdx.x; i < s_hi; i += 256) v += (uint64_t)alist[i] + 1;
+  for (int i = s_rng[0] + threadIdx.x; i < s_rng[1]; i += 256) v += (uint64_t)alist[i] + 1;
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
   if (threadIdx.x == 0) *sum_a = part[0] + part[1] + part[2] + part[3];
+}
+
+__global__ __launch_bounds__(256) void k_window_ranges(const int32_t* __restrict__ alist, int nA,
+                                                       int q0, int q1, int32_t* __restrict__ rng,
+                                                       uint64_t* __restrict__ sum_a) {
+  __shared__ int32_t s_rng[4];
+  window_ranges(alist, nA, q0, q1, rng, sum_a, s_rng);
 }
 
 hipError_t launch_window(const int32_t* alist, int nA, int q0, int q1, int d_rope, double base,
@@ -396,12 +403,13 @@ hipError_t launch_window(const int32_t* alist, int nA, int q0, int q1, int d_rop
 // of tiles of the other list that sort before it (equal costs: F tiles first). Only the first
 // nF_act / nG_act tiles of each stream hold rows (a row window can fill less than the host's
 // sizing); the empty ones take the last ranks, so `work` stays a permutation of all tiles.
-__global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
+__device__ __forceinline__ void worklist_tiles(const TileMap& m, int32_t* __restrict__ work,
+                                               int first, int stride) {
   const int n = m.nF + m.nG;
   const int nF_act = (int)(((int64_t)(m.rng[1] - m.rng[0]) * m.HF + kTileQ - 1) / kTileQ);
   const int nG_act = (int)(((int64_t)(m.rng[3] - m.rng[2]) * m.HG + kTileQ - 1) / kTileQ);
   const int n_act = nF_act + nG_act;
-  for (int tile = blockIdx.x * blockDim.x + threadIdx.x; tile < n; tile += gridDim.x * blockDim.x) {
+  for (int tile = first; tile < n; tile += stride) {
     int rank;
     if (tile < m.nF) {
       if (tile >= nF_act) {
@@ -432,6 +440,39 @@ __global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
     }
     work[rank] = tile;
   }
+}
+
+__global__ void k_worklist(TileMap m, int32_t* __restrict__ work) {
+  worklist_tiles(m, work, blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
+}
+
+// A window of a few rows (the next decode row of a plan): its RoPE rows, its ranges and the
+// work list in one workgroup, so that moving the plan is one launch instead of three. The
+// ranges reach the work list through shared memory.
+__global__ __launch_bounds__(256) void k_window_small(const int32_t* __restrict__ alist, int nA,
+                                                      int d_rope, double base,
+                                                      float2* __restrict__ rowcs, TileMap m,
+                                                      uint64_t* __restrict__ sum_a,
+                                                      int32_t* __restrict__ work) {
+  __shared__ int32_t s_rng[4];
+  const int q0 = m.q0, q1 = m.q0 + m.nq, half = d_rope / 2;
+  for (int i = threadIdx.x; i < (q1 - q0) * half; i += 256) {
+    const int r = i / half, k = i - r * half;
+    double s, c;
+    sincos((double)(q0 + r) * rope_theta(base, k, d_rope), &s, &c);
+    rowcs[i] = make_float2((float)c, (float)s);
+  }
+  window_ranges(alist, nA, q0, q1, const_cast<int32_t*>(m.rng), sum_a, s_rng);  // ends in a barrier
+  TileMap ms = m;
+  ms.rng = s_rng;
+  worklist_tiles(ms, work, threadIdx.x, 256);
+}
+
+hipError_t launch_window_small(const int32_t* alist, int nA, int d_rope, double base, float2* rowcs,
+                               TileMap map, uint64_t* sum_a, int32_t* work, hipStream_t stream) {
+  hipLaunchKernelGGL(k_window_small, dim3(1), dim3(256), 0, stream, alist, nA, d_rope, base, rowcs,
+                     map, sum_a, work);
+  return hipGetLastError();
 }
 
 hipError_t launch_worklist(TileMap map, int32_t* work, hipStream_t stream) {

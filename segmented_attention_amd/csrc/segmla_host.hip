@@ -794,10 +794,18 @@ segmla_status segmla_plan_set_window(segmla_plan* p, int64_t q_begin, int64_t q_
   const segmla_status st = size_window(p, (int32_t)q_begin, (int32_t)q_end, p->ws_capacity);
   if (st != SEGMLA_OK) return st;  // the plan is unchanged
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_window(p->at<int32_t>(p->o_alist), (int)p->nA, p->q0, p->q1, p->d_rope,
-                               p->rope_base, p->at<float2>(p->o_rowcs), p->at<int32_t>(p->o_rng),
-                               p->at<uint64_t>(p->o_sum_a), s);
-  if (e == hipSuccess && p->nF + p->nG > 0) e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
+  hipError_t e = hipSuccess;
+  if ((int64_t)(p->q1 - p->q0) * (p->d_rope / 2) <= kWindowSmallPairs &&
+      p->nF + p->nG <= kWindowSmallTiles) {  // the next decode row: one launch
+    e = launch_window_small(p->at<int32_t>(p->o_alist), (int)p->nA, p->d_rope, p->rope_base,
+                            p->at<float2>(p->o_rowcs), tile_map(p), p->at<uint64_t>(p->o_sum_a),
+                            p->at<int32_t>(p->o_work), s);
+  } else {
+    e = launch_window(p->at<int32_t>(p->o_alist), (int)p->nA, p->q0, p->q1, p->d_rope,
+                      p->rope_base, p->at<float2>(p->o_rowcs), p->at<int32_t>(p->o_rng),
+                      p->at<uint64_t>(p->o_sum_a), s);
+    if (e == hipSuccess && p->nF + p->nG > 0) e = launch_worklist(tile_map(p), p->at<int32_t>(p->o_work), s);
+  }
   if (e != hipSuccess) {
     p->built = false;
     return SEGMLA_E_HIP;
