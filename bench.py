@@ -18,7 +18,8 @@ rows, W, and the row's q, out and z moved once). The main workload over a paged 
 projected state in groups of 8 heads (z and the cache per group) the "grouped" figure. The
 main request as DeepSeek-V4 compressed-history layers (a CSA layer: 128-token window and
 512-entry lists of 4-to-1 entries; an HCA layer: 128-token window and every 128-to-1 entry),
-every row and the last row alone, are the "dual_pool" figures.
+every row and the last row alone, are the "dual_pool" figures. The main request prefilled in
+eight row windows on one plan moved by segmla_plan_set_window is the "chunked_prefill" figure.
 Throughput is algorithmic
 attention TFLOP/s, 2 * (576 + 576) FLOP per computed (row, head, key) triple, divided by the
 step time.
@@ -26,7 +27,7 @@ step time.
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-secondary]
                 [--no-target] [--no-fp8] [--many-short NAME] [--window NAMES] [--no-cpu-baseline]
                 [--decode-rows N] [--decode-only] [--paged-rows P] [--grouped NAME]
-                [--dual SPECS] [--dual-only]
+                [--dual SPECS] [--dual-only] [--chunks N]
 """
 import argparse
 import json
@@ -166,6 +167,63 @@ def measure_decode_walk(inp, cfg, n_steps, warmup=3):
     plan.close()
     steps = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n_steps)]
     return dict(steps=n_steps, step_us_median=statistics.median(steps), step_us_min=min(steps))
+
+
+def measure_chunked(cfg_name, n_chunks, steps, warmup=2):
+    """Chunked prefill: the request's rows in n_chunks consecutive windows computed one after
+    another on one plan, moved from chunk to chunk by segmla_plan_set_window (geometry, RoPE
+    tables and the protected set built once). HIP-event time of the whole sequence (window
+    updates and forwards) per prefill; the algorithmic FLOP are the whole request's."""
+    import torch
+    from segmented_attention_amd import segmla as S
+    from workload import config_by_name, make_inputs
+
+    cfg = config_by_name(cfg_name)
+    log("workload %s: chunked prefill in %d windows (set_window + forward)" % (cfg_name, n_chunks))
+    inp = make_inputs(cfg, "cuda")
+    T, H = inp["T"], cfg["n_heads"]
+    dt = inp["q"].dtype
+    out = torch.empty((T, H, inp["d_v"]), dtype=dt, device="cuda")
+    z = torch.empty((T, H, cfg["d_state"]), dtype=dt, device="cuda")
+    whole = S.Plan.for_inputs(inp)
+    whole.build(inp["scores"])
+    whole.forward(inp, out, z)
+    torch.cuda.synchronize()
+    ws = S.segmla_plan_workspace_bytes(whole.handle)
+    pairs = sum(whole.pairs())
+    whole.close()
+    edges = [T * k // n_chunks for k in range(n_chunks + 1)]
+    for k in range(n_chunks):  # room for every chunk's window (host-side sizing only)
+        pk = S.Plan.for_inputs(inp, q_range=(edges[k], edges[k + 1]))
+        ws = max(ws, S.segmla_plan_workspace_bytes(pk.handle))
+        pk.close()
+    plan = S.Plan.for_inputs(inp, q_range=(edges[0], edges[1]))
+    plan.build(inp["scores"], min_bytes=ws)
+
+    def prefill():
+        for k in range(n_chunks):
+            q0, q1 = edges[k], edges[k + 1]
+            if k > 0 or plan.q0 != q0:
+                plan.set_window(q0, q1)
+            plan.forward(inp, out[q0:q1], z[q0:q1])
+
+    for _ in range(warmup):
+        prefill()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        prefill()
+    b.record()
+    torch.cuda.synchronize()
+    plan.close()
+    ms = a.elapsed_time(b) / steps
+    flops = flops_per_pair(cfg) * pairs
+    del inp, out, z
+    torch.cuda.empty_cache()
+    return {"workload": cfg_name, "chunks": n_chunks, "rows_per_chunk": edges[1] - edges[0],
+            "ms_per_prefill": round(ms, 3), "tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+            "over": "window updates and forwards of every chunk; the plan is built once"}
 
 
 def measure_prefetch(cfg_name, steps):
@@ -514,6 +572,8 @@ def main():
                     help="many-short-segments workload (256 documents, 256-way merge per row) "
                          "reported alongside; '' for none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunks", type=int, default=8,
+                    help="chunked-prefill figure: the main workload in this many row windows (0: off)")
     ap.add_argument("--decode-rows", type=int, default=1,
                     help="decode window (last rows of the secondary workload) reported alongside; 0: none")
     ap.add_argument("--grouped", default="flash_32k_grouped_bf16",
@@ -585,6 +645,7 @@ def main():
     if args.prefetch:
         log("workload %s: forward with a concurrent artifact prefetch" % args.workload)
         pfx = measure_prefetch(args.workload, 5)
+    chk = measure_chunked(args.workload, args.chunks, max(3, args.steps // 4)) if args.chunks > 0 else None
     gr = None
     if args.grouped:
         gr = measure(args.grouped, max(2, args.steps // 2), 1, also_e4m3=True)
@@ -675,6 +736,9 @@ def main():
         } for w in wins]
     if pfx is not None:
         line["prefetch"] = pfx
+    if chk is not None:
+        chk["whole_request_ms"] = round(r["fwd_ms_median"] + r["build_ms"], 3)
+        line["chunked_prefill"] = chk
     if gr is not None:
         line["grouped"] = {
             "workload": gr["cfg"]["name"], "group_heads": gr["cfg"]["group_heads"],
