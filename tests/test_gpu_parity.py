@@ -71,6 +71,42 @@ def test_parity_degenerate(cfg):
         assert inp["T"] == 210
 
 
+@pytest.mark.parametrize("d_state", [192, 1024])
+def test_parity_projected_state_widths(d_state):
+    """Projected-state widths other than the workloads' 512 (any multiple of 64 up to 4096 is
+    accepted for bf16): 192 (a partial set of 32-column blocks per wave, three thin-projection
+    column blocks, no fused decode kernel) and 1024 (two column passes of the tile projection,
+    eight column blocks of the fused decode kernel), with the replacement copy of wider and
+    narrower rows. The whole request, then its last row and a row outside A as decode windows
+    with 64-key splits, against the oracle."""
+    from segmented_attention_amd import segmla as S
+    from segmented_attention_amd.segmla import Plan
+    cfg = dict(SMALL_CONFIGS[1], name="flash_small_state%d_bf16" % d_state, d_state=d_state)
+    inp, _, _ = _full_case(cfg)
+    T, H = inp["T"], cfg["n_heads"]
+    plan = Plan.for_inputs(inp)
+    plan.build(inp["scores"])
+    A = plan.protected()
+    plan.close()
+    outside = np.setdiff1d(np.arange(100, T - 50), A)
+    oi = oracle_inputs(inp)
+    for t in [T - 1] + ([int(outside[len(outside) // 2])] if len(outside) else []):
+        say("  decode row %d split 64" % t)
+        plan = Plan.for_inputs(inp, 64, q_range=(t, t + 1))
+        plan.build(inp["scores"])
+        assert S.segmla_plan_get_info(plan.handle)["n_split"] == (t + 64) // 64
+        dt = inp["q"].dtype
+        out = torch.full((1, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+        z = torch.full((1, H, d_state), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+        plan.forward(inp, out, z, lse)
+        torch.cuda.synchronize()
+        plan.close()
+        ref = O.layer_forward(oi, rows=np.arange(t, t + 1))
+        e = compare(cfg, ref, out, z, lse, None, rows=np.arange(1))
+        say("    max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+
+
 @pytest.mark.parametrize("base", [SMALL_CONFIGS[1], SMALL_CONFIGS[5], SMALL_CONFIGS[4]],
                          ids=lambda c: c["name"])
 def test_relocation_invariance_on_gpu(base):
