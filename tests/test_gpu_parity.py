@@ -107,6 +107,43 @@ def test_parity_projected_state_widths(d_state):
         say("    max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
+@pytest.mark.parametrize("n_heads", [40, 100])
+def test_parity_head_counts(n_heads):
+    """Head counts that do not divide a 128-vector tile (the workloads use 64 and 128): tiles of
+    rows of A hold 3.2 (40 heads) or 1.28 (100 heads) rows, tiles of the other rows 25.6 or 9.8
+    rows of the Global heads (one per group of eight: 5 and 13 of them). The whole request, then
+    its last row and a row outside A as decode windows with 64-key splits: with 40 heads the
+    decode kernel's second 32-vector group holds 8 real vectors; 100 heads exceed its 64 and take
+    the prefill kernel with a split."""
+    from segmented_attention_amd import segmla as S
+    from segmented_attention_amd.segmla import Plan
+    cfg = dict(SMALL_CONFIGS[1], name="flash_small_h%d_bf16" % n_heads, n_heads=n_heads,
+               global_heads=list(range(0, n_heads, 8)))
+    inp, _, _ = _full_case(cfg)
+    T, H = inp["T"], n_heads
+    plan = Plan.for_inputs(inp)
+    plan.build(inp["scores"])
+    A = plan.protected()
+    plan.close()
+    outside = np.setdiff1d(np.arange(100, T - 50), A)
+    oi = oracle_inputs(inp)
+    for t in [T - 1] + ([int(outside[len(outside) // 2])] if len(outside) else []):
+        say("  decode row %d split 64" % t)
+        plan = Plan.for_inputs(inp, 64, q_range=(t, t + 1))
+        plan.build(inp["scores"])
+        assert S.segmla_plan_get_info(plan.handle)["n_split"] == (t + 64) // 64
+        dt = inp["q"].dtype
+        out = torch.full((1, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+        z = torch.full((1, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+        plan.forward(inp, out, z, lse)
+        torch.cuda.synchronize()
+        plan.close()
+        ref = O.layer_forward(oi, rows=np.arange(t, t + 1))
+        e = compare(cfg, ref, out, z, lse, None, rows=np.arange(1))
+        say("    max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+
+
 @pytest.mark.parametrize("base", [SMALL_CONFIGS[1], SMALL_CONFIGS[5], SMALL_CONFIGS[4]],
                          ids=lambda c: c["name"])
 def test_relocation_invariance_on_gpu(base):
