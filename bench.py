@@ -597,8 +597,8 @@ def main():
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every GPU box has one "
-              "GPU); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library runs one layer on one GPU and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

@@ -386,7 +386,7 @@ def test_parity_full_size_sampled(idx):
     # every new row of the 32K and many-short layers; 64 seeded new rows of the longer ones
     max_new = None if cfg["name"] in ("flash_32k_bf16", "many_short_bf16") else 64
     # 512 seeded rows inside A and 512 outside (about 1.5 minutes of oracle time for all five
-    # layers on the GPU machine's host)
+    # layers on a 16-thread host)
     rows = _sample_rows(inp, prot["A"], np.random.default_rng(idx), n_a=512, n_na=512,
                         max_new=max_new)
     n_seg_ends = len(set(inp["offsets"].tolist()) | set((inp["offsets"] + inp["lens"] - 1).tolist()))
