@@ -1,0 +1,96 @@
+"""GPU parity on seeded random layers: combinations of shapes, roles and placements that the
+named configurations do not spell out one by one.
+
+Each layer draws, from its own seed:
+* the latent and io dtypes (fp32, bf16, or an E4M3 latent with bf16 io);
+* the head count, and for fp32 the nope / RoPE / state widths;
+* the head roles: Global, Local and, in some layers, sink + window heads;
+* one to seven segments of any kind and order (prefix, document, new), many of them a few
+  rows long, so that key tiles, segment runs and protected-row edges fall anywhere;
+* the protected-row rule (edge rows, tail rows, Indexer budget) and values with or without the
+  RoPE dims;
+* the latent pool placement (identity, shuffled with gaps, or aliased documents) and the key
+  split (none, 64 or 128 keys).
+
+Every (row, head) of the forward is compared with the fp64 oracle, to the tolerances of the
+named layers, and the geometry and the protected rows bit for bit.
+"""
+import numpy as np
+import pytest
+
+from oracle import segmla_oracle as O
+from tests.gpu_common import compare, oracle_inputs, run_gpu, say
+from workload import make_inputs
+from workload.configs import _cfg, _windowed
+
+N_LAYERS = 16
+
+
+def random_layer(k):
+    """The k-th random layer: (cfg, pool placement, split_keys)."""
+    rng = np.random.default_rng([k, 0x5E6])
+    kind = str(rng.choice(["f32", "bf16", "e4m3"], p=[0.3, 0.45, 0.25]))
+    segs = []
+    for _ in range(int(rng.integers(1, 8))):
+        sk = str(rng.choice(["prefix", "doc", "new"], p=[0.15, 0.7, 0.15]))
+        n = int(rng.integers(1, 6)) if rng.random() < 0.3 else int(rng.integers(6, 140))
+        segs.append((sk, n))
+    if kind == "f32":
+        H = int(rng.choice([1, 5, 8, 12]))
+        d_nope, d_rope = int(rng.choice([16, 64, 96])), int(rng.choice([4, 16, 32]))
+        d_state = int(rng.choice([16, 64, 96]))
+    else:
+        H = int(rng.choice([8, 40, 64, 128]))
+        d_nope, d_rope = 512, 64
+        d_state = int(rng.choice([192, 512]))
+    cfg = _cfg("random_%02d_%s" % (k, kind), None, "f32" if kind == "f32" else "bf16", H, d_nope,
+               d_rope, d_state, segs, edge_rows=int(rng.choice([0, 4, 16])),
+               tail_rows=int(rng.choice([0, 8, 64])),
+               budget_permille=int(rng.choice([0, 100, 300])), seed=200 + k,
+               v_has_rope=int(rng.integers(0, 2)), kv_dtype="e4m3" if kind == "e4m3" else None)
+    frac = float(rng.choice([0.0, 0.15, 0.5, 1.0]))
+    roles = rng.random(H)
+    glob = [h for h in range(H) if roles[h] < frac]
+    if rng.random() < 0.3 and len(glob) < H:  # some of the other heads as sink + window heads
+        win = [h for h in range(H) if h not in glob and rng.random() < 0.5]
+        if win:
+            cfg = _windowed(cfg, cfg["name"] + "_win", win, n_sink=int(rng.choice([0, 3])),
+                            window=int(rng.choice([1, 17, 64])), global_heads=glob)
+    cfg["global_heads"] = glob
+    pool = str(rng.choice(["identity", "shuffled", "aliased"]))
+    split = int(rng.choice([0, 0, 64, 128]))
+    return cfg, pool, split
+
+
+CASES = [random_layer(k) for k in range(N_LAYERS)]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(N_LAYERS), ids=[c[0]["name"] for c in CASES])
+def test_random_layer_matches_oracle(k):
+    cfg, pool, split = CASES[k]
+    say("case %s H=%d segments=%s pool=%s split=%d global=%d window=%d" % (
+        cfg["name"], cfg["n_heads"], cfg["segments"], pool, split, len(cfg["global_heads"]),
+        len(cfg.get("window_heads", ()))))
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    plan, out, z, lse = run_gpu(inp, split)
+    ref = O.layer_forward(oracle_inputs(inp))
+    seg, pool_row = plan.geometry()
+    np.testing.assert_array_equal(seg, ref["geom"]["seg_of_row"])
+    np.testing.assert_array_equal(pool_row, ref["geom"]["pool_of_row"])
+    np.testing.assert_array_equal(plan.protected(), ref["A"])
+    e = compare(cfg, ref, out, z, lse, None)
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+    plan.close()
+
+
+def test_random_layers_cover_the_combinations():
+    """(CPU) The seeds reach every dtype, every pool placement, split and unsplit runs, window heads,
+    layers without Global heads and layers with one-row segments."""
+    kinds = {c["kv_dtype"] if c["kv_dtype"] == "e4m3" else c["dtype"] for c, _, _ in CASES}
+    assert kinds == {"f32", "bf16", "e4m3"}
+    assert {p for _, p, _ in CASES} == {"identity", "shuffled", "aliased"}
+    assert {s > 0 for _, _, s in CASES} == {True, False}
+    assert any(c.get("window_heads") for c, _, _ in CASES)
+    assert any(not c["global_heads"] for c, _, _ in CASES)
+    assert any(n == 1 for c, _, _ in CASES for _, n in c["segments"])
