@@ -17,8 +17,10 @@ named layers, and the geometry and the protected rows bit for bit.
 """
 import numpy as np
 import pytest
+import torch
 
 from oracle import segmla_oracle as O
+from segmented_attention_amd.segmla import Plan
 from tests.gpu_common import compare, oracle_inputs, run_gpu, say
 from workload import make_inputs
 from workload.configs import _cfg, _windowed
@@ -84,6 +86,43 @@ def test_random_layer_matches_oracle(k):
     plan.close()
 
 
+def random_window(k, T):
+    """The k-th layer's row window: one row (decode-shaped, keys split every 64) or a range of
+    rows, anywhere in the request; (q0, q1, split_keys)."""
+    rng = np.random.default_rng([k, 0x3D0])
+    if rng.random() < 0.5:
+        q0 = int(rng.integers(0, T))
+        return q0, q0 + 1, 64
+    q0 = int(rng.integers(0, T))
+    q1 = int(rng.integers(q0 + 1, T + 1))
+    return q0, q1, int(rng.choice([0, 64]))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(N_LAYERS), ids=[c[0]["name"] for c in CASES])
+def test_random_layer_window_matches_oracle(k):
+    """A row window of the same random layer (a plan created for those rows only): its rows
+    against the oracle's rows of the whole request."""
+    cfg, pool, _ = CASES[k]
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    T, H = inp["T"], cfg["n_heads"]
+    q0, q1, split = random_window(k, T)
+    say("case %s window [%d, %d) of %d split=%d" % (cfg["name"], q0, q1, T, split))
+    plan = Plan.for_inputs(inp, split, q_range=(q0, q1))
+    plan.build(inp["scores"])
+    dt = inp["q"].dtype
+    out = torch.full((q1 - q0, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+    z = torch.full((q1 - q0, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+    lse = torch.full((q1 - q0, H), float("nan"), dtype=torch.float32, device="cuda")
+    plan.forward(inp, out, z, lse)
+    torch.cuda.synchronize()
+    ref = O.layer_forward(oracle_inputs(inp), rows=np.arange(q0, q1))
+    np.testing.assert_array_equal(plan.protected(), ref["A"])
+    plan.close()
+    e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+
+
 def test_random_layers_cover_the_combinations():
     """(CPU) The seeds reach every dtype, every pool placement, split and unsplit runs, window heads,
     layers without Global heads and layers with one-row segments."""
@@ -94,3 +133,8 @@ def test_random_layers_cover_the_combinations():
     assert any(c.get("window_heads") for c, _, _ in CASES)
     assert any(not c["global_heads"] for c, _, _ in CASES)
     assert any(n == 1 for c, _, _ in CASES for _, n in c["segments"])
+    wins = [random_window(k, sum(n for _, n in CASES[k][0]["segments"])) for k in range(N_LAYERS)]
+    # one-row windows with a key split on bf16 layers (the decode kernel), and longer windows
+    assert any(q1 - q0 == 1 and q1 > s > 0 and CASES[k][0]["kv_dtype"] == "bf16"
+               for k, (q0, q1, s) in enumerate(wins))
+    assert any(q1 - q0 > 1 for q0, q1, _ in wins)
