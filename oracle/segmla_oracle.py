@@ -364,8 +364,10 @@ def layer_forward_grouped(inp, rows=None):
     Heads gG .. gG+G-1 form group g (G = cfg["group_heads"]). For request row t:
     z[t][g] = sum over the group's Global and sink + window heads of W_h u_h(t)
               + (t in A ? sum over its Local heads of W_h u_h(t) : z_cached[pool_row(t)][g]),
-    with z_cached [n_pool, n_groups, d_state] the cached Local contribution per group. O, lse
-    and A are those of layer_forward. Returns its dict with Z [n, n_groups, d_state].
+    with z_cached [n_pool, n_groups, d_state] the cached Local contribution per group. A layer
+    without Local heads has no Local contribution (z_L = 0 in Eq. 3), so nothing cached is added
+    and z_cached is not read. O, lse and A are those of layer_forward. Returns its dict with
+    Z [n, n_groups, d_state].
     """
     cfg = inp["cfg"]
     G = int(cfg["group_heads"])
@@ -378,10 +380,11 @@ def layer_forward_grouped(inp, rows=None):
     in_A[A] = True
     Zh = res["Z"]                                             # [n, H, d_state]
     Zg = Zh.reshape(len(res["rows"]), H // G, G, -1).sum(axis=2)
-    Zc = inp["z_cached"]
-    for i, t in enumerate(res["rows"]):
-        if not in_A[t]:
-            Zg[i] += np.asarray(Zc[geom["pool_of_row"][t]], dtype=np.float64)
+    if (role == 0).any():
+        Zc = inp["z_cached"]
+        for i, t in enumerate(res["rows"]):
+            if not in_A[t]:
+                Zg[i] += np.asarray(Zc[geom["pool_of_row"][t]], dtype=np.float64)
     res["Z"] = Zg
     return res
 

@@ -24,14 +24,15 @@ def _check(cfg, ref, out, z, lse, rows):
     o = out[idx].double().cpu().numpy()
     comp = ref["computed"]
     assert np.all(np.isfinite(o[comp])) and np.all(np.isnan(o[~comp]))
-    e_o = O.rel_err_rows(o[comp], ref["O"][comp])
+    # (a window of Local-only rows outside A computes no head: z is the cache alone)
+    e_o = O.rel_err_rows(o[comp], ref["O"][comp]) if comp.any() else np.zeros(1)
     assert e_o.max() <= tol, "O max rel err %.3g" % e_o.max()
     zz = z[idx].double().cpu().numpy()
     assert np.all(np.isfinite(zz))
     e_z = O.rel_err_rows(zz.reshape(-1, zz.shape[-1]), ref["Z"].reshape(-1, zz.shape[-1]))
     assert e_z.max() <= tol, "grouped Z max rel err %.3g" % e_z.max()
     ls = lse[idx].double().cpu().numpy()
-    e_l = float(np.abs(ls[comp] - ref["lse"][comp]).max())
+    e_l = float(np.abs(ls[comp] - ref["lse"][comp]).max()) if comp.any() else 0.0
     assert e_l <= lse_tol_of(cfg), "lse max abs err %.3g > %.1g" % (e_l, lse_tol_of(cfg))
     return float(e_o.max()), float(e_z.max()), e_l
 

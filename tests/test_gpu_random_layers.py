@@ -123,6 +123,48 @@ def test_random_layer_window_matches_oracle(k):
     say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
 
 
+def grouped_paged_variant(k):
+    """The k-th layer with a grouped projected state (a group size drawn from the divisors 2..8
+    of H; None when H has none) over a paged latent pool, and a row window (the whole request
+    or a seeded range); (cfg, pool, q0, q1, split_keys) or None."""
+    cfg = CASES[k][0]
+    H = cfg["n_heads"]
+    sizes = [g for g in range(2, min(H, 8) + 1) if H % g == 0]
+    if not sizes:
+        return None
+    rng = np.random.default_rng([k, 0x6A9])
+    cfg = dict(cfg, name=cfg["name"] + "_grouped_paged", group_heads=int(rng.choice(sizes)))
+    pool = "paged:%d" % int(rng.choice([1, 16, 48, 64]))
+    T = sum(n for _, n in cfg["segments"])
+    q0, q1 = 0, T
+    if rng.random() < 0.5:
+        q0 = int(rng.integers(0, T))
+        q1 = int(rng.integers(q0 + 1, T + 1))
+    return cfg, pool, q0, q1, int(rng.choice([0, 64]))
+
+
+GP = [v for v in (grouped_paged_variant(k) for k in range(N_LAYERS)) if v is not None]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(len(GP)), ids=[v[0]["name"] for v in GP])
+def test_random_layer_grouped_paged_matches_oracle(i):
+    """Grouped projected state over a paged latent pool, on a row window of a random layer:
+    z per group against the oracle's grouped state, out and lse per head."""
+    from tests.test_gpu_grouped import _check, _run
+
+    cfg, pool, q0, q1, split = GP[i]
+    say("case %s G=%d pool=%s window [%d, %d) split=%d" % (cfg["name"], cfg["group_heads"], pool,
+                                                          q0, q1, split))
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    plan, out, z, lse = _run(inp, split, q_range=(q0, q1))
+    ref = O.layer_forward_grouped(oracle_inputs(inp), rows=np.arange(q0, q1))
+    np.testing.assert_array_equal(plan.protected(), ref["A"])
+    plan.close()
+    say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % _check(cfg, ref, out, z, lse,
+                                                                      np.arange(q1 - q0)))
+
+
 def test_random_layers_cover_the_combinations():
     """(CPU) The seeds reach every dtype, every pool placement, split and unsplit runs, window heads,
     layers without Global heads and layers with one-row segments."""
@@ -138,3 +180,4 @@ def test_random_layers_cover_the_combinations():
     assert any(q1 - q0 == 1 and q1 > s > 0 and CASES[k][0]["kv_dtype"] == "bf16"
                for k, (q0, q1, s) in enumerate(wins))
     assert any(q1 - q0 > 1 for q0, q1, _ in wins)
+    assert len(GP) >= 10 and {v[2] == 0 and v[3] == sum(n for _, n in v[0]["segments"]) for v in GP} == {True, False}

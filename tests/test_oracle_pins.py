@@ -570,6 +570,23 @@ def test_grouped_state_is_the_group_sum_of_per_head_state():
                                rtol=0, atol=0)
 
 
+def test_grouped_state_without_local_heads_reads_no_cache():
+    """A grouped layer whose heads are all Global has no Local contribution (Eq. 3 with
+    z_L = 0): its grouped z is the group sum of the per-head z on every row, whatever the
+    cached state holds (here NaN: it is not read)."""
+    from workload.configs import GROUPED_CONFIGS
+    cfg = dict(GROUPED_CONFIGS[0], name="tiny_fp32_grouped_all_global",
+               global_heads=list(range(GROUPED_CONFIGS[0]["n_heads"])))
+    inp = _oracle_inputs(make_inputs(cfg, "cpu"))
+    G, H = cfg["group_heads"], cfg["n_heads"]
+    per_head = O.layer_forward(dict(inp, z_cached=np.zeros((inp["n_pool"], 0, cfg["d_state"]))))
+    nan_cache = np.full((inp["n_pool"], H // G, cfg["d_state"]), np.nan)
+    grouped = O.layer_forward_grouped(dict(inp, z_cached=nan_cache))
+    assert len(grouped["A"]) < inp["T"]  # rows outside A exist
+    ref = per_head["Z"].reshape(len(per_head["rows"]), H // G, G, -1).sum(axis=2)
+    np.testing.assert_allclose(grouped["Z"], ref, rtol=0, atol=1e-12)
+
+
 def test_grouped_exact_cache_identity():
     """When the cached Local contribution of every group equals the full recomputation's (the
     cache was produced in the same context), the grouped state equals full recomputation on
