@@ -20,6 +20,7 @@ import pytest
 import torch
 
 from oracle import segmla_oracle as O
+from segmented_attention_amd import segmla as S
 from segmented_attention_amd.segmla import Plan
 from tests.gpu_common import compare, oracle_inputs, run_gpu, say
 from workload import make_inputs
@@ -163,6 +164,51 @@ def test_random_layer_grouped_paged_matches_oracle(i):
     plan.close()
     say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % _check(cfg, ref, out, z, lse,
                                                                       np.arange(q1 - q0)))
+
+
+def moved_windows(k, T):
+    """Four windows, in seeded order, that one plan of the k-th layer is moved through: single
+    rows and ranges anywhere in the request; and the key split of that plan."""
+    rng = np.random.default_rng([k, 0x4E1])
+    wins = []
+    for _ in range(4):
+        q0 = int(rng.integers(0, T))
+        q1 = q0 + 1 if rng.random() < 0.5 else int(rng.integers(q0 + 1, T + 1))
+        wins.append((q0, q1))
+    return wins, int(rng.choice([0, 64]))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(N_LAYERS), ids=[c[0]["name"] for c in CASES])
+def test_random_layer_plan_moved_over_windows(k):
+    """One plan of a random layer, built once, moved by set_window through four seeded windows
+    (rows before and after the previous window, single rows and ranges); each window's rows
+    against the oracle, and A stays the request's."""
+    cfg, pool, _ = CASES[k]
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    T, H = inp["T"], cfg["n_heads"]
+    wins, split = moved_windows(k, T)
+    whole = Plan.for_inputs(inp, split)
+    cap = S.segmla_plan_workspace_bytes(whole.handle)
+    whole.close()
+    plan = Plan.for_inputs(inp, split, q_range=wins[0])
+    plan.build(inp["scores"], min_bytes=cap)
+    oi = oracle_inputs(inp)
+    dt = inp["q"].dtype
+    for i, (q0, q1) in enumerate(wins):
+        say("case %s window %d [%d, %d) of %d split=%d" % (cfg["name"], i, q0, q1, T, split))
+        if i > 0:
+            plan.set_window(q0, q1)
+        out = torch.full((q1 - q0, H, inp["d_v"]), float("nan"), dtype=dt, device="cuda")
+        z = torch.full((q1 - q0, H, cfg["d_state"]), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((q1 - q0, H), float("nan"), dtype=torch.float32, device="cuda")
+        plan.forward(inp, out, z, lse)
+        torch.cuda.synchronize()
+        ref = O.layer_forward(oi, rows=np.arange(q0, q1))
+        np.testing.assert_array_equal(plan.protected(), ref["A"])
+        e = compare(cfg, ref, out, z, lse, None, rows=np.arange(q1 - q0))
+        say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
+    plan.close()
 
 
 def test_random_layers_cover_the_combinations():
