@@ -211,6 +211,54 @@ def test_random_layer_plan_moved_over_windows(k):
     plan.close()
 
 
+def dual_variant(k):
+    """The k-th layer as a compressed-history (CSA / HCA) layer, for bf16 and E4M3 layers (an
+    E4M3 layer keeps its shapes with a bf16 latent; the dual-pool path takes bf16 only): entry
+    ratio, raw window, list width (0: HCA, every available entry), compressed-pool placement,
+    list rewrite and row window drawn from the seed; (cfg, pool, ratio, window, top_k, cpool,
+    variant, q0, q1) or None."""
+    cfg, pool, _ = CASES[k]
+    if cfg["dtype"] != "bf16":
+        return None
+    rng = np.random.default_rng([k, 0xD0A])
+    cfg = dict(cfg, name=cfg["name"] + "_dual", kv_dtype="bf16")
+    ratio = int(rng.choice([1, 2, 3, 4, 16]))
+    window = int(rng.choice([0, 5, 40, 127]))
+    top_k = int(rng.choice([0, 0, 7, 40, 100]))
+    cpool = str(rng.choice(["identity", "shuffled"]))
+    variant = str(rng.choice(["none", "shuffle", "dups+cut"])) if top_k else "none"
+    T = sum(n for _, n in cfg["segments"])
+    q0, q1 = 0, T
+    if rng.random() < 0.5:
+        q0 = int(rng.integers(0, T))
+        q1 = q0 + 1 if rng.random() < 0.5 else int(rng.integers(q0 + 1, T + 1))
+    return cfg, pool, ratio, window, top_k, cpool, variant, q0, q1
+
+
+DUAL = [v for v in (dual_variant(k) for k in range(N_LAYERS)) if v is not None]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(len(DUAL)), ids=[v[0]["name"] for v in DUAL])
+def test_random_layer_dual_pool_matches_oracle(i):
+    """The compressed-history attention of a random layer's rows (raw window and compressed
+    entries in one softmax) against the oracle, every (row, head) of the window."""
+    from tests.test_gpu_dual import _check, _lists_variant, _oracle, _run
+    from workload import make_dual_inputs
+
+    cfg, pool, ratio, window, top_k, cpool, variant, q0, q1 = DUAL[i]
+    say("case %s pool=%s ratio=%d window=%d top_k=%d cpool=%s lists=%s rows [%d, %d)" % (
+        cfg["name"], pool, ratio, window, top_k, cpool, variant, q0, q1))
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    dual = make_dual_inputs(inp, ratio, window, top_k, "cuda", pool=cpool)
+    n_entries = int((np.asarray(inp["lens"]) // ratio).sum())
+    dual = _lists_variant(dual, None if variant == "none" else variant, n_entries, cfg["seed"])
+    out, lse, n_dev = _run(inp, dual, q_range=(q0, q1))
+    assert n_dev == n_entries
+    rows = np.arange(q0, q1)
+    _check(cfg, _oracle(inp, dual, rows), out, lse, np.arange(q1 - q0))
+
+
 def test_random_layers_cover_the_combinations():
     """(CPU) The seeds reach every dtype, every pool placement, split and unsplit runs, window heads,
     layers without Global heads and layers with one-row segments."""
@@ -226,4 +274,5 @@ def test_random_layers_cover_the_combinations():
     assert any(q1 - q0 == 1 and q1 > s > 0 and CASES[k][0]["kv_dtype"] == "bf16"
                for k, (q0, q1, s) in enumerate(wins))
     assert any(q1 - q0 > 1 for q0, q1, _ in wins)
+    assert len(DUAL) >= 10 and {v[4] > 0 for v in DUAL} == {True, False}
     assert len(GP) >= 10 and {v[2] == 0 and v[3] == sum(n for _, n in v[0]["segments"]) for v in GP} == {True, False}
