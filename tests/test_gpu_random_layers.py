@@ -7,8 +7,8 @@ Each layer draws, from its own seed:
 * the head roles: Global, Local and, in some layers, sink + window heads;
 * one to seven segments of any kind and order (prefix, document, new), many of them a few
   rows long, so that key tiles, segment runs and protected-row edges fall anywhere;
-* the protected-row rule (edge rows, tail rows, Indexer budget) and values with or without the
-  RoPE dims;
+* the protected-row rule (edge rows, tail rows, Indexer budget, in half of the layers a few
+  caller-listed dirty rows, unsorted and repeated) and values with or without the RoPE dims;
 * the latent pool placement (identity, shuffled with gaps, or aliased documents) and the key
   split (none, 64 or 128 keys).
 
@@ -62,6 +62,12 @@ def random_layer(k):
     cfg["global_heads"] = glob
     pool = str(rng.choice(["identity", "shuffled", "aliased"]))
     split = int(rng.choice([0, 0, 64, 128]))
+    # caller-listed dirty rows (forced into A), unsorted and possibly repeated, in half of the
+    # layers; drawn from a stream of their own
+    drng = np.random.default_rng([k, 0xD17])
+    if drng.random() < 0.5:
+        T = sum(n for _, n in segs)
+        cfg["dirty_rows"] = [int(x) for x in drng.integers(0, T, int(drng.integers(1, 8)))]
     return cfg, pool, split
 
 
@@ -269,6 +275,8 @@ def test_random_layers_cover_the_combinations():
     assert any(c.get("window_heads") for c, _, _ in CASES)
     assert any(not c["global_heads"] for c, _, _ in CASES)
     assert any(n == 1 for c, _, _ in CASES for _, n in c["segments"])
+    dirty = [c["dirty_rows"] for c, _, _ in CASES if c.get("dirty_rows")]
+    assert len(dirty) >= 4 and any(len(set(d)) < len(d) or d != sorted(d) for d in dirty)
     wins = [random_window(k, sum(n for _, n in CASES[k][0]["segments"])) for k in range(N_LAYERS)]
     # one-row windows with a key split on bf16 layers (the decode kernel), and longer windows
     assert any(q1 - q0 == 1 and q1 > s > 0 and CASES[k][0]["kv_dtype"] == "bf16"
