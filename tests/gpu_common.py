@@ -25,7 +25,10 @@ def tol_of(cfg):
 
 
 def lse_tol_of(cfg):
-    return LSE_TOL["e4m3"] if cfg["kv_dtype"] == "e4m3" else LSE_TOL[cfg["dtype"]]
+    """LSE_TOL at softmax scale sigma = 1. lse = log sum_k exp(sigma s_k), so a rounding error
+    in the score s_k enters multiplied by sigma: the bound scales with max(1, sigma)."""
+    base = LSE_TOL["e4m3"] if cfg["kv_dtype"] == "e4m3" else LSE_TOL[cfg["dtype"]]
+    return base * max(1.0, float(cfg.get("softmax_scale", 1.0)))
 
 
 def say(msg):

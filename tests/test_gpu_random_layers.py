@@ -9,6 +9,7 @@ Each layer draws, from its own seed:
   rows long, so that key tiles, segment runs and protected-row edges fall anywhere;
 * the protected-row rule (edge rows, tail rows, Indexer budget, in half of the layers a few
   caller-listed dirty rows, unsorted and repeated) and values with or without the RoPE dims;
+* the softmax scale (1, 0.6 or 1.7) and the RoPE base (10000, 500 or 10^6);
 * the latent pool placement (identity, shuffled with gaps, or aliased documents) and the key
   split (none, 64 or 128 keys).
 
@@ -68,6 +69,10 @@ def random_layer(k):
     if drng.random() < 0.5:
         T = sum(n for _, n in segs)
         cfg["dirty_rows"] = [int(x) for x in drng.integers(0, T, int(drng.integers(1, 8)))]
+    # softmax scale and RoPE base (the named layers use 1 and 10000), from a stream of their own
+    srng = np.random.default_rng([k, 0x5CA])
+    cfg["softmax_scale"] = float(srng.choice([1.0, 1.0, 0.6, 1.7]))
+    cfg["rope_base"] = float(srng.choice([10000.0, 10000.0, 500.0, 1e6]))
     return cfg, pool, split
 
 
@@ -275,6 +280,8 @@ def test_random_layers_cover_the_combinations():
     assert any(c.get("window_heads") for c, _, _ in CASES)
     assert any(not c["global_heads"] for c, _, _ in CASES)
     assert any(n == 1 for c, _, _ in CASES for _, n in c["segments"])
+    assert {c["softmax_scale"] != 1.0 for c, _, _ in CASES} == {True, False}
+    assert {c["rope_base"] != 10000.0 for c, _, _ in CASES} == {True, False}
     dirty = [c["dirty_rows"] for c, _, _ in CASES if c.get("dirty_rows")]
     assert len(dirty) >= 4 and any(len(set(d)) < len(d) or d != sorted(d) for d in dirty)
     wins = [random_window(k, sum(n for _, n in CASES[k][0]["segments"])) for k in range(N_LAYERS)]
