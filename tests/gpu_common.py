@@ -13,10 +13,11 @@ TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3": 6e-2}
 # The fp32 path carries no rounding beyond fp32; the bf16 path rounds the segment-rotated RoPE
 # query to bf16 (about 2^-9 |s_rope| per score) and the E4M3 path also rounds code x scale to
 # bf16 (about 2^-9 |s| per score): on the synthetic workloads |s| is a few units. Measured over
-# every parity case: at most 8.7e-7 (fp32), 8.8e-4 (bf16) and 5.0e-3 (E4M3), except a seeded
-# random bf16 layer whose sink + window heads see one or two keys (1.8e-3: there the lse is
-# about one score, and that score's rounding is not averaged over many keys). Tests that drive
-# the scores far larger pass their own bound.
+# the named parity cases (softmax scale 1): at most 8.7e-7 (fp32), 8.8e-4 (bf16) and 5.0e-3
+# (E4M3). Seeded random layers reach 1.5e-3 per unit of scale on bf16 where sink + window heads
+# see one or two keys (the lse is then about one score, whose rounding is not averaged over many
+# keys). The bounds hold at scale 1 and grow with it (lse_tol_of). Tests that drive the scores
+# far larger pass their own bound.
 LSE_TOL = {"f32": 1e-5, "bf16": 2e-3, "e4m3": 1e-2}
 
 
