@@ -3,7 +3,7 @@ named configurations do not spell out one by one.
 
 Each layer draws, from its own seed:
 * the latent and io dtypes (fp32, bf16, or an E4M3 latent with bf16 io);
-* the head count, and for fp32 the nope / RoPE / state widths;
+* the head count and the state width (64 to 512), and for fp32 the nope and RoPE widths;
 * the head roles: Global, Local and, in some layers, sink + window heads;
 * one to seven segments of any kind and order (prefix, document, new), many of them a few
   rows long, so that key tiles, segment runs and protected-row edges fall anywhere;
@@ -47,6 +47,9 @@ def random_layer(k):
         H = int(rng.choice([8, 40, 64, 128]))
         d_nope, d_rope = 512, 64
         d_state = int(rng.choice([192, 512]))
+        wrng = np.random.default_rng([k, 0xD57])
+        if wrng.random() < 0.4:  # state widths the named layers do not use
+            d_state = int(wrng.choice([64, 128, 256]))
     cfg = _cfg("random_%02d_%s" % (k, kind), None, "f32" if kind == "f32" else "bf16", H, d_nope,
                d_rope, d_state, segs, edge_rows=int(rng.choice([0, 4, 16])),
                tail_rows=int(rng.choice([0, 8, 64])),
@@ -280,6 +283,7 @@ def test_random_layers_cover_the_combinations():
     assert any(c.get("window_heads") for c, _, _ in CASES)
     assert any(not c["global_heads"] for c, _, _ in CASES)
     assert any(n == 1 for c, _, _ in CASES for _, n in c["segments"])
+    assert {c["d_state"] for c, _, _ in CASES if c["dtype"] == "bf16"} >= {64, 192, 512}
     assert {c["softmax_scale"] != 1.0 for c, _, _ in CASES} == {True, False}
     assert {c["rope_base"] != 10000.0 for c, _, _ in CASES} == {True, False}
     dirty = [c["dirty_rows"] for c, _, _ in CASES if c.get("dirty_rows")]
