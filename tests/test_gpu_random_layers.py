@@ -27,13 +27,15 @@ from tests.gpu_common import compare, oracle_inputs, run_gpu, say
 from workload import make_inputs
 from workload.configs import _cfg, _windowed
 
-N_LAYERS = 16
+N_LAYERS = 18  # layers 16 and 17 are bf16 and E4M3 layers with 192 and 256 heads
 
 
 def random_layer(k):
     """The k-th random layer: (cfg, pool placement, split_keys)."""
     rng = np.random.default_rng([k, 0x5E6])
     kind = str(rng.choice(["f32", "bf16", "e4m3"], p=[0.3, 0.45, 0.25]))
+    if k >= 16:
+        kind = ("bf16", "e4m3")[k % 2]
     segs = []
     for _ in range(int(rng.integers(1, 8))):
         sk = str(rng.choice(["prefix", "doc", "new"], p=[0.15, 0.7, 0.15]))
@@ -44,7 +46,7 @@ def random_layer(k):
         d_nope, d_rope = int(rng.choice([16, 64, 96])), int(rng.choice([4, 16, 32]))
         d_state = int(rng.choice([16, 64, 96]))
     else:
-        H = int(rng.choice([8, 40, 64, 128]))
+        H = int(rng.choice([8, 40, 64, 128])) if k < 16 else (192, 256)[k % 2]
         d_nope, d_rope = 512, 64
         d_state = int(rng.choice([192, 512]))
         wrng = np.random.default_rng([k, 0xD57])
