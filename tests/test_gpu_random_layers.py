@@ -227,6 +227,36 @@ def test_random_layer_plan_moved_over_windows(k):
     plan.close()
 
 
+E4 = [v for v in GP if v[0]["dtype"] == "bf16" and v[0]["d_state"] % 128 == 0]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(len(E4)), ids=[v[0]["name"] + "_e4m3_state" for v in E4])
+def test_random_layer_e4m3_state(i):
+    """The grouped state of the same variants emitted as 1x128 E4M3 blocks: the oracle's
+    quantizer applied to the library's own bf16 state gives the library's codes and scales bit
+    for bit, and the decoded state matches the fp64 grouped oracle within 6e-2."""
+    from tests.test_gpu_e4m3_state import E4M3_TOL, _run as run_state
+
+    cfg, pool, q0, q1, split = E4[i]
+    say("case %s e4m3 state G=%d pool=%s window [%d, %d) split=%d" % (
+        cfg["name"], cfg["group_heads"], pool, q0, q1, split))
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    out_b, z_b, _ = run_state(inp, cfg, (q0, q1), split)
+    out_e, codes, scales = run_state(inp, dict(cfg, z_e4m3=1), (q0, q1), split)
+    assert torch.equal(out_b.view(torch.int16), out_e.view(torch.int16))
+    want_c, want_s = O.quantize_e4m3_b128_fp32(z_b.float().cpu().numpy())
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    np.testing.assert_array_equal(got_s.view(np.uint32), want_s.view(np.uint32))
+    np.testing.assert_array_equal(got_c, want_c)
+    deq = (O.e4m3_decode(got_c).reshape(*got_c.shape[:-1], -1, 128)
+           * got_s[..., None].astype(np.float64)).reshape(got_c.shape)
+    ref = O.layer_forward_grouped(oracle_inputs(inp), rows=np.arange(q0, q1))
+    e = O.rel_err_rows(deq.reshape(-1, deq.shape[-1]), ref["Z"].reshape(-1, deq.shape[-1]))
+    say("  decoded state max rel err %.3g" % e.max())
+    assert e.max() <= E4M3_TOL
+
+
 def dual_variant(k):
     """The k-th layer as a compressed-history (CSA / HCA) layer, for bf16 and E4M3 layers (an
     E4M3 layer keeps its shapes with a bf16 latent; the dual-pool path takes bf16 only): entry
@@ -296,4 +326,5 @@ def test_random_layers_cover_the_combinations():
                for k, (q0, q1, s) in enumerate(wins))
     assert any(q1 - q0 > 1 for q0, q1, _ in wins)
     assert len(DUAL) >= 10 and {v[4] > 0 for v in DUAL} == {True, False}
+    assert len(E4) >= 4
     assert len(GP) >= 10 and {v[2] == 0 and v[3] == sum(n for _, n in v[0]["segments"]) for v in GP} == {True, False}
