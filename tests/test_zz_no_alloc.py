@@ -78,3 +78,30 @@ def test_noalloc_matches_plan_build_and_forward():
     assert _same(o5, o) and _same(z5, z) and _same(l5, l)
     for r in runs:
         r[3].close()
+
+
+def test_noalloc_on_random_layers():
+    """The seeded random layers (every dtype, head roles, pool placements, key splits, dirty
+    rows), each through segmla_forward_noalloc and through plan_build + forward: bit for bit."""
+    from tests.test_gpu_random_layers import CASES
+
+    done = 0
+    for cfg, pool, split in CASES:
+        inp = make_inputs(cfg, "cuda", pool=pool)
+        plan = S.Plan.for_inputs(inp, split_keys=split)
+        ws = S.segmla_plan_workspace_bytes(plan.handle)
+        if ws > S.NOALLOC_MAX_BYTES:
+            plan.close()
+            continue
+        say("case noalloc %s pool=%s split=%d workspace=%d" % (cfg["name"], pool, split, ws))
+        o, z, l = _outputs(inp, None)
+        S.segmla_forward_noalloc(plan.handle, inp["scores"], inp["q"], inp["kv"], inp["w"], o, z,
+                                 inp.get("z_cached"), inp.get("kv_scale"), inp.get("kv_rope"), l)
+        plan.build(inp["scores"])
+        o1, z1, l1 = _outputs(inp, None)
+        plan.forward(inp, o1, z1, l1)
+        torch.cuda.synchronize()
+        assert _same(o, o1) and _same(z, z1) and _same(l, l1), cfg["name"]
+        plan.close()
+        done += 1
+    assert done >= 12, done
