@@ -305,6 +305,41 @@ def test_random_layer_dual_pool_matches_oracle(i):
     _check(cfg, _oracle(inp, dual, rows), out, lse, np.arange(q1 - q0))
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(N_LAYERS), ids=[c[0]["name"] for c in CASES])
+def test_random_layer_window_graph_replays(k):
+    """The forward of each random layer's seeded window captured in a HIP graph and replayed
+    twice, with eager forwards of the same plan in between: every replay equals the eager
+    forward bit for bit."""
+    from tests.test_gpu_graph import _bits, _bufs
+
+    cfg, pool, _ = CASES[k]
+    inp = make_inputs(cfg, "cuda", pool=pool)
+    q0, q1, split = random_window(k, inp["T"])
+    say("case %s graph of window [%d, %d) split=%d" % (cfg["name"], q0, q1, split))
+    plan = Plan.for_inputs(inp, split, q_range=(q0, q1))
+    plan.build(inp["scores"])
+    ref = _bufs(inp, q1 - q0)
+    plan.forward(inp, *ref)
+    torch.cuda.synchronize()
+    got, other = _bufs(inp, q1 - q0), _bufs(inp, q1 - q0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.forward(inp, *got)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for t in got + other:
+            t.fill_(float("nan"))
+        plan.forward(inp, *other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got + other, ref + ref):
+            assert torch.equal(_bits(a), _bits(b)), "replay %d differs" % rep
+    del g
+    plan.close()
+
+
 def test_random_layers_cover_the_combinations():
     """(CPU) The seeds reach every dtype, every pool placement, split and unsplit runs, window heads,
     layers without Global heads and layers with one-row segments."""
