@@ -34,7 +34,7 @@ def random_layer(k):
     """The k-th random layer: (cfg, pool placement, split_keys)."""
     rng = np.random.default_rng([k, 0x5E6])
     kind = str(rng.choice(["f32", "bf16", "e4m3"], p=[0.3, 0.45, 0.25]))
-    if k >= 16:
+    if k in (16, 17):
         kind = ("bf16", "e4m3")[k % 2]
     segs = []
     for _ in range(int(rng.integers(1, 8))):
@@ -46,7 +46,7 @@ def random_layer(k):
         d_nope, d_rope = int(rng.choice([16, 64, 96])), int(rng.choice([4, 16, 32]))
         d_state = int(rng.choice([16, 64, 96]))
     else:
-        H = int(rng.choice([8, 40, 64, 128])) if k < 16 else (192, 256)[k % 2]
+        H = int(rng.choice([8, 40, 64, 128])) if k not in (16, 17) else (192, 256)[k % 2]
         d_nope, d_rope = 512, 64
         d_state = int(rng.choice([192, 512]))
         wrng = np.random.default_rng([k, 0xD57])
