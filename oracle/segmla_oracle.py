@@ -183,7 +183,7 @@ def rot_blocks(pos, theta):
 
 def apply_blocks(R, x_rope):
     """Apply per-pair 2x2 blocks R [..., d_rope/2, 2, 2] to x_rope [..., d_rope]."""
-    xp = x_rope.reshape(x_rope.shape[:-1] + (-1, 2))
+    xp = x_rope.reshape(x_rope.shape[:-1] + (x_rope.shape[-1] // 2, 2))  # also for zero rows
     y = np.einsum("...kab,...kb->...ka", R, xp)
     return y.reshape(x_rope.shape)
 

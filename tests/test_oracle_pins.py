@@ -570,6 +570,15 @@ def test_grouped_state_is_the_group_sum_of_per_head_state():
                                rtol=0, atol=0)
 
 
+def test_rope_blocks_on_zero_rows():
+    """The RoPE helper on an empty set of rows (a request whose segments hold no compressed
+    entry) returns an empty result instead of failing."""
+    theta = O.rope_theta(64, 10000.0)
+    R = O.rot_blocks(np.zeros(0), theta)
+    y = O.apply_blocks(R, np.zeros((0, 64)))
+    assert y.shape == (0, 64)
+
+
 def test_grouped_state_without_local_heads_reads_no_cache():
     """A grouped layer whose heads are all Global has no Local contribution (Eq. 3 with
     z_L = 0): its grouped z is the group sum of the per-head z on every row, whatever the
