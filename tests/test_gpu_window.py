@@ -166,3 +166,23 @@ def test_misaligned_tensor_is_rejected():
     plan.close()
     torch.cuda.synchronize()
     assert torch.count_nonzero(big).item() == 0 and torch.count_nonzero(z).item() == 0
+
+
+@pytest.mark.parametrize("ci,n_rows", [(1, 12), (2, 8), (3, 6), (4, 6)],
+                         ids=["32k_12_rows", "128k_8_rows", "many_short_6_rows", "64k_e4m3_6_rows"])
+def test_decode_rows_at_seeded_positions(ci, n_rows):
+    """One-row windows at seeded positions anywhere in the full-size layers (documents,
+    their edges, rows in and outside A, the 256-segment layer, the E4M3 latent), each with the
+    library's own key split, against the oracle."""
+    cfg = CONFIGS[ci]
+    inp = make_inputs(cfg, "cuda")
+    T = inp["T"]
+    oi = oracle_inputs(inp, lazy=True)
+    for r in np.random.default_rng([ci, 0xDEC]).integers(1, T, n_rows):
+        q0, q1 = int(r), int(r) + 1
+        say("case decode %s row %d" % (cfg["name"], q0))
+        plan, out, z, lse = _run_window(inp, q0, q1)
+        plan.close()
+        ref = O.layer_forward(oi, rows=np.arange(q0, q1))
+        e = compare(cfg, ref, out, z, lse, None, rows=np.arange(1))
+        say("  max rel err O %.2e Z %.2e, lse max abs err %.2e" % e)
